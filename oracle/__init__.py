@@ -1,0 +1,190 @@
+"""CPU oracle for MoE expert-parallel layout / scan / scatter / combine.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, the package smoke check in
+``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
+import this package. The product path (``permute_ep_layout_amd``) never
+imports it, and the two share no code: the arithmetic lives in
+``epl_oracle.c`` (plain single-threaded C), and this module only moves numpy
+arrays in and out of it.
+
+Each function cites, in ``epl_oracle.c``, the passage of the pages it
+follows. Where no pin exists for a choice the function says so.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+from . import build as _build
+
+_c_i64 = ctypes.c_int64
+_c_i32 = ctypes.c_int32
+_ptr = ctypes.c_void_p
+
+OK = 0
+EINVAL = -1
+ERANGE = -2
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what} failed with oracle code {code}")
+        self.code = code
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(rc: int, what: str):
+    if rc != OK:
+        raise OracleError(rc, what)
+
+
+class Oracle:
+    """numpy front end of one build of ``epl_oracle.c`` (``path``)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        lib.epl_oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        lib.epl_oracle_bf16_to_double.restype = ctypes.c_double
+        lib.epl_oracle_bf16_from_double.argtypes = [ctypes.c_double]
+        lib.epl_oracle_bf16_from_double.restype = ctypes.c_uint16
+        lib.epl_oracle_layout.argtypes = [_c_i64, _c_i32, _c_i32, _c_i32, _ptr, _ptr, _ptr, _ptr]
+        lib.epl_oracle_layout.restype = ctypes.c_int
+        lib.epl_oracle_scan.argtypes = [_c_i32, _ptr, _ptr, _ptr]
+        lib.epl_oracle_scan.restype = ctypes.c_int
+        lib.epl_oracle_scatter.argtypes = [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
+                                           _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr]
+        lib.epl_oracle_scatter.restype = ctypes.c_int
+        lib.epl_oracle_expert_scale.argtypes = [_c_i64, _c_i32, _ptr, _ptr, _ptr]
+        lib.epl_oracle_expert_scale.restype = ctypes.c_int
+        lib.epl_oracle_combine.argtypes = [_c_i64, _c_i32, _c_i32, _ptr, _c_i64, _ptr, _ptr,
+                                           _ptr, _c_i64, _ptr]
+        lib.epl_oracle_combine.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    def bf16_to_double(self, bits: int) -> float:
+        return float(self.lib.epl_oracle_bf16_to_double(int(bits)))
+
+    def bf16_from_double(self, v: float) -> int:
+        return int(self.lib.epl_oracle_bf16_from_double(float(v)))
+
+    def bf16_from_double_array(self, v: np.ndarray) -> np.ndarray:
+        f = self.lib.epl_oracle_bf16_from_double
+        flat = np.asarray(v, dtype=np.float64).ravel()
+        return np.array([f(float(a)) for a in flat], dtype=np.uint16).reshape(np.shape(v))
+
+    def layout(self, topk_idx: np.ndarray, num_experts: int, num_ranks: int):
+        """Returns (num_tokens_per_expert [E] i32, num_tokens_per_rank [R] i32,
+        is_token_in_rank [T, R] u8)."""
+        topk = _c(topk_idx, np.int64)
+        T, K = topk.shape
+        cnt = np.empty(num_experts, np.int32)
+        per_rank = np.empty(num_ranks, np.int32)
+        in_rank = np.empty((T, num_ranks), np.uint8)
+        _check(self.lib.epl_oracle_layout(T, K, num_experts, num_ranks, _p(topk), _p(cnt),
+                                          _p(per_rank), _p(in_rank)), "layout")
+        return cnt, per_rank, in_rank
+
+    def scan(self, num_tokens_per_expert: np.ndarray):
+        """Returns (expert_start_loc [E] i32, total int)."""
+        cnt = _c(num_tokens_per_expert, np.int32)
+        start = np.empty(cnt.size, np.int32)
+        total = np.zeros(1, np.int64)
+        _check(self.lib.epl_oracle_scan(cnt.size, _p(cnt), _p(start), _p(total)), "scan")
+        return start, int(total[0])
+
+    def scatter(self, x: Optional[np.ndarray], x_scale: Optional[np.ndarray],
+                topk_idx: np.ndarray, expert_start_loc: np.ndarray, total: int,
+                copy_rows: bool = True):
+        """Returns (out [N, H] u16 or None, out_scale [N, S] f32 or None,
+        m_indices [N] i32, output_index [T, K] i32). ``copy_rows=False``
+        computes only the indices."""
+        topk = _c(topk_idx, np.int64)
+        T, K = topk.shape
+        start = _c(expert_start_loc, np.int32)
+        E = start.size
+        H = int(x.shape[1]) if x is not None else 0
+        S = int(x_scale.shape[1]) if x_scale is not None else 0
+        xx = _c(x, np.uint16) if (x is not None and copy_rows) else None
+        xs = _c(x_scale, np.float32) if (x_scale is not None and copy_rows) else None
+        out = np.empty((total, H), np.uint16) if xx is not None else None
+        out_scale = np.empty((total, S), np.float32) if xs is not None else None
+        m_idx = np.empty(total, np.int32)
+        oi = np.empty((T, K), np.int32)
+        _check(self.lib.epl_oracle_scatter(T, K, E, H, S, _p(xx), _p(xs), _p(topk), _p(start),
+                                           _p(out), _p(out_scale), _p(m_idx), _p(oi)),
+               "scatter")
+        return out, out_scale, m_idx, oi
+
+    def expert_scale(self, rows: np.ndarray, m_indices: np.ndarray) -> np.ndarray:
+        """The large-batch workload's synthetic expert: bf16(row * (1 + e/256))."""
+        r = _c(rows, np.uint16)
+        m = _c(m_indices, np.int32)
+        N, H = r.shape
+        out = np.empty_like(r)
+        _check(self.lib.epl_oracle_expert_scale(N, H, _p(r), _p(m), _p(out)), "expert_scale")
+        return out
+
+    def combine(self, expert_out: np.ndarray, output_index: np.ndarray,
+                topk_weights: np.ndarray, tokens: Optional[np.ndarray] = None) -> np.ndarray:
+        """fp64 y [n, H] for the selected tokens (all tokens by default)."""
+        eo = _c(expert_out, np.uint16)
+        oi = _c(output_index, np.int32)
+        w = _c(topk_weights, np.float32)
+        T, K = oi.shape
+        rows, H = eo.shape
+        tk = None if tokens is None else _c(tokens, np.int64)
+        n = T if tk is None else tk.size
+        y = np.empty((n, H), np.float64)
+        _check(self.lib.epl_oracle_combine(T, K, H, _p(eo), rows, _p(oi), _p(w), _p(tk), n,
+                                           _p(y)), "combine")
+        return y
+
+    def run_all(self, x, x_scale, topk_idx, topk_weights, num_experts, num_ranks,
+                expert_fn="identity"):
+        """The whole path on the CPU: layout, scan, scatter, (expert), combine."""
+        cnt, per_rank, in_rank = self.layout(topk_idx, num_experts, num_ranks)
+        start, total = self.scan(cnt)
+        out, out_scale, m_idx, oi = self.scatter(x, x_scale, topk_idx, start, total)
+        eo = out if expert_fn == "identity" else self.expert_scale(out, m_idx)
+        y = self.combine(eo, oi, topk_weights)
+        return dict(num_tokens_per_expert=cnt, num_tokens_per_rank=per_rank,
+                    is_token_in_rank=in_rank, expert_start_loc=start, total=total,
+                    out=out, out_scale=out_scale, m_indices=m_idx, output_index=oi,
+                    expert_out=eo, y=y)
+
+
+_DEFAULT = None
+
+
+def default() -> Oracle:
+    """The oracle built from ``epl_oracle.c`` (rebuilt when the source is newer)."""
+    global _DEFAULT
+    if _DEFAULT is None:
+        path, src = _build.LIB, _build.SRC
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(src):
+            _build.build()
+        _DEFAULT = Oracle(path)
+    return _DEFAULT
+
+
+def lib_path() -> str:
+    return _build.LIB
+
+
+def __getattr__(name):
+    # module-level shorthands: oracle.layout(...), oracle.scan(...), ...
+    if name in ("bf16_to_double", "bf16_from_double", "bf16_from_double_array", "layout",
+                "scan", "scatter", "expert_scale", "combine", "run_all"):
+        return getattr(default(), name)
+    raise AttributeError(name)

@@ -1,0 +1,272 @@
+/*
+ * CPU oracle for MoE expert-parallel layout / scan / scatter / combine.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link,
+ * load or call this file. Only the test suite, the package smoke check and
+ * the benchmark's CPU-baseline leg use it. It shares no code, header, table
+ * or helper with the HIP library: every routine below is written out from
+ * the definitions, plainly, single-threaded, with no blocking or fusion.
+ *
+ * Build: gcc -std=c11 -O2 -ffp-contract=off -fPIC -shared (see build.py).
+ *
+ * Sources (page title, section):
+ *   [DEEPEP]  "[MoE] Deepseek的All-to-all通信: DeepEP代码解读" (hqwc.cn),
+ *             section "Dispatch": get_dispatch_layout returns, per expert and
+ *             per rank, how many tokens go there, and a [tokens, ranks]
+ *             boolean telling whether a token goes to a rank; topk_idx is
+ *             int64 [tokens, topk] with -1 meaning "no selection".
+ *   [ANATOMY] "高性能专家并行（EP）内核解剖学解读" (aimsg.uk), part on the
+ *             high-throughput path, subsections 1 (dispatch gathers the rows
+ *             bound for each expert into one dense buffer for the grouped
+ *             GEMM), 3 (exact allocation sized by the real counts) and 5
+ *             (buffer layout by prefix sum: the first source starts at 0,
+ *             each next one where the previous ended); section
+ *             "任务设定与数据流" (results are brought back to where they
+ *             came from).
+ *   [SGLANG]  "参考sglang代码，重构vllm021中EP高吞吐代码，消除空泡问题"
+ *             (rkmt.cn), section 2.2 (ep_scatter writes the ragged buffer,
+ *             its scales, m_indices and output_index; the total row count is
+ *             the sum of the counts) and section 3.3 (output_index / inv_perm
+ *             is int32 with -1 for slots that are not placed; m_indices holds
+ *             the expert id of every row).
+ *
+ * Readings where the pages leave a step open:
+ *   - rank r owns the contiguous experts [r*E/R, (r+1)*E/R);
+ *   - per-rank counts count tokens, once per rank, not slots;
+ *   - within an expert, rows are ordered by (token, k) ascending;
+ *   - the prefix sum is exclusive and starts at 0;
+ *   - combine: y[t] = sum over valid k, ascending, of w[t,k] * row, where the
+ *     row is the expert output at output_index[t,k]. Evaluated here in fp64.
+ *
+ * Parity pins (tests/test_oracle_pins.py): worked examples from the pages,
+ * an O((TK)^2) brute force of the placement definition, numpy's stable
+ * argsort, closed forms for combine on exactly representable values,
+ * torch's float->bf16 rounding for the bf16 encoder, and invariants.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL (-1)
+#define ORACLE_ERANGE (-2)
+
+/* ---------------------------------------------------------------- bf16 -- */
+
+/* bf16 is the upper half of an IEEE binary32: widen by appending 16 zero
+ * bits, then convert the float exactly to double. */
+double epl_oracle_bf16_to_double(uint16_t b)
+{
+    uint32_t u = ((uint32_t)b) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a double to the nearest bf16 value, ties to even, and return its
+ * bit pattern. Written from the number format: bf16 keeps 8 significant
+ * bits (exponent range of binary32), so a finite value is a multiple of
+ * 2^(e-7) where 2^e <= |v| < 2^(e+1), or of 2^-133 in the subnormal range.
+ * nearbyint() rounds the scaled value to an integer with ties to even under
+ * the default rounding mode. */
+uint16_t epl_oracle_bf16_from_double(double v)
+{
+    if (isnan(v))
+        return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0x0000;
+    double a = fabs(v);
+    if (a == 0.0)
+        return sign;
+    if (isinf(a))
+        return (uint16_t)(sign | 0x7F80);
+    int e2;
+    (void)frexp(a, &e2);              /* a = m * 2^e2, 0.5 <= m < 1 */
+    int quantum = (e2 - 1) - 7;       /* spacing of bf16 values in this binade */
+    if (quantum < -133)
+        quantum = -133;               /* subnormal spacing */
+    double q = nearbyint(ldexp(a, -quantum));
+    double r = ldexp(q, quantum);
+    if (r >= ldexp(1.0, 128))
+        return (uint16_t)(sign | 0x7F80);   /* overflow to infinity */
+    float f = (float)r;               /* exact: r has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (uint16_t)(u >> 16));
+}
+
+/* -------------------------------------------------------------- layout -- */
+
+static int check_shape(int64_t T, int32_t K, int32_t E, int32_t R)
+{
+    if (T < 0 || K < 1 || E < 1 || R < 1 || E % R != 0)
+        return ORACLE_EINVAL;
+    return ORACLE_OK;
+}
+
+/* [DEEPEP] get_dispatch_layout: counts per expert, the token/rank mask and
+ * the number of tokens each rank receives. A token that picks two experts of
+ * the same rank is sent to that rank once. Ids outside [-1, E) are rejected. */
+int epl_oracle_layout(int64_t T, int32_t K, int32_t E, int32_t R,
+                      const int64_t *topk_idx,
+                      int32_t *num_tokens_per_expert,
+                      int32_t *num_tokens_per_rank,
+                      uint8_t *is_token_in_rank)
+{
+    if (check_shape(T, K, E, R) != ORACLE_OK)
+        return ORACLE_EINVAL;
+    int64_t experts_per_rank = E / R;
+
+    for (int64_t i = 0; i < T * (int64_t)K; ++i)
+        if (topk_idx[i] < -1 || topk_idx[i] >= E)
+            return ORACLE_ERANGE;
+
+    for (int32_t e = 0; e < E; ++e)
+        num_tokens_per_expert[e] = 0;
+    for (int32_t r = 0; r < R; ++r)
+        num_tokens_per_rank[r] = 0;
+    for (int64_t i = 0; i < T * (int64_t)R; ++i)
+        is_token_in_rank[i] = 0;
+
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int64_t e = topk_idx[t * K + k];
+            if (e < 0)
+                continue;                       /* -1: no selection */
+            num_tokens_per_expert[e] += 1;
+            is_token_in_rank[t * R + e / experts_per_rank] = 1;
+        }
+    }
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t r = 0; r < R; ++r)
+            num_tokens_per_rank[r] += is_token_in_rank[t * R + r];
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------- scan -- */
+
+/* [ANATOMY] subsection 5 / [SGLANG] section 2.2: each expert's block starts
+ * where the previous one ended, the first at 0; the buffer holds the sum of
+ * all counts. */
+int epl_oracle_scan(int32_t E, const int32_t *num_tokens_per_expert,
+                    int32_t *expert_start_loc, int64_t *total)
+{
+    if (E < 1)
+        return ORACLE_EINVAL;
+    int64_t running = 0;
+    for (int32_t e = 0; e < E; ++e) {
+        if (num_tokens_per_expert[e] < 0)
+            return ORACLE_EINVAL;
+        expert_start_loc[e] = (int32_t)running;
+        running += num_tokens_per_expert[e];
+    }
+    *total = running;
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------- scatter -- */
+
+/* [ANATOMY] subsection 1, [SGLANG] sections 2.2 and 3.3: every valid slot
+ * (t, k) gets its own row in its expert's block, in (t, k) order (a counting
+ * sort: a cursor per expert starts at the expert's offset and advances by
+ * one per placed row). The row receives a bit copy of x[t] and, when scales
+ * are present, of x_scale[t]; m_indices[row] = expert; output_index[t, k] =
+ * row, or -1 for a -1 slot. Any of out / out_scale may be NULL to skip the
+ * row copies (used when only the indices are compared). */
+int epl_oracle_scatter(int64_t T, int32_t K, int32_t E, int32_t H, int32_t S,
+                       const uint16_t *x, const float *x_scale,
+                       const int64_t *topk_idx, const int32_t *expert_start_loc,
+                       uint16_t *out, float *out_scale,
+                       int32_t *m_indices, int32_t *output_index)
+{
+    if (T < 0 || K < 1 || E < 1 || H < 0 || S < 0)
+        return ORACLE_EINVAL;
+    int64_t *cursor = (int64_t *)malloc(sizeof(int64_t) * (size_t)E);
+    if (!cursor)
+        return ORACLE_EINVAL;
+    for (int32_t e = 0; e < E; ++e)
+        cursor[e] = expert_start_loc[e];
+
+    int rc = ORACLE_OK;
+    for (int64_t t = 0; t < T && rc == ORACLE_OK; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int64_t e = topk_idx[t * K + k];
+            if (e < -1 || e >= E) {
+                rc = ORACLE_ERANGE;
+                break;
+            }
+            if (e < 0) {
+                output_index[t * K + k] = -1;
+                continue;
+            }
+            int64_t row = cursor[e];
+            cursor[e] += 1;
+            output_index[t * K + k] = (int32_t)row;
+            m_indices[row] = (int32_t)e;
+            if (out)
+                memcpy(out + row * (int64_t)H, x + t * (int64_t)H, sizeof(uint16_t) * (size_t)H);
+            if (out_scale && S > 0)
+                memcpy(out_scale + row * (int64_t)S, x_scale + t * (int64_t)S, sizeof(float) * (size_t)S);
+        }
+    }
+    free(cursor);
+    return rc;
+}
+
+/* ------------------------------------------------------- expert stand-in -- */
+
+/* The synthetic expert of the large-batch workload: expert e multiplies its
+ * row by (1 + e/256) and the result is stored as bf16 (nearest, ties to even).
+ * The product is exact in double, so the only rounding is the final one. */
+int epl_oracle_expert_scale(int64_t N, int32_t H, const uint16_t *rows,
+                            const int32_t *m_indices, uint16_t *expert_out)
+{
+    if (N < 0 || H < 0)
+        return ORACLE_EINVAL;
+    for (int64_t p = 0; p < N; ++p) {
+        double factor = 1.0 + (double)m_indices[p] / 256.0;
+        for (int32_t h = 0; h < H; ++h) {
+            double v = epl_oracle_bf16_to_double(rows[p * (int64_t)H + h]);
+            expert_out[p * (int64_t)H + h] = epl_oracle_bf16_from_double(v * factor);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------- combine -- */
+
+/* [ANATOMY] "任务设定与数据流" / [SGLANG] section 2.2 (the state kept for the
+ * way back: topk ids, topk weights, output_index): for each token t,
+ *     y[t, :] = sum over valid k (ascending) of w[t, k] * expert_out[output_index[t, k], :]
+ * accumulated in double from +0. A token with no valid slot yields zeros.
+ * ``tokens`` (length n_tokens) selects which tokens to evaluate; NULL means
+ * all T in order. y has one H-wide row per evaluated token. */
+int epl_oracle_combine(int64_t T, int32_t K, int32_t H,
+                       const uint16_t *expert_out, int64_t expert_rows,
+                       const int32_t *output_index, const float *topk_weights,
+                       const int64_t *tokens, int64_t n_tokens, double *y)
+{
+    if (T < 0 || K < 1 || H < 0 || expert_rows < 0)
+        return ORACLE_EINVAL;
+    int64_t count = tokens ? n_tokens : T;
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t t = tokens ? tokens[i] : i;
+        if (t < 0 || t >= T)
+            return ORACLE_EINVAL;
+        double *yrow = y + i * (int64_t)H;
+        for (int32_t h = 0; h < H; ++h)
+            yrow[h] = 0.0;
+        for (int32_t k = 0; k < K; ++k) {
+            int64_t row = output_index[t * K + k];
+            if (row < 0)
+                continue;
+            if (row >= expert_rows)
+                return ORACLE_ERANGE;
+            double w = (double)topk_weights[t * K + k];
+            const uint16_t *src = expert_out + row * (int64_t)H;
+            for (int32_t h = 0; h < H; ++h)
+                yrow[h] = yrow[h] + w * epl_oracle_bf16_to_double(src[h]);
+        }
+    }
+    return ORACLE_OK;
+}

@@ -1,0 +1,181 @@
+"""Planted mistakes: each copy of the oracle below carries one plausible bug
+(a dropped term, a wrong sign or index, a transposed operand, an off-by-one)
+and must fail at least one pin. The mistakes are planted in a temporary copy
+of the C source, on the CPU; the committed oracle is never modified. Each
+mutant runs in its own process, because a mutant that writes out of bounds
+may abort; an abort counts as a failed pin."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from conftest import load_golden
+from oracle import Oracle, OracleError
+from test_oracle_pins import brute_force
+
+SRC = open(os.path.join(os.path.dirname(oracle.__file__), "epl_oracle.c"), encoding="utf-8").read()
+
+MUTANTS = {
+    "cursor_advances_by_two": ("cursor[e] += 1;", "cursor[e] += 2;"),
+    "round_robin_owner": ("is_token_in_rank[t * R + e / experts_per_rank] = 1;",
+                          "is_token_in_rank[t * R + e % R] = 1;"),
+    "inclusive_scan": ("expert_start_loc[e] = (int32_t)running;\n        running += num_tokens_per_expert[e];",
+                       "running += num_tokens_per_expert[e];\n        expert_start_loc[e] = (int32_t)running;"),
+    "per_rank_counts_every_token": ("num_tokens_per_rank[r] += is_token_in_rank[t * R + r];",
+                                    "num_tokens_per_rank[r] += 1;"),
+    "weight_of_mirrored_slot": ("double w = (double)topk_weights[t * K + k];",
+                                "double w = (double)topk_weights[t * K + (K - 1 - k)];"),
+    "transposed_output_index": ("int64_t row = output_index[t * K + k];",
+                                "int64_t row = output_index[k * T + t];"),
+    "dropped_accumulator": ("yrow[h] = yrow[h] + w * epl_oracle_bf16_to_double(src[h]);",
+                            "yrow[h] = w * epl_oracle_bf16_to_double(src[h]);"),
+    "bf16_one_bit_short": ("int quantum = (e2 - 1) - 7;", "int quantum = (e2 - 1) - 6;"),
+    "bf16_truncates": ("double q = nearbyint(ldexp(a, -quantum));",
+                       "double q = floor(ldexp(a, -quantum));"),
+    "bf16_ties_away": ("double q = nearbyint(ldexp(a, -quantum));",
+                       "double q = round(ldexp(a, -quantum));"),
+    "invalid_slot_marked_zero": ("output_index[t * K + k] = -1;\n                continue;",
+                                 "output_index[t * K + k] = 0;\n                continue;"),
+    "expert_factor_255": ("1.0 + (double)m_indices[p] / 256.0", "1.0 + (double)m_indices[p] / 255.0"),
+    "slots_in_reverse_k": ("for (int32_t k = 0; k < K; ++k) {\n            int64_t e = topk_idx[t * K + k];\n            if (e < -1",
+                           "for (int32_t k = K - 1; k >= 0; --k) {\n            int64_t e = topk_idx[t * K + k];\n            if (e < -1"),
+    "scale_row_of_wrong_token": ("x_scale + t * (int64_t)S", "x_scale + (T - 1 - t) * (int64_t)S"),
+}
+
+
+def _build_mutant(tmp_path, name, find, repl):
+    assert SRC.count(find) == 1, f"mutation {name}: pattern must occur exactly once"
+    src = tmp_path / f"{name}.c"
+    src.write_text(SRC.replace(find, repl), encoding="utf-8")
+    lib = tmp_path / f"lib{name}.so"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fPIC", "-shared",
+                    str(src), "-o", str(lib), "-lm"], check=True)
+    return str(lib)
+
+
+def _battery(orc: Oracle):
+    """Quick pins, each as a boolean; returns the names of the pins that fail."""
+    failed = []
+
+    def pin(name, fn):
+        try:
+            if not fn():
+                failed.append(name)
+        except (OracleError, AssertionError, IndexError, ValueError):
+            failed.append(name)
+
+    def golden_scan():
+        g = load_golden("scan_prefix_example.txt")
+        start, total = orc.scan(np.array(g["counts"]))
+        return start.tolist() == g["expert_start_loc"] and total == g["total"][0]
+
+    def golden_hand():
+        g = load_golden("scatter_hand_example.txt")
+        E, R = g["num_experts"][0], g["num_ranks"][0]
+        topk = np.array(g["topk_idx"], np.int64)
+        cnt, per_rank, _ = orc.layout(topk, E, R)
+        start, total = orc.scan(cnt)
+        _, _, m, oi = orc.scatter(None, None, topk, start, total)
+        return (oi.tolist() == g["output_index"] and m.tolist() == g["m_indices"]
+                and per_rank.tolist() == g["num_tokens_per_rank"])
+
+    def brute():
+        rng = np.random.default_rng(99)
+        for _ in range(30):
+            R = int(rng.integers(1, 5))
+            E = R * int(rng.integers(1, 5))
+            T, K = int(rng.integers(1, 10)), int(rng.integers(1, 5))
+            topk = rng.integers(-1, E, size=(T, K)).astype(np.int64)
+            want = brute_force(topk, E, R)
+            cnt, per_rank, in_rank = orc.layout(topk, E, R)
+            start, total = orc.scan(cnt)
+            _, _, m, oi = orc.scatter(None, None, topk, start, total)
+            if not (np.array_equal(cnt, want["cnt"]) and np.array_equal(per_rank, want["per_rank"])
+                    and np.array_equal(in_rank, want["in_rank"]) and np.array_equal(start, want["start"])
+                    and np.array_equal(oi, want["oi"]) and np.array_equal(m, want["m"])):
+                return False
+        return True
+
+    def rows_and_scales():
+        rng = np.random.default_rng(5)
+        T, K, E, R, H = 20, 3, 8, 4, 128
+        topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+        x = rng.integers(0, 1 << 15, size=(T, H), dtype=np.uint16)
+        xs = rng.uniform(0.01, 1, size=(T, 1)).astype(np.float32)
+        cnt, _, _ = orc.layout(topk, E, R)
+        start, total = orc.scan(cnt)
+        out, out_scale, _, oi = orc.scatter(x, xs, topk, start, total)
+        tt, kk = np.nonzero(topk >= 0)
+        return (np.array_equal(out[oi[tt, kk]], x[tt])
+                and np.array_equal(out_scale[oi[tt, kk]], xs[tt]))
+
+    def one_hot_combine():
+        rng = np.random.default_rng(3)
+        T, K, N = 6, 3, 18
+        oi = rng.permutation(N).reshape(T, K).astype(np.int32)
+        oi[1, 2] = -1
+        eye = (np.eye(N, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        w = rng.uniform(0.1, 1, (T, K)).astype(np.float32)
+        y = orc.combine(eye, oi, w)
+        expect = np.zeros((T, N))
+        for t in range(T):
+            for k in range(K):
+                if oi[t, k] >= 0:
+                    expect[t, oi[t, k]] += np.float64(w[t, k])
+        return np.array_equal(y, expect)
+
+    def bf16_vs_torch():
+        import torch
+        rng = np.random.default_rng(11)
+        f = rng.standard_normal(3000).astype(np.float32)
+        ties = (np.arange(1, 300, dtype=np.uint32) << 16 | np.uint32(0x8000)).view(np.float32)
+        f = np.concatenate([f, ties, ties * np.float32(3e30)])
+        f = f[np.isfinite(f)]
+        want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        return np.array_equal(orc.bf16_from_double_array(f.astype(np.float64)), want)
+
+    def expert_scale_hand():
+        rows = np.array([[0x3F80], [0x3F80], [0x3F81], [0x3F80]], np.uint16)
+        m = np.array([255, 128, 1, 1], np.int32)
+        return orc.expert_scale(rows, m)[:, 0].tolist() == [0x4000, 0x3FC0, 0x3F82, 0x3F80]
+
+    for name, fn in [("golden_scan", golden_scan), ("golden_hand", golden_hand), ("brute", brute),
+                     ("rows_and_scales", rows_and_scales), ("one_hot_combine", one_hot_combine),
+                     ("bf16_vs_torch", bf16_vs_torch), ("expert_scale_hand", expert_scale_hand)]:
+        pin(name, fn)
+    return failed
+
+
+def _run_battery_in_subprocess(lib):
+    here = os.path.dirname(os.path.abspath(__file__))
+    env = dict(os.environ)
+    env["PYTHONPATH"] = os.pathsep.join([os.path.dirname(here), here, env.get("PYTHONPATH", "")])
+    return subprocess.run([sys.executable, os.path.abspath(__file__), lib], cwd=here, env=env,
+                          capture_output=True, text=True, timeout=300)
+
+
+def test_unmutated_oracle_passes_the_battery():
+    assert _battery(oracle.default()) == []
+    # the subprocess route itself works, so a mutant's non-zero exit is its own
+    proc = _run_battery_in_subprocess(oracle.default().path)
+    assert proc.returncode == 0, proc.stderr
+    assert json.loads(proc.stdout.strip().splitlines()[-1]) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(tmp_path, name):
+    find, repl = MUTANTS[name]
+    lib = _build_mutant(tmp_path, name, find, repl)
+    proc = _run_battery_in_subprocess(lib)
+    if proc.returncode != 0:
+        return          # the mutant crashed inside a pin: caught
+    failed = json.loads(proc.stdout.strip().splitlines()[-1])
+    assert failed, f"planted mistake {name!r} passed every pin"
+
+
+if __name__ == "__main__":
+    print(json.dumps(_battery(Oracle(sys.argv[1]))))

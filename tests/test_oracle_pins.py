@@ -1,0 +1,346 @@
+"""Pins for the CPU oracle: each test ties it to something other than itself.
+
+Kinds of pin used here:
+  * worked examples from the pages (tests/golden, each with its citation);
+  * a brute force of the placement definition, O((T*K)^2), that shares
+    nothing with the oracle's counting-sort algorithm, run exhaustively on
+    tiny inputs and on random small ones;
+  * a library routine: numpy's stable argsort gives the row -> slot map;
+  * closed forms for combine on exactly representable values (one-hot rows,
+    K = 1 with weight 1, identity expert with weights summing to 1);
+  * torch's float -> bf16 conversion (round to nearest even) for the bf16
+    encoder, and hand-checked ties for the large-batch expert stand-in;
+  * invariants (counts sum, contiguous blocks, bijection, row copies).
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+from conftest import load_golden
+from oracle import OracleError
+
+
+# --------------------------------------------------------------- helpers --
+
+def brute_force(topk, E, R):
+    """Every quantity straight from its definition, by enumeration."""
+    T, K = topk.shape
+    slots = [(t, k) for t in range(T) for k in range(K)]
+    epr = E // R
+    cnt = [sum(1 for (t, k) in slots if topk[t, k] == e) for e in range(E)]
+    in_rank = [[int(any(topk[t, k] >= 0 and topk[t, k] // epr == r for k in range(K)))
+                for r in range(R)] for t in range(T)]
+    per_rank = [sum(in_rank[t][r] for t in range(T)) for r in range(R)]
+    start = [sum(cnt[:e]) for e in range(E)]
+    oi = [[-1] * K for _ in range(T)]
+    for (t, k) in slots:
+        e = topk[t, k]
+        if e < 0:
+            continue
+        earlier = sum(1 for (t2, k2) in slots if topk[t2, k2] == e and (t2, k2) < (t, k))
+        oi[t][k] = start[e] + earlier
+    N = sum(cnt)
+    m = [None] * N
+    for (t, k) in slots:
+        if oi[t][k] >= 0:
+            m[oi[t][k]] = topk[t, k]
+    return dict(cnt=np.array(cnt), per_rank=np.array(per_rank), in_rank=np.array(in_rank),
+                start=np.array(start), total=N, oi=np.array(oi), m=np.array(m, dtype=np.int64))
+
+
+def run_oracle(topk, E, R, x=None, x_scale=None, orc=None):
+    orc = orc or oracle.default()
+    cnt, per_rank, in_rank = orc.layout(topk, E, R)
+    start, total = orc.scan(cnt)
+    out, out_scale, m, oi = orc.scatter(x, x_scale, topk, start, total)
+    return dict(cnt=cnt, per_rank=per_rank, in_rank=in_rank, start=start, total=total,
+                out=out, out_scale=out_scale, m=m, oi=oi)
+
+
+def assert_same_as_brute(topk, E, R, orc=None):
+    got = run_oracle(topk, E, R, orc=orc)
+    want = brute_force(topk, E, R)
+    np.testing.assert_array_equal(got["cnt"], want["cnt"])
+    np.testing.assert_array_equal(got["per_rank"], want["per_rank"])
+    np.testing.assert_array_equal(got["in_rank"], want["in_rank"].reshape(got["in_rank"].shape))
+    np.testing.assert_array_equal(got["start"], want["start"])
+    assert got["total"] == want["total"]
+    np.testing.assert_array_equal(got["oi"], want["oi"].reshape(got["oi"].shape))
+    np.testing.assert_array_equal(got["m"], want["m"])
+
+
+# ------------------------------------------------------ worked examples --
+
+def test_golden_scan_prefix_example():
+    g = load_golden("scan_prefix_example.txt")
+    start, total = oracle.scan(np.array(g["counts"]))
+    assert start.tolist() == g["expert_start_loc"]
+    assert total == g["total"][0]
+
+
+def test_golden_route_token_3_7():
+    g = load_golden("route_token_3_7.txt")
+    E, R = g["num_experts"][0], g["num_ranks"][0]
+    topk = np.array([g["topk_idx"]], dtype=np.int64)
+    cnt, per_rank, in_rank = oracle.layout(topk, E, R)
+    assert cnt.tolist() == g["num_tokens_per_expert"]
+    assert per_rank.tolist() == g["num_tokens_per_rank"]
+    assert in_rank[0].tolist() == g["is_token_in_rank"]
+
+
+def test_golden_scatter_hand_example():
+    g = load_golden("scatter_hand_example.txt")
+    E, R = g["num_experts"][0], g["num_ranks"][0]
+    topk = np.array(g["topk_idx"], dtype=np.int64)
+    T, K = topk.shape
+    H = 8
+    x = (np.arange(T * H, dtype=np.uint16) + 1).reshape(T, H)
+    got = run_oracle(topk, E, R, x=x)
+    assert got["cnt"].tolist() == g["num_tokens_per_expert"]
+    assert got["start"].tolist() == g["expert_start_loc"]
+    assert got["total"] == g["total"][0]
+    assert got["oi"].tolist() == g["output_index"]
+    assert got["m"].tolist() == g["m_indices"]
+    assert got["per_rank"].tolist() == g["num_tokens_per_rank"]
+    for row, src in enumerate(g["row_source_token"]):
+        np.testing.assert_array_equal(got["out"][row], x[src])
+
+
+# ------------------------------------------------------------ brute force --
+
+EXHAUSTIVE_SHAPES = [
+    # (T, K, E, R)
+    (1, 3, 4, 4),
+    (2, 2, 4, 2),
+    (3, 2, 3, 3),
+    (3, 2, 3, 1),
+    (4, 1, 2, 1),
+    (2, 3, 2, 2),
+]
+
+
+@pytest.mark.parametrize("T,K,E,R", EXHAUSTIVE_SHAPES)
+def test_exhaustive_tiny_against_brute_force(T, K, E, R):
+    """Every topk_idx matrix with entries in {-1, 0, .., E-1}: duplicates
+    within a token, all -1 rows and empty experts included."""
+    for vals in itertools.product(range(-1, E), repeat=T * K):
+        topk = np.array(vals, dtype=np.int64).reshape(T, K)
+        assert_same_as_brute(topk, E, R)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_small_against_brute_force(seed):
+    rng = np.random.default_rng(1000 + seed)
+    R = int(rng.integers(1, 5))
+    E = R * int(rng.integers(1, 5))
+    T = int(rng.integers(0, 14))
+    K = int(rng.integers(1, 5))
+    topk = rng.integers(-1, E, size=(T, K)).astype(np.int64)
+    assert_same_as_brute(topk, E, R)
+
+
+# ------------------------------------------------- library routine: argsort --
+
+@pytest.mark.parametrize("seed", range(5))
+def test_row_order_is_numpy_stable_argsort(seed):
+    """Rows in expert order, ties by (token, k): exactly a stable sort of the
+    flattened slot keys with the -1 slots (which sort first) dropped."""
+    rng = np.random.default_rng(seed)
+    T, K, E, R = 700, 6, 48, 8
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    topk[rng.random(topk.shape) < 0.1] = -1
+    got = run_oracle(topk, E, R)
+    flat = topk.ravel()
+    order = np.argsort(flat, kind="stable")
+    order = order[flat[order] >= 0]
+    N = order.size
+    assert got["total"] == N
+    np.testing.assert_array_equal(got["oi"].ravel()[order], np.arange(N))
+    np.testing.assert_array_equal(got["m"], flat[order])
+    np.testing.assert_array_equal(got["oi"].ravel()[flat < 0], -1)
+
+
+# ------------------------------------------------------------- invariants --
+
+def test_invariants_on_generated_workload():
+    from permute_ep_layout_amd import workloads
+    w = workloads.get("small").with_(num_tokens=300, hidden=64)
+    inp = workloads.make_inputs(w)
+    topk, x = inp["topk_idx"], inp["x"]
+    E, R = w.num_experts, w.num_ranks
+    got = run_oracle(topk, E, R, x=x)
+    valid = topk >= 0
+    assert got["cnt"].sum() == valid.sum() == got["total"]
+    # each expert's rows are the contiguous block starting at its offset
+    for e in range(E):
+        blk = got["m"][got["start"][e]:got["start"][e] + got["cnt"][e]]
+        assert (blk == e).all()
+    assert (np.diff(got["m"]) >= 0).all()
+    # output_index is a bijection from the valid slots onto [0, N)
+    placed = got["oi"][valid]
+    assert np.array_equal(np.sort(placed), np.arange(got["total"]))
+    assert (got["oi"][~valid] == -1).all()
+    # every placed row is a bit copy of its token's row
+    tt, kk = np.nonzero(valid)
+    np.testing.assert_array_equal(got["out"][got["oi"][tt, kk]], x[tt])
+    # per-rank counts: column sums of the mask, bounded by the rank's slot count
+    np.testing.assert_array_equal(got["per_rank"], got["in_rank"].sum(axis=0))
+    epr = E // R
+    for r in range(R):
+        assert got["per_rank"][r] <= got["cnt"][r * epr:(r + 1) * epr].sum()
+    assert got["total"] <= topk.size
+
+
+def test_scale_rows_follow_their_rows():
+    rng = np.random.default_rng(7)
+    T, K, E, R, H = 50, 4, 16, 4, 256
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    x = rng.integers(0, 1 << 16, size=(T, H), dtype=np.uint16)
+    xs = rng.uniform(0.01, 1.0, size=(T, H // 128)).astype(np.float32)
+    got = run_oracle(topk, E, R, x=x, x_scale=xs)
+    tt, kk = np.nonzero(topk >= 0)
+    rows = got["oi"][tt, kk]
+    np.testing.assert_array_equal(got["out_scale"][rows].view(np.uint32), xs[tt].view(np.uint32))
+
+
+def test_empty_and_all_invalid():
+    E, R = 8, 4
+    got = run_oracle(np.zeros((0, 3), np.int64), E, R)
+    assert got["total"] == 0 and got["cnt"].sum() == 0 and (got["start"] == 0).all()
+    topk = -np.ones((5, 3), np.int64)
+    got = run_oracle(topk, E, R)
+    assert got["total"] == 0 and (got["oi"] == -1).all() and got["in_rank"].sum() == 0
+    y = oracle.combine(np.zeros((0, 16), np.uint16), got["oi"], np.ones((5, 3), np.float32))
+    assert (y == 0).all() and not np.signbit(y).any()
+
+
+def test_errors():
+    with pytest.raises(OracleError) as ei:
+        oracle.layout(np.array([[0, 8]], np.int64), 8, 4)
+    assert ei.value.code == oracle.ERANGE
+    with pytest.raises(OracleError) as ei:
+        oracle.layout(np.array([[0, -2]], np.int64), 8, 4)
+    assert ei.value.code == oracle.ERANGE
+    with pytest.raises(OracleError) as ei:
+        oracle.layout(np.array([[0, 1]], np.int64), 9, 4)       # E % R != 0
+    assert ei.value.code == oracle.EINVAL
+
+
+# ---------------------------------------------------------------- combine --
+
+def _bf16(values):
+    return np.asarray(np.asarray(values, np.float32).view(np.uint32) >> 16, dtype=np.uint16)
+
+
+def test_combine_one_hot_rows():
+    """With row p of the expert output equal to the unit vector e_p, token t's
+    result holds w[t,k] in column output_index[t,k] and zeros elsewhere:
+    this pins which row each slot reads and which weight multiplies it."""
+    rng = np.random.default_rng(3)
+    T, K, E, R = 12, 3, 8, 2
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    topk[rng.random(topk.shape) < 0.2] = -1
+    got = run_oracle(topk, E, R)
+    N = got["total"]
+    eye = _bf16(np.eye(N, dtype=np.float32))
+    w = rng.uniform(0.05, 1.0, size=(T, K)).astype(np.float32)
+    y = oracle.combine(eye, got["oi"], w)
+    expect = np.zeros((T, N))
+    for t in range(T):
+        for k in range(K):
+            if topk[t, k] >= 0:
+                expect[t, got["oi"][t, k]] = np.float64(w[t, k])
+    np.testing.assert_array_equal(y, expect)
+
+
+def test_combine_k1_weight1_is_identity():
+    rng = np.random.default_rng(4)
+    T, E, R, H = 40, 8, 4, 96
+    topk = rng.integers(0, E, size=(T, 1)).astype(np.int64)
+    x = _bf16(rng.standard_normal((T, H)).astype(np.float32))
+    got = run_oracle(topk, E, R, x=x)
+    y = oracle.combine(got["out"], got["oi"], np.ones((T, 1), np.float32))
+    np.testing.assert_array_equal(y, (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+
+
+def test_combine_identity_expert_returns_input():
+    """Scatter then an identity-expert combine with weights that sum to 1
+    returns x, up to the weights' own fp32 rounding (|sum w - 1|)."""
+    from permute_ep_layout_amd import workloads
+    w = workloads.get("small").with_(num_tokens=200, hidden=128)
+    inp = workloads.make_inputs(w)
+    topk, x, wt = inp["topk_idx"], inp["x"], inp["topk_weights"]
+    got = run_oracle(topk, w.num_experts, w.num_ranks, x=x)
+    y = oracle.combine(got["out"], got["oi"], wt)
+    xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    has = (topk >= 0).any(axis=1)
+    wsum = wt.astype(np.float64).sum(axis=1, keepdims=True)
+    assert np.abs(wsum[has] - 1).max() < 1e-6
+    bound = (np.abs(wsum - 1) + 1e-15) * np.abs(xf)
+    assert (np.abs(y - xf)[has] <= bound[has]).all()
+    assert (y[~has] == 0).all()
+
+
+def test_combine_rejects_row_beyond_expert_output():
+    with pytest.raises(OracleError):
+        oracle.combine(np.zeros((2, 4), np.uint16), np.array([[0, 2]], np.int32),
+                       np.ones((1, 2), np.float32))
+
+
+def test_combine_token_subset_matches_full():
+    rng = np.random.default_rng(5)
+    T, K, E, R, H = 30, 4, 16, 4, 32
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    x = _bf16(rng.standard_normal((T, H)).astype(np.float32))
+    got = run_oracle(topk, E, R, x=x)
+    wt = rng.uniform(0, 1, (T, K)).astype(np.float32)
+    full = oracle.combine(got["out"], got["oi"], wt)
+    sel = np.array([29, 0, 7, 7])
+    np.testing.assert_array_equal(oracle.combine(got["out"], got["oi"], wt, tokens=sel), full[sel])
+
+
+# ------------------------------------------------------------------ bf16 --
+
+def test_bf16_decode_is_upper_half_of_binary32():
+    bits = np.arange(0, 1 << 16, 97, dtype=np.uint16)
+    want32 = (bits.astype(np.uint32) << 16).view(np.float32)
+    finite = np.isfinite(want32)
+    want = want32[finite].astype(np.float64)
+    got = np.array([oracle.bf16_to_double(int(b)) for b in bits[finite]])
+    np.testing.assert_array_equal(got, want)
+
+
+def test_bf16_encoder_matches_torch_round_to_nearest_even():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(11)
+    u = rng.integers(0, 1 << 32, size=20000, dtype=np.uint64).astype(np.uint32)
+    f = u.view(np.float32)
+    f = f[np.isfinite(f)]
+    # add exact ties and near-ties around a few binades, subnormals, extremes
+    ties = (np.arange(1, 2000, dtype=np.uint32) << 16 | np.uint32(0x8000)).view(np.float32)
+    extra = np.array([0.0, -0.0, 1e-45, -1e-45, 1.17549435e-38, 3.4028235e38, -3.4028235e38,
+                      3.3895314e38, 3.3961776e38], dtype=np.float32)
+    f = np.concatenate([f, ties, -ties, extra])
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.bf16_from_double_array(f.astype(np.float64))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_expert_scale_hand_checked_values():
+    """bf16(x * (1 + e/256)) on hand-worked cases, including an exact tie."""
+    cases = [
+        (0x3F80, 0, 0x3F80),     # 1 * 1 = 1
+        (0x3F80, 128, 0x3FC0),   # 1 * 1.5 = 1.5
+        (0x3F80, 255, 0x4000),   # 1 + 255/256: exactly half an ulp above 1.9921875 -> even -> 2
+        (0x3F80, 254, 0x3FFF),   # 1 + 254/256 = 1.9921875, representable
+        (0x3F81, 1, 0x3F82),     # (1+2^-7)(1+2^-8) = 1+2^-7+2^-8+2^-15 > halfway -> up
+        (0x3F80, 1, 0x3F80),     # 1 + 2^-8: exactly halfway between 1 and 1+2^-7 -> even -> 1
+        (0xBF80, 64, 0xBFA0),    # -1 * 1.25 = -1.25
+        (0x0000, 200, 0x0000),
+    ]
+    rows = np.array([[c[0]] for c in cases], np.uint16)
+    m = np.array([c[1] for c in cases], np.int32)
+    got = oracle.expert_scale(rows, m)[:, 0]
+    assert [hex(v) for v in got] == [hex(c[2]) for c in cases]
