@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark: MoE expert-parallel dispatch + combine on one MI355X.
+
+One step = one pass of the whole hot path over the workload: layout, scan,
+scatter (rows + scale rows + m_indices + output_index) and combine (fp32
+top-k-weighted sum back to token order), through the C ABI of libepl.so,
+all on one HIP stream, with inputs resident in HBM. The default workload is
+the DeepSeek-V3-shaped batch (4096 tokens, hidden 7168 bf16 + 56 fp32 scales
+per row, 256 experts, top-8, 32 virtual ranks, identity expert).
+
+Prints one JSON line: routed rows/s (value), ms per step, per-kernel times,
+the roofline of the dominant kernel (algorithmic bytes / HIP-event-measured
+average duration vs the 8 TB/s HBM peak), and the CPU oracle timed on this
+host's cores as a reference baseline.
+
+  python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload dsv3]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w, N, T_any, out_dtype_bytes=4):
+    """Bytes each kernel must move (reads + writes), by its definition."""
+    T, K, E, R, H, S = (w.num_tokens, w.num_topk, w.num_experts, w.num_ranks, w.hidden,
+                        w.scale_cols)
+    return {
+        "layout": 8 * T * K + 4 * E + 4 * R + T * R,
+        "scan": 4 * E + 4 * E + 4,
+        "scatter": (2 * H * T_any + 4 * S * T_any + 8 * T * K + 4 * E) +
+                   (2 * H * N + 4 * S * N + 4 * N + 4 * T * K),
+        "expert": 2 * H * N + 4 * N + 2 * H * N,
+        "combine": 2 * H * N + 4 * T * K + 4 * T * K + out_dtype_bytes * T * H,
+    }
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for rel in ("permute_ep_layout_amd/csrc/epl_kernels.h", "permute_ep_layout_amd/csrc/epl.hip"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    only if it was taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(workload, {}).get(kernel)
+    if not entry or entry.get("source_digest") != source_digest():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, seconds):
+    """The CPU oracle as it stands, single-threaded, over full passes of the
+    same workload until about `seconds` of work."""
+    import oracle
+
+    orc = oracle.default()
+    passes, rows, t0 = 0, 0, time.perf_counter()
+    while True:
+        r = orc.run_all(inp["x"], inp["x_scale"], inp["topk_idx"], inp["topk_weights"],
+                        w.num_experts, w.num_ranks, expert_fn=w.expert_fn)
+        passes += 1
+        rows += r["total"]
+        el = time.perf_counter() - t0
+        if el >= seconds or passes >= 50:
+            break
+    return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} full pass(es) of the {w.name} workload "
+                      f"(layout, scan, scatter with row copies, fp64 combine), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--out-dtype", choices=["f32", "bf16"], default="f32")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the inter-GPU transfer is outside this library, "
+              "so there is no multi-GPU step to time (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import permute_ep_layout_amd as epl
+    from permute_ep_layout_amd import workloads
+
+    if not epl.is_built():
+        epl.ensure_built()
+    epl.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.get(args.workload)
+    T, K, E, R, H, S = (w.num_tokens, w.num_topk, w.num_experts, w.num_ranks, w.hidden,
+                        w.scale_cols)
+    log(f"workload {w.name}: T={T} K={K} E={E} R={R} H={H} S={S}; generating inputs")
+    inp = workloads.make_inputs(w)
+    N = int((inp["topk_idx"] >= 0).sum())
+    T_any = int((inp["topk_idx"] >= 0).any(axis=1).sum())
+
+    topk = torch.from_numpy(inp["topk_idx"]).to(dev)
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    xs = torch.from_numpy(inp["x_scale"]).to(dev) if S else None
+    wt = torch.from_numpy(inp["topk_weights"]).to(dev)
+    p = epl.Problem.make(T, K, E, R, H, S)
+    cap = T * K
+    i32 = torch.int32
+    ws = torch.empty(epl.epl_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    cnt = torch.empty(E, dtype=i32, device=dev)
+    per_rank = torch.empty(R, dtype=i32, device=dev)
+    in_rank = torch.empty((T, R), dtype=torch.uint8, device=dev)
+    start = torch.empty(E, dtype=i32, device=dev)
+    total_host = torch.zeros(1, dtype=i32).pin_memory()
+    out = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+    out_scale = torch.empty((cap, S), dtype=torch.float32, device=dev) if S else None
+    m_idx = torch.empty(cap, dtype=i32, device=dev)
+    oi = torch.empty((T, K), dtype=i32, device=dev)
+    scaled = w.expert_fn == "scale"
+    eo = torch.empty_like(out) if scaled else out
+    out_code = epl.EPL_OUT_F32 if args.out_dtype == "f32" else epl.EPL_OUT_BF16
+    y = torch.empty((T, H), dtype=torch.float32 if out_code == epl.EPL_OUT_F32 else torch.bfloat16,
+                    device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    names = ["layout", "scan", "scatter"] + (["expert"] if scaled else []) + ["combine"]
+
+    def step(events=None):
+        def mark(i):
+            if events is not None:
+                events[i].record(stream)
+        mark(0)
+        epl.epl_layout(p, topk, cnt, per_rank, in_rank, ws)
+        mark(1)
+        epl.epl_scan(p, cnt, start, total_host, ws)
+        mark(2)
+        epl.epl_scatter(p, x, xs, topk, start, ws, cap, out, out_scale, m_idx, oi)
+        mark(3)
+        j = 3
+        if scaled:
+            epl.epl_expert_scale(p, out, m_idx, cap, eo, ws)
+            j += 1
+            mark(j)
+        epl.epl_combine(p, eo, cap, oi, wt, out_code, y, ws)
+        mark(j + 1)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if epl.epl_status(ws) != epl.EPL_OK or int(total_host[0]) != N:
+        raise RuntimeError(f"dispatch failed: status {epl.epl_status(ws)}, total "
+                           f"{int(total_host[0])} != {N}")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    per_kernel_ms = {
+        n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+    assert epl.epl_status(ws) == epl.EPL_OK
+
+    # The same path through the fused entry point (layout + scan + scatter in
+    # one call), untimed by events, for reference.
+    def fused_step():
+        epl.epl_dispatch(p, topk, x, xs, cap, cnt, per_rank, in_rank, start, total_host, out,
+                         out_scale, m_idx, oi, ws)
+        if scaled:
+            epl.epl_expert_scale(p, out, m_idx, cap, eo, ws)
+        epl.epl_combine(p, eo, cap, oi, wt, out_code, y, ws)
+
+    for _ in range(args.warmup):
+        fused_step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        fused_step()
+    torch.cuda.synchronize()
+    fused_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+
+    nbytes = algorithmic_bytes(w, N, T_any, 4 if out_code == epl.EPL_OUT_F32 else 2)
+    gbps = {n: nbytes[n] / (per_kernel_ms[n] * 1e-3) / 1e9 for n in names}
+    dominant = max(("scatter", "combine"), key=lambda n: per_kernel_ms[n])
+    sc_ms = per_kernel_ms["scatter"] + per_kernel_ms["combine"]
+    sc_gbps = (nbytes["scatter"] + nbytes["combine"]) / (sc_ms * 1e-3) / 1e9
+    traffic = measured_traffic(w.name, dominant)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s, 1 thread)")
+        cpu = cpu_baseline(w, inp, args.cpu_seconds)
+
+    result = {
+        "metric": "routed token-rows/s (dispatch+combine)",
+        "value": N / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "num_tokens": T, "hidden": H, "num_experts": E, "num_topk": K,
+            "num_virtual_ranks": R, "scale_cols": S, "routing": w.routing,
+            "drop_rate": w.drop_rate, "expert_fn": w.expert_fn, "routed_rows": N,
+            "combine_out": args.out_dtype, "capacity_rows": cap,
+        },
+        "per_kernel_ms": per_kernel_ms,
+        "per_kernel_gbps": gbps,
+        "scatter_combine": {"ms": sc_ms, "gbps": sc_gbps, "frac_of_peak": sc_gbps / HBM_PEAK_GBPS},
+        "fused_dispatch_ms_per_step": fused_ms,
+        "roofline": {
+            "kernel": dominant,
+            "bound": "hbm",
+            "achieved": gbps[dominant],
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": gbps[dominant] / HBM_PEAK_GBPS,
+            "algorithmic_bytes": nbytes[dominant],
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

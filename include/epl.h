@@ -1,0 +1,185 @@
+/*
+ * epl.h -- C ABI of libepl.so: MoE expert-parallel token layout, dispatch
+ * into an expert-contiguous ragged buffer, and weighted combine, for one
+ * rank on an MI355X (gfx950) GPU.
+ *
+ * The calls follow the problem statement of the pages:
+ *   1. layout   -- per-expert / per-rank token counts and the token->rank
+ *                  mask, computed from topk_idx on the GPU
+ *                  ("[MoE] Deepseek的All-to-all通信: DeepEP代码解读", section
+ *                  Dispatch, get_dispatch_layout);
+ *   2. scan     -- exclusive prefix sum of the counts: where each expert's
+ *                  block starts and the exact buffer size
+ *                  ("高性能专家并行（EP）内核解剖学解读", high-throughput part,
+ *                  subsections 3 and 5);
+ *   3. scatter  -- copy each routed token row (and its scale row) into its
+ *                  expert's block, writing m_indices and output_index
+ *                  ("参考sglang代码，重构vllm021中EP高吞吐代码，消除空泡问题",
+ *                  sections 2.2 and 3.3, ep_scatter and its outputs);
+ *   4. combine  -- gather the expert-output rows back into token order as a
+ *                  top-k-weighted sum ("高性能专家并行（EP）内核解剖学解读",
+ *                  section 任务设定与数据流: results return to where the
+ *                  tokens came from; sglang section 2.2 keeps topk ids,
+ *                  weights and output_index for that step).
+ * epl_dispatch runs 1-3 in one call with no host round-trip.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensor arguments are DEVICE pointers to row-major, densely packed
+ *   arrays, except `total_host` (pinned host memory, see epl_scan).
+ * - The caller owns every buffer, including the workspace. The library
+ *   allocates no memory and keeps no global state between calls.
+ * - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *   enqueues work on that stream; none synchronises it except epl_status.
+ * - Return value: EPL_OK (0) or a negative EPL_E* code. Argument errors are
+ *   detected on the host before anything is enqueued (EPL_EINVAL).
+ *   Data errors that only the GPU can see (an expert id outside [-1, E), too
+ *   few capacity rows, an output_index beyond the expert output) are
+ *   recorded in a status word inside the workspace and returned by
+ *   epl_status; the offending slot is then treated as "no selection", and
+ *   nothing is ever written out of bounds.
+ * - Ownership of experts by virtual ranks: rank r owns the contiguous
+ *   experts [r*E/R, (r+1)*E/R); E must be a multiple of R.
+ * - Row order inside an expert's block: by token, then by top-k slot. The
+ *   result is therefore deterministic (bit-identical from run to run).
+ */
+#ifndef EPL_H
+#define EPL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define EPL_OK          0
+#define EPL_EINVAL    (-1)  /* bad problem, NULL or misaligned pointer, bad size */
+#define EPL_ERANGE    (-2)  /* device: a topk id outside [-1, E), or an
+                               output_index at or beyond expert_rows */
+#define EPL_ECAPACITY (-3)  /* device: routed rows exceed capacity_rows */
+#define EPL_EHIP      (-4)  /* a HIP runtime call or kernel launch failed */
+
+/* ---- combine output types ---------------------------------------------- */
+#define EPL_OUT_F32   0     /* y is float32 [T, H] */
+#define EPL_OUT_BF16  1     /* y is bf16 [T, H], round to nearest even of the f32 sum */
+
+/* ---- problem description ----------------------------------------------- */
+typedef struct epl_problem {
+    int64_t num_tokens;   /* T >= 0                                           */
+    int32_t num_topk;     /* K, 1 <= K <= 64                                  */
+    int32_t num_experts;  /* E, 1 <= E <= 2048                                */
+    int32_t num_ranks;    /* R >= 1, E % R == 0                               */
+    int32_t hidden;       /* H >= 8, H % 8 == 0 (16-byte rows of bf16)        */
+    int32_t scale_cols;   /* S: 0 (no scales) or H / 128 (needs H % 128 == 0) */
+    int32_t reserved;     /* must be 0                                        */
+} epl_problem;
+/* Also required: T * K <= INT32_MAX (row indices are int32). */
+
+/* Host-only check of a problem description. Needs no GPU. */
+int epl_validate(const epl_problem *p);
+
+/* Bytes of device workspace that the calls below need for problem `p`
+ * (0 if `p` is invalid). The workspace carries the per-block counts that
+ * make the row order deterministic, the per-slot ranks, the device copy of
+ * the total row count and the status word. It needs no initialisation;
+ * epl_layout / epl_dispatch write every byte that later calls read. Its
+ * address must be 256-byte aligned. Host-only; needs no GPU. */
+size_t epl_workspace_bytes(const epl_problem *p);
+
+/* Step 1 -- layout. Reads topk_idx [T, K] int64 (-1 = no selection).
+ * Writes num_tokens_per_expert [E] int32 (routed slots per expert),
+ * num_tokens_per_rank [R] int32 (tokens sent to each rank, a token counted
+ * once per rank however many of its experts live there) and
+ * is_token_in_rank [T, R] uint8 (1 if any valid slot of the token goes to
+ * the rank, else 0). Also fills the workspace for epl_scatter and resets
+ * the status word (bit for out-of-range ids set if any was seen; such an
+ * id counts as -1). */
+int epl_layout(const epl_problem *p, const int64_t *topk_idx,
+               int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,
+               uint8_t *is_token_in_rank, void *workspace, void *stream);
+
+/* Step 2 -- scan. expert_start_loc[e] = sum of num_tokens_per_expert[e'] for
+ * e' < e (exclusive, expert_start_loc[0] = 0); the total N = sum of all
+ * counts is stored in the workspace and, if `total_host` is not NULL, copied
+ * asynchronously to *total_host, which must be pinned host memory
+ * (hipHostMalloc / torch pin_memory). *total_host is valid once the stream
+ * has reached this point (after any later synchronisation of the stream). */
+int epl_scan(const epl_problem *p, const int32_t *num_tokens_per_expert,
+             int32_t *expert_start_loc, int32_t *total_host,
+             void *workspace, void *stream);
+
+/* Step 3 -- scatter. For every valid slot (t, k) with expert e:
+ *   row = expert_start_loc[e] + (number of valid slots of expert e that come
+ *         before (t, k) in (token, k) order)
+ *   out[row, :] = x[t, :] (bit copy, H bf16 values), out_scale[row, :] =
+ *   x_scale[t, :] (S floats) when S > 0, m_indices[row] = e,
+ *   output_index[t, k] = row. Slots with -1 get output_index = -1.
+ * `out` / `out_scale` / `m_indices` have room for `capacity_rows` rows
+ * (capacity_rows >= N; T * K always suffices); rows >= N are not written.
+ * If N > capacity_rows the rows past the capacity are skipped and the
+ * status word records EPL_ECAPACITY. Requires that epl_layout and then
+ * epl_scan (with the counts epl_layout produced) ran on the same
+ * workspace and stream. x / out: 16-byte aligned; x_scale / out_scale may be
+ * NULL iff S == 0. */
+int epl_scatter(const epl_problem *p, const uint16_t *x, const float *x_scale,
+                const int64_t *topk_idx, const int32_t *expert_start_loc,
+                void *workspace, int64_t capacity_rows,
+                uint16_t *out, float *out_scale, int32_t *m_indices,
+                int32_t *output_index, void *stream);
+
+/* Steps 1-3 in one call, all on `stream`, with no host wait between them:
+ * layout, scan (the total is copied to *total_host if it is not NULL) and
+ * scatter, with the arguments and results described above. */
+int epl_dispatch(const epl_problem *p, const int64_t *topk_idx,
+                 const uint16_t *x, const float *x_scale, int64_t capacity_rows,
+                 int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,
+                 uint8_t *is_token_in_rank, int32_t *expert_start_loc,
+                 int32_t *total_host, uint16_t *out, float *out_scale,
+                 int32_t *m_indices, int32_t *output_index,
+                 void *workspace, void *stream);
+
+/* Step 4 -- combine. For every token t:
+ *   y[t, :] = sum over k ascending with output_index[t, k] >= 0 of
+ *             topk_weights[t, k] * expert_out[output_index[t, k], :]
+ * accumulated in fp32 from +0 (a token with no valid slot gets zeros).
+ * expert_out is bf16 [expert_rows, H] (it may be the scatter's `out`);
+ * topk_weights is fp32 [T, K]; y is fp32 or bf16 [T, H] per `out_dtype`.
+ * An output_index >= expert_rows is skipped and, if `workspace` is not
+ * NULL, recorded as EPL_ERANGE in its status word. expert_out / y: 16-byte
+ * aligned. */
+int epl_combine(const epl_problem *p, const uint16_t *expert_out,
+                int64_t expert_rows, const int32_t *output_index,
+                const float *topk_weights, int out_dtype, void *y,
+                void *workspace, void *stream);
+
+/* The synthetic expert of the large-batch workload (not a step of the
+ * dispatch path; it stands in for the grouped GEMM between scatter and
+ * combine): rows_out[p, :] = bf16_rne(float(rows_in[p, :]) * (1 + m_indices[p]/256))
+ * for p < min(N, capacity_rows), N being the total that the last
+ * epl_scan / epl_dispatch on `workspace` stored. rows_in may equal rows_out. */
+int epl_expert_scale(const epl_problem *p, const uint16_t *rows_in,
+                     const int32_t *m_indices, int64_t capacity_rows,
+                     uint16_t *rows_out, const void *workspace, void *stream);
+
+/* Synchronises `stream`, then returns the status recorded in `workspace`
+ * since the last epl_layout / epl_dispatch: EPL_OK, EPL_ERANGE or
+ * EPL_ECAPACITY (EPL_ERANGE first if both occurred), or EPL_EHIP. */
+int epl_status(const void *workspace, void *stream);
+
+/* Synchronises `stream` and returns the total row count N stored in
+ * `workspace` by the last scan, or a negative EPL_E* code. */
+int64_t epl_total(const void *workspace, void *stream);
+
+/* Static text for a status code. */
+const char *epl_strerror(int code);
+
+/* Library version, e.g. 0x000100 for 0.1.0. */
+int epl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EPL_H */

@@ -1,0 +1,380 @@
+// libepl.so host side: argument validation, workspace carving and kernel
+// launches for the C ABI declared in include/epl.h. Every entry point
+// checks its arguments on the host before it enqueues anything, then only
+// enqueues on the caller's stream (epl_status / epl_total synchronise it).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cstddef>
+#include <cstdint>
+
+#include "epl.h"
+#include "epl_kernels.h"
+
+namespace {
+
+using epl::WsHeader;
+
+constexpr size_t kWsAlign = 256;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool problem_ok(const epl_problem *p)
+{
+    if (!p)
+        return false;
+    if (p->num_tokens < 0 || p->num_topk < 1 || p->num_topk > epl::kMaxTopk)
+        return false;
+    if (p->num_experts < 1 || p->num_experts > epl::kMaxExperts)
+        return false;
+    if (p->num_ranks < 1 || p->num_ranks > p->num_experts || p->num_experts % p->num_ranks != 0)
+        return false;
+    if (p->hidden < 8 || p->hidden % 8 != 0)
+        return false;
+    if (p->scale_cols != 0 && (p->hidden % 128 != 0 || p->scale_cols != p->hidden / 128))
+        return false;
+    if (p->reserved != 0)
+        return false;
+    if (p->num_tokens * (int64_t)p->num_topk > (int64_t)INT32_MAX)
+        return false;
+    return true;
+}
+
+// Tokens per layout block: enough blocks to spread the work (about 64), but
+// at most 256 tokens (one per thread) and at most 2048 slots (the LDS key
+// buffer), and at least 16 tokens so the per-block count matrix stays small.
+int layout_block_tokens(const epl_problem &p)
+{
+    const int64_t cap = std::min<int64_t>(epl::kLayoutThreads, epl::kMaxSlotsPerBlock / p.num_topk);
+    int64_t want = (p.num_tokens + 63) / 64;
+    want = std::max<int64_t>(16, want);
+    return (int)std::min<int64_t>(want, cap);
+}
+
+struct WsLayout {
+    int block_tokens;
+    int64_t num_blocks;
+    size_t block_count, block_rank, block_err, slot_rank, bytes;
+};
+
+WsLayout ws_layout(const epl_problem &p)
+{
+    WsLayout w{};
+    w.block_tokens = layout_block_tokens(p);
+    w.num_blocks = (p.num_tokens + w.block_tokens - 1) / w.block_tokens;
+    size_t off = round_up(sizeof(WsHeader), kWsAlign);
+    w.block_count = off;
+    off += round_up((size_t)w.num_blocks * (size_t)p.num_experts * 4, kWsAlign);
+    w.block_rank = off;
+    off += round_up((size_t)w.num_blocks * (size_t)p.num_ranks * 4, kWsAlign);
+    w.block_err = off;
+    off += round_up((size_t)w.num_blocks * 4, kWsAlign);
+    w.slot_rank = off;
+    off += round_up((size_t)p.num_tokens * (size_t)p.num_topk * 4, kWsAlign);
+    w.bytes = off;
+    return w;
+}
+
+template <typename T>
+T *at(void *ws, size_t off)
+{
+    return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+size_t layout_lds_bytes(const epl_problem &p, int block_tokens)
+{
+    return sizeof(int32_t) * ((size_t)2 * block_tokens * p.num_topk +
+                              (size_t)epl::kLayoutWaves * p.num_experts + p.num_ranks + 1);
+}
+
+int launch_status() { return hipGetLastError() == hipSuccess ? EPL_OK : EPL_EHIP; }
+
+int enqueue_layout(const epl_problem &p, const WsLayout &w, const int64_t *topk, uint8_t *in_rank,
+                   void *ws, hipStream_t s)
+{
+    if (w.num_blocks == 0)
+        return EPL_OK;
+    const bool vec16 = (p.num_ranks % 16 == 0) && aligned(in_rank, 16);
+    hipLaunchKernelGGL(epl::ep_layout_kernel, dim3((unsigned)w.num_blocks), dim3(epl::kLayoutThreads),
+                       layout_lds_bytes(p, w.block_tokens), s, topk, p.num_tokens, p.num_topk,
+                       p.num_experts, p.num_ranks, p.num_experts / p.num_ranks, w.block_tokens,
+                       in_rank, vec16, at<int32_t>(ws, w.block_count), at<int32_t>(ws, w.block_rank),
+                       at<uint32_t>(ws, w.block_err), at<int32_t>(ws, w.slot_rank));
+    return launch_status();
+}
+
+int enqueue_scan(const epl_problem &p, const WsLayout &w, int mode, int32_t *cnt, int32_t *per_rank,
+                 int32_t *start, int32_t *total_host, void *ws, hipStream_t s)
+{
+    hipLaunchKernelGGL(epl::ep_scan_kernel, dim3(1), dim3(epl::kScanThreads), 0, s, mode,
+                       w.num_blocks, p.num_experts, p.num_ranks, at<int32_t>(ws, w.block_count),
+                       at<int32_t>(ws, w.block_rank), at<uint32_t>(ws, w.block_err), cnt, per_rank,
+                       start, at<WsHeader>(ws, 0));
+    int rc = launch_status();
+    if (rc != EPL_OK)
+        return rc;
+    if ((mode & epl::kScanPrefix) && total_host) {
+        if (hipMemcpyAsync(total_host, &at<WsHeader>(ws, 0)->total, sizeof(int32_t),
+                           hipMemcpyDeviceToHost, s) != hipSuccess)
+            return EPL_EHIP;
+    }
+    return EPL_OK;
+}
+
+template <int VPT>
+void launch_scatter(const epl_problem &p, const WsLayout &w, const uint16_t *x, const float *xs,
+                    const int64_t *topk, const int32_t *start, void *ws, int64_t cap,
+                    uint16_t *out, float *out_scale, int32_t *m_idx, int32_t *oi, hipStream_t s)
+{
+    hipLaunchKernelGGL(epl::ep_scatter_kernel<VPT>, dim3((unsigned)p.num_tokens),
+                       dim3(epl::kRowThreads), 0, s, x, xs, topk, start,
+                       at<const int32_t>(ws, w.block_count), at<const int32_t>(ws, w.slot_rank),
+                       p.num_topk, p.num_experts, p.hidden, p.scale_cols, w.block_tokens, cap,
+                       out, out_scale, m_idx, oi, &at<WsHeader>(ws, 0)->status);
+}
+
+int enqueue_scatter(const epl_problem &p, const WsLayout &w, const uint16_t *x, const float *xs,
+                    const int64_t *topk, const int32_t *start, void *ws, int64_t cap,
+                    uint16_t *out, float *out_scale, int32_t *m_idx, int32_t *oi, hipStream_t s)
+{
+    if (p.num_tokens == 0)
+        return EPL_OK;
+    const int nvec = p.hidden / 8;
+    const int vpt = std::min(8, (nvec + epl::kRowThreads - 1) / epl::kRowThreads);
+    switch (vpt) {
+#define EPL_SCATTER_CASE(V)                                                                        \
+    case V:                                                                                        \
+        launch_scatter<V>(p, w, x, xs, topk, start, ws, cap, out, out_scale, m_idx, oi, s);       \
+        break;
+        EPL_SCATTER_CASE(1)
+        EPL_SCATTER_CASE(2)
+        EPL_SCATTER_CASE(3)
+        EPL_SCATTER_CASE(4)
+        EPL_SCATTER_CASE(5)
+        EPL_SCATTER_CASE(6)
+        EPL_SCATTER_CASE(7)
+        EPL_SCATTER_CASE(8)
+#undef EPL_SCATTER_CASE
+    default:
+        return EPL_EINVAL;
+    }
+    return launch_status();
+}
+
+bool scatter_args_ok(const epl_problem &p, const uint16_t *x, const float *xs,
+                     const int64_t *topk, int64_t cap, uint16_t *out, float *out_scale,
+                     int32_t *m_idx, int32_t *oi)
+{
+    const bool any_tokens = p.num_tokens > 0;
+    if (cap < 0)
+        return false;
+    if (any_tokens && (!topk || !aligned(topk, 8) || !oi || !aligned(oi, 4) || !x ||
+                       !aligned(x, 16)))
+        return false;
+    if (cap > 0 && (!out || !aligned(out, 16) || !m_idx || !aligned(m_idx, 4)))
+        return false;
+    if (p.scale_cols > 0) {
+        if (any_tokens && (!xs || !aligned(xs, 4)))
+            return false;
+        if (cap > 0 && (!out_scale || !aligned(out_scale, 4)))
+            return false;
+    }
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int epl_version(void) { return 0x000100; }
+
+int epl_validate(const epl_problem *p) { return problem_ok(p) ? EPL_OK : EPL_EINVAL; }
+
+size_t epl_workspace_bytes(const epl_problem *p)
+{
+    if (!problem_ok(p))
+        return 0;
+    return ws_layout(*p).bytes;
+}
+
+const char *epl_strerror(int code)
+{
+    switch (code) {
+    case EPL_OK:
+        return "success";
+    case EPL_EINVAL:
+        return "invalid argument (problem, pointer, alignment or size)";
+    case EPL_ERANGE:
+        return "index out of range (topk id outside [-1, E) or output_index beyond expert rows)";
+    case EPL_ECAPACITY:
+        return "routed rows exceed the capacity of the output buffers";
+    case EPL_EHIP:
+        return "HIP runtime error";
+    default:
+        return "unknown status code";
+    }
+}
+
+int epl_layout(const epl_problem *p, const int64_t *topk_idx, int32_t *num_tokens_per_expert,
+               int32_t *num_tokens_per_rank, uint8_t *is_token_in_rank, void *workspace,
+               void *stream)
+{
+    if (!problem_ok(p))
+        return EPL_EINVAL;
+    if (!workspace || !aligned(workspace, kWsAlign) || !num_tokens_per_expert ||
+        !aligned(num_tokens_per_expert, 4) || !num_tokens_per_rank || !aligned(num_tokens_per_rank, 4))
+        return EPL_EINVAL;
+    if (p->num_tokens > 0 && (!topk_idx || !aligned(topk_idx, 8) || !is_token_in_rank))
+        return EPL_EINVAL;
+    const WsLayout w = ws_layout(*p);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int rc = enqueue_layout(*p, w, topk_idx, is_token_in_rank, workspace, s);
+    if (rc != EPL_OK)
+        return rc;
+    return enqueue_scan(*p, w, epl::kScanReduce, num_tokens_per_expert, num_tokens_per_rank,
+                        nullptr, nullptr, workspace, s);
+}
+
+int epl_scan(const epl_problem *p, const int32_t *num_tokens_per_expert, int32_t *expert_start_loc,
+             int32_t *total_host, void *workspace, void *stream)
+{
+    if (!problem_ok(p))
+        return EPL_EINVAL;
+    if (!workspace || !aligned(workspace, kWsAlign) || !num_tokens_per_expert ||
+        !aligned(num_tokens_per_expert, 4) || !expert_start_loc || !aligned(expert_start_loc, 4) ||
+        (total_host && !aligned(total_host, 4)))
+        return EPL_EINVAL;
+    const WsLayout w = ws_layout(*p);
+    return enqueue_scan(*p, w, epl::kScanPrefix, const_cast<int32_t *>(num_tokens_per_expert),
+                        nullptr, expert_start_loc, total_host, workspace,
+                        static_cast<hipStream_t>(stream));
+}
+
+int epl_scatter(const epl_problem *p, const uint16_t *x, const float *x_scale,
+                const int64_t *topk_idx, const int32_t *expert_start_loc, void *workspace,
+                int64_t capacity_rows, uint16_t *out, float *out_scale, int32_t *m_indices,
+                int32_t *output_index, void *stream)
+{
+    if (!problem_ok(p))
+        return EPL_EINVAL;
+    if (!workspace || !aligned(workspace, kWsAlign) || !expert_start_loc ||
+        !aligned(expert_start_loc, 4))
+        return EPL_EINVAL;
+    if (!scatter_args_ok(*p, x, x_scale, topk_idx, capacity_rows, out, out_scale, m_indices,
+                         output_index))
+        return EPL_EINVAL;
+    const WsLayout w = ws_layout(*p);
+    return enqueue_scatter(*p, w, x, x_scale, topk_idx, expert_start_loc, workspace, capacity_rows,
+                           out, out_scale, m_indices, output_index, static_cast<hipStream_t>(stream));
+}
+
+int epl_dispatch(const epl_problem *p, const int64_t *topk_idx, const uint16_t *x,
+                 const float *x_scale, int64_t capacity_rows, int32_t *num_tokens_per_expert,
+                 int32_t *num_tokens_per_rank, uint8_t *is_token_in_rank,
+                 int32_t *expert_start_loc, int32_t *total_host, uint16_t *out, float *out_scale,
+                 int32_t *m_indices, int32_t *output_index, void *workspace, void *stream)
+{
+    if (!problem_ok(p))
+        return EPL_EINVAL;
+    if (!workspace || !aligned(workspace, kWsAlign) || !num_tokens_per_expert ||
+        !aligned(num_tokens_per_expert, 4) || !num_tokens_per_rank ||
+        !aligned(num_tokens_per_rank, 4) || !expert_start_loc || !aligned(expert_start_loc, 4) ||
+        (total_host && !aligned(total_host, 4)))
+        return EPL_EINVAL;
+    if (p->num_tokens > 0 && !is_token_in_rank)
+        return EPL_EINVAL;
+    if (!scatter_args_ok(*p, x, x_scale, topk_idx, capacity_rows, out, out_scale, m_indices,
+                         output_index))
+        return EPL_EINVAL;
+    const WsLayout w = ws_layout(*p);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int rc = enqueue_layout(*p, w, topk_idx, is_token_in_rank, workspace, s);
+    if (rc == EPL_OK)
+        rc = enqueue_scan(*p, w, epl::kScanReduce | epl::kScanPrefix, num_tokens_per_expert,
+                          num_tokens_per_rank, expert_start_loc, total_host, workspace, s);
+    if (rc == EPL_OK)
+        rc = enqueue_scatter(*p, w, x, x_scale, topk_idx, expert_start_loc, workspace,
+                             capacity_rows, out, out_scale, m_indices, output_index, s);
+    return rc;
+}
+
+int epl_combine(const epl_problem *p, const uint16_t *expert_out, int64_t expert_rows,
+                const int32_t *output_index, const float *topk_weights, int out_dtype, void *y,
+                void *workspace, void *stream)
+{
+    if (!problem_ok(p))
+        return EPL_EINVAL;
+    if (out_dtype != EPL_OUT_F32 && out_dtype != EPL_OUT_BF16)
+        return EPL_EINVAL;
+    if (expert_rows < 0 || (workspace && !aligned(workspace, kWsAlign)))
+        return EPL_EINVAL;
+    if (p->num_tokens == 0)
+        return EPL_OK;
+    if (!output_index || !aligned(output_index, 4) || !topk_weights || !aligned(topk_weights, 4) ||
+        !y || !aligned(y, 16) || (expert_rows > 0 && (!expert_out || !aligned(expert_out, 16))))
+        return EPL_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t *status = workspace ? &at<WsHeader>(workspace, 0)->status : nullptr;
+    if (out_dtype == EPL_OUT_BF16)
+        hipLaunchKernelGGL(epl::ep_combine_kernel<true>, dim3((unsigned)p->num_tokens),
+                           dim3(epl::kRowThreads), 0, s, expert_out, expert_rows, output_index,
+                           topk_weights, p->num_topk, p->hidden, y, status);
+    else
+        hipLaunchKernelGGL(epl::ep_combine_kernel<false>, dim3((unsigned)p->num_tokens),
+                           dim3(epl::kRowThreads), 0, s, expert_out, expert_rows, output_index,
+                           topk_weights, p->num_topk, p->hidden, y, status);
+    return launch_status();
+}
+
+int epl_expert_scale(const epl_problem *p, const uint16_t *rows_in, const int32_t *m_indices,
+                     int64_t capacity_rows, uint16_t *rows_out, const void *workspace,
+                     void *stream)
+{
+    if (!problem_ok(p) || capacity_rows < 0 || !workspace || !aligned(workspace, kWsAlign))
+        return EPL_EINVAL;
+    if (capacity_rows == 0)
+        return EPL_OK;
+    if (!rows_in || !aligned(rows_in, 16) || !rows_out || !aligned(rows_out, 16) || !m_indices ||
+        !aligned(m_indices, 4))
+        return EPL_EINVAL;
+    const unsigned grid = (unsigned)std::min<int64_t>(capacity_rows, 1 << 16);
+    hipLaunchKernelGGL(epl::ep_expert_scale_kernel, dim3(grid), dim3(epl::kRowThreads), 0,
+                       static_cast<hipStream_t>(stream), rows_in, m_indices, capacity_rows,
+                       static_cast<const WsHeader *>(workspace), p->hidden, rows_out);
+    return launch_status();
+}
+
+int epl_status(const void *workspace, void *stream)
+{
+    if (!workspace || !aligned(workspace, kWsAlign))
+        return EPL_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t st = 0;
+    if (hipMemcpyAsync(&st, &static_cast<const WsHeader *>(workspace)->status, sizeof st,
+                       hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return EPL_EHIP;
+    if (st & (epl::kStatusBadExpert | epl::kStatusBadRow))
+        return EPL_ERANGE;
+    if (st & epl::kStatusCapacity)
+        return EPL_ECAPACITY;
+    return EPL_OK;
+}
+
+int64_t epl_total(const void *workspace, void *stream)
+{
+    if (!workspace || !aligned(workspace, kWsAlign))
+        return EPL_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t total = 0;
+    if (hipMemcpyAsync(&total, &static_cast<const WsHeader *>(workspace)->total, sizeof total,
+                       hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return EPL_EHIP;
+    return total;
+}
+
+}  // extern "C"

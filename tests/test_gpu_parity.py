@@ -1,0 +1,416 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Layout, scan, m_indices, output_index, scattered rows and scale rows must be
+bit-exact. Combine (fp32 accumulation) must satisfy, element by element,
+    |y_gpu - y_oracle| <= 1e-5 * sum_k |w[t,k]| * |v_k|
+where y_oracle is the fp64 sum and the right-hand side is the same sum over
+absolute values (also computed by the oracle): "1e-5 relative" measured
+against the size of the terms, so cancellation cannot make it meaningless.
+bf16 combine output must be within half a bf16 ulp of that (RNE of the fp32
+sum). Output buffers are poisoned before every call so that a slot the
+kernels forget to write cannot pass.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import permute_ep_layout_amd as epl  # noqa: E402
+from permute_ep_layout_amd import workloads  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+POISON = 0x5A
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    epl.load()
+
+
+DEV = torch.device("cuda:0")
+ORC = None
+
+
+def orc():
+    global ORC
+    if ORC is None:
+        ORC = oracle.default()
+    return ORC
+
+
+def to_bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def u16(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def poisoned(shape, dtype, byte=POISON):
+    t = torch.empty(shape, dtype=dtype, device=DEV)
+    t.view(torch.uint8).fill_(byte)
+    return t
+
+
+def gpu_dispatch(topk, x, xs, E, R, cap=None, byte=POISON, stream=None, split=False):
+    """Run dispatch through the C ABI on poisoned buffers; returns tensors."""
+    T, K = topk.shape
+    H = x.shape[1]
+    S = 0 if xs is None else xs.shape[1]
+    p = epl.Problem.make(T, K, E, R, H, S)
+    cap = T * K if cap is None else cap
+    ws = poisoned(epl.epl_workspace_bytes(p), torch.uint8, byte)
+    r = dict(
+        cnt=poisoned(E, torch.int32, byte), per_rank=poisoned(R, torch.int32, byte),
+        in_rank=poisoned((T, R), torch.uint8, byte), start=poisoned(E, torch.int32, byte),
+        out=poisoned((cap, H), torch.bfloat16, byte),
+        out_scale=poisoned((cap, S), torch.float32, byte) if S else None,
+        m=poisoned(cap, torch.int32, byte), oi=poisoned((T, K), torch.int32, byte),
+        total_host=torch.full((1,), -7, dtype=torch.int32).pin_memory(), ws=ws, p=p, cap=cap)
+    tk = torch.from_numpy(topk).to(DEV)
+    xd = to_bf16(x)
+    xsd = None if xs is None else torch.from_numpy(xs).to(DEV)
+    if split:
+        epl.epl_layout(p, tk, r["cnt"], r["per_rank"], r["in_rank"], ws, stream)
+        epl.epl_scan(p, r["cnt"], r["start"], r["total_host"], ws, stream)
+        epl.epl_scatter(p, xd, xsd, tk, r["start"], ws, cap, r["out"], r["out_scale"], r["m"],
+                        r["oi"], stream)
+    else:
+        epl.epl_dispatch(p, tk, xd, xsd, cap, r["cnt"], r["per_rank"], r["in_rank"], r["start"],
+                         r["total_host"], r["out"], r["out_scale"], r["m"], r["oi"], ws, stream)
+    r["x"], r["topk"] = xd, tk
+    return r
+
+
+def gpu_combine(r, eo, w, out_dtype, byte=POISON, stream=None):
+    T, K = r["oi"].shape
+    H = eo.shape[1]
+    p = epl.Problem.make(T, K, r["p"].num_experts, r["p"].num_ranks, H, 0)
+    y = poisoned((T, H), torch.float32 if out_dtype == epl.EPL_OUT_F32 else torch.bfloat16, byte)
+    wd = torch.from_numpy(w).to(DEV)
+    epl.epl_combine(p, eo, eo.shape[0], r["oi"], wd, out_dtype, y, r["ws"], stream)
+    return y
+
+
+def check_layout_and_scatter(r, ref, x, xs):
+    torch.cuda.synchronize()
+    N = ref["total"]
+    assert int(r["total_host"][0]) == N
+    assert epl.epl_total(r["ws"]) == N
+    np.testing.assert_array_equal(r["cnt"].cpu().numpy(), ref["num_tokens_per_expert"])
+    np.testing.assert_array_equal(r["per_rank"].cpu().numpy(), ref["num_tokens_per_rank"])
+    np.testing.assert_array_equal(r["in_rank"].cpu().numpy(), ref["is_token_in_rank"])
+    np.testing.assert_array_equal(r["start"].cpu().numpy(), ref["expert_start_loc"])
+    np.testing.assert_array_equal(r["oi"].cpu().numpy(), ref["output_index"])
+    np.testing.assert_array_equal(r["m"][:N].cpu().numpy(), ref["m_indices"])
+    if ref.get("out") is not None:
+        np.testing.assert_array_equal(u16(r["out"][:N]), ref["out"])
+    if xs is not None:
+        np.testing.assert_array_equal(r["out_scale"][:N].cpu().numpy().view(np.uint32),
+                                      ref["out_scale"].view(np.uint32))
+
+
+def combine_bound(eo_u16, oi, w, tokens=None):
+    return orc().combine(eo_u16 & np.uint16(0x7FFF), oi, np.abs(w), tokens=tokens)
+
+
+def check_combine_f32(y_gpu, y_ref, bound):
+    d = np.abs(y_gpu.astype(np.float64) - y_ref)
+    bad = d > 1e-5 * bound
+    assert not bad.any(), (f"{bad.sum()} elements beyond 1e-5 * sum|w v|; worst excess "
+                           f"{(d - 1e-5 * bound).max():.3e}")
+
+
+def check_combine_bf16(y_gpu_u16, y_ref, bound):
+    yg = (y_gpu_u16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    eps = 1e-5 * bound
+    lim = 2.0 ** -8 * (np.abs(y_ref) + eps) + eps
+    bad = np.abs(yg - y_ref) > lim
+    assert not bad.any(), f"{bad.sum()} bf16 elements beyond half an ulp of the fp32 bound"
+
+
+def full_parity(w: workloads.Workload, inp=None, split=False):
+    inp = inp or workloads.make_inputs(w)
+    topk, x, xs, wt = inp["topk_idx"], inp["x"], inp["x_scale"], inp["topk_weights"]
+    E, R = w.num_experts, w.num_ranks
+    ref = orc().run_all(x, xs, topk, wt, E, R, expert_fn=w.expert_fn)
+    r = gpu_dispatch(topk, x, xs, E, R, split=split)
+    assert epl.epl_status(r["ws"]) == epl.EPL_OK
+    check_layout_and_scatter(r, ref, x, xs)
+    N = ref["total"]
+    if w.expert_fn == "identity":
+        eo = r["out"]
+    else:
+        eo = torch.empty_like(r["out"])
+        epl.epl_expert_scale(r["p"], r["out"], r["m"], r["cap"], eo, r["ws"])
+        np.testing.assert_array_equal(u16(eo[:N]), ref["expert_out"])
+    y = gpu_combine(r, eo, wt, epl.EPL_OUT_F32)
+    yb = gpu_combine(r, eo, wt, epl.EPL_OUT_BF16)
+    bound = combine_bound(ref["expert_out"], ref["output_index"], wt)
+    check_combine_f32(y.cpu().numpy(), ref["y"], bound)
+    check_combine_bf16(u16(yb), ref["y"], bound)
+    assert epl.epl_status(r["ws"]) == epl.EPL_OK
+    return r, y
+
+
+# ------------------------------------------------------------ workloads --
+
+@pytest.mark.parametrize("name", ["tiny", "small", "dsv3", "skew"])
+def test_workload_full_parity(name):
+    print(f"[parity] workload={name}", flush=True)
+    full_parity(workloads.get(name))
+
+
+def test_dsv3_split_calls_match_oracle():
+    full_parity(workloads.get("dsv3").with_(num_tokens=1500), split=True)
+
+
+def test_deterministic_bitwise_repeat():
+    w = workloads.get("dsv3").with_(num_tokens=2000)
+    inp = workloads.make_inputs(w)
+    a = gpu_dispatch(inp["topk_idx"], inp["x"], inp["x_scale"], w.num_experts, w.num_ranks,
+                     byte=0x5A)
+    b = gpu_dispatch(inp["topk_idx"], inp["x"], inp["x_scale"], w.num_experts, w.num_ranks,
+                     byte=0xA5)
+    torch.cuda.synchronize()
+    N = int(a["total_host"][0])
+    for key in ("cnt", "per_rank", "in_rank", "start", "oi"):
+        assert torch.equal(a[key], b[key]), key
+    for key in ("out", "out_scale", "m"):
+        assert torch.equal(a[key][:N].view(torch.uint8), b[key][:N].view(torch.uint8)), key
+    ya = gpu_combine(a, a["out"], inp["topk_weights"], epl.EPL_OUT_F32)
+    yb = gpu_combine(b, b["out"], inp["topk_weights"], epl.EPL_OUT_F32, byte=0xA5)
+    assert torch.equal(ya.view(torch.int32), yb.view(torch.int32))
+
+
+def test_large_batch_sampled_parity():
+    """The 65536-token workload at full size: indices compared in full, rows
+    compared in full through the oracle's index map, the expert stand-in and
+    combine compared on sampled rows / tokens that the oracle computes one by
+    one."""
+    w = workloads.get("large")
+    print("[parity] workload=large (generating inputs)", flush=True)
+    topk = workloads.make_topk(w)
+    wt = workloads.make_weights(w, topk)
+    x = workloads.make_x(w)
+    E, R, T, K, H = w.num_experts, w.num_ranks, w.num_tokens, w.num_topk, w.hidden
+    cnt, per_rank, in_rank = orc().layout(topk, E, R)
+    start, N = orc().scan(cnt)
+    _, _, m_ref, oi_ref = orc().scatter(None, None, topk, start, N, copy_rows=False)
+    ref = dict(num_tokens_per_expert=cnt, num_tokens_per_rank=per_rank, is_token_in_rank=in_rank,
+               expert_start_loc=start, total=N, m_indices=m_ref, output_index=oi_ref)
+    r = gpu_dispatch(topk, x, None, E, R)
+    eo = torch.empty_like(r["out"])
+    epl.epl_expert_scale(r["p"], r["out"], r["m"], r["cap"], eo, r["ws"])
+    y = gpu_combine(r, eo, wt, epl.EPL_OUT_F32)
+    assert epl.epl_status(r["ws"]) == epl.EPL_OK
+    check_layout_and_scatter(r, ref, x, None)
+    # every scattered row against the token the oracle placed there
+    tt, kk = np.nonzero(topk >= 0)
+    src = np.empty(N, np.int64)
+    src[oi_ref[tt, kk]] = tt
+    src_d = torch.from_numpy(src).to(DEV)
+    xd = r["x"].view(torch.int16)
+    outd = r["out"].view(torch.int16)
+    for p0 in range(0, N, 1 << 16):
+        p1 = min(N, p0 + (1 << 16))
+        assert torch.equal(outd[p0:p1], xd[src_d[p0:p1]]), f"rows {p0}:{p1}"
+    # expert stand-in on sampled rows
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(N, 4096, replace=False))
+    want = orc().expert_scale(x[src[rows]], m_ref[rows])
+    np.testing.assert_array_equal(u16(eo[torch.from_numpy(rows).to(DEV)]), want)
+    # combine on sampled tokens: a sub-problem holding only their rows
+    toks = np.sort(rng.choice(T, 512, replace=False))
+    sub_oi = -np.ones((toks.size, K), np.int32)
+    sub_rows, sub_m = [], []
+    for i, t in enumerate(toks):
+        for k in range(K):
+            if oi_ref[t, k] >= 0:
+                sub_oi[i, k] = len(sub_rows)
+                sub_rows.append(t)
+                sub_m.append(m_ref[oi_ref[t, k]])
+    sub_eo = orc().expert_scale(x[np.array(sub_rows)], np.array(sub_m, np.int32))
+    y_ref = orc().combine(sub_eo, sub_oi, wt[toks])
+    bound = combine_bound(sub_eo, sub_oi, wt[toks])
+    check_combine_f32(y[torch.from_numpy(toks).to(DEV)].cpu().numpy(), y_ref, bound)
+
+
+# ----------------------------------------------------------- ragged shapes --
+
+RAGGED = [
+    # name, T, K, E, R, H, scales, drop
+    ("ragged_tail_h264", 1001, 5, 24, 6, 264, False, 0.1),
+    ("two_passes_h9000", 333, 3, 16, 4, 9000, False, 0.0),
+    ("scales_s70", 517, 4, 32, 8, 8960, True, 0.05),
+    ("scales_s3", 250, 6, 40, 10, 384, True, 0.2),
+    ("k64_e128", 100, 64, 128, 16, 64, False, 0.1),
+    ("e2048_r2048", 300, 8, 2048, 2048, 64, False, 0.0),
+    ("r1", 700, 8, 64, 1, 128, False, 0.0),
+    ("k1", 900, 1, 8, 8, 136, False, 0.0),
+    ("e1", 64, 1, 1, 1, 8, False, 0.3),
+    ("r_not_mult16", 400, 4, 36, 12, 96, False, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=[c[0] for c in RAGGED])
+def test_ragged_shapes(case):
+    name, T, K, E, R, H, scales, drop = case
+    print(f"[parity] ragged case={name}", flush=True)
+    w = workloads.Workload(name, seed=77, num_tokens=T, hidden=H, num_experts=E, num_topk=K,
+                           num_ranks=R, scales=scales, routing="uniform", drop_rate=drop)
+    full_parity(w)
+
+
+# ------------------------------------------------------------- edge cases --
+
+def _mk(topk, H=64, seed=0, scales=False):
+    rng = np.random.default_rng(seed)
+    T = topk.shape[0]
+    x = workloads.fp32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    xs = rng.uniform(0.01, 1, (T, H // 128)).astype(np.float32) if scales else None
+    wt = rng.uniform(0, 1, topk.shape).astype(np.float32)
+    return x, xs, wt
+
+
+def _edge(topk, E, R, H=64, scales=False, seed=0):
+    x, xs, wt = _mk(topk, H, seed, scales)
+    ref = orc().run_all(x, xs, topk, wt, E, R)
+    r = gpu_dispatch(topk, x, xs, E, R)
+    assert epl.epl_status(r["ws"]) == epl.EPL_OK
+    check_layout_and_scatter(r, ref, x, xs)
+    y = gpu_combine(r, r["out"], wt, epl.EPL_OUT_F32)
+    check_combine_f32(y.cpu().numpy(), ref["y"], combine_bound(ref["expert_out"],
+                                                                ref["output_index"], wt))
+    return r, ref, y
+
+
+def test_zero_tokens():
+    topk = np.zeros((0, 4), np.int64)
+    r, ref, y = _edge(topk, 16, 4)
+    assert ref["total"] == 0 and y.shape == (0, 64)
+
+
+def test_all_slots_invalid():
+    topk = -np.ones((300, 4), np.int64)
+    r, ref, y = _edge(topk, 16, 4)
+    assert (r["oi"] == -1).all() and (y == 0).all()
+
+
+def test_duplicate_experts_within_a_token():
+    rng = np.random.default_rng(5)
+    topk = rng.integers(-1, 4, size=(500, 6)).astype(np.int64)
+    _edge(topk, 4, 2)
+
+
+def test_k1_weight1_returns_x_exactly():
+    rng = np.random.default_rng(6)
+    T, H = 777, 256
+    topk = rng.integers(0, 32, size=(T, 1)).astype(np.int64)
+    x, _, _ = _mk(topk, H)
+    r = gpu_dispatch(topk, x, None, 32, 8)
+    y = gpu_combine(r, r["out"], np.ones((T, 1), np.float32), epl.EPL_OUT_F32)
+    yb = gpu_combine(r, r["out"], np.ones((T, 1), np.float32), epl.EPL_OUT_BF16)
+    xf = (x.astype(np.uint32) << 16).view(np.float32)
+    np.testing.assert_array_equal(y.cpu().numpy(), xf)
+    np.testing.assert_array_equal(u16(yb), x)
+
+
+def test_out_of_range_ids_flagged_and_ignored():
+    rng = np.random.default_rng(7)
+    E, R = 16, 4
+    topk = rng.integers(-1, E, size=(400, 3)).astype(np.int64)
+    topk[3, 1] = E
+    topk[77, 0] = 1 << 40
+    topk[200, 2] = -5
+    x, xs, wt = _mk(topk)
+    clean = np.where((topk < -1) | (topk >= E), -1, topk)
+    ref = orc().run_all(x, xs, clean, wt, E, R)
+    r = gpu_dispatch(topk, x, xs, E, R)
+    assert epl.epl_status(r["ws"]) == epl.EPL_ERANGE
+    check_layout_and_scatter(r, ref, x, xs)
+    # the status resets on the next layout over clean ids
+    r2 = gpu_dispatch(clean, x, xs, E, R)
+    assert epl.epl_status(r2["ws"]) == epl.EPL_OK
+
+
+def test_capacity_overflow_flagged_without_out_of_bounds_writes():
+    rng = np.random.default_rng(8)
+    E, R, T, K, H = 8, 2, 200, 4, 64
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    x, _, wt = _mk(topk, H)
+    ref = orc().run_all(x, None, topk, wt, E, R)
+    N = ref["total"]
+    cap, guard = N - 37, 64
+    p = epl.Problem.make(T, K, E, R, H, 0)
+    ws = poisoned(epl.epl_workspace_bytes(p), torch.uint8)
+    out_full = poisoned((cap + guard, H), torch.bfloat16)
+    m_full = poisoned(cap + guard, torch.int32)
+    out, m = out_full[:cap], m_full[:cap]
+    cnt, per_rank = poisoned(E, torch.int32), poisoned(R, torch.int32)
+    in_rank, start = poisoned((T, R), torch.uint8), poisoned(E, torch.int32)
+    oi = poisoned((T, K), torch.int32)
+    epl.epl_dispatch(p, torch.from_numpy(topk).to(DEV), to_bf16(x), None, cap, cnt, per_rank,
+                     in_rank, start, None, out, None, m, oi, ws)
+    assert epl.epl_status(ws) == epl.EPL_ECAPACITY
+    np.testing.assert_array_equal(oi.cpu().numpy(), ref["output_index"])
+    np.testing.assert_array_equal(u16(out), ref["out"][:cap])
+    np.testing.assert_array_equal(m.cpu().numpy(), ref["m_indices"][:cap])
+    assert (out_full[cap:].view(torch.uint8) == POISON).all()
+    assert (m_full[cap:].view(torch.uint8) == POISON).all()
+
+
+def test_combine_flags_row_beyond_expert_output():
+    T, K, H = 10, 2, 64
+    rng = np.random.default_rng(9)
+    eo = workloads.fp32_to_bf16_bits(rng.standard_normal((20, H), dtype=np.float32))
+    oi = rng.integers(-1, 20, size=(T, K)).astype(np.int32)
+    oi[4, 1] = 20
+    wt = rng.uniform(0, 1, (T, K)).astype(np.float32)
+    p = epl.Problem.make(T, K, 4, 2, H, 0)
+    ws = poisoned(epl.epl_workspace_bytes(p), torch.uint8)
+    # a clean layout resets the status word
+    epl.epl_layout(p, torch.zeros((T, K), dtype=torch.int64, device=DEV),
+                   torch.empty(4, dtype=torch.int32, device=DEV),
+                   torch.empty(2, dtype=torch.int32, device=DEV),
+                   torch.empty((T, 2), dtype=torch.uint8, device=DEV), ws)
+    y = poisoned((T, H), torch.float32)
+    epl.epl_combine(p, to_bf16(eo), 20, torch.from_numpy(oi).to(DEV),
+                    torch.from_numpy(wt).to(DEV), epl.EPL_OUT_F32, y, ws)
+    assert epl.epl_status(ws) == epl.EPL_ERANGE
+    clean = np.where(oi >= 20, -1, oi)
+    y_ref = orc().combine(eo, clean, wt)
+    check_combine_f32(y.cpu().numpy(), y_ref, combine_bound(eo, clean, wt))
+
+
+def test_exact_mode_matches_capacity_mode():
+    w = workloads.get("small").with_(num_tokens=1200)
+    inp = workloads.make_inputs(w)
+    tk = torch.from_numpy(inp["topk_idx"]).to(DEV)
+    xd = to_bf16(inp["x"])
+    a = epl.dispatch(xd, tk, w.num_experts, w.num_ranks, mode="capacity")
+    b = epl.dispatch(xd, tk, w.num_experts, w.num_ranks, mode="exact")
+    n = a.total()
+    assert n == b.total() == b.out.shape[0]
+    assert torch.equal(a.output_index, b.output_index)
+    assert torch.equal(a.out[:n].view(torch.int16), b.out.view(torch.int16))
+    assert torch.equal(a.m_indices[:n], b.m_indices)
+
+
+def test_runs_on_a_side_stream():
+    w = workloads.get("small").with_(num_tokens=800)
+    inp = workloads.make_inputs(w)
+    ref = orc().run_all(inp["x"], None, inp["topk_idx"], inp["topk_weights"], w.num_experts,
+                        w.num_ranks)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        r = gpu_dispatch(inp["topk_idx"], inp["x"], None, w.num_experts, w.num_ranks)
+        y = gpu_combine(r, r["out"], inp["topk_weights"], epl.EPL_OUT_F32)
+    s.synchronize()
+    check_layout_and_scatter(r, ref, inp["x"], None)
+    check_combine_f32(y.cpu().numpy(), ref["y"],
+                      combine_bound(ref["out"], ref["output_index"], inp["topk_weights"]))
