@@ -18,7 +18,6 @@ host's cores as a reference baseline.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -29,7 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.md")
 
 
 def log(msg):
@@ -50,26 +49,30 @@ def algorithmic_bytes(w, N, T_any, out_dtype_bytes=4):
     }
 
 
-def source_digest():
-    h = hashlib.sha256()
-    for rel in ("permute_ep_layout_amd/csrc/epl_kernels.h", "permute_ep_layout_amd/csrc/epl.hip"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(workload, kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary,
     only if it was taken on the current kernel sources."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            data = json.load(f)
-    except (OSError, ValueError):
+    from permute_ep_layout_amd import profiling
+
+    data = profiling.read_traffic(TRAFFIC_FILE.format(workload=workload))
+    if not data or data.get("source_digest") != profiling.source_digest():
         return None
-    entry = data.get(workload, {}).get(kernel)
-    if not entry or entry.get("source_digest") != source_digest():
-        return None
-    return entry.get("bytes_per_launch")
+    entry = data.get("kernels", {}).get(kernel)
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+def copy_calibration(nbytes):
+    """A plain copy kernel of known size (fp32 elementwise: read once, write
+    once) for scaling the HBM byte counters."""
+    import torch
+
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
 
 
 def cpu_baseline(w, inp, seconds):
@@ -101,12 +104,18 @@ def main():
     ap.add_argument("--out-dtype", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, metavar="BYTES", default=0,
+                    help="only run a plain copy kernel of BYTES bytes (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the inter-GPU transfer is outside this library, "
               "so there is no multi-GPU step to time (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import numpy as np
     import torch
@@ -153,24 +162,48 @@ def main():
 
     names = ["layout", "scan", "scatter"] + (["expert"] if scaled else []) + ["combine"]
 
-    def step(events=None):
-        def mark(i):
+    # One checked pass through the argument-validating wrappers, then the
+    # timed loop calls the C entry points directly with the same arguments.
+    epl.epl_layout(p, topk, cnt, per_rank, in_rank, ws)
+    epl.epl_scan(p, cnt, start, total_host, ws)
+    epl.epl_scatter(p, x, xs, topk, start, ws, cap, out, out_scale, m_idx, oi)
+    if scaled:
+        epl.epl_expert_scale(p, out, m_idx, cap, eo, ws)
+    epl.epl_combine(p, eo, cap, oi, wt, out_code, y, ws)
+    epl.epl_dispatch(p, topk, x, xs, cap, cnt, per_rank, in_rank, start, total_host, out,
+                     out_scale, m_idx, oi, ws)
+    calls = [
+        epl.prepare("epl_layout", p, topk, cnt, per_rank, in_rank, ws),
+        epl.prepare("epl_scan", p, cnt, start, total_host, ws),
+        epl.prepare("epl_scatter", p, x, xs, topk, start, ws, cap, out, out_scale, m_idx, oi),
+    ]
+    if scaled:
+        calls.append(epl.prepare("epl_expert_scale", p, out, m_idx, cap, eo, ws))
+    calls.append(epl.prepare("epl_combine", p, eo, cap, oi, wt, out_code, y, ws))
+    fused_calls = [epl.prepare("epl_dispatch", p, topk, x, xs, cap, cnt, per_rank, in_rank, start,
+                               total_host, out, out_scale, m_idx, oi, ws)] + calls[3:]
+
+    def step_split(events=None):
+        for i, call in enumerate(calls):
             if events is not None:
                 events[i].record(stream)
-        mark(0)
-        epl.epl_layout(p, topk, cnt, per_rank, in_rank, ws)
-        mark(1)
-        epl.epl_scan(p, cnt, start, total_host, ws)
-        mark(2)
-        epl.epl_scatter(p, x, xs, topk, start, ws, cap, out, out_scale, m_idx, oi)
-        mark(3)
-        j = 3
-        if scaled:
-            epl.epl_expert_scale(p, out, m_idx, cap, eo, ws)
-            j += 1
-            mark(j)
-        epl.epl_combine(p, eo, cap, oi, wt, out_code, y, ws)
-        mark(j + 1)
+            call()
+        if events is not None:
+            events[len(calls)].record(stream)
+
+    # The timed step: layout + scan + scatter through the fused entry point,
+    # then (for the large-batch workload) the expert stand-in, then combine.
+    dispatch_call, middle, combine_call = fused_calls[0], fused_calls[1:-1], fused_calls[-1]
+
+    def step(ev_mid=None, ev_end=None):
+        dispatch_call()
+        for call in middle:
+            call()
+        if ev_mid is not None:
+            ev_mid.record(stream)
+        combine_call()
+        if ev_end is not None:
+            ev_end.record(stream)
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -180,42 +213,52 @@ def main():
         raise RuntimeError(f"dispatch failed: status {epl.epl_status(ws)}, total "
                            f"{int(total_host[0])} != {N}")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    # Timed region: exactly `steps` steps, two HIP events per step on the
+    # stream the kernels run on (before combine, after combine): combine's
+    # duration is measured exactly, and the interval from the previous step's
+    # end to this step's combine is the dispatch (+ expert) part.
+    ev0 = torch.cuda.Event(enable_timing=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        step(evs[i])
+        step(*evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
-    per_kernel_ms = {
-        n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+    prev = [ev0] + [e[1] for e in evs[:-1]]
+    timed_ms = {
+        "dispatch" + ("+expert" if scaled else ""): float(np.mean(
+            [a.elapsed_time(m) for a, (m, _) in zip(prev, evs)])),
+        "combine": float(np.mean([m.elapsed_time(e) for m, e in evs])),
+    }
     assert epl.epl_status(ws) == epl.EPL_OK
 
-    # The same path through the fused entry point (layout + scan + scatter in
-    # one call), untimed by events, for reference.
-    def fused_step():
-        epl.epl_dispatch(p, topk, x, xs, cap, cnt, per_rank, in_rank, start, total_host, out,
-                         out_scale, m_idx, oi, ws)
-        if scaled:
-            epl.epl_expert_scale(p, out, m_idx, cap, eo, ws)
-        epl.epl_combine(p, eo, cap, oi, wt, out_code, y, ws)
-
+    # Per-kernel breakdown: the same kernels through the individual entry
+    # points (layout, scan, scatter, ...), an event around every launch.
     for _ in range(args.warmup):
-        fused_step()
+        step_split()
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for _ in range(args.steps):
-        fused_step()
+    for i in range(args.steps):
+        step_split(sev[i])
     torch.cuda.synchronize()
-    fused_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+    per_kernel_ms = {
+        n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in sev])) for i, n in enumerate(names)}
+    assert epl.epl_status(ws) == epl.EPL_OK
 
     nbytes = algorithmic_bytes(w, N, T_any, 4 if out_code == epl.EPL_OUT_F32 else 2)
     gbps = {n: nbytes[n] / (per_kernel_ms[n] * 1e-3) / 1e9 for n in names}
-    dominant = max(("scatter", "combine"), key=lambda n: per_kernel_ms[n])
-    sc_ms = per_kernel_ms["scatter"] + per_kernel_ms["combine"]
+    # combine's duration in the timed region is exact; scatter's comes from
+    # the per-kernel breakdown
+    kernel_ms = dict(per_kernel_ms, combine=timed_ms["combine"])
+    dominant = max(("scatter", "combine"), key=lambda n: kernel_ms[n])
+    dom_gbps = nbytes[dominant] / (kernel_ms[dominant] * 1e-3) / 1e9
+    sc_ms = kernel_ms["scatter"] + kernel_ms["combine"]
     sc_gbps = (nbytes["scatter"] + nbytes["combine"]) / (sc_ms * 1e-3) / 1e9
     traffic = measured_traffic(w.name, dominant)
 
@@ -244,18 +287,20 @@ def main():
             "drop_rate": w.drop_rate, "expert_fn": w.expert_fn, "routed_rows": N,
             "combine_out": args.out_dtype, "capacity_rows": cap,
         },
+        "timed_region_ms": timed_ms,
         "per_kernel_ms": per_kernel_ms,
         "per_kernel_gbps": gbps,
+        "algorithmic_bytes": nbytes,
         "scatter_combine": {"ms": sc_ms, "gbps": sc_gbps, "frac_of_peak": sc_gbps / HBM_PEAK_GBPS},
-        "fused_dispatch_ms_per_step": fused_ms,
         "roofline": {
             "kernel": dominant,
             "bound": "hbm",
-            "achieved": gbps[dominant],
+            "achieved": dom_gbps,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": gbps[dominant] / HBM_PEAK_GBPS,
+            "frac": dom_gbps / HBM_PEAK_GBPS,
             "algorithmic_bytes": nbytes[dominant],
+            "avg_launch_ms": kernel_ms[dominant],
             "traffic": traffic,
         },
         "cpu_baseline": cpu,

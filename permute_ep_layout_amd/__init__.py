@@ -24,7 +24,7 @@ __all__ = [
     "epl_dispatch", "epl_combine", "epl_expert_scale", "epl_status", "epl_total",
     "epl_strerror", "epl_version", "dispatch", "combine", "expert_scale", "DispatchResult",
     "EPL_OK", "EPL_EINVAL", "EPL_ERANGE", "EPL_ECAPACITY", "EPL_EHIP", "EPL_OUT_F32",
-    "EPL_OUT_BF16",
+    "EPL_OUT_BF16", "prepare",
 ]
 
 EPL_OK = 0
@@ -330,6 +330,32 @@ def epl_total(workspace, stream=None) -> int:
     if n < 0:
         raise EplError(n, "epl_total")
     return n
+
+
+def prepare(name: str, *args, stream=None):
+    """A zero-overhead caller of C entry point `name` with fixed arguments:
+    tensors become their device addresses, a Problem is passed by reference,
+    and the stream (default: torch's current stream) is resolved once. The
+    arguments are not checked here: call the checked ``epl_*`` wrapper with
+    the same arguments first (e.g. in a warm-up). Raises EplError on a non-zero
+    return code."""
+    import torch
+    fn = getattr(load(), name)
+    cargs = []
+    for a in args:
+        if isinstance(a, Problem):
+            cargs.append(ctypes.byref(a))
+        elif isinstance(a, torch.Tensor):
+            cargs.append(ctypes.c_void_p(a.data_ptr()))
+        else:
+            cargs.append(a)
+    cargs.append(ctypes.c_void_p(_stream(stream)))
+
+    def call():
+        rc = fn(*cargs)
+        if rc != EPL_OK:
+            raise EplError(rc, name)
+    return call
 
 
 # ------------------------------------------------------- tensor helpers --

@@ -48,10 +48,13 @@ bool problem_ok(const epl_problem *p)
 // buffer), and at least 16 tokens so the per-block count matrix stays small.
 int layout_block_tokens(const epl_problem &p)
 {
-    const int64_t cap = std::min<int64_t>(epl::kLayoutThreads, epl::kMaxSlotsPerBlock / p.num_topk);
+    int64_t cap = std::min<int64_t>(epl::kLayoutThreads, epl::kMaxSlotsPerBlock / p.num_topk);
+    // the LDS bound: keys and ranks take 8 bytes per slot
+    const size_t fixed = epl::layout_lds_bytes(0, p.num_topk, p.num_experts, p.num_ranks);
+    cap = std::min<int64_t>(cap, (int64_t)((epl::kLayoutLdsBytes - fixed) / (8 * (size_t)p.num_topk)));
     int64_t want = (p.num_tokens + 63) / 64;
     want = std::max<int64_t>(16, want);
-    return (int)std::min<int64_t>(want, cap);
+    return (int)std::max<int64_t>(1, std::min<int64_t>(want, cap));
 }
 
 struct WsLayout {
@@ -84,13 +87,9 @@ T *at(void *ws, size_t off)
     return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
 }
 
-size_t layout_lds_bytes(const epl_problem &p, int block_tokens)
-{
-    return sizeof(int32_t) * ((size_t)2 * block_tokens * p.num_topk +
-                              (size_t)epl::kLayoutWaves * p.num_experts + p.num_ranks + 1);
-}
-
 int launch_status() { return hipGetLastError() == hipSuccess ? EPL_OK : EPL_EHIP; }
+
+unsigned row_grid(int64_t tokens, int limit) { return (unsigned)std::min<int64_t>(tokens, limit); }
 
 int enqueue_layout(const epl_problem &p, const WsLayout &w, const int64_t *topk, uint8_t *in_rank,
                    void *ws, hipStream_t s)
@@ -99,24 +98,41 @@ int enqueue_layout(const epl_problem &p, const WsLayout &w, const int64_t *topk,
         return EPL_OK;
     const bool vec16 = (p.num_ranks % 16 == 0) && aligned(in_rank, 16);
     hipLaunchKernelGGL(epl::ep_layout_kernel, dim3((unsigned)w.num_blocks), dim3(epl::kLayoutThreads),
-                       layout_lds_bytes(p, w.block_tokens), s, topk, p.num_tokens, p.num_topk,
+                       epl::layout_lds_bytes(w.block_tokens, p.num_topk, p.num_experts, p.num_ranks),
+                       s, topk, p.num_tokens, p.num_topk,
                        p.num_experts, p.num_ranks, p.num_experts / p.num_ranks, w.block_tokens,
                        in_rank, vec16, at<int32_t>(ws, w.block_count), at<int32_t>(ws, w.block_rank),
                        at<uint32_t>(ws, w.block_err), at<int32_t>(ws, w.slot_rank));
     return launch_status();
 }
 
+// The device address through which a kernel can store straight into the
+// caller's pinned host word, or null if the runtime cannot map it (then the
+// total is copied with hipMemcpyAsync after the scan).
+int32_t *mapped_host_word(int32_t *host)
+{
+    if (!host)
+        return nullptr;
+    void *dev = nullptr;
+    if (hipHostGetDevicePointer(&dev, host, 0) != hipSuccess) {
+        (void)hipGetLastError();   // not mapped: clear the error, use the copy
+        return nullptr;
+    }
+    return static_cast<int32_t *>(dev);
+}
+
 int enqueue_scan(const epl_problem &p, const WsLayout &w, int mode, int32_t *cnt, int32_t *per_rank,
                  int32_t *start, int32_t *total_host, void *ws, hipStream_t s)
 {
+    int32_t *mapped = (mode & epl::kScanPrefix) ? mapped_host_word(total_host) : nullptr;
     hipLaunchKernelGGL(epl::ep_scan_kernel, dim3(1), dim3(epl::kScanThreads), 0, s, mode,
                        w.num_blocks, p.num_experts, p.num_ranks, at<int32_t>(ws, w.block_count),
                        at<int32_t>(ws, w.block_rank), at<uint32_t>(ws, w.block_err), cnt, per_rank,
-                       start, at<WsHeader>(ws, 0));
+                       start, at<WsHeader>(ws, 0), mapped);
     int rc = launch_status();
     if (rc != EPL_OK)
         return rc;
-    if ((mode & epl::kScanPrefix) && total_host) {
+    if ((mode & epl::kScanPrefix) && total_host && !mapped) {
         if (hipMemcpyAsync(total_host, &at<WsHeader>(ws, 0)->total, sizeof(int32_t),
                            hipMemcpyDeviceToHost, s) != hipSuccess)
             return EPL_EHIP;
@@ -129,11 +145,13 @@ void launch_scatter(const epl_problem &p, const WsLayout &w, const uint16_t *x, 
                     const int64_t *topk, const int32_t *start, void *ws, int64_t cap,
                     uint16_t *out, float *out_scale, int32_t *m_idx, int32_t *oi, hipStream_t s)
 {
-    hipLaunchKernelGGL(epl::ep_scatter_kernel<VPT>, dim3((unsigned)p.num_tokens),
-                       dim3(epl::kRowThreads), 0, s, x, xs, topk, start,
+    hipLaunchKernelGGL(epl::ep_scatter_kernel<VPT>, dim3(row_grid(p.num_tokens, epl::kScatterGrid)),
+                       dim3(epl::kScatterThreads), 0, s, x, xs, topk, start,
                        at<const int32_t>(ws, w.block_count), at<const int32_t>(ws, w.slot_rank),
-                       p.num_topk, p.num_experts, p.hidden, p.scale_cols, w.block_tokens, cap,
-                       out, out_scale, m_idx, oi, &at<WsHeader>(ws, 0)->status);
+                       p.num_tokens, p.num_topk, p.num_experts, p.hidden, p.scale_cols,
+                       p.scale_cols % 4 == 0 && aligned(xs, 16) && aligned(out_scale, 16),
+                       w.block_tokens, cap, out, out_scale, m_idx, oi,
+                       &at<WsHeader>(ws, 0)->status);
 }
 
 int enqueue_scatter(const epl_problem &p, const WsLayout &w, const uint16_t *x, const float *xs,
@@ -143,7 +161,7 @@ int enqueue_scatter(const epl_problem &p, const WsLayout &w, const uint16_t *x, 
     if (p.num_tokens == 0)
         return EPL_OK;
     const int nvec = p.hidden / 8;
-    const int vpt = std::min(8, (nvec + epl::kRowThreads - 1) / epl::kRowThreads);
+    const int vpt = std::min(8, (nvec + epl::kScatterThreads - 1) / epl::kScatterThreads);
     switch (vpt) {
 #define EPL_SCATTER_CASE(V)                                                                        \
     case V:                                                                                        \
@@ -318,14 +336,15 @@ int epl_combine(const epl_problem *p, const uint16_t *expert_out, int64_t expert
         return EPL_EINVAL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint32_t *status = workspace ? &at<WsHeader>(workspace, 0)->status : nullptr;
+    const dim3 grid(row_grid(p->num_tokens, epl::kCombineGrid));
     if (out_dtype == EPL_OUT_BF16)
-        hipLaunchKernelGGL(epl::ep_combine_kernel<true>, dim3((unsigned)p->num_tokens),
-                           dim3(epl::kRowThreads), 0, s, expert_out, expert_rows, output_index,
-                           topk_weights, p->num_topk, p->hidden, y, status);
+        hipLaunchKernelGGL(epl::ep_combine_kernel<true>, grid, dim3(epl::kCombineThreads), 0, s,
+                           expert_out, expert_rows, output_index, topk_weights, p->num_tokens,
+                           p->num_topk, p->hidden, y, status);
     else
-        hipLaunchKernelGGL(epl::ep_combine_kernel<false>, dim3((unsigned)p->num_tokens),
-                           dim3(epl::kRowThreads), 0, s, expert_out, expert_rows, output_index,
-                           topk_weights, p->num_topk, p->hidden, y, status);
+        hipLaunchKernelGGL(epl::ep_combine_kernel<false>, grid, dim3(epl::kCombineThreads), 0, s,
+                           expert_out, expert_rows, output_index, topk_weights, p->num_tokens,
+                           p->num_topk, p->hidden, y, status);
     return launch_status();
 }
 

@@ -35,7 +35,28 @@ constexpr int kMaxSlotsPerBlock = 2048;   // B * K per layout block
 constexpr int kMaxTopk = 64;
 constexpr int kMaxExperts = 2048;
 constexpr int kScanThreads = 1024;
-constexpr int kRowThreads = 128;          // scatter / combine / expert-scale workgroup
+constexpr int kRowThreads = 128;          // expert-scale workgroup
+
+// Launch shape of the two bandwidth kernels. Build-time knobs (-D...) so the
+// shape can be swept on the target; the defaults are the measured best on
+// MI355X for hidden 7168.
+#ifndef EPL_SCATTER_THREADS
+#define EPL_SCATTER_THREADS 128
+#endif
+#ifndef EPL_COMBINE_THREADS
+#define EPL_COMBINE_THREADS 128
+#endif
+#ifndef EPL_COMBINE_UNROLL
+#define EPL_COMBINE_UNROLL 2
+#endif
+#ifndef EPL_SCATTER_GRID
+#define EPL_SCATTER_GRID 1024
+#endif
+#ifndef EPL_COMBINE_GRID
+#define EPL_COMBINE_GRID 4096
+#endif
+constexpr int kScatterThreads = EPL_SCATTER_THREADS;
+constexpr int kCombineThreads = EPL_COMBINE_THREADS;
 
 // Status word bits (workspace header).
 constexpr uint32_t kStatusBadExpert = 1u;      // topk id outside [-1, E)
@@ -84,11 +105,23 @@ __device__ __forceinline__ void store_mask_bytes(uint8_t *dst, uint64_t mask, in
     }
 }
 
-// One workgroup per block of B tokens (B * K <= kMaxSlotsPerBlock).
-// Outputs: in_rank rows of the block's tokens; block_count[b][e] (slots of
-// expert e in block b); block_rank[b][r] (tokens of block b sent to rank r);
-// block_err[b]; slot_rank[t*K+k] = rank of slot (t,k) among the block's
-// earlier slots of the same expert, or -1 for an invalid slot.
+// Dynamic LDS of the layout kernel for E experts, R ranks, B tokens of K
+// slots. Kept <= kLayoutLdsBytes by the host's choice of B.
+constexpr size_t kLayoutLdsBytes = 65536;
+__host__ __device__ constexpr size_t layout_lds_bytes(int B, int K, int E, int R)
+{
+    return sizeof(int32_t) * ((size_t)2 * B * K              // keys, ranks
+                              + (size_t)kLayoutWaves * E      // running count per wave and expert
+                              + (size_t)kLayoutWaves * ((E + 3) / 4)   // per-chunk byte counters
+                              + (size_t)R + 1);               // tokens per rank, error flag
+}
+
+// One workgroup per block of B tokens (B <= kLayoutThreads, B * K <=
+// kMaxSlotsPerBlock). Outputs: in_rank rows of the block's tokens;
+// block_count[b][e] (slots of expert e in block b); block_rank[b][r] (tokens
+// of block b sent to rank r); block_err[b]; slot_rank[t*K+k] = rank of slot
+// (t,k) among the block's earlier slots of the same expert, or -1 for an
+// invalid slot.
 __global__ __launch_bounds__(kLayoutThreads) void ep_layout_kernel(
     const int64_t *__restrict__ topk, int64_t T, int K, int E, int R, int experts_per_rank,
     int B, uint8_t *__restrict__ in_rank, bool in_rank_vec16,
@@ -97,11 +130,13 @@ __global__ __launch_bounds__(kLayoutThreads) void ep_layout_kernel(
 {
     extern __shared__ int32_t lds[];
     const int max_slots = B * K;
-    int32_t *keys = lds;                                  // [B*K]
-    int32_t *lrank = keys + max_slots;                    // [B*K] rank within the owning wave
-    int32_t *wave_cnt = lrank + max_slots;                // [waves][E]
-    int32_t *rank_cnt = wave_cnt + kLayoutWaves * E;      // [R]
-    int32_t *s_err = rank_cnt + R;                        // [1]
+    const int cwords = (E + 3) / 4;
+    int32_t *keys = lds;                                   // [B*K] key | owner << 16, or -1
+    int32_t *lrank = keys + max_slots;                     // [B*K] rank within the owning wave
+    int32_t *wave_cnt = lrank + max_slots;                 // [waves][E]
+    uint32_t *chunk_cnt = reinterpret_cast<uint32_t *>(wave_cnt + kLayoutWaves * E);  // [waves][E/4]
+    int32_t *rank_cnt = reinterpret_cast<int32_t *>(chunk_cnt + kLayoutWaves * cwords); // [R]
+    int32_t *s_err = rank_cnt + R;                         // [1]
 
     const int64_t b = blockIdx.x;
     const int64_t t0 = b * B;
@@ -113,52 +148,71 @@ __global__ __launch_bounds__(kLayoutThreads) void ep_layout_kernel(
 
     for (int i = tid; i < kLayoutWaves * E; i += kLayoutThreads)
         wave_cnt[i] = 0;
+    for (int i = tid; i < kLayoutWaves * cwords; i += kLayoutThreads)
+        chunk_cnt[i] = 0;
     for (int i = tid; i < R; i += kLayoutThreads)
         rank_cnt[i] = 0;
     if (tid == 0)
         *s_err = 0;
 
-    // Keys of the block's slots, in (token, k) order; bad ids become -1.
+    // Keys of the block's slots, in (token, k) order, packed with the owning
+    // rank; bad ids become -1.
     const int64_t *src = topk + t0 * K;
     bool bad = false;
     for (int s = tid; s < ns; s += kLayoutThreads) {
         const int64_t e = src[s];
-        int key = (int)e;
-        if (e < -1 || e >= E) {
+        int packed = -1;
+        if (e >= 0 && e < E)
+            packed = (int)e | (((int)e / experts_per_rank) << 16);
+        else if (e != -1)
             bad = true;
-            key = -1;
-        }
-        keys[s] = key;
+        keys[s] = packed;
     }
     __syncthreads();
     if (bad)
         atomicOr(reinterpret_cast<uint32_t *>(s_err), 1u);
 
     // Rank of each slot among the earlier slots with the same key. Wave w
-    // owns a contiguous run of 64-slot chunks and walks it in order; inside a
-    // chunk, lanes holding the same key are found with one ballot per
-    // distinct key, and a lane's rank is the number of lower lanes in that
-    // ballot plus the wave's running count for the key.
+    // owns a contiguous run of 64-slot chunks and walks it in order. For a
+    // chunk, each lane first counts its key in a per-wave byte histogram
+    // (a key occurs at most 64 times in a chunk); lanes whose key occurs
+    // once have in-chunk rank 0, and only the repeated keys go through the
+    // ballot loop, where a lane's rank is the number of lower lanes holding
+    // its key. Then every lane adds the wave's running count for its key, and
+    // the lowest lane of each key advances that count and clears the byte.
     const int nchunks = (ns + kWave - 1) / kWave;
     const int cpw = (nchunks + kLayoutWaves - 1) / kLayoutWaves;
     {
         int32_t *my_cnt = wave_cnt + wave * E;
+        uint32_t *my_chunk = chunk_cnt + wave * cwords;
         const int c_end = min(nchunks, (wave + 1) * cpw);
         const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
         for (int c = wave * cpw; c < c_end; ++c) {
             const int s = c * kWave + lane;
-            const int key = (s < ns) ? keys[s] : -1;
-            uint64_t todo = wave_ballot(key >= 0);
+            const int packed = (s < ns) ? keys[s] : -1;
+            const bool valid = packed >= 0;
+            const int k16 = valid ? (packed & 0xFFFF) : 0;
+            const int shift = 8 * (k16 & 3);
+            if (valid)
+                atomicAdd(&my_chunk[k16 >> 2], 1u << shift);
+            const int group = valid ? (int)((my_chunk[k16 >> 2] >> shift) & 0xFFu) : 0;
+            int rank = 0;
+            uint64_t todo = wave_ballot(group > 1);
             while (todo) {
                 const int leader = (int)__builtin_ctzll(todo);
-                const int lkey = __builtin_amdgcn_readlane(key, leader);
-                const uint64_t same = wave_ballot(key == lkey);
-                const int base = my_cnt[lkey];
-                if (key == lkey)
-                    lrank[s] = base + __popcll(same & lower);
-                if (lane == leader)
-                    my_cnt[lkey] = base + __popcll(same);
+                const int lkey = __builtin_amdgcn_readlane(k16, leader);
+                const uint64_t same = wave_ballot(valid && k16 == lkey);
+                if (valid && k16 == lkey)
+                    rank = __popcll(same & lower);
                 todo &= ~same;
+            }
+            if (valid) {
+                const int base = my_cnt[k16];
+                lrank[s] = base + rank;
+                if (rank == 0) {
+                    my_cnt[k16] = base + group;
+                    atomicAnd(&my_chunk[k16 >> 2], ~(0xFFu << shift));
+                }
             }
         }
     }
@@ -172,9 +226,9 @@ __global__ __launch_bounds__(kLayoutThreads) void ep_layout_kernel(
             uint64_t mask = 0;
             if (tok) {
                 for (int k = 0; k < K; ++k) {
-                    const int e = keys[tid * K + k];
-                    if (e >= 0) {
-                        const int r = e / experts_per_rank - w0;
+                    const int packed = keys[tid * K + k];
+                    if (packed >= 0) {
+                        const int r = (packed >> 16) - w0;
                         if (r >= 0 && r < wr)
                             mask |= 1ull << r;
                     }
@@ -207,9 +261,9 @@ __global__ __launch_bounds__(kLayoutThreads) void ep_layout_kernel(
         block_err[b] = (uint32_t)*s_err;
 
     for (int s = tid; s < ns; s += kLayoutThreads) {
-        const int key = keys[s];
+        const int packed = keys[s];
         const int w = (s / kWave) / cpw;
-        slot_rank[t0 * K + s] = key >= 0 ? lrank[s] + wave_cnt[w * E + key] : -1;
+        slot_rank[t0 * K + s] = packed >= 0 ? lrank[s] + wave_cnt[w * E + (packed & 0xFFFF)] : -1;
     }
 }
 
@@ -243,20 +297,45 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int *s_wave)
     return v + (wave > 0 ? s_wave[wave - 1] : 0);
 }
 
+// Sums of one column segment [b0, b1) of a row-major [nb, ncols] matrix,
+// loading 16 rows at a time so the loads of a batch are in flight together.
+__device__ __forceinline__ int segment_sum(const int32_t *m, int ncols, int col, int64_t b0,
+                                           int64_t b1)
+{
+    int sum = 0;
+    for (int64_t bb = b0; bb < b1; bb += 16) {
+        int v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            v[j] = (bb + j < b1) ? m[(bb + j) * ncols + col] : 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            sum += v[j];
+    }
+    return sum;
+}
+
 // Single workgroup. kScanReduce: column sums of block_count / block_rank
 // give num_tokens_per_expert / num_tokens_per_rank, block_count is replaced
 // by its exclusive prefix over blocks, and the status word is reset to the
 // layout's error bits. kScanPrefix: exclusive prefix of the per-expert
 // counts (read from `cnt` unless kScanReduce produced them) into
-// expert_start_loc, total into the header.
+// expert_start_loc, total into the header and, if `total_out` is not null,
+// into that (host-mapped) word too.
+//
+// The columns are split into P segments of L blocks each so that all 1024
+// threads have work: thread (column, segment) sums its segment, a short
+// per-column scan over the P segment sums gives each segment's offset, and
+// the thread then rewrites its segment as a running prefix.
 __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
     int mode, int64_t nb, int E, int R, int32_t *__restrict__ block_count,
     const int32_t *__restrict__ block_rank, const uint32_t *__restrict__ block_err,
     int32_t *__restrict__ cnt, int32_t *__restrict__ per_rank, int32_t *__restrict__ start,
-    WsHeader *__restrict__ hdr)
+    WsHeader *__restrict__ hdr, int32_t *__restrict__ total_out)
 {
     __shared__ int s_cnt[kMaxExperts];
-    __shared__ int s_seg[kScanThreads > kMaxExperts ? kScanThreads : kMaxExperts];
+    __shared__ int s_seg[kMaxExperts];
+    __shared__ int s_rseg[kMaxExperts];
     __shared__ int s_wave[kScanThreads / kWave];
     __shared__ uint32_t s_err;
     const int tid = threadIdx.x;
@@ -264,17 +343,33 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
     if (mode & kScanReduce) {
         if (tid == 0)
             s_err = 0;
-        // Columns split into P segments of blocks so all threads have work.
         const int P = E <= kScanThreads ? kScanThreads / E : 1;
         const int64_t L = (nb + P - 1) / P;
+        const int PR = R <= kScanThreads ? kScanThreads / R : 1;
+        const int64_t LR = (nb + PR - 1) / PR;
+        // When every thread owns at most one segment of at most 16 blocks,
+        // the segment stays in registers between the sum and the rewrite.
+        const bool held = E * P <= kScanThreads && L <= 16;
+        int seg[16];
         for (int col = tid; col < E * P; col += kScanThreads) {
-            const int e = col % E;
-            const int q = col / E;
+            const int e = col % E, q = col / E;
             const int64_t b0 = q * L, b1 = min(nb, b0 + L);
-            int sum = 0;
-            for (int64_t bb = b0; bb < b1; ++bb)
-                sum += block_count[bb * E + e];
-            s_seg[q * E + e] = sum;
+            if (held) {
+                int sum = 0;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    seg[j] = (b0 + j < b1) ? block_count[(b0 + j) * E + e] : 0;
+                    sum += seg[j];
+                }
+                s_seg[q * E + e] = sum;
+            } else {
+                s_seg[q * E + e] = segment_sum(block_count, E, e, b0, b1);
+            }
+        }
+        for (int col = tid; col < R * PR; col += kScanThreads) {
+            const int r = col % R, q = col / R;
+            const int64_t b0 = q * LR;
+            s_rseg[q * R + r] = segment_sum(block_rank, R, r, b0, min(nb, b0 + LR));
         }
         uint32_t err = 0;
         for (int64_t bb = tid; bb < nb; bb += kScanThreads)
@@ -292,14 +387,28 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
             s_cnt[e] = run;
             cnt[e] = run;
         }
+        for (int r = tid; r < R; r += kScanThreads) {
+            int run = 0;
+            for (int q = 0; q < PR; ++q)
+                run += s_rseg[q * R + r];
+            per_rank[r] = run;
+        }
         __syncthreads();
-        // Rewrite block_count as the exclusive prefix over blocks; loads of
-        // a batch are issued together before its stores.
+        // Rewrite block_count as the exclusive prefix over blocks.
         for (int col = tid; col < E * P; col += kScanThreads) {
-            const int e = col % E;
-            const int q = col / E;
+            const int e = col % E, q = col / E;
             const int64_t b0 = q * L, b1 = min(nb, b0 + L);
             int run = s_seg[q * E + e];
+            if (held) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    if (b0 + j < b1) {
+                        block_count[(b0 + j) * E + e] = run;
+                        run += seg[j];
+                    }
+                }
+                continue;
+            }
             for (int64_t bb = b0; bb < b1; bb += 16) {
                 int v[16];
 #pragma unroll
@@ -314,13 +423,6 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
                 }
             }
         }
-        for (int r = tid; r < R; r += kScanThreads) {
-            int sum = 0;
-            for (int64_t bb = 0; bb < nb; ++bb)
-                sum += block_rank[bb * R + r];
-            per_rank[r] = sum;
-        }
-        __syncthreads();
         if (tid == 0)
             hdr->status = s_err ? kStatusBadExpert : 0u;
     } else if (mode & kScanPrefix) {
@@ -340,85 +442,219 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
             start[i0] = excl;
         if (i1 < E)
             start[i1] = excl + a0;
-        if (tid == kScanThreads - 1)
+        if (tid == kScanThreads - 1) {
             hdr->total = incl;
+            if (total_out)
+                *total_out = incl;
+        }
     }
 }
 
 // -------------------------------------------------------------- scatter --
 
-// One workgroup per token row. The row is read once (16-byte vectors, VPT
-// per thread per pass) and written to each of the token's K destination
-// rows; the scale row follows it; m_indices and output_index are written by
-// the first K threads.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Workgroup counts of the row kernels: one token per workgroup while that is
+// at most the limit, otherwise the limit, each workgroup striding over tokens
+// (4 scatter / 16 combine workgroups per CU on 256 CUs).
+constexpr int kScatterGrid = EPL_SCATTER_GRID;
+constexpr int kCombineGrid = EPL_COMBINE_GRID;
+
+#ifndef EPL_XCD_MAP
+#define EPL_XCD_MAP 1
+#endif
+#ifndef EPL_SCALE_NT
+#define EPL_SCALE_NT 0
+#endif
+constexpr int kNumXcd = 8;   // MI355X: 8 XCDs, workgroup i runs on XCD i % 8
+
+// Tokens of one workgroup of a grid-stride row kernel: first, first + stride,
+// ... below end. With the XCD-aware mapping each XCD owns one contiguous
+// range of ceil(T / 8) tokens, so rows written for neighbouring tokens (the
+// neighbouring rows of an expert's block, their scale rows and m_indices
+// entries) meet in the same L2, where partial-line writes can merge before
+// they reach HBM.
+struct TokenRange {
+    int64_t first, stride, end;
+};
+
+__device__ __forceinline__ TokenRange token_range(int64_t T)
+{
+    const int64_t G = gridDim.x, w = blockIdx.x;
+    if (EPL_XCD_MAP && G % kNumXcd == 0 && G >= kNumXcd) {
+        const int64_t per = (T + kNumXcd - 1) / kNumXcd;
+        const int64_t xcd = w % kNumXcd;
+        return {xcd * per + w / kNumXcd, G / kNumXcd, min(T, (xcd + 1) * per)};
+    }
+    return {w, G, T};
+}
+
+// Workgroup barrier that orders LDS accesses only. __syncthreads() also
+// orders global memory, which on CDNA makes every wave wait for all of its
+// outstanding global stores (they share the vmcnt counter with loads) before
+// the barrier; the row kernels below only publish small LDS tables through
+// their barriers and must keep their row stores streaming across tokens.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Scale rows are small (S floats): written back through L2 by default so that
+// the partial lines of neighbouring rows can merge there.
+template <typename V>
+__device__ __forceinline__ void store_scale(V *dst, const V &v)
+{
+    if (EPL_SCALE_NT)
+        __builtin_nontemporal_store(v, dst);
+    else
+        *dst = v;
+}
+
+// One workgroup per token row, grid-stride over tokens. The row is read once
+// (16-byte vectors, VPT per thread per pass) and stored to each of the
+// token's K destination rows with non-temporal stores: the buffer is written
+// once and read much later, so the stores should not displace cached data.
+// The scale row is fetched together with the row and follows it.
+//
+// Destination rows come from two dependent lookups per slot (expert id and
+// slot rank, then expert offset and block offset). The first K threads run
+// them ahead of the data: while token t streams, they already hold the
+// offsets of token t + G and the ids of token t + 2G (G = grid size), so no
+// token waits for its own lookups. The rows live in a double-buffered LDS
+// table, so one barrier per token suffices: a thread can only overwrite a
+// buffer after every thread has passed the barrier of the token in between,
+// i.e. has finished reading that buffer.
 template <int VPT>
-__global__ __launch_bounds__(kRowThreads) void ep_scatter_kernel(
+__global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ x_scale,
     const int64_t *__restrict__ topk, const int32_t *__restrict__ start,
-    const int32_t *__restrict__ block_base, const int32_t *__restrict__ slot_rank, int K,
-    int E, int H, int S, int B, int64_t capacity, uint16_t *__restrict__ out,
-    float *__restrict__ out_scale, int32_t *__restrict__ m_indices,
+    const int32_t *__restrict__ block_base, const int32_t *__restrict__ slot_rank, int64_t T,
+    int K, int E, int H, int S, bool scale_vec16, int B, int64_t capacity,
+    uint16_t *__restrict__ out, float *__restrict__ out_scale, int32_t *__restrict__ m_indices,
     int32_t *__restrict__ output_index, uint32_t *__restrict__ status)
 {
-    __shared__ int64_t s_row[kMaxTopk];
-    const int64_t t = blockIdx.x;
+    __shared__ int64_t s_row[2][kMaxTopk];
     const int tid = threadIdx.x;
+    const int nvec = H >> 3;
+    const int nq = scale_vec16 ? (S >> 2) : 0;
+    const TokenRange tr = token_range(T);
+    const int64_t step = tr.stride, t_end = tr.end;
+    const bool lead = tid < K;
 
-    if (tid < K) {
-        const int64_t e = topk[t * K + tid];
-        const int r = slot_rank[t * K + tid];
-        int pos = -1;
-        int64_t row = -1;
-        if (e >= 0 && e < E) {
-            const int64_t p = (int64_t)start[e] + block_base[(t / B) * E + e] + r;
-            pos = (int)p;
-            if (p >= 0 && p < capacity) {
-                row = p;
-                m_indices[p] = (int32_t)e;
-            } else {
-                atomicOr(status, kStatusCapacity);
-            }
+    // Lookup pipeline of the first K threads (slot tid of the token):
+    //   (e1, r1): expert id and block rank of the next token;
+    //   (e0, r0, s0, b0): expert id, block rank, expert offset and block offset
+    //   of the current one. The two offsets are kept apart (and added only when
+    //   used, one token later) so that no wave waits for them early.
+    int64_t e0 = -1, e1 = -1;
+    int r0 = 0, r1 = 0, s0 = 0, b0 = 0;
+    auto valid = [E](int64_t e) { return e >= 0 && e < E; };
+    if (lead && tr.first < t_end) {
+        const int64_t t = tr.first;
+        e0 = topk[t * K + tid];
+        r0 = slot_rank[t * K + tid];
+        if (valid(e0)) {
+            s0 = start[e0];
+            b0 = block_base[(t / B) * E + e0];
         }
-        output_index[t * K + tid] = pos;
-        s_row[tid] = row;
+        if (t + step < t_end) {
+            e1 = topk[(t + step) * K + tid];
+            r1 = slot_rank[(t + step) * K + tid];
+        }
     }
 
-    const int nvec = H >> 3;
-    const uint4 *xrow = reinterpret_cast<const uint4 *>(x + t * H);
-    bool first = true;
-    for (int base = 0; base < nvec; base += kRowThreads * VPT) {
-        uint4 v[VPT];
+    int it = 0;
+    for (int64_t t = tr.first; t < t_end; t += step, ++it) {
+        int64_t *rows = s_row[it & 1];
+        const u32x4 *xrow = reinterpret_cast<const u32x4 *>(x + t * H);
+        u32x4 v[VPT];
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int idx = base + i * kRowThreads + tid;
+            const int idx = i * kScatterThreads + tid;
             if (idx < nvec)
                 v[i] = xrow[idx];
         }
-        if (first) {
-            __syncthreads();
-            first = false;
-        }
-        for (int k = 0; k < K; ++k) {
-            const int64_t row = s_row[k];
-            if (row < 0)
-                continue;
-            uint4 *orow = reinterpret_cast<uint4 *>(out + row * H);
-#pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                const int idx = base + i * kRowThreads + tid;
-                if (idx < nvec)
-                    orow[idx] = v[i];
+        f32x4 sv = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (tid < nq)
+            sv = reinterpret_cast<const f32x4 *>(x_scale + t * S)[tid];
+
+        if (lead) {
+            int pos = -1;
+            int64_t row = -1;
+            if (valid(e0)) {
+                const int64_t p = (int64_t)s0 + b0 + r0;
+                pos = (int)p;
+                if (p >= 0 && p < capacity) {
+                    row = p;
+                    m_indices[p] = (int32_t)e0;
+                } else {
+                    atomicOr(status, kStatusCapacity);
+                }
+            }
+            output_index[t * K + tid] = pos;
+            rows[tid] = row;
+            // advance the pipeline: offsets of the next token, ids of the one after
+            e0 = e1;
+            r0 = r1;
+            s0 = 0;
+            b0 = 0;
+            if (t + step < t_end && valid(e0)) {
+                s0 = start[e0];
+                b0 = block_base[((t + step) / B) * E + e0];
+            }
+            e1 = -1;
+            if (t + 2 * step < t_end) {
+                e1 = topk[(t + 2 * step) * K + tid];
+                r1 = slot_rank[(t + 2 * step) * K + tid];
             }
         }
-    }
-    if (first)
-        __syncthreads();
-    for (int j = tid; j < S; j += kRowThreads) {
-        const float f = x_scale[t * S + j];
-        for (int k = 0; k < K; ++k) {
-            const int64_t row = s_row[k];
-            if (row >= 0)
-                out_scale[row * S + j] = f;
+        lds_barrier();
+        for (int base = 0;;) {
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int idx = base + i * kScatterThreads + tid;
+                if (idx < nvec) {
+                    for (int k = 0; k < K; ++k) {
+                        const int64_t row = rows[k];
+                        if (row >= 0)
+                            __builtin_nontemporal_store(
+                                v[i], reinterpret_cast<u32x4 *>(out + row * H) + idx);
+                    }
+                }
+            }
+            base += kScatterThreads * VPT;
+            if (base >= nvec)
+                break;
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int idx = base + i * kScatterThreads + tid;
+                if (idx < nvec)
+                    v[i] = xrow[idx];
+            }
+        }
+        if (scale_vec16) {
+            // 16-byte pieces of the scale row (S % 4 == 0 and 16-byte aligned bases);
+            // threads beyond the first kScatterThreads pieces (S > 512) take the rest.
+            for (int j = tid; j < nq; j += kScatterThreads) {
+                const f32x4 f = j == tid ? sv : reinterpret_cast<const f32x4 *>(x_scale + t * S)[j];
+                for (int k = 0; k < K; ++k) {
+                    const int64_t row = rows[k];
+                    if (row >= 0)
+                        store_scale(reinterpret_cast<f32x4 *>(out_scale + row * S) + j, f);
+                }
+            }
+        } else {
+            for (int j = tid; j < S; j += kScatterThreads) {
+                const float f = x_scale[t * S + j];
+                for (int k = 0; k < K; ++k) {
+                    const int64_t row = rows[k];
+                    if (row >= 0)
+                        store_scale(out_scale + row * S + j, f);
+                }
+            }
         }
     }
 }
@@ -442,81 +678,123 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
-// One workgroup per token: y[t] = sum over valid k (ascending) of
-// w[t,k] * expert_out[output_index[t,k]], fp32 accumulation. Each thread
-// owns 8 columns at a time and keeps up to 8 gathered rows in flight.
-template <bool OUT_BF16>
-__global__ __launch_bounds__(kRowThreads) void ep_combine_kernel(
-    const uint16_t *__restrict__ expert_out, int64_t rows, const int32_t *__restrict__ oi,
-    const float *__restrict__ w, int K, int H, void *__restrict__ y, uint32_t *__restrict__ status)
+__device__ __forceinline__ void fma_bf16x8(float *acc, float w, const u32x4 &v)
 {
-    __shared__ int64_t s_row[kMaxTopk];
-    __shared__ float s_w[kMaxTopk];
-    __shared__ int s_n;
-    const int64_t t = blockIdx.x;
-    const int tid = threadIdx.x;
+    acc[0] = fmaf(w, bf16_lo(v.x), acc[0]);
+    acc[1] = fmaf(w, bf16_hi(v.x), acc[1]);
+    acc[2] = fmaf(w, bf16_lo(v.y), acc[2]);
+    acc[3] = fmaf(w, bf16_hi(v.y), acc[3]);
+    acc[4] = fmaf(w, bf16_lo(v.z), acc[4]);
+    acc[5] = fmaf(w, bf16_hi(v.z), acc[5]);
+    acc[6] = fmaf(w, bf16_lo(v.w), acc[6]);
+    acc[7] = fmaf(w, bf16_hi(v.w), acc[7]);
+}
 
-    if (tid < kWave) {
-        // Compact the valid slots, keeping ascending k: lane k finds its
-        // place among the lower valid lanes with one ballot (K <= 64).
-        int64_t p = -1;
-        float wt = 0.0f;
-        if (tid < K) {
-            p = oi[t * K + tid];
-            wt = w[t * K + tid];
+constexpr int kCombineUnroll = EPL_COMBINE_UNROLL;   // column vectors per thread per pass
+
+// One workgroup per token (grid-stride over tokens): y[t] = sum over valid k
+// (ascending) of w[t,k] * expert_out[output_index[t,k]], fp32 accumulation.
+// Each thread owns kCombineUnroll 8-column vectors per pass and issues the
+// loads of up to 8 gathered rows for all of them before accumulating, so
+// 8 * kCombineUnroll row loads per thread are in flight. The gathered rows
+// are read once, so the loads are non-temporal. The first wave fetches the
+// next token's output_index / weights while the current token streams; the
+// compacted slot table is double-buffered in LDS (see ep_scatter_kernel).
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kCombineThreads) void ep_combine_kernel(
+    const uint16_t *__restrict__ expert_out, int64_t rows, const int32_t *__restrict__ oi,
+    const float *__restrict__ w, int64_t T, int K, int H, void *__restrict__ y,
+    uint32_t *__restrict__ status)
+{
+    __shared__ int64_t s_row[2][kMaxTopk];
+    __shared__ float s_w[2][kMaxTopk];
+    __shared__ int s_n[2];
+    const int tid = threadIdx.x;
+    const int nvec = H >> 3;
+    const TokenRange tr = token_range(T);
+    const int64_t step = tr.stride, t_end = tr.end;
+    constexpr int U = kCombineUnroll;
+
+    int64_t p_next = -1;
+    float w_next = 0.0f;
+    if (tid < K && tr.first < t_end) {
+        p_next = oi[tr.first * K + tid];
+        w_next = w[tr.first * K + tid];
+    }
+
+    int it = 0;
+    for (int64_t t = tr.first; t < t_end; t += step, ++it) {
+        const int buf = it & 1;
+        if (tid < kWave) {
+            // Compact the valid slots, keeping ascending k: lane k finds its
+            // place among the lower valid lanes with one ballot (K <= 64).
+            int64_t p = p_next;
+            const float wt = w_next;
+            if (tid < K && t + step < t_end) {
+                p_next = oi[(t + step) * K + tid];
+                w_next = w[(t + step) * K + tid];
+            }
             if (p >= rows) {
                 if (status)
                     atomicOr(status, kStatusBadRow);
                 p = -1;
             }
+            const bool ok = p >= 0;
+            const uint64_t valid = wave_ballot(ok);
+            const uint64_t lower = (tid == 0) ? 0ull : (~0ull >> (kWave - tid));
+            if (ok) {
+                const int slot = __popcll(valid & lower);
+                s_row[buf][slot] = p;
+                s_w[buf][slot] = wt;
+            }
+            if (tid == 0)
+                s_n[buf] = __popcll(valid);
         }
-        const bool ok = p >= 0;
-        const uint64_t valid = wave_ballot(ok);
-        const uint64_t lower = (tid == 0) ? 0ull : (~0ull >> (kWave - tid));
-        if (ok) {
-            const int slot = __popcll(valid & lower);
-            s_row[slot] = p;
-            s_w[slot] = wt;
-        }
-        if (tid == 0)
-            s_n = __popcll(valid);
-    }
-    __syncthreads();
-    const int n = s_n;
-    const int nvec = H >> 3;
+        lds_barrier();
+        const int n = s_n[buf];
+        const int64_t *srow = s_row[buf];
+        const float *sw = s_w[buf];
 
-    for (int idx = tid; idx < nvec; idx += kRowThreads) {
-        float acc[8];
+        for (int base = tid; base < nvec; base += kCombineThreads * U) {
+            float acc[U][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            acc[j] = 0.0f;
-        for (int g = 0; g < n; g += 8) {
-            uint4 v[8];
+            for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (g + j < n)
-                    v[j] = reinterpret_cast<const uint4 *>(expert_out + s_row[g + j] * H)[idx];
+                for (int j = 0; j < 8; ++j)
+                    acc[u][j] = 0.0f;
+            for (int g = 0; g < n; g += 8) {
+                u32x4 v[U][8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (g + j < n) {
-                    const float wt = s_w[g + j];
-                    const uint32_t q[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+                for (int u = 0; u < U; ++u) {
+                    const int idx = base + u * kCombineThreads;
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        acc[2 * c] = fmaf(wt, bf16_lo(q[c]), acc[2 * c]);
-                        acc[2 * c + 1] = fmaf(wt, bf16_hi(q[c]), acc[2 * c + 1]);
-                    }
+                    for (int j = 0; j < 8; ++j)
+                        if (g + j < n && idx < nvec)
+                            v[u][j] = __builtin_nontemporal_load(
+                                reinterpret_cast<const u32x4 *>(expert_out + srow[g + j] * H) + idx);
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        if (g + j < n)
+                            fma_bf16x8(acc[u], sw[g + j], v[u][j]);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int idx = base + u * kCombineThreads;
+                if (idx >= nvec)
+                    continue;
+                if (OUT_BF16) {
+                    u32x4 o = {pack_bf16x2(acc[u][0], acc[u][1]), pack_bf16x2(acc[u][2], acc[u][3]),
+                               pack_bf16x2(acc[u][4], acc[u][5]), pack_bf16x2(acc[u][6], acc[u][7])};
+                    reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(y) + t * H)[idx] = o;
+                } else {
+                    f32x4 *yr = reinterpret_cast<f32x4 *>(static_cast<float *>(y) + t * H) + 2 * idx;
+                    yr[0] = f32x4{acc[u][0], acc[u][1], acc[u][2], acc[u][3]};
+                    yr[1] = f32x4{acc[u][4], acc[u][5], acc[u][6], acc[u][7]};
                 }
             }
-        }
-        if (OUT_BF16) {
-            uint4 o = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                                 pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
-            reinterpret_cast<uint4 *>(static_cast<uint16_t *>(y) + t * H)[idx] = o;
-        } else {
-            float4 *yr = reinterpret_cast<float4 *>(static_cast<float *>(y) + t * H);
-            yr[2 * idx] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-            yr[2 * idx + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
         }
     }
 }
@@ -534,14 +812,14 @@ __global__ __launch_bounds__(kRowThreads) void ep_expert_scale_kernel(
     const int nvec = H >> 3;
     for (int64_t p = blockIdx.x; p < n; p += gridDim.x) {
         const float f = 1.0f + (float)m_indices[p] * (1.0f / 256.0f);
-        const uint4 *src = reinterpret_cast<const uint4 *>(in + p * H);
-        uint4 *dst = reinterpret_cast<uint4 *>(out + p * H);
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(in + p * H);
+        u32x4 *dst = reinterpret_cast<u32x4 *>(out + p * H);
         for (int idx = threadIdx.x; idx < nvec; idx += kRowThreads) {
-            const uint4 v = src[idx];
-            dst[idx] = make_uint4(pack_bf16x2(bf16_lo(v.x) * f, bf16_hi(v.x) * f),
-                                  pack_bf16x2(bf16_lo(v.y) * f, bf16_hi(v.y) * f),
-                                  pack_bf16x2(bf16_lo(v.z) * f, bf16_hi(v.z) * f),
-                                  pack_bf16x2(bf16_lo(v.w) * f, bf16_hi(v.w) * f));
+            const u32x4 v = src[idx];
+            dst[idx] = u32x4{pack_bf16x2(bf16_lo(v.x) * f, bf16_hi(v.x) * f),
+                             pack_bf16x2(bf16_lo(v.y) * f, bf16_hi(v.y) * f),
+                             pack_bf16x2(bf16_lo(v.z) * f, bf16_hi(v.z) * f),
+                             pack_bf16x2(bf16_lo(v.w) * f, bf16_hi(v.w) * f)};
         }
     }
 }
