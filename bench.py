@@ -104,6 +104,9 @@ def main():
     ap.add_argument("--out-dtype", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--timed-only", action="store_true",
+                    help="skip the per-kernel, bubble and cold-cache loops (for profiling "
+                         "the timed region alone)")
     ap.add_argument("--copy-calibration", type=int, metavar="BYTES", default=0,
                     help="only run a plain copy kernel of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -237,29 +240,90 @@ def main():
     }
     assert epl.epl_status(ws) == epl.EPL_OK
 
-    # Per-kernel breakdown: the same kernels through the individual entry
-    # points (layout, scan, scatter, ...), an event around every launch.
-    for _ in range(args.warmup):
-        step_split()
-    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step_split(sev[i])
-    torch.cuda.synchronize()
-    per_kernel_ms = {
-        n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in sev])) for i, n in enumerate(names)}
-    assert epl.epl_status(ws) == epl.EPL_OK
+    per_kernel_ms, bubble, cold_ms = {}, {}, {}
+    if not args.timed_only:
+        # Per-kernel breakdown: the same kernels through the individual entry
+        # points (layout, scan, scatter, ...), an event around every launch.
+        for _ in range(args.warmup):
+            step_split()
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            step_split(sev[i])
+        torch.cuda.synchronize()
+        per_kernel_ms = {
+            n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in sev])) for i, n in enumerate(names)}
+        assert epl.epl_status(ws) == epl.EPL_OK
+
+        # The pages' "bubble": idle GPU time between the scan that yields the row
+        # count and the scatter that consumes it. Capacity mode enqueues the
+        # scatter right behind the scan; exact mode first brings N to the host,
+        # allocates exactly N rows and only then enqueues the scatter.
+        bubble = {}
+        for mode in ("capacity", "exact"):
+            gaps = []
+            for _ in range(args.warmup + 10):
+                ev_a = torch.cuda.Event(enable_timing=True)
+                ev_b = torch.cuda.Event(enable_timing=True)
+                calls[0]()
+                calls[1]()
+                ev_a.record(stream)
+                if mode == "exact":
+                    stream.synchronize()
+                    n_rows = int(total_host[0])
+                    o = torch.empty((n_rows, H), dtype=torch.bfloat16, device=dev)
+                    o_s = torch.empty((n_rows, S), dtype=torch.float32, device=dev) if S else None
+                    m_i = torch.empty(n_rows, dtype=i32, device=dev)
+                    ev_b.record(stream)
+                    epl.epl_scatter(p, x, xs, topk, start, ws, n_rows, o, o_s, m_i, oi)
+                else:
+                    ev_b.record(stream)
+                    calls[2]()
+                gaps.append((ev_a, ev_b))
+            torch.cuda.synchronize()
+            bubble[mode] = float(np.median([a.elapsed_time(b) for a, b in gaps[args.warmup:]]) * 1e3)
+        assert epl.epl_status(ws) == epl.EPL_OK
+
+        # Cold-cache kernel times: before each of scatter and combine, a 1 GiB read
+        # sweep evicts L2 and the Infinity Cache and lets earlier dirty lines drain
+        # outside the timed kernel, so these are HBM-only rates.
+        flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        cold = {"scatter": [], "combine": []}
+        for i in range(args.warmup + 10):
+            evc = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            calls[0]()
+            calls[1]()
+            flush_buf.sum()
+            evc[0].record(stream)
+            calls[2]()
+            evc[1].record(stream)
+            for call in calls[3:-1]:
+                call()
+            flush_buf.sum()
+            evc[2].record(stream)
+            calls[-1]()
+            evc[3].record(stream)
+            if i >= args.warmup:
+                cold["scatter"].append(evc)
+                cold["combine"].append(evc)
+        torch.cuda.synchronize()
+        cold_ms = {"scatter": float(np.median([e[0].elapsed_time(e[1]) for e in cold["scatter"]])),
+                   "combine": float(np.median([e[2].elapsed_time(e[3]) for e in cold["combine"]]))}
+        del flush_buf
+        assert epl.epl_status(ws) == epl.EPL_OK
 
     nbytes = algorithmic_bytes(w, N, T_any, 4 if out_code == epl.EPL_OUT_F32 else 2)
-    gbps = {n: nbytes[n] / (per_kernel_ms[n] * 1e-3) / 1e9 for n in names}
+    gbps = {n: nbytes[n] / (per_kernel_ms[n] * 1e-3) / 1e9 for n in per_kernel_ms}
     # combine's duration in the timed region is exact; scatter's comes from
     # the per-kernel breakdown
     kernel_ms = dict(per_kernel_ms, combine=timed_ms["combine"])
+    if args.timed_only:
+        kernel_ms["scatter"] = 0.0
     dominant = max(("scatter", "combine"), key=lambda n: kernel_ms[n])
     dom_gbps = nbytes[dominant] / (kernel_ms[dominant] * 1e-3) / 1e9
     sc_ms = kernel_ms["scatter"] + kernel_ms["combine"]
-    sc_gbps = (nbytes["scatter"] + nbytes["combine"]) / (sc_ms * 1e-3) / 1e9
+    sc_gbps = (nbytes["scatter"] + nbytes["combine"]) / (sc_ms * 1e-3) / 1e9 if sc_ms else 0.0
     traffic = measured_traffic(w.name, dominant)
 
     cpu = None
@@ -292,6 +356,13 @@ def main():
         "per_kernel_gbps": gbps,
         "algorithmic_bytes": nbytes,
         "scatter_combine": {"ms": sc_ms, "gbps": sc_gbps, "frac_of_peak": sc_gbps / HBM_PEAK_GBPS},
+        "scan_to_scatter_gap_us": bubble,
+        "cold_cache": None if not cold_ms else {
+            "ms": cold_ms,
+            "gbps": {k: nbytes[k] / (v * 1e-3) / 1e9 for k, v in cold_ms.items()},
+            "scatter_combine_frac_of_peak": (nbytes["scatter"] + nbytes["combine"]) /
+            ((cold_ms["scatter"] + cold_ms["combine"]) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        },
         "roofline": {
             "kernel": dominant,
             "bound": "hbm",

@@ -89,7 +89,13 @@ T *at(void *ws, size_t off)
 
 int launch_status() { return hipGetLastError() == hipSuccess ? EPL_OK : EPL_EHIP; }
 
-unsigned row_grid(int64_t tokens, int limit) { return (unsigned)std::min<int64_t>(tokens, limit); }
+// Workgroups for a row kernel: min(tokens, limit), and never more than 2^24
+// (the dispatch packet counts work-items in 32 bits); the kernels stride over
+// any tokens beyond the grid.
+unsigned row_grid(int64_t tokens, int64_t limit)
+{
+    return (unsigned)std::min<int64_t>(tokens, std::min<int64_t>(limit, int64_t(1) << 24));
+}
 
 int enqueue_layout(const epl_problem &p, const WsLayout &w, const int64_t *topk, uint8_t *in_rank,
                    void *ws, hipStream_t s)
@@ -145,7 +151,10 @@ void launch_scatter(const epl_problem &p, const WsLayout &w, const uint16_t *x, 
                     const int64_t *topk, const int32_t *start, void *ws, int64_t cap,
                     uint16_t *out, float *out_scale, int32_t *m_idx, int32_t *oi, hipStream_t s)
 {
-    hipLaunchKernelGGL(epl::ep_scatter_kernel<VPT>, dim3(row_grid(p.num_tokens, epl::kScatterGrid)),
+    const unsigned grid = p.num_tokens >= epl::kScatterGridFrom
+                              ? row_grid(p.num_tokens, p.num_tokens)
+                              : row_grid(p.num_tokens, epl::kScatterGrid);
+    hipLaunchKernelGGL(epl::ep_scatter_kernel<VPT>, dim3(grid),
                        dim3(epl::kScatterThreads), 0, s, x, xs, topk, start,
                        at<const int32_t>(ws, w.block_count), at<const int32_t>(ws, w.slot_rank),
                        p.num_tokens, p.num_topk, p.num_experts, p.hidden, p.scale_cols,

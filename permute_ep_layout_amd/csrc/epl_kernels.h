@@ -52,8 +52,11 @@ constexpr int kRowThreads = 128;          // expert-scale workgroup
 #ifndef EPL_SCATTER_GRID
 #define EPL_SCATTER_GRID 1024
 #endif
+#ifndef EPL_SCATTER_GRID_FROM
+#define EPL_SCATTER_GRID_FROM 8192
+#endif
 #ifndef EPL_COMBINE_GRID
-#define EPL_COMBINE_GRID 4096
+#define EPL_COMBINE_GRID (1 << 30)
 #endif
 constexpr int kScatterThreads = EPL_SCATTER_THREADS;
 constexpr int kCombineThreads = EPL_COMBINE_THREADS;
@@ -455,10 +458,13 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Workgroup counts of the row kernels: one token per workgroup while that is
-// at most the limit, otherwise the limit, each workgroup striding over tokens
-// (4 scatter / 16 combine workgroups per CU on 256 CUs).
+// Workgroup counts of the row kernels. Combine: one workgroup per token (the
+// dispatcher starts a new workgroup as soon as one retires, which balances
+// better than striding). Scatter: also one per token from
+// kScatterGridFrom tokens on; below that, kScatterGrid workgroups striding
+// over the tokens, which measured faster at a few thousand tokens.
 constexpr int kScatterGrid = EPL_SCATTER_GRID;
+constexpr int64_t kScatterGridFrom = EPL_SCATTER_GRID_FROM;
 constexpr int kCombineGrid = EPL_COMBINE_GRID;
 
 #ifndef EPL_XCD_MAP
@@ -466,6 +472,9 @@ constexpr int kCombineGrid = EPL_COMBINE_GRID;
 #endif
 #ifndef EPL_SCALE_NT
 #define EPL_SCALE_NT 0
+#endif
+#ifndef EPL_ROW_NT
+#define EPL_ROW_NT 1
 #endif
 constexpr int kNumXcd = 8;   // MI355X: 8 XCDs, workgroup i runs on XCD i % 8
 
@@ -619,9 +628,13 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
                 if (idx < nvec) {
                     for (int k = 0; k < K; ++k) {
                         const int64_t row = rows[k];
-                        if (row >= 0)
-                            __builtin_nontemporal_store(
-                                v[i], reinterpret_cast<u32x4 *>(out + row * H) + idx);
+                        if (row >= 0) {
+                            u32x4 *dst = reinterpret_cast<u32x4 *>(out + row * H) + idx;
+                            if (EPL_ROW_NT)
+                                __builtin_nontemporal_store(v[i], dst);
+                            else
+                                *dst = v[i];
+                        }
                     }
                 }
             }
