@@ -59,10 +59,10 @@ class Oracle:
         lib.epl_oracle_bf16_from_double.restype = ctypes.c_uint16
         lib.epl_oracle_layout.argtypes = [_c_i64, _c_i32, _c_i32, _c_i32, _ptr, _ptr, _ptr, _ptr]
         lib.epl_oracle_layout.restype = ctypes.c_int
-        lib.epl_oracle_scan.argtypes = [_c_i32, _ptr, _ptr, _ptr]
+        lib.epl_oracle_scan.argtypes = [_c_i32, _ptr, _c_i32, _ptr, _ptr]
         lib.epl_oracle_scan.restype = ctypes.c_int
         lib.epl_oracle_scatter.argtypes = [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
-                                           _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr]
+                                           _ptr, _ptr, _ptr, _ptr, _c_i64, _ptr, _ptr, _ptr, _ptr]
         lib.epl_oracle_scatter.restype = ctypes.c_int
         lib.epl_oracle_expert_scale.argtypes = [_c_i64, _c_i32, _ptr, _ptr, _ptr]
         lib.epl_oracle_expert_scale.restype = ctypes.c_int
@@ -95,12 +95,14 @@ class Oracle:
                                           _p(per_rank), _p(in_rank)), "layout")
         return cnt, per_rank, in_rank
 
-    def scan(self, num_tokens_per_expert: np.ndarray):
-        """Returns (expert_start_loc [E] i32, total int)."""
+    def scan(self, num_tokens_per_expert: np.ndarray, alignment: int = 0):
+        """Returns (expert_start_loc [E] i32, total int); with alignment a > 1
+        each expert's block is its count rounded up to a multiple of a."""
         cnt = _c(num_tokens_per_expert, np.int32)
         start = np.empty(cnt.size, np.int32)
         total = np.zeros(1, np.int64)
-        _check(self.lib.epl_oracle_scan(cnt.size, _p(cnt), _p(start), _p(total)), "scan")
+        _check(self.lib.epl_oracle_scan(cnt.size, _p(cnt), int(alignment), _p(start), _p(total)),
+               "scan")
         return start, int(total[0])
 
     def scatter(self, x: Optional[np.ndarray], x_scale: Optional[np.ndarray],
@@ -122,12 +124,13 @@ class Oracle:
         m_idx = np.empty(total, np.int32)
         oi = np.empty((T, K), np.int32)
         _check(self.lib.epl_oracle_scatter(T, K, E, H, S, _p(xx), _p(xs), _p(topk), _p(start),
-                                           _p(out), _p(out_scale), _p(m_idx), _p(oi)),
+                                           total, _p(out), _p(out_scale), _p(m_idx), _p(oi)),
                "scatter")
         return out, out_scale, m_idx, oi
 
     def expert_scale(self, rows: np.ndarray, m_indices: np.ndarray) -> np.ndarray:
-        """The large-batch workload's synthetic expert: bf16(row * (1 + e/256))."""
+        """The large-batch workload's synthetic expert: bf16(row * (1 + e/256)).
+        (Rows marked -1 are alignment padding; their output is not meaningful.)"""
         r = _c(rows, np.uint16)
         m = _c(m_indices, np.int32)
         N, H = r.shape
@@ -151,10 +154,10 @@ class Oracle:
         return y
 
     def run_all(self, x, x_scale, topk_idx, topk_weights, num_experts, num_ranks,
-                expert_fn="identity"):
+                expert_fn="identity", alignment=0):
         """The whole path on the CPU: layout, scan, scatter, (expert), combine."""
         cnt, per_rank, in_rank = self.layout(topk_idx, num_experts, num_ranks)
-        start, total = self.scan(cnt)
+        start, total = self.scan(cnt, alignment)
         out, out_scale, m_idx, oi = self.scatter(x, x_scale, topk_idx, start, total)
         eo = out if expert_fn == "identity" else self.expert_scale(out, m_idx)
         y = self.combine(eo, oi, topk_weights)

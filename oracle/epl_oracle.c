@@ -147,18 +147,24 @@ int epl_oracle_layout(int64_t T, int32_t K, int32_t E, int32_t R,
 
 /* [ANATOMY] subsection 5 / [SGLANG] section 2.2: each expert's block starts
  * where the previous one ended, the first at 0; the buffer holds the sum of
- * all counts. */
-int epl_oracle_scan(int32_t E, const int32_t *num_tokens_per_expert,
+ * all block sizes. With an alignment a > 1 ([DEEPEP] Dispatch, the
+ * expert_alignment argument; [SGLANG] section 3.3, block_m for the grouped
+ * GEMM) an expert's block size is its count rounded up to a multiple of a;
+ * a <= 1 means no rounding. */
+int epl_oracle_scan(int32_t E, const int32_t *num_tokens_per_expert, int32_t alignment,
                     int32_t *expert_start_loc, int64_t *total)
 {
-    if (E < 1)
+    if (E < 1 || alignment < 0)
         return ORACLE_EINVAL;
+    int64_t a = alignment > 1 ? alignment : 1;
     int64_t running = 0;
     for (int32_t e = 0; e < E; ++e) {
         if (num_tokens_per_expert[e] < 0)
             return ORACLE_EINVAL;
         expert_start_loc[e] = (int32_t)running;
-        running += num_tokens_per_expert[e];
+        int64_t c = num_tokens_per_expert[e];
+        int64_t blocks = c / a + (c % a != 0);
+        running += blocks * a;
     }
     *total = running;
     return ORACLE_OK;
@@ -171,16 +177,21 @@ int epl_oracle_scan(int32_t E, const int32_t *num_tokens_per_expert,
  * sort: a cursor per expert starts at the expert's offset and advances by
  * one per placed row). The row receives a bit copy of x[t] and, when scales
  * are present, of x_scale[t]; m_indices[row] = expert; output_index[t, k] =
- * row, or -1 for a -1 slot. Any of out / out_scale may be NULL to skip the
- * row copies (used when only the indices are compared). */
+ * row, or -1 for a -1 slot. A row of the total_rows that receives no slot
+ * (alignment padding at the end of an expert's block) has m_indices = -1,
+ * the marker the grouped GEMM skips ([SGLANG] section 3.3). Any of out /
+ * out_scale may be NULL to skip the row copies (used when only the indices
+ * are compared). */
 int epl_oracle_scatter(int64_t T, int32_t K, int32_t E, int32_t H, int32_t S,
                        const uint16_t *x, const float *x_scale,
                        const int64_t *topk_idx, const int32_t *expert_start_loc,
-                       uint16_t *out, float *out_scale,
+                       int64_t total_rows, uint16_t *out, float *out_scale,
                        int32_t *m_indices, int32_t *output_index)
 {
-    if (T < 0 || K < 1 || E < 1 || H < 0 || S < 0)
+    if (T < 0 || K < 1 || E < 1 || H < 0 || S < 0 || total_rows < 0)
         return ORACLE_EINVAL;
+    for (int64_t p = 0; p < total_rows; ++p)
+        m_indices[p] = -1;
     int64_t *cursor = (int64_t *)malloc(sizeof(int64_t) * (size_t)E);
     if (!cursor)
         return ORACLE_EINVAL;

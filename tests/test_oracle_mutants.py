@@ -23,8 +23,12 @@ MUTANTS = {
     "cursor_advances_by_two": ("cursor[e] += 1;", "cursor[e] += 2;"),
     "round_robin_owner": ("is_token_in_rank[t * R + e / experts_per_rank] = 1;",
                           "is_token_in_rank[t * R + e % R] = 1;"),
-    "inclusive_scan": ("expert_start_loc[e] = (int32_t)running;\n        running += num_tokens_per_expert[e];",
-                       "running += num_tokens_per_expert[e];\n        expert_start_loc[e] = (int32_t)running;"),
+    "inclusive_scan": ("expert_start_loc[e] = (int32_t)running;\n        int64_t c = num_tokens_per_expert[e];\n        int64_t blocks = c / a + (c % a != 0);\n        running += blocks * a;",
+                       "int64_t c = num_tokens_per_expert[e];\n        int64_t blocks = c / a + (c % a != 0);\n        running += blocks * a;\n        expert_start_loc[e] = (int32_t)running;"),
+    "alignment_rounds_down": ("int64_t blocks = c / a + (c % a != 0);", "int64_t blocks = c / a;"),
+    "alignment_always_one_extra_block": ("int64_t blocks = c / a + (c % a != 0);", "int64_t blocks = c / a + 1;"),
+    "padding_marked_zero": ("for (int64_t p = 0; p < total_rows; ++p)\n        m_indices[p] = -1;",
+                            "for (int64_t p = 0; p < total_rows; ++p)\n        m_indices[p] = 0;"),
     "per_rank_counts_every_token": ("num_tokens_per_rank[r] += is_token_in_rank[t * R + r];",
                                     "num_tokens_per_rank[r] += 1;"),
     "weight_of_mirrored_slot": ("double w = (double)topk_weights[t * K + k];",
@@ -113,6 +117,28 @@ def _battery(orc: Oracle):
         return (np.array_equal(out[oi[tt, kk]], x[tt])
                 and np.array_equal(out_scale[oi[tt, kk]], xs[tt]))
 
+    def golden_alignment():
+        g = load_golden("scan_alignment_example.txt")
+        start, total = orc.scan(np.array(g["counts"]), g["alignment"][0])
+        return start.tolist() == g["expert_start_loc"] and total == g["total"][0]
+
+    def brute_aligned():
+        rng = np.random.default_rng(77)
+        for _ in range(20):
+            R = int(rng.integers(1, 4))
+            E = R * int(rng.integers(1, 4))
+            T, K = int(rng.integers(1, 9)), int(rng.integers(1, 4))
+            a = int(rng.integers(2, 6))
+            topk = rng.integers(-1, E, size=(T, K)).astype(np.int64)
+            want = brute_force(topk, E, R, alignment=a)
+            cnt, _, _ = orc.layout(topk, E, R)
+            start, total = orc.scan(cnt, a)
+            _, _, m, oi = orc.scatter(None, None, topk, start, total)
+            if not (np.array_equal(start, want["start"]) and total == want["total"]
+                    and np.array_equal(oi, want["oi"]) and np.array_equal(m, want["m"])):
+                return False
+        return True
+
     def one_hot_combine():
         rng = np.random.default_rng(3)
         T, K, N = 6, 3, 18
@@ -144,6 +170,7 @@ def _battery(orc: Oracle):
         return orc.expert_scale(rows, m)[:, 0].tolist() == [0x4000, 0x3FC0, 0x3F82, 0x3F80]
 
     for name, fn in [("golden_scan", golden_scan), ("golden_hand", golden_hand), ("brute", brute),
+                     ("golden_alignment", golden_alignment), ("brute_aligned", brute_aligned),
                      ("rows_and_scales", rows_and_scales), ("one_hot_combine", one_hot_combine),
                      ("bf16_vs_torch", bf16_vs_torch), ("expert_scale_hand", expert_scale_hand)]:
         pin(name, fn)

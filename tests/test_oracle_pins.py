@@ -24,8 +24,10 @@ from oracle import OracleError
 
 # --------------------------------------------------------------- helpers --
 
-def brute_force(topk, E, R):
-    """Every quantity straight from its definition, by enumeration."""
+def brute_force(topk, E, R, alignment=0):
+    """Every quantity straight from its definition, by enumeration. With an
+    alignment a > 1, expert e's block holds the smallest multiple of a that
+    is >= its count, and rows holding no slot are marked -1."""
     T, K = topk.shape
     slots = [(t, k) for t in range(T) for k in range(K)]
     epr = E // R
@@ -33,7 +35,9 @@ def brute_force(topk, E, R):
     in_rank = [[int(any(topk[t, k] >= 0 and topk[t, k] // epr == r for k in range(K)))
                 for r in range(R)] for t in range(T)]
     per_rank = [sum(in_rank[t][r] for t in range(T)) for r in range(R)]
-    start = [sum(cnt[:e]) for e in range(E)]
+    a = max(alignment, 1)
+    size = [min(m for m in range(0, c + a, a) if m >= c) for c in cnt]
+    start = [sum(size[:e]) for e in range(E)]
     oi = [[-1] * K for _ in range(T)]
     for (t, k) in slots:
         e = topk[t, k]
@@ -41,8 +45,8 @@ def brute_force(topk, E, R):
             continue
         earlier = sum(1 for (t2, k2) in slots if topk[t2, k2] == e and (t2, k2) < (t, k))
         oi[t][k] = start[e] + earlier
-    N = sum(cnt)
-    m = [None] * N
+    N = sum(size)
+    m = [-1] * N
     for (t, k) in slots:
         if oi[t][k] >= 0:
             m[oi[t][k]] = topk[t, k]
@@ -50,18 +54,18 @@ def brute_force(topk, E, R):
                 start=np.array(start), total=N, oi=np.array(oi), m=np.array(m, dtype=np.int64))
 
 
-def run_oracle(topk, E, R, x=None, x_scale=None, orc=None):
+def run_oracle(topk, E, R, x=None, x_scale=None, orc=None, alignment=0):
     orc = orc or oracle.default()
     cnt, per_rank, in_rank = orc.layout(topk, E, R)
-    start, total = orc.scan(cnt)
+    start, total = orc.scan(cnt, alignment)
     out, out_scale, m, oi = orc.scatter(x, x_scale, topk, start, total)
     return dict(cnt=cnt, per_rank=per_rank, in_rank=in_rank, start=start, total=total,
                 out=out, out_scale=out_scale, m=m, oi=oi)
 
 
-def assert_same_as_brute(topk, E, R, orc=None):
-    got = run_oracle(topk, E, R, orc=orc)
-    want = brute_force(topk, E, R)
+def assert_same_as_brute(topk, E, R, orc=None, alignment=0):
+    got = run_oracle(topk, E, R, orc=orc, alignment=alignment)
+    want = brute_force(topk, E, R, alignment=alignment)
     np.testing.assert_array_equal(got["cnt"], want["cnt"])
     np.testing.assert_array_equal(got["per_rank"], want["per_rank"])
     np.testing.assert_array_equal(got["in_rank"], want["in_rank"].reshape(got["in_rank"].shape))
@@ -139,6 +143,53 @@ def test_random_small_against_brute_force(seed):
     K = int(rng.integers(1, 5))
     topk = rng.integers(-1, E, size=(T, K)).astype(np.int64)
     assert_same_as_brute(topk, E, R)
+
+
+@pytest.mark.parametrize("T,K,E,R,a", [(2, 2, 3, 3, 2), (3, 2, 2, 1, 3), (1, 3, 4, 2, 4)])
+def test_exhaustive_tiny_aligned_against_brute_force(T, K, E, R, a):
+    for vals in itertools.product(range(-1, E), repeat=T * K):
+        topk = np.array(vals, dtype=np.int64).reshape(T, K)
+        assert_same_as_brute(topk, E, R, alignment=a)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_small_aligned_against_brute_force(seed):
+    rng = np.random.default_rng(3000 + seed)
+    R = int(rng.integers(1, 4))
+    E = R * int(rng.integers(1, 4))
+    T, K = int(rng.integers(0, 12)), int(rng.integers(1, 4))
+    a = int(rng.integers(0, 7))
+    topk = rng.integers(-1, E, size=(T, K)).astype(np.int64)
+    assert_same_as_brute(topk, E, R, alignment=a)
+
+
+def test_golden_alignment_example():
+    g = load_golden("scan_alignment_example.txt")
+    start, total = oracle.scan(np.array(g["counts"]), g["alignment"][0])
+    assert start.tolist() == g["expert_start_loc"]
+    assert total == g["total"][0]
+
+
+@pytest.mark.parametrize("a", [1, 2, 16, 256])
+def test_aligned_total_within_the_pages_upper_bound(a):
+    """The vLLM fork's bound for the permuted row count with block_m padding:
+    round_up(T*K + E*(a-1), a) ([SGLANG] section 4, compute_aligned_M). Every
+    block is a multiple of a, holds its expert's rows first and pads with
+    fewer than a rows marked -1."""
+    from permute_ep_layout_amd import workloads
+    w = workloads.get("small").with_(num_tokens=700)
+    topk = workloads.make_topk(w)
+    E, R = w.num_experts, w.num_ranks
+    T, K = topk.shape
+    got = run_oracle(topk, E, R, alignment=a)
+    bound = -(-(T * K + E * (a - 1)) // a) * a
+    assert got["total"] <= bound and got["total"] % a == 0
+    ends = list(got["start"][1:]) + [got["total"]]
+    for e in range(E):
+        size = ends[e] - got["start"][e]
+        assert size % a == 0 and 0 <= size - got["cnt"][e] < a
+        blk = got["m"][got["start"][e]:ends[e]]
+        assert (blk[:got["cnt"][e]] == e).all() and (blk[got["cnt"][e]:] == -1).all()
 
 
 # ------------------------------------------------- library routine: argsort --
