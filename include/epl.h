@@ -73,9 +73,13 @@ typedef struct epl_problem {
     int32_t num_ranks;    /* R >= 1, E % R == 0                               */
     int32_t hidden;       /* H >= 8, H % 8 == 0 (16-byte rows of bf16)        */
     int32_t scale_cols;   /* S: 0 (no scales) or H / 128 (needs H % 128 == 0) */
-    int32_t reserved;     /* must be 0                                        */
+    int32_t expert_alignment; /* a: 0 or 1 = no padding; a > 1 (<= 65536): each
+                             expert's block is padded to a multiple of a rows
+                             (the grouped GEMM's block_m; DeepEP's
+                             expert_alignment). Padding rows get m_indices = -1
+                             and are otherwise not written.               */
 } epl_problem;
-/* Also required: T * K <= INT32_MAX (row indices are int32). */
+/* Also required: T * K + E * (a - 1) <= INT32_MAX (row indices are int32). */
 
 /* Host-only check of a problem description. Needs no GPU. */
 int epl_validate(const epl_problem *p);
@@ -87,6 +91,12 @@ int epl_validate(const epl_problem *p);
  * epl_layout / epl_dispatch write every byte that later calls read. Its
  * address must be 256-byte aligned. Host-only; needs no GPU. */
 size_t epl_workspace_bytes(const epl_problem *p);
+
+/* Rows that always suffice for the ragged buffer of problem `p`: T * K
+ * without alignment, else round_up(T * K + E * (a - 1), a) (the bound of the
+ * vLLM fork's compute_aligned_M in "参考sglang代码，重构vllm021中EP高吞吐代码，
+ * 消除空泡问题", section 4). -1 if `p` is invalid. Host-only. */
+int64_t epl_capacity_rows(const epl_problem *p);
 
 /* Step 1 -- layout. Reads topk_idx [T, K] int64 (-1 = no selection).
  * Writes num_tokens_per_expert [E] int32 (routed slots per expert),
@@ -100,9 +110,12 @@ int epl_layout(const epl_problem *p, const int64_t *topk_idx,
                int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,
                uint8_t *is_token_in_rank, void *workspace, void *stream);
 
-/* Step 2 -- scan. expert_start_loc[e] = sum of num_tokens_per_expert[e'] for
- * e' < e (exclusive, expert_start_loc[0] = 0); the total N = sum of all
- * counts is stored in the workspace and, if `total_host` is not NULL, copied
+/* Step 2 -- scan. expert_start_loc[e] = sum of block sizes of experts e' < e
+ * (exclusive, expert_start_loc[0] = 0), where an expert's block size is its
+ * count, rounded up to a multiple of the expert alignment when a > 1 ("高性能
+ * 专家并行（EP）内核解剖学解读", high-throughput part, subsections 3 and 5).
+ * The total N = sum of all block sizes (the ragged buffer's row count) is
+ * stored in the workspace and, if `total_host` is not NULL, copied
  * asynchronously to *total_host, which must be pinned host memory
  * (hipHostMalloc / torch pin_memory). *total_host is valid once the stream
  * has reached this point (after any later synchronisation of the stream). */
@@ -115,9 +128,12 @@ int epl_scan(const epl_problem *p, const int32_t *num_tokens_per_expert,
  *         before (t, k) in (token, k) order)
  *   out[row, :] = x[t, :] (bit copy, H bf16 values), out_scale[row, :] =
  *   x_scale[t, :] (S floats) when S > 0, m_indices[row] = e,
- *   output_index[t, k] = row. Slots with -1 get output_index = -1.
+ *   output_index[t, k] = row. Slots with -1 get output_index = -1. With an
+ *   expert alignment a > 1 the rows between an expert's last row and the
+ *   end of its padded block get m_indices = -1 (nothing else is written).
  * `out` / `out_scale` / `m_indices` have room for `capacity_rows` rows
- * (capacity_rows >= N; T * K always suffices); rows >= N are not written.
+ * (capacity_rows >= N; epl_capacity_rows() always suffices); rows >= N are
+ * not written.
  * If N > capacity_rows the rows past the capacity are skipped and the
  * status word records EPL_ECAPACITY. Requires that epl_layout and then
  * epl_scan (with the counts epl_layout produced) ran on the same
@@ -157,8 +173,9 @@ int epl_combine(const epl_problem *p, const uint16_t *expert_out,
 /* The synthetic expert of the large-batch workload (not a step of the
  * dispatch path; it stands in for the grouped GEMM between scatter and
  * combine): rows_out[p, :] = bf16_rne(float(rows_in[p, :]) * (1 + m_indices[p]/256))
- * for p < min(N, capacity_rows), N being the total that the last
- * epl_scan / epl_dispatch on `workspace` stored. rows_in may equal rows_out. */
+ * for p < min(N, capacity_rows) with m_indices[p] >= 0 (padding rows are
+ * skipped), N being the total that the last epl_scan / epl_dispatch on
+ * `workspace` stored. rows_in may equal rows_out. */
 int epl_expert_scale(const epl_problem *p, const uint16_t *rows_in,
                      const int32_t *m_indices, int64_t capacity_rows,
                      uint16_t *rows_out, const void *workspace, void *stream);
@@ -175,7 +192,7 @@ int64_t epl_total(const void *workspace, void *stream);
 /* Static text for a status code. */
 const char *epl_strerror(int code);
 
-/* Library version, e.g. 0x000100 for 0.1.0. */
+/* Library version, e.g. 0x000200 for 0.2.0. */
 int epl_version(void);
 
 #ifdef __cplusplus

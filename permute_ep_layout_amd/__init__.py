@@ -20,8 +20,8 @@ from . import build as _build
 
 __all__ = [
     "EplError", "Problem", "lib_path", "load", "is_built", "ensure_built",
-    "epl_validate", "epl_workspace_bytes", "epl_layout", "epl_scan", "epl_scatter",
-    "epl_dispatch", "epl_combine", "epl_expert_scale", "epl_status", "epl_total",
+    "epl_validate", "epl_workspace_bytes", "epl_capacity_rows", "epl_layout", "epl_scan",
+    "epl_scatter", "epl_dispatch", "epl_combine", "epl_expert_scale", "epl_status", "epl_total",
     "epl_strerror", "epl_version", "dispatch", "combine", "expert_scale", "DispatchResult",
     "EPL_OK", "EPL_EINVAL", "EPL_ERANGE", "EPL_ECAPACITY", "EPL_EHIP", "EPL_OUT_F32",
     "EPL_OUT_BF16", "prepare",
@@ -37,8 +37,8 @@ EPL_OUT_BF16 = 1
 
 # Every function include/epl.h declares; tests check the library exports them.
 C_ENTRY_POINTS = (
-    "epl_validate", "epl_workspace_bytes", "epl_layout", "epl_scan", "epl_scatter",
-    "epl_dispatch", "epl_combine", "epl_expert_scale", "epl_status", "epl_total",
+    "epl_validate", "epl_workspace_bytes", "epl_capacity_rows", "epl_layout", "epl_scan",
+    "epl_scatter", "epl_dispatch", "epl_combine", "epl_expert_scale", "epl_status", "epl_total",
     "epl_strerror", "epl_version",
 )
 
@@ -62,17 +62,19 @@ class Problem(ctypes.Structure):
         ("num_ranks", ctypes.c_int32),
         ("hidden", ctypes.c_int32),
         ("scale_cols", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("expert_alignment", ctypes.c_int32),
     ]
 
     @classmethod
-    def make(cls, num_tokens, num_topk, num_experts, num_ranks, hidden, scale_cols=0):
+    def make(cls, num_tokens, num_topk, num_experts, num_ranks, hidden, scale_cols=0,
+             expert_alignment=0):
         return cls(int(num_tokens), int(num_topk), int(num_experts), int(num_ranks), int(hidden),
-                   int(scale_cols), 0)
+                   int(scale_cols), int(expert_alignment))
 
     def __repr__(self):
         return (f"Problem(T={self.num_tokens}, K={self.num_topk}, E={self.num_experts}, "
-                f"R={self.num_ranks}, H={self.hidden}, S={self.scale_cols})")
+                f"R={self.num_ranks}, H={self.hidden}, S={self.scale_cols}, "
+                f"a={self.expert_alignment})")
 
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -115,6 +117,8 @@ def load() -> ctypes.CDLL:
     lib.epl_validate.restype = i32
     lib.epl_workspace_bytes.argtypes = [_PP]
     lib.epl_workspace_bytes.restype = ctypes.c_size_t
+    lib.epl_capacity_rows.argtypes = [_PP]
+    lib.epl_capacity_rows.restype = i64
     lib.epl_layout.argtypes = [_PP, _P, _P, _P, _P, _P, _P]
     lib.epl_layout.restype = i32
     lib.epl_scan.argtypes = [_PP, _P, _P, _P, _P, _P]
@@ -204,6 +208,10 @@ def epl_validate(p: Problem) -> int:
 
 def epl_workspace_bytes(p: Problem) -> int:
     return int(load().epl_workspace_bytes(_prob(p)))
+
+
+def epl_capacity_rows(p: Problem) -> int:
+    return int(load().epl_capacity_rows(_prob(p)))
 
 
 def epl_layout(p: Problem, topk_idx, num_tokens_per_expert, num_tokens_per_rank,
@@ -389,19 +397,19 @@ def workspace_for(p: Problem, device):
 
 def dispatch(x, topk_idx, num_experts: int, num_ranks: int, x_scale=None,
              capacity: Optional[int] = None, mode: str = "capacity", workspace=None,
-             stream=None) -> DispatchResult:
+             stream=None, expert_alignment: int = 0) -> DispatchResult:
     """Layout + scan + scatter.
 
     mode="capacity" (default): one epl_dispatch call; the output buffers have
-    `capacity` rows (default T*K, which always suffices) and no host wait
-    happens. mode="exact": epl_layout + epl_scan, then the host waits for the
+    `capacity` rows (default epl_capacity_rows, which always suffices) and no
+    host wait happens. mode="exact": epl_layout + epl_scan, then the host waits for the
     total N, allocates exactly N rows and calls epl_scatter.
     """
     torch = _torch()
     T, H = x.shape
     K = topk_idx.shape[1]
     S = 0 if x_scale is None else x_scale.shape[1]
-    p = Problem.make(T, K, num_experts, num_ranks, H, S)
+    p = Problem.make(T, K, num_experts, num_ranks, H, S, expert_alignment)
     _check(epl_validate(p), "epl_validate")
     dev = x.device
     ws = workspace if workspace is not None else workspace_for(p, dev)
@@ -413,7 +421,7 @@ def dispatch(x, topk_idx, num_experts: int, num_ranks: int, x_scale=None,
     oi = torch.empty((T, K), dtype=i32, device=dev)
     total_host = torch.zeros(1, dtype=i32, pin_memory=True)
     if mode == "capacity":
-        cap = T * K if capacity is None else int(capacity)
+        cap = epl_capacity_rows(p) if capacity is None else int(capacity)
         out = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
         out_scale = torch.empty((cap, S), dtype=torch.float32, device=dev) if S else None
         m_idx = torch.empty(cap, dtype=i32, device=dev)

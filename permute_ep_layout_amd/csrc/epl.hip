@@ -22,6 +22,16 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+int alignment_of(const epl_problem &p) { return p.expert_alignment > 1 ? p.expert_alignment : 1; }
+
+// Rows that always suffice: T*K, or round_up(T*K + E*(a-1), a) with padding.
+int64_t capacity_bound(const epl_problem &p)
+{
+    const int64_t a = alignment_of(p);
+    const int64_t rows = p.num_tokens * (int64_t)p.num_topk + (int64_t)p.num_experts * (a - 1);
+    return (rows + a - 1) / a * a;
+}
+
 bool problem_ok(const epl_problem *p)
 {
     if (!p)
@@ -36,9 +46,9 @@ bool problem_ok(const epl_problem *p)
         return false;
     if (p->scale_cols != 0 && (p->hidden % 128 != 0 || p->scale_cols != p->hidden / 128))
         return false;
-    if (p->reserved != 0)
+    if (p->expert_alignment < 0 || p->expert_alignment > epl::kMaxAlignment)
         return false;
-    if (p->num_tokens * (int64_t)p->num_topk > (int64_t)INT32_MAX)
+    if (capacity_bound(*p) > (int64_t)INT32_MAX)
         return false;
     return true;
 }
@@ -60,7 +70,7 @@ int layout_block_tokens(const epl_problem &p)
 struct WsLayout {
     int block_tokens;
     int64_t num_blocks;
-    size_t block_count, block_rank, block_err, slot_rank, bytes;
+    size_t counts, block_count, block_rank, block_err, slot_rank, bytes;
 };
 
 WsLayout ws_layout(const epl_problem &p)
@@ -69,6 +79,8 @@ WsLayout ws_layout(const epl_problem &p)
     w.block_tokens = layout_block_tokens(p);
     w.num_blocks = (p.num_tokens + w.block_tokens - 1) / w.block_tokens;
     size_t off = round_up(sizeof(WsHeader), kWsAlign);
+    w.counts = off;
+    off += round_up((size_t)p.num_experts * 4, kWsAlign);
     w.block_count = off;
     off += round_up((size_t)w.num_blocks * (size_t)p.num_experts * 4, kWsAlign);
     w.block_rank = off;
@@ -132,9 +144,10 @@ int enqueue_scan(const epl_problem &p, const WsLayout &w, int mode, int32_t *cnt
 {
     int32_t *mapped = (mode & epl::kScanPrefix) ? mapped_host_word(total_host) : nullptr;
     hipLaunchKernelGGL(epl::ep_scan_kernel, dim3(1), dim3(epl::kScanThreads), 0, s, mode,
-                       w.num_blocks, p.num_experts, p.num_ranks, at<int32_t>(ws, w.block_count),
-                       at<int32_t>(ws, w.block_rank), at<uint32_t>(ws, w.block_err), cnt, per_rank,
-                       start, at<WsHeader>(ws, 0), mapped);
+                       w.num_blocks, p.num_experts, p.num_ranks, alignment_of(p),
+                       at<int32_t>(ws, w.block_count), at<int32_t>(ws, w.block_rank),
+                       at<uint32_t>(ws, w.block_err), cnt, per_rank, start,
+                       at<int32_t>(ws, w.counts), at<WsHeader>(ws, 0), mapped);
     int rc = launch_status();
     if (rc != EPL_OK)
         return rc;
@@ -159,8 +172,8 @@ void launch_scatter(const epl_problem &p, const WsLayout &w, const uint16_t *x, 
                        at<const int32_t>(ws, w.block_count), at<const int32_t>(ws, w.slot_rank),
                        p.num_tokens, p.num_topk, p.num_experts, p.hidden, p.scale_cols,
                        p.scale_cols % 4 == 0 && aligned(xs, 16) && aligned(out_scale, 16),
-                       w.block_tokens, cap, out, out_scale, m_idx, oi,
-                       &at<WsHeader>(ws, 0)->status);
+                       w.block_tokens, alignment_of(p), at<const int32_t>(ws, w.counts), cap,
+                       out, out_scale, m_idx, oi, &at<WsHeader>(ws, 0)->status);
 }
 
 int enqueue_scatter(const epl_problem &p, const WsLayout &w, const uint16_t *x, const float *xs,
@@ -216,9 +229,11 @@ bool scatter_args_ok(const epl_problem &p, const uint16_t *x, const float *xs,
 
 extern "C" {
 
-int epl_version(void) { return 0x000100; }
+int epl_version(void) { return 0x000200; }
 
 int epl_validate(const epl_problem *p) { return problem_ok(p) ? EPL_OK : EPL_EINVAL; }
+
+int64_t epl_capacity_rows(const epl_problem *p) { return problem_ok(p) ? capacity_bound(*p) : -1; }
 
 size_t epl_workspace_bytes(const epl_problem *p)
 {

@@ -34,6 +34,7 @@ constexpr int kLayoutWaves = kLayoutThreads / kWave;
 constexpr int kMaxSlotsPerBlock = 2048;   // B * K per layout block
 constexpr int kMaxTopk = 64;
 constexpr int kMaxExperts = 2048;
+constexpr int kMaxAlignment = 65536;
 constexpr int kScanThreads = 1024;
 constexpr int kRowThreads = 128;          // expert-scale workgroup
 
@@ -321,20 +322,22 @@ __device__ __forceinline__ int segment_sum(const int32_t *m, int ncols, int col,
 // Single workgroup. kScanReduce: column sums of block_count / block_rank
 // give num_tokens_per_expert / num_tokens_per_rank, block_count is replaced
 // by its exclusive prefix over blocks, and the status word is reset to the
-// layout's error bits. kScanPrefix: exclusive prefix of the per-expert
-// counts (read from `cnt` unless kScanReduce produced them) into
-// expert_start_loc, total into the header and, if `total_out` is not null,
-// into that (host-mapped) word too.
+// layout's error bits. kScanPrefix: exclusive prefix of the per-expert block
+// sizes (the counts, read from `cnt` unless kScanReduce produced them,
+// rounded up to a multiple of `alignment`) into expert_start_loc, total into
+// the header and, if `total_out` is not null, into that (host-mapped) word
+// too. Either mode keeps a copy of the counts in `ws_counts` for the
+// scatter's padding rows.
 //
 // The columns are split into P segments of L blocks each so that all 1024
 // threads have work: thread (column, segment) sums its segment, a short
 // per-column scan over the P segment sums gives each segment's offset, and
 // the thread then rewrites its segment as a running prefix.
 __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
-    int mode, int64_t nb, int E, int R, int32_t *__restrict__ block_count,
+    int mode, int64_t nb, int E, int R, int alignment, int32_t *__restrict__ block_count,
     const int32_t *__restrict__ block_rank, const uint32_t *__restrict__ block_err,
     int32_t *__restrict__ cnt, int32_t *__restrict__ per_rank, int32_t *__restrict__ start,
-    WsHeader *__restrict__ hdr, int32_t *__restrict__ total_out)
+    int32_t *__restrict__ ws_counts, WsHeader *__restrict__ hdr, int32_t *__restrict__ total_out)
 {
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_seg[kMaxExperts];
@@ -389,6 +392,7 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
             }
             s_cnt[e] = run;
             cnt[e] = run;
+            ws_counts[e] = run;
         }
         for (int r = tid; r < R; r += kScanThreads) {
             int run = 0;
@@ -429,16 +433,19 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
         if (tid == 0)
             hdr->status = s_err ? kStatusBadExpert : 0u;
     } else if (mode & kScanPrefix) {
-        for (int e = tid; e < E; e += kScanThreads)
+        for (int e = tid; e < E; e += kScanThreads) {
             s_cnt[e] = cnt[e];
+            ws_counts[e] = s_cnt[e];
+        }
         __syncthreads();
     }
 
     if (mode & kScanPrefix) {
         // Two consecutive experts per thread (E <= 2 * kScanThreads).
         const int i0 = 2 * tid, i1 = 2 * tid + 1;
-        const int a0 = i0 < E ? s_cnt[i0] : 0;
-        const int a1 = i1 < E ? s_cnt[i1] : 0;
+        auto block = [alignment](int c) { return (c + alignment - 1) / alignment * alignment; };
+        const int a0 = i0 < E ? block(s_cnt[i0]) : 0;
+        const int a1 = i1 < E ? block(s_cnt[i1]) : 0;
         const int incl = block_inclusive_scan(a0 + a1, s_wave);
         const int excl = incl - (a0 + a1);
         if (i0 < E)
@@ -541,13 +548,30 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ x_scale,
     const int64_t *__restrict__ topk, const int32_t *__restrict__ start,
     const int32_t *__restrict__ block_base, const int32_t *__restrict__ slot_rank, int64_t T,
-    int K, int E, int H, int S, bool scale_vec16, int B, int64_t capacity,
-    uint16_t *__restrict__ out, float *__restrict__ out_scale, int32_t *__restrict__ m_indices,
+    int K, int E, int H, int S, bool scale_vec16, int B, int alignment,
+    const int32_t *__restrict__ counts, int64_t capacity, uint16_t *__restrict__ out,
+    float *__restrict__ out_scale, int32_t *__restrict__ m_indices,
     int32_t *__restrict__ output_index, uint32_t *__restrict__ status)
 {
     __shared__ int64_t s_row[2][kMaxTopk];
     const int tid = threadIdx.x;
     const int nvec = H >> 3;
+
+    // Padding rows of the aligned blocks: between an expert's last row and
+    // the end of its block, marked -1 (workgroup w takes experts w, w + G, ...).
+    if (alignment > 1) {
+        for (int e = blockIdx.x; e < E; e += gridDim.x) {
+            const int64_t c = counts[e];
+            const int64_t p0 = (int64_t)start[e] + c;
+            const int64_t p1 = (int64_t)start[e] + (c + alignment - 1) / alignment * alignment;
+            for (int64_t p = p0 + tid; p < p1; p += kScatterThreads) {
+                if (p < capacity)
+                    m_indices[p] = -1;
+                else
+                    atomicOr(status, kStatusCapacity);
+            }
+        }
+    }
     const int nq = scale_vec16 ? (S >> 2) : 0;
     const TokenRange tr = token_range(T);
     const int64_t step = tr.stride, t_end = tr.end;
@@ -824,6 +848,8 @@ __global__ __launch_bounds__(kRowThreads) void ep_expert_scale_kernel(
     const int64_t n = min((int64_t)hdr->total, capacity);
     const int nvec = H >> 3;
     for (int64_t p = blockIdx.x; p < n; p += gridDim.x) {
+        if (m_indices[p] < 0)
+            continue;   // padding row of an aligned block
         const float f = 1.0f + (float)m_indices[p] * (1.0f / 256.0f);
         const u32x4 *src = reinterpret_cast<const u32x4 *>(in + p * H);
         u32x4 *dst = reinterpret_cast<u32x4 *>(out + p * H);

@@ -50,7 +50,7 @@ def test_no_oracle_in_the_product_path():
 
 def test_problem_struct_layout():
     assert ctypes.sizeof(epl.Problem) == 32
-    assert epl.Problem.num_topk.offset == 8 and epl.Problem.reserved.offset == 28
+    assert epl.Problem.num_topk.offset == 8 and epl.Problem.expert_alignment.offset == 28
 
 
 def P(**kw):
@@ -85,10 +85,32 @@ def test_validate(lib, kw, ok):
     assert (epl.epl_workspace_bytes(p) > 0) == ok
 
 
-def test_reserved_field_must_be_zero(lib):
-    p = P()
-    p.reserved = 1
-    assert epl.epl_validate(p) == epl.EPL_EINVAL
+@pytest.mark.parametrize("a,ok", [(0, True), (1, True), (2, True), (256, True), (65536, True),
+                                  (65537, False), (-1, False)])
+def test_expert_alignment_range(lib, a, ok):
+    p = P(expert_alignment=a)
+    assert (epl.epl_validate(p) == epl.EPL_OK) == ok
+
+
+@pytest.mark.parametrize("T,K,E,a,want", [
+    (4096, 8, 256, 0, 4096 * 8),
+    (4096, 8, 256, 1, 4096 * 8),
+    (4096, 8, 256, 256, ((4096 * 8 + 256 * 255 + 255) // 256) * 256),
+    (100, 3, 16, 7, ((300 + 16 * 6 + 6) // 7) * 7),
+    (0, 4, 8, 16, 8 * 15 + 8),     # round_up(0 + 8*15, 16) = 128
+])
+def test_capacity_rows_is_the_aligned_bound(lib, T, K, E, a, want):
+    p = P(num_tokens=T, num_topk=K, num_experts=E, num_ranks=E if E < 32 else 32, scale_cols=0,
+          expert_alignment=a)
+    assert epl.epl_capacity_rows(p) == want
+
+
+def test_capacity_bound_must_fit_int32(lib):
+    T = (1 << 31) // 8 - 1          # T*K fits ...
+    assert epl.epl_validate(P(num_tokens=T)) == epl.EPL_OK
+    # ... but not once 256 experts may each add up to 255 padding rows
+    assert epl.epl_validate(P(num_tokens=T, expert_alignment=256)) == epl.EPL_EINVAL
+    assert epl.epl_capacity_rows(P(num_tokens=T, expert_alignment=256)) == -1
 
 
 def test_workspace_scales_with_problem(lib):

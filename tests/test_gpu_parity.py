@@ -56,13 +56,14 @@ def poisoned(shape, dtype, byte=POISON):
     return t
 
 
-def gpu_dispatch(topk, x, xs, E, R, cap=None, byte=POISON, stream=None, split=False):
+def gpu_dispatch(topk, x, xs, E, R, cap=None, byte=POISON, stream=None, split=False,
+                 alignment=0):
     """Run dispatch through the C ABI on poisoned buffers; returns tensors."""
     T, K = topk.shape
     H = x.shape[1]
     S = 0 if xs is None else xs.shape[1]
-    p = epl.Problem.make(T, K, E, R, H, S)
-    cap = T * K if cap is None else cap
+    p = epl.Problem.make(T, K, E, R, H, S, alignment)
+    cap = epl.epl_capacity_rows(p) if cap is None else cap
     ws = poisoned(epl.epl_workspace_bytes(p), torch.uint8, byte)
     r = dict(
         cnt=poisoned(E, torch.int32, byte), per_rank=poisoned(R, torch.int32, byte),
@@ -107,11 +108,13 @@ def check_layout_and_scatter(r, ref, x, xs):
     np.testing.assert_array_equal(r["start"].cpu().numpy(), ref["expert_start_loc"])
     np.testing.assert_array_equal(r["oi"].cpu().numpy(), ref["output_index"])
     np.testing.assert_array_equal(r["m"][:N].cpu().numpy(), ref["m_indices"])
+    # rows that hold a routed slot (alignment padding rows are not written)
+    real = ref["m_indices"] >= 0
     if ref.get("out") is not None:
-        np.testing.assert_array_equal(u16(r["out"][:N]), ref["out"])
+        np.testing.assert_array_equal(u16(r["out"][:N])[real], ref["out"][real])
     if xs is not None:
-        np.testing.assert_array_equal(r["out_scale"][:N].cpu().numpy().view(np.uint32),
-                                      ref["out_scale"].view(np.uint32))
+        np.testing.assert_array_equal(r["out_scale"][:N].cpu().numpy().view(np.uint32)[real],
+                                      ref["out_scale"].view(np.uint32)[real])
 
 
 def combine_bound(eo_u16, oi, w, tokens=None):
@@ -133,12 +136,12 @@ def check_combine_bf16(y_gpu_u16, y_ref, bound):
     assert not bad.any(), f"{bad.sum()} bf16 elements beyond half an ulp of the fp32 bound"
 
 
-def full_parity(w: workloads.Workload, inp=None, split=False):
+def full_parity(w: workloads.Workload, inp=None, split=False, alignment=0):
     inp = inp or workloads.make_inputs(w)
     topk, x, xs, wt = inp["topk_idx"], inp["x"], inp["x_scale"], inp["topk_weights"]
     E, R = w.num_experts, w.num_ranks
-    ref = orc().run_all(x, xs, topk, wt, E, R, expert_fn=w.expert_fn)
-    r = gpu_dispatch(topk, x, xs, E, R, split=split)
+    ref = orc().run_all(x, xs, topk, wt, E, R, expert_fn=w.expert_fn, alignment=alignment)
+    r = gpu_dispatch(topk, x, xs, E, R, split=split, alignment=alignment)
     assert epl.epl_status(r["ws"]) == epl.EPL_OK
     check_layout_and_scatter(r, ref, x, xs)
     N = ref["total"]
@@ -147,7 +150,8 @@ def full_parity(w: workloads.Workload, inp=None, split=False):
     else:
         eo = torch.empty_like(r["out"])
         epl.epl_expert_scale(r["p"], r["out"], r["m"], r["cap"], eo, r["ws"])
-        np.testing.assert_array_equal(u16(eo[:N]), ref["expert_out"])
+        real = ref["m_indices"] >= 0
+        np.testing.assert_array_equal(u16(eo[:N])[real], ref["expert_out"][real])
     y = gpu_combine(r, eo, wt, epl.EPL_OUT_F32)
     yb = gpu_combine(r, eo, wt, epl.EPL_OUT_BF16)
     bound = combine_bound(ref["expert_out"], ref["output_index"], wt)
@@ -238,6 +242,37 @@ def test_large_batch_sampled_parity():
     y_ref = orc().combine(sub_eo, sub_oi, wt[toks])
     bound = combine_bound(sub_eo, sub_oi, wt[toks])
     check_combine_f32(y[torch.from_numpy(toks).to(DEV)].cpu().numpy(), y_ref, bound)
+
+
+# -------------------------------------------------------- expert alignment --
+
+@pytest.mark.parametrize("name,a", [("tiny", 4), ("small", 256), ("dsv3", 128), ("skew", 64),
+                                    ("small", 3)])
+def test_aligned_blocks_parity(name, a):
+    """Per-expert blocks padded to a multiple of a rows; padding rows carry
+    m_indices = -1; everything else as without padding."""
+    print(f"[parity] workload={name} alignment={a}", flush=True)
+    full_parity(workloads.get(name), alignment=a)
+
+
+def test_aligned_split_calls_and_expert_stand_in():
+    w = workloads.get("small").with_(num_tokens=900, expert_fn="scale", drop_rate=0.2)
+    full_parity(w, split=True, alignment=32)
+
+
+def test_aligned_capacity_overflow_in_padding_is_flagged():
+    rng = np.random.default_rng(12)
+    E, R, T, K, H, a = 8, 2, 100, 3, 64, 16
+    # the last expert gets exactly one slot, so its block ends with 15 padding rows
+    topk = np.stack([rng.permutation(E - 1)[:K] for _ in range(T)]).astype(np.int64)
+    topk[50, 1] = E - 1
+    x, _, wt = _mk(topk, H)
+    ref = orc().run_all(x, None, topk, wt, E, R, alignment=a)
+    N = ref["total"]
+    assert (ref["m_indices"][N - (a - 1):] == -1).all()
+    r = gpu_dispatch(topk, x, None, E, R, cap=N - 1, alignment=a)
+    assert epl.epl_status(r["ws"]) == epl.EPL_ECAPACITY
+    np.testing.assert_array_equal(r["m"].cpu().numpy(), ref["m_indices"][:N - 1])
 
 
 # ----------------------------------------------------------- ragged shapes --
@@ -387,18 +422,22 @@ def test_combine_flags_row_beyond_expert_output():
     check_combine_f32(y.cpu().numpy(), y_ref, combine_bound(eo, clean, wt))
 
 
-def test_exact_mode_matches_capacity_mode():
+@pytest.mark.parametrize("alignment", [0, 64])
+def test_exact_mode_matches_capacity_mode(alignment):
     w = workloads.get("small").with_(num_tokens=1200)
     inp = workloads.make_inputs(w)
     tk = torch.from_numpy(inp["topk_idx"]).to(DEV)
     xd = to_bf16(inp["x"])
-    a = epl.dispatch(xd, tk, w.num_experts, w.num_ranks, mode="capacity")
-    b = epl.dispatch(xd, tk, w.num_experts, w.num_ranks, mode="exact")
+    a = epl.dispatch(xd, tk, w.num_experts, w.num_ranks, mode="capacity",
+                     expert_alignment=alignment)
+    b = epl.dispatch(xd, tk, w.num_experts, w.num_ranks, mode="exact",
+                     expert_alignment=alignment)
     n = a.total()
     assert n == b.total() == b.out.shape[0]
     assert torch.equal(a.output_index, b.output_index)
-    assert torch.equal(a.out[:n].view(torch.int16), b.out.view(torch.int16))
     assert torch.equal(a.m_indices[:n], b.m_indices)
+    real = b.m_indices >= 0
+    assert torch.equal(a.out[:n][real].view(torch.int16), b.out[real].view(torch.int16))
 
 
 def test_runs_on_a_side_stream():
