@@ -35,15 +35,16 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(w, N, T_any, out_dtype_bytes=4):
-    """Bytes each kernel must move (reads + writes), by its definition."""
+def algorithmic_bytes(w, N, T_any, out_dtype_bytes=4, pad_rows=0):
+    """Bytes each kernel must move (reads + writes), by its definition;
+    alignment padding rows only get their m_indices entry."""
     T, K, E, R, H, S = (w.num_tokens, w.num_topk, w.num_experts, w.num_ranks, w.hidden,
                         w.scale_cols)
     return {
         "layout": 8 * T * K + 4 * E + 4 * R + T * R,
         "scan": 4 * E + 4 * E + 4,
         "scatter": (2 * H * T_any + 4 * S * T_any + 8 * T * K + 4 * E) +
-                   (2 * H * N + 4 * S * N + 4 * N + 4 * T * K),
+                   (2 * H * N + 4 * S * N + 4 * N + 4 * T * K + 4 * pad_rows),
         "expert": 2 * H * N + 4 * N + 2 * H * N,
         "combine": 2 * H * N + 4 * T * K + 4 * T * K + out_dtype_bytes * T * H,
     }
@@ -102,6 +103,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--out-dtype", choices=["f32", "bf16"], default="f32")
+    ap.add_argument("--alignment", type=int, default=0,
+                    help="expert alignment (block_m padding of each expert's rows)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--timed-only", action="store_true",
@@ -143,8 +146,8 @@ def main():
     x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
     xs = torch.from_numpy(inp["x_scale"]).to(dev) if S else None
     wt = torch.from_numpy(inp["topk_weights"]).to(dev)
-    p = epl.Problem.make(T, K, E, R, H, S)
-    cap = T * K
+    p = epl.Problem.make(T, K, E, R, H, S, args.alignment)
+    cap = epl.epl_capacity_rows(p)
     i32 = torch.int32
     ws = torch.empty(epl.epl_workspace_bytes(p), dtype=torch.uint8, device=dev)
     cnt = torch.empty(E, dtype=i32, device=dev)
@@ -212,9 +215,10 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    if epl.epl_status(ws) != epl.EPL_OK or int(total_host[0]) != N:
-        raise RuntimeError(f"dispatch failed: status {epl.epl_status(ws)}, total "
-                           f"{int(total_host[0])} != {N}")
+    n_rows = int(total_host[0])      # buffer rows, including alignment padding
+    if epl.epl_status(ws) != epl.EPL_OK or n_rows < N or (not args.alignment and n_rows != N):
+        raise RuntimeError(f"dispatch failed: status {epl.epl_status(ws)}, total {n_rows}, "
+                           f"routed {N}")
 
     # Timed region: exactly `steps` steps, two HIP events per step on the
     # stream the kernels run on (before combine, after combine): combine's
@@ -271,12 +275,12 @@ def main():
                 ev_a.record(stream)
                 if mode == "exact":
                     stream.synchronize()
-                    n_rows = int(total_host[0])
-                    o = torch.empty((n_rows, H), dtype=torch.bfloat16, device=dev)
-                    o_s = torch.empty((n_rows, S), dtype=torch.float32, device=dev) if S else None
-                    m_i = torch.empty(n_rows, dtype=i32, device=dev)
+                    n_ex = int(total_host[0])
+                    o = torch.empty((n_ex, H), dtype=torch.bfloat16, device=dev)
+                    o_s = torch.empty((n_ex, S), dtype=torch.float32, device=dev) if S else None
+                    m_i = torch.empty(n_ex, dtype=i32, device=dev)
                     ev_b.record(stream)
-                    epl.epl_scatter(p, x, xs, topk, start, ws, n_rows, o, o_s, m_i, oi)
+                    epl.epl_scatter(p, x, xs, topk, start, ws, n_ex, o, o_s, m_i, oi)
                 else:
                     ev_b.record(stream)
                     calls[2]()
@@ -313,7 +317,8 @@ def main():
         del flush_buf
         assert epl.epl_status(ws) == epl.EPL_OK
 
-    nbytes = algorithmic_bytes(w, N, T_any, 4 if out_code == epl.EPL_OUT_F32 else 2)
+    nbytes = algorithmic_bytes(w, N, T_any, 4 if out_code == epl.EPL_OUT_F32 else 2,
+                               n_rows - N)
     gbps = {n: nbytes[n] / (per_kernel_ms[n] * 1e-3) / 1e9 for n in per_kernel_ms}
     # combine's duration in the timed region is exact; scatter's comes from
     # the per-kernel breakdown
@@ -349,6 +354,7 @@ def main():
             "num_tokens": T, "hidden": H, "num_experts": E, "num_topk": K,
             "num_virtual_ranks": R, "scale_cols": S, "routing": w.routing,
             "drop_rate": w.drop_rate, "expert_fn": w.expert_fn, "routed_rows": N,
+            "expert_alignment": args.alignment, "buffer_rows": n_rows,
             "combine_out": args.out_dtype, "capacity_rows": cap,
         },
         "timed_region_ms": timed_ms,

@@ -64,6 +64,10 @@ class Oracle:
         lib.epl_oracle_scatter.argtypes = [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
                                            _ptr, _ptr, _ptr, _ptr, _c_i64, _ptr, _ptr, _ptr, _ptr]
         lib.epl_oracle_scatter.restype = ctypes.c_int
+        lib.epl_oracle_scatter_rows.argtypes = [_c_i64, _c_i32, _c_i32, _c_i64, _ptr, _c_i32,
+                                                _c_i32, _ptr, _ptr, _ptr, _c_i64, _c_i64, _ptr,
+                                                _ptr, _ptr, _ptr]
+        lib.epl_oracle_scatter_rows.restype = ctypes.c_int
         lib.epl_oracle_expert_scale.argtypes = [_c_i64, _c_i32, _ptr, _ptr, _ptr]
         lib.epl_oracle_expert_scale.restype = ctypes.c_int
         lib.epl_oracle_combine.argtypes = [_c_i64, _c_i32, _c_i32, _ptr, _c_i64, _ptr, _ptr,
@@ -126,6 +130,38 @@ class Oracle:
         _check(self.lib.epl_oracle_scatter(T, K, E, H, S, _p(xx), _p(xs), _p(topk), _p(start),
                                            total, _p(out), _p(out_scale), _p(m_idx), _p(oi)),
                "scatter")
+        return out, out_scale, m_idx, oi
+
+    SCALE_NONE, SCALE_ROWS, SCALE_COLS = 0, 1, 2
+
+    def scatter_rows(self, x_bytes: Optional[np.ndarray], x_scale_words: Optional[np.ndarray],
+                     scale_format: int, topk_idx: np.ndarray, expert_start_loc: np.ndarray,
+                     total: int, scale_ld: Optional[int] = None, copy_rows: bool = True):
+        """Byte-row scatter (FP8 payload). x_bytes [T, B] uint8; x_scale_words
+        [T, W] uint32. Returns (out [total, B] u8, out_scale, m_indices,
+        output_index), out_scale being [total, W] (SCALE_ROWS) or the flat
+        column-major buffer [W * scale_ld] (SCALE_COLS, default scale_ld = total)."""
+        topk = _c(topk_idx, np.int64)
+        T, K = topk.shape
+        start = _c(expert_start_loc, np.int32)
+        xb = None if x_bytes is None else _c(x_bytes, np.uint8)
+        B = 0 if xb is None else xb.shape[1]
+        xs = None if x_scale_words is None else _c(x_scale_words, np.uint32)
+        W = 0 if xs is None else xs.shape[1]
+        ld = total if scale_ld is None else int(scale_ld)
+        out = np.empty((total, B), np.uint8) if (copy_rows and xb is not None) else None
+        if xs is None or not copy_rows or scale_format == self.SCALE_NONE:
+            out_scale = None
+        elif scale_format == self.SCALE_ROWS:
+            out_scale = np.empty((total, W), np.uint32)
+        else:
+            out_scale = np.empty(W * ld, np.uint32)
+        m_idx = np.empty(total, np.int32)
+        oi = np.empty((T, K), np.int32)
+        _check(self.lib.epl_oracle_scatter_rows(T, K, start.size, B, _p(xb), int(scale_format), W,
+                                                _p(xs), _p(topk), _p(start), total, ld,
+                                                _p(out), _p(out_scale), _p(m_idx), _p(oi)),
+               "scatter_rows")
         return out, out_scale, m_idx, oi
 
     def expert_scale(self, rows: np.ndarray, m_indices: np.ndarray) -> np.ndarray:

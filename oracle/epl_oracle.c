@@ -224,6 +224,70 @@ int epl_oracle_scatter(int64_t T, int32_t K, int32_t E, int32_t H, int32_t S,
     return rc;
 }
 
+/* Scale formats of the byte-row scatter. */
+#define ORACLE_SCALE_NONE 0
+#define ORACLE_SCALE_ROWS 1   /* W words per row, row-major in and out            */
+#define ORACLE_SCALE_COLS 2   /* W words per token row-major in; out column-major */
+
+/* The scatter for rows given as raw bytes: an FP8 (e4m3) payload of H bytes
+ * per row, as DeepEP dispatches it ([DEEPEP] Dispatch, the x argument's
+ * tuple form), with per-row scale words. Placement is the same counting sort
+ * as epl_oracle_scatter. Scale rows of W 4-byte words follow their row:
+ * ORACLE_SCALE_ROWS writes them row-major ([rows, W]); ORACLE_SCALE_COLS
+ * writes the layout sglang allocates for UE8M0 scales ([SGLANG] section 2.2:
+ * an int32 [ceil(S/4), rows] buffer viewed transposed), i.e. word j of row p
+ * at out_scale[j * scale_ld + p], scale_ld being the buffer's row capacity.
+ * The words are moved as opaque bits. Rows that receive no slot get
+ * m_indices = -1. */
+int epl_oracle_scatter_rows(int64_t T, int32_t K, int32_t E, int64_t row_bytes,
+                            const uint8_t *x, int32_t scale_format, int32_t scale_words,
+                            const uint32_t *x_scale, const int64_t *topk_idx,
+                            const int32_t *expert_start_loc, int64_t total_rows,
+                            int64_t scale_ld, uint8_t *out, uint32_t *out_scale,
+                            int32_t *m_indices, int32_t *output_index)
+{
+    if (T < 0 || K < 1 || E < 1 || row_bytes < 0 || scale_words < 0 || total_rows < 0)
+        return ORACLE_EINVAL;
+    if (scale_format == ORACLE_SCALE_COLS && scale_ld < total_rows)
+        return ORACLE_EINVAL;
+    for (int64_t p = 0; p < total_rows; ++p)
+        m_indices[p] = -1;              /* rows without a slot: padding */
+    int64_t *next = (int64_t *)malloc(sizeof(int64_t) * (size_t)E);
+    if (!next)
+        return ORACLE_EINVAL;
+    for (int32_t e = 0; e < E; ++e)
+        next[e] = expert_start_loc[e];
+
+    int rc = ORACLE_OK;
+    for (int64_t t = 0; t < T && rc == ORACLE_OK; ++t) {
+        for (int32_t k = 0; k < K; ++k) {   /* the token's slots in order */
+            int64_t e = topk_idx[t * K + k];
+            if (e < -1 || e >= E) {
+                rc = ORACLE_ERANGE;
+                break;
+            }
+            if (e == -1) {
+                output_index[t * K + k] = -1;   /* no selection: no row */
+                continue;
+            }
+            int64_t p = next[e]++;
+            output_index[t * K + k] = (int32_t)p;
+            m_indices[p] = (int32_t)e;
+            if (out)
+                memcpy(out + p * row_bytes, x + t * row_bytes, (size_t)row_bytes);
+            if (out_scale && scale_format == ORACLE_SCALE_ROWS) {
+                for (int32_t j = 0; j < scale_words; ++j)
+                    out_scale[p * scale_words + j] = x_scale[t * scale_words + j];
+            } else if (out_scale && scale_format == ORACLE_SCALE_COLS) {
+                for (int32_t j = 0; j < scale_words; ++j)
+                    out_scale[j * scale_ld + p] = x_scale[t * scale_words + j];
+            }
+        }
+    }
+    free(next);
+    return rc;
+}
+
 /* ------------------------------------------------------- expert stand-in -- */
 
 /* The synthetic expert of the large-batch workload: expert e multiplies its

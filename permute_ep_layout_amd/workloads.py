@@ -55,10 +55,19 @@ class Workload:
     zipf_s: float = 1.2
     cold_experts: int = 0    # experts with zero routing probability (zipf only)
     expert_fn: str = "identity"   # "identity" or "scale" (row * (1 + e/256), bf16)
+    payload: str = "bf16"         # "bf16" or "fp8" (e4m3, one byte per element)
+    scale_format: str = "f32"     # "f32" (fp32 per 128 columns) or "ue8m0" (packed exponents)
 
     @property
     def scale_cols(self) -> int:
         return self.hidden // 128 if self.scales else 0
+
+    @property
+    def scale_words(self) -> int:
+        """32-bit words per scale row: S floats, or ceil(S/4) packed UE8M0 words."""
+        if not self.scales:
+            return 0
+        return self.scale_cols if self.scale_format == "f32" else (self.scale_cols + 3) // 4
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -80,6 +89,11 @@ WORKLOADS = {
     "large": Workload("large", seed=5, num_tokens=65536, hidden=7168, num_experts=256,
                       num_topk=8, num_ranks=64, scales=False, routing="uniform",
                       expert_fn="scale"),
+    # the DeepSeek-V3-shaped batch as DeepEP dispatches it for an FP8 grouped
+    # GEMM: e4m3 rows and power-of-two (UE8M0) scales packed 4 per int32
+    "dsv3_fp8": Workload("dsv3_fp8", seed=3, num_tokens=4096, hidden=7168, num_experts=256,
+                         num_topk=8, num_ranks=32, scales=True, routing="uniform",
+                         payload="fp8", scale_format="ue8m0"),
 }
 
 
@@ -212,15 +226,46 @@ def make_scales(w: Workload) -> Optional[np.ndarray]:
     return np.ascontiguousarray(s.astype(np.float32))
 
 
+def make_x_fp8(w: Workload) -> np.ndarray:
+    """Hidden rows [T, H] as FP8 e4m3 bytes (uint8): the same N(0,1) fp32
+    draws as make_x, rounded to e4m3 by torch's float8_e4m3fn conversion."""
+    import torch
+
+    T, H = w.num_tokens, w.hidden
+    rng = _rng(w.seed, STREAM_X)
+    out = np.empty((T, H), dtype=np.uint8)
+    chunk = max(1, (1 << 24) // max(H, 1))
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        f = torch.from_numpy(rng.standard_normal((t1 - t0, H), dtype=np.float32))
+        out[t0:t1] = f.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return out
+
+
+def make_scales_ue8m0(w: Workload) -> Optional[np.ndarray]:
+    """Per-128-column power-of-two scales as UE8M0 exponent bytes (2^k with
+    k uniform in [-10, 2], byte = 127 + k), packed four per little-endian
+    uint32 word: [T, ceil(S/4)]; bytes past S in the last word are 0."""
+    if not w.scales:
+        return None
+    S, W = w.scale_cols, w.scale_words
+    k = _rng(w.seed, STREAM_SCALE).integers(-10, 3, size=(w.num_tokens, S))
+    b = np.zeros((w.num_tokens, 4 * W), dtype=np.uint8)
+    b[:, :S] = (127 + k).astype(np.uint8)
+    return np.ascontiguousarray(b).view("<u4").reshape(w.num_tokens, W).astype(np.uint32)
+
+
 def make_inputs(w: Workload, with_x: bool = True) -> dict:
     """All inputs of one workload as host numpy arrays."""
     topk = make_topk(w)
-    return {
-        "topk_idx": topk,
-        "topk_weights": make_weights(w, topk),
-        "x": make_x(w) if with_x else None,
-        "x_scale": make_scales(w),
-    }
+    fp8 = w.payload == "fp8"
+    if fp8:
+        x = make_x_fp8(w) if with_x else None
+        xs = make_scales_ue8m0(w) if w.scale_format == "ue8m0" else make_scales(w)
+    else:
+        x = make_x(w) if with_x else None
+        xs = make_scales(w)
+    return {"topk_idx": topk, "topk_weights": make_weights(w, topk), "x": x, "x_scale": xs}
 
 
 def get(name: str) -> Workload:

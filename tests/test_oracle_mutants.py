@@ -27,8 +27,20 @@ MUTANTS = {
                        "int64_t c = num_tokens_per_expert[e];\n        int64_t blocks = c / a + (c % a != 0);\n        running += blocks * a;\n        expert_start_loc[e] = (int32_t)running;"),
     "alignment_rounds_down": ("int64_t blocks = c / a + (c % a != 0);", "int64_t blocks = c / a;"),
     "alignment_always_one_extra_block": ("int64_t blocks = c / a + (c % a != 0);", "int64_t blocks = c / a + 1;"),
-    "padding_marked_zero": ("for (int64_t p = 0; p < total_rows; ++p)\n        m_indices[p] = -1;",
-                            "for (int64_t p = 0; p < total_rows; ++p)\n        m_indices[p] = 0;"),
+    "scale_words_row_major_in_cols_layout": ("out_scale[j * scale_ld + p] = x_scale[t * scale_words + j];",
+                                             "out_scale[p * scale_words + j] = x_scale[t * scale_words + j];"),
+    "scale_cols_leading_dim_is_total": ("out_scale[j * scale_ld + p] = x_scale[t * scale_words + j];",
+                                        "out_scale[j * total_rows + p] = x_scale[t * scale_words + j];"),
+    "byte_row_of_wrong_token": ("memcpy(out + p * row_bytes, x + t * row_bytes, (size_t)row_bytes);",
+                                "memcpy(out + p * row_bytes, x + (T - 1 - t) * row_bytes, (size_t)row_bytes);"),
+    "rows_invalid_slot_marked_zero": ("output_index[t * K + k] = -1;   /* no selection: no row */",
+                                      "output_index[t * K + k] = 0;   /* no selection: no row */"),
+    "rows_slots_in_reverse_k": ("for (int32_t k = 0; k < K; ++k) {   /* the token's slots in order */",
+                                "for (int32_t k = K - 1; k >= 0; --k) {   /* the token's slots in order */"),
+    "padding_marked_zero": ("for (int64_t p = 0; p < total_rows; ++p)\n        m_indices[p] = -1;\n    int64_t *cursor",
+                            "for (int64_t p = 0; p < total_rows; ++p)\n        m_indices[p] = 0;\n    int64_t *cursor"),
+    "rows_padding_marked_zero": ("m_indices[p] = -1;              /* rows without a slot: padding */",
+                                 "m_indices[p] = 0;              /* rows without a slot: padding */"),
     "per_rank_counts_every_token": ("num_tokens_per_rank[r] += is_token_in_rank[t * R + r];",
                                     "num_tokens_per_rank[r] += 1;"),
     "weight_of_mirrored_slot": ("double w = (double)topk_weights[t * K + k];",
@@ -139,6 +151,49 @@ def _battery(orc: Oracle):
                 return False
         return True
 
+    def scale_cols_layout():
+        g = load_golden("scatter_scale_cols_example.txt")
+        E, R = g["num_experts"][0], g["num_ranks"][0]
+        topk = np.array(g["topk_idx"], np.int64)
+        words = np.array(g["scale_words"], np.uint32)
+        x = np.arange(3 * 16, dtype=np.uint8).reshape(3, 16)
+        cnt, _, _ = orc.layout(topk, E, R)
+        start, total = orc.scan(cnt)
+        out, cols, _, oi = orc.scatter_rows(x, words, orc.SCALE_COLS, topk, start, total,
+                                            scale_ld=g["ld"][0])
+        ok = all(int(cols[i]) == v for i, v in enumerate(g["out_scale_flat"]) if v >= 0)
+        ok = ok and oi.tolist() == [[1, 3], [4, -1], [2, 0]]
+        src = [2, 0, 2, 0, 1]
+        return ok and all(np.array_equal(out[p], x[src[p]]) for p in range(5))
+
+    def brute_rows():
+        rng = np.random.default_rng(41)
+        for _ in range(25):
+            R = int(rng.integers(1, 4))
+            E = R * int(rng.integers(1, 3))
+            T, K = int(rng.integers(1, 9)), int(rng.integers(2, 5))
+            topk = rng.integers(-1, E, size=(T, K)).astype(np.int64)   # duplicates likely
+            want = brute_force(topk, E, R, alignment=2)
+            cnt, _, _ = orc.layout(topk, E, R)
+            start, total = orc.scan(cnt, 2)
+            x = rng.integers(0, 256, size=(T, 16), dtype=np.uint8)
+            out, _, m, oi = orc.scatter_rows(x, None, orc.SCALE_NONE, topk, start, total)
+            if not (np.array_equal(oi, want["oi"]) and np.array_equal(m, want["m"])):
+                return False
+            tt, kk = np.nonzero(topk >= 0)
+            if not np.array_equal(out[oi[tt, kk]], x[tt]):
+                return False
+        return True
+
+    def rows_aligned_padding():
+        g = load_golden("scatter_hand_example.txt")
+        E, R = g["num_experts"][0], g["num_ranks"][0]
+        topk = np.array(g["topk_idx"], np.int64)
+        cnt, _, _ = orc.layout(topk, E, R)
+        start, total = orc.scan(cnt, 4)          # blocks of 4: e1 [0,4), e3 [4,8), e7 [8,12)
+        _, _, m, _ = orc.scatter_rows(None, None, orc.SCALE_NONE, topk, start, total)
+        return m.tolist() == [1, -1, -1, -1, 3, 3, -1, -1, 7, 7, -1, -1]
+
     def one_hot_combine():
         rng = np.random.default_rng(3)
         T, K, N = 6, 3, 18
@@ -171,6 +226,8 @@ def _battery(orc: Oracle):
 
     for name, fn in [("golden_scan", golden_scan), ("golden_hand", golden_hand), ("brute", brute),
                      ("golden_alignment", golden_alignment), ("brute_aligned", brute_aligned),
+                     ("scale_cols_layout", scale_cols_layout),
+                     ("rows_aligned_padding", rows_aligned_padding), ("brute_rows", brute_rows),
                      ("rows_and_scales", rows_and_scales), ("one_hot_combine", one_hot_combine),
                      ("bf16_vs_torch", bf16_vs_torch), ("expert_scale_hand", expert_scale_hand)]:
         pin(name, fn)

@@ -213,6 +213,68 @@ def test_row_order_is_numpy_stable_argsort(seed):
     np.testing.assert_array_equal(got["oi"].ravel()[flat < 0], -1)
 
 
+# ------------------------------------------------- byte rows, scale words --
+
+def test_golden_scale_words_column_major():
+    g = load_golden("scatter_scale_cols_example.txt")
+    E, R = g["num_experts"][0], g["num_ranks"][0]
+    topk = np.array(g["topk_idx"], dtype=np.int64)
+    words = np.array(g["scale_words"], dtype=np.uint32)
+    orc = oracle.default()
+    cnt, _, _ = orc.layout(topk, E, R)
+    start, total = orc.scan(cnt)
+    _, out_scale, m, oi = orc.scatter_rows(None, words, orc.SCALE_COLS, topk, start, total,
+                                          scale_ld=g["ld"][0])
+    want = g["out_scale_flat"]
+    for i, v in enumerate(want):
+        if v >= 0:
+            assert int(out_scale[i]) == v, i
+
+
+@pytest.mark.parametrize("seed,ld_extra", [(0, 0), (1, 5), (2, 1000)])
+def test_byte_rows_and_transposed_scales_match_numpy(seed, ld_extra):
+    """FP8 rows move as bytes; the column-major scale buffer, read back with
+    numpy's transpose, holds each row's token's words (row -> token map from
+    numpy's stable argsort)."""
+    rng = np.random.default_rng(seed)
+    T, K, E, R, B, W = 300, 5, 24, 6, 96, 3
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    topk[rng.random(topk.shape) < 0.1] = -1
+    x = rng.integers(0, 256, size=(T, B), dtype=np.uint8)
+    words = rng.integers(0, 1 << 32, size=(T, W), dtype=np.uint64).astype(np.uint32)
+    orc = oracle.default()
+    cnt, _, _ = orc.layout(topk, E, R)
+    start, total = orc.scan(cnt)
+    ld = total + ld_extra
+    out, cols, m, oi = orc.scatter_rows(x, words, orc.SCALE_COLS, topk, start, total, scale_ld=ld)
+    _, rows, m2, oi2 = orc.scatter_rows(x, words, orc.SCALE_ROWS, topk, start, total)
+    flat = topk.ravel()
+    order = np.argsort(flat, kind="stable")
+    src = (order[flat[order] >= 0]) // K            # token of each row
+    np.testing.assert_array_equal(out, x[src])
+    np.testing.assert_array_equal(cols.reshape(W, ld)[:, :total].T, words[src])
+    np.testing.assert_array_equal(rows, words[src])
+    np.testing.assert_array_equal(m, m2)
+    np.testing.assert_array_equal(oi, oi2)
+
+
+def test_byte_rows_agree_with_bf16_scatter():
+    from permute_ep_layout_amd import workloads
+    w = workloads.get("dsv3").with_(num_tokens=200, hidden=256)
+    inp = workloads.make_inputs(w)
+    orc = oracle.default()
+    cnt, _, _ = orc.layout(inp["topk_idx"], w.num_experts, w.num_ranks)
+    start, total = orc.scan(cnt, 8)
+    out, out_s, m, oi = orc.scatter(inp["x"], inp["x_scale"], inp["topk_idx"], start, total)
+    outb, rows, mb, oib = orc.scatter_rows(inp["x"].view(np.uint8), inp["x_scale"].view(np.uint32),
+                                           orc.SCALE_ROWS, inp["topk_idx"], start, total)
+    real = m >= 0
+    np.testing.assert_array_equal(outb.view(np.uint16)[real], out[real])
+    np.testing.assert_array_equal(rows[real], out_s.view(np.uint32)[real])
+    np.testing.assert_array_equal(mb, m)
+    np.testing.assert_array_equal(oib, oi)
+
+
 # ------------------------------------------------------------- invariants --
 
 def test_invariants_on_generated_workload():
