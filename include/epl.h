@@ -65,6 +65,18 @@ extern "C" {
 #define EPL_OUT_F32   0     /* y is float32 [T, H] */
 #define EPL_OUT_BF16  1     /* y is bf16 [T, H], round to nearest even of the f32 sum */
 
+/* ---- scale formats of the FP8 calls -------------------------------------- */
+#define EPL_SCALE_NONE  0   /* no scale rows                                     */
+#define EPL_SCALE_F32   1   /* x_scale fp32 [T, S] -> out_scale fp32 [capacity, S]
+                               (row-major, as in the bf16 calls)                  */
+#define EPL_SCALE_UE8M0 2   /* x_scale int32 [T, W], W = ceil(S/4), each word four
+                               packed 8-bit power-of-two exponents (moved as
+                               opaque bits) -> out_scale int32 column-major
+                               [W, capacity]: word j of row p at
+                               out_scale[j * capacity + p], the transposed layout
+                               sglang allocates for UE8M0 scales ("参考sglang代码，
+                               重构vllm021中EP高吞吐代码，消除空泡问题", section 2.2) */
+
 /* ---- problem description ----------------------------------------------- */
 typedef struct epl_problem {
     int64_t num_tokens;   /* T >= 0                                           */
@@ -155,6 +167,27 @@ int epl_dispatch(const epl_problem *p, const int64_t *topk_idx,
                  int32_t *total_host, uint16_t *out, float *out_scale,
                  int32_t *m_indices, int32_t *output_index,
                  void *workspace, void *stream);
+
+/* Steps 3 and 1-3 for an FP8 (e4m3) payload, as DeepEP dispatches it
+ * ("[MoE] Deepseek的All-to-all通信: DeepEP代码解读", section Dispatch: x as a
+ * (fp8 [T, H], fp32 [T, H/128]) tuple): rows are H bytes (requires
+ * H % 16 == 0), moved bit for bit like the bf16 rows; the scale rows follow
+ * in `scale_format` (EPL_SCALE_*; with a format other than NONE the problem
+ * needs scale_cols = H/128 and the scale pointers must be 4-byte aligned).
+ * Everything else (row placement, m_indices, output_index, alignment
+ * padding, status) is as in epl_scatter / epl_dispatch. */
+int epl_scatter_fp8(const epl_problem *p, const uint8_t *x, const void *x_scale,
+                    int scale_format, const int64_t *topk_idx,
+                    const int32_t *expert_start_loc, void *workspace, int64_t capacity_rows,
+                    uint8_t *out, void *out_scale, int32_t *m_indices, int32_t *output_index,
+                    void *stream);
+int epl_dispatch_fp8(const epl_problem *p, const int64_t *topk_idx, const uint8_t *x,
+                     const void *x_scale, int scale_format, int64_t capacity_rows,
+                     int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,
+                     uint8_t *is_token_in_rank, int32_t *expert_start_loc,
+                     int32_t *total_host, uint8_t *out, void *out_scale,
+                     int32_t *m_indices, int32_t *output_index, void *workspace,
+                     void *stream);
 
 /* Step 4 -- combine. For every token t:
  *   y[t, :] = sum over k ascending with output_index[t, k] >= 0 of

@@ -24,7 +24,8 @@ __all__ = [
     "epl_scatter", "epl_dispatch", "epl_combine", "epl_expert_scale", "epl_status", "epl_total",
     "epl_strerror", "epl_version", "dispatch", "combine", "expert_scale", "DispatchResult",
     "EPL_OK", "EPL_EINVAL", "EPL_ERANGE", "EPL_ECAPACITY", "EPL_EHIP", "EPL_OUT_F32",
-    "EPL_OUT_BF16", "prepare",
+    "EPL_OUT_BF16", "prepare", "epl_scatter_fp8", "epl_dispatch_fp8", "EPL_SCALE_NONE",
+    "EPL_SCALE_F32", "EPL_SCALE_UE8M0",
 ]
 
 EPL_OK = 0
@@ -34,12 +35,15 @@ EPL_ECAPACITY = -3
 EPL_EHIP = -4
 EPL_OUT_F32 = 0
 EPL_OUT_BF16 = 1
+EPL_SCALE_NONE = 0
+EPL_SCALE_F32 = 1
+EPL_SCALE_UE8M0 = 2
 
 # Every function include/epl.h declares; tests check the library exports them.
 C_ENTRY_POINTS = (
     "epl_validate", "epl_workspace_bytes", "epl_capacity_rows", "epl_layout", "epl_scan",
-    "epl_scatter", "epl_dispatch", "epl_combine", "epl_expert_scale", "epl_status", "epl_total",
-    "epl_strerror", "epl_version",
+    "epl_scatter", "epl_dispatch", "epl_scatter_fp8", "epl_dispatch_fp8", "epl_combine",
+    "epl_expert_scale", "epl_status", "epl_total", "epl_strerror", "epl_version",
 )
 
 
@@ -127,6 +131,11 @@ def load() -> ctypes.CDLL:
     lib.epl_scatter.restype = i32
     lib.epl_dispatch.argtypes = [_PP, _P, _P, _P, i64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.epl_dispatch.restype = i32
+    lib.epl_scatter_fp8.argtypes = [_PP, _P, _P, i32, _P, _P, _P, i64, _P, _P, _P, _P, _P]
+    lib.epl_scatter_fp8.restype = i32
+    lib.epl_dispatch_fp8.argtypes = [_PP, _P, _P, _P, i32, i64, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     _P, _P, _P]
+    lib.epl_dispatch_fp8.restype = i32
     lib.epl_combine.argtypes = [_PP, _P, i64, _P, _P, i32, _P, _P, _P]
     lib.epl_combine.restype = i32
     lib.epl_expert_scale.argtypes = [_PP, _P, _P, i64, _P, _P, _P]
@@ -297,6 +306,70 @@ def epl_dispatch(p: Problem, topk_idx, x, x_scale, capacity_rows, num_tokens_per
                                _ptr(expert_start_loc), _ptr(total_host), _ptr(out),
                                _ptr(out_scale), _ptr(m_indices), _ptr(output_index),
                                _ptr(workspace), _stream(stream, dev)), "epl_dispatch")
+
+
+def _check_fp8_args(p, x, x_scale, scale_format, topk_idx, capacity_rows, out, out_scale,
+                    m_indices, output_index):
+    torch = _torch()
+    T, K, H, S = p.num_tokens, p.num_topk, p.hidden, p.scale_cols
+    _need(topk_idx, "topk_idx", torch.int64, (T, K))
+    dev = topk_idx.device
+    _need(x, "x", torch.uint8, (T, H), dev)
+    _need(out, "out", torch.uint8, (capacity_rows, H), dev)
+    _need(m_indices, "m_indices", torch.int32, (capacity_rows,), dev)
+    _need(output_index, "output_index", torch.int32, (T, K), dev)
+    if scale_format == EPL_SCALE_F32:
+        _need(x_scale, "x_scale", torch.float32, (T, S), dev)
+        _need(out_scale, "out_scale", torch.float32, (capacity_rows, S), dev)
+    elif scale_format == EPL_SCALE_UE8M0:
+        W = (S + 3) // 4
+        _need(x_scale, "x_scale", torch.int32, (T, W), dev)
+        _need(out_scale, "out_scale (column-major storage [W, capacity])", torch.int32,
+              (W, capacity_rows), dev)
+    elif scale_format != EPL_SCALE_NONE:
+        raise ValueError(f"unknown scale format {scale_format}")
+    return dev
+
+
+def epl_scatter_fp8(p: Problem, x, x_scale, scale_format, topk_idx, expert_start_loc, workspace,
+                    capacity_rows, out, out_scale, m_indices, output_index, stream=None):
+    """FP8 rows as uint8 [T, H] (view a float8_e4m3fn tensor as uint8); the
+    UE8M0 output scale buffer is int32 [W, capacity] (its transpose is the
+    [capacity, W] view the grouped GEMM reads)."""
+    torch = _torch()
+    dev = _check_fp8_args(p, x, x_scale, scale_format, topk_idx, capacity_rows, out, out_scale,
+                          m_indices, output_index)
+    _need(expert_start_loc, "expert_start_loc", torch.int32, (p.num_experts,), dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
+    _check(load().epl_scatter_fp8(_prob(p), _ptr(x), _ptr(x_scale), int(scale_format),
+                                  _ptr(topk_idx), _ptr(expert_start_loc), _ptr(workspace),
+                                  int(capacity_rows), _ptr(out), _ptr(out_scale), _ptr(m_indices),
+                                  _ptr(output_index), _stream(stream, dev)), "epl_scatter_fp8")
+
+
+def epl_dispatch_fp8(p: Problem, topk_idx, x, x_scale, scale_format, capacity_rows,
+                     num_tokens_per_expert, num_tokens_per_rank, is_token_in_rank,
+                     expert_start_loc, total_host, out, out_scale, m_indices, output_index,
+                     workspace, stream=None):
+    torch = _torch()
+    dev = _check_fp8_args(p, x, x_scale, scale_format, topk_idx, capacity_rows, out, out_scale,
+                          m_indices, output_index)
+    E, R, T = p.num_experts, p.num_ranks, p.num_tokens
+    _need(num_tokens_per_expert, "num_tokens_per_expert", torch.int32, (E,), dev)
+    _need(num_tokens_per_rank, "num_tokens_per_rank", torch.int32, (R,), dev)
+    _need(is_token_in_rank, "is_token_in_rank", torch.uint8, (T, R), dev)
+    _need(expert_start_loc, "expert_start_loc", torch.int32, (E,), dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
+    if total_host is not None and (total_host.device.type != "cpu" or not total_host.is_pinned()
+                                   or total_host.dtype != torch.int32):
+        raise ValueError("total_host must be a pinned CPU int32 tensor")
+    _check(load().epl_dispatch_fp8(_prob(p), _ptr(topk_idx), _ptr(x), _ptr(x_scale),
+                                   int(scale_format), int(capacity_rows),
+                                   _ptr(num_tokens_per_expert), _ptr(num_tokens_per_rank),
+                                   _ptr(is_token_in_rank), _ptr(expert_start_loc),
+                                   _ptr(total_host), _ptr(out), _ptr(out_scale), _ptr(m_indices),
+                                   _ptr(output_index), _ptr(workspace), _stream(stream, dev)),
+           "epl_dispatch_fp8")
 
 
 def epl_combine(p: Problem, expert_out, expert_rows, output_index, topk_weights, out_dtype, y,

@@ -53,6 +53,17 @@ bool problem_ok(const epl_problem *p)
     return true;
 }
 
+// FP8 rows are H bytes (16-byte vectors need H % 16 == 0); scales, when
+// requested, need a problem with scale_cols > 0.
+bool fp8_problem_ok(const epl_problem *p, int scale_format)
+{
+    if (!problem_ok(p) || p->hidden % 16 != 0)
+        return false;
+    if (scale_format == EPL_SCALE_NONE)
+        return true;
+    return (scale_format == EPL_SCALE_F32 || scale_format == EPL_SCALE_UE8M0) && p->scale_cols > 0;
+}
+
 // Tokens per layout block: enough blocks to spread the work (about 64), but
 // at most 256 tokens (one per thread) and at most 2048 slots (the LDS key
 // buffer), and at least 16 tokens so the per-block count matrix stays small.
@@ -159,35 +170,50 @@ int enqueue_scan(const epl_problem &p, const WsLayout &w, int mode, int32_t *cnt
     return EPL_OK;
 }
 
+// What the scatter moves per token: the row as opaque bytes, and optional
+// scale words in one of the kernel's layouts.
+struct RowArgs {
+    const uint8_t *x;
+    int64_t row_bytes;
+    int scale_mode;            // epl::kScaleNone / kScaleRows / kScaleCols
+    const uint32_t *x_scale;
+    int words;                 // scale words per row
+    int64_t scale_ld;          // leading dimension of the column-major layout
+    uint8_t *out;
+    uint32_t *out_scale;
+};
+
 template <int VPT>
-void launch_scatter(const epl_problem &p, const WsLayout &w, const uint16_t *x, const float *xs,
+void launch_scatter(const epl_problem &p, const WsLayout &w, const RowArgs &ra,
                     const int64_t *topk, const int32_t *start, void *ws, int64_t cap,
-                    uint16_t *out, float *out_scale, int32_t *m_idx, int32_t *oi, hipStream_t s)
+                    int32_t *m_idx, int32_t *oi, hipStream_t s)
 {
     const unsigned grid = p.num_tokens >= epl::kScatterGridFrom
                               ? row_grid(p.num_tokens, p.num_tokens)
                               : row_grid(p.num_tokens, epl::kScatterGrid);
-    hipLaunchKernelGGL(epl::ep_scatter_kernel<VPT>, dim3(grid),
-                       dim3(epl::kScatterThreads), 0, s, x, xs, topk, start,
-                       at<const int32_t>(ws, w.block_count), at<const int32_t>(ws, w.slot_rank),
-                       p.num_tokens, p.num_topk, p.num_experts, p.hidden, p.scale_cols,
-                       p.scale_cols % 4 == 0 && aligned(xs, 16) && aligned(out_scale, 16),
-                       w.block_tokens, alignment_of(p), at<const int32_t>(ws, w.counts), cap,
-                       out, out_scale, m_idx, oi, &at<WsHeader>(ws, 0)->status);
+    const bool vec16 = ra.scale_mode == epl::kScaleRows && ra.words % 4 == 0 &&
+                       aligned(ra.x_scale, 16) && aligned(ra.out_scale, 16);
+    hipLaunchKernelGGL(epl::ep_scatter_kernel<VPT>, dim3(grid), dim3(epl::kScatterThreads), 0, s,
+                       ra.x, ra.row_bytes, ra.scale_mode, ra.x_scale, ra.words, vec16,
+                       ra.scale_ld, topk, start, at<const int32_t>(ws, w.block_count),
+                       at<const int32_t>(ws, w.slot_rank), p.num_tokens, p.num_topk,
+                       p.num_experts, w.block_tokens, alignment_of(p),
+                       at<const int32_t>(ws, w.counts), cap, ra.out, ra.out_scale, m_idx, oi,
+                       &at<WsHeader>(ws, 0)->status);
 }
 
-int enqueue_scatter(const epl_problem &p, const WsLayout &w, const uint16_t *x, const float *xs,
+int enqueue_scatter(const epl_problem &p, const WsLayout &w, const RowArgs &ra,
                     const int64_t *topk, const int32_t *start, void *ws, int64_t cap,
-                    uint16_t *out, float *out_scale, int32_t *m_idx, int32_t *oi, hipStream_t s)
+                    int32_t *m_idx, int32_t *oi, hipStream_t s)
 {
     if (p.num_tokens == 0)
         return EPL_OK;
-    const int nvec = p.hidden / 8;
-    const int vpt = std::min(8, (nvec + epl::kScatterThreads - 1) / epl::kScatterThreads);
+    const int64_t nvec = ra.row_bytes / 16;
+    const int vpt = (int)std::min<int64_t>(8, (nvec + epl::kScatterThreads - 1) / epl::kScatterThreads);
     switch (vpt) {
 #define EPL_SCATTER_CASE(V)                                                                        \
     case V:                                                                                        \
-        launch_scatter<V>(p, w, x, xs, topk, start, ws, cap, out, out_scale, m_idx, oi, s);       \
+        launch_scatter<V>(p, w, ra, topk, start, ws, cap, m_idx, oi, s);                           \
         break;
         EPL_SCATTER_CASE(1)
         EPL_SCATTER_CASE(2)
@@ -204,22 +230,49 @@ int enqueue_scatter(const epl_problem &p, const WsLayout &w, const uint16_t *x, 
     return launch_status();
 }
 
-bool scatter_args_ok(const epl_problem &p, const uint16_t *x, const float *xs,
-                     const int64_t *topk, int64_t cap, uint16_t *out, float *out_scale,
-                     int32_t *m_idx, int32_t *oi)
+RowArgs bf16_rows(const epl_problem &p, const uint16_t *x, const float *xs, uint16_t *out,
+                  float *out_scale)
+{
+    return RowArgs{reinterpret_cast<const uint8_t *>(x), 2 * (int64_t)p.hidden,
+                   p.scale_cols > 0 ? epl::kScaleRows : epl::kScaleNone,
+                   reinterpret_cast<const uint32_t *>(xs), p.scale_cols, 0,
+                   reinterpret_cast<uint8_t *>(out), reinterpret_cast<uint32_t *>(out_scale)};
+}
+
+// FP8 rows: H bytes; scales per the caller's format (see epl.h).
+RowArgs fp8_rows(const epl_problem &p, const uint8_t *x, const void *xs, int scale_format,
+                 int64_t cap, uint8_t *out, void *out_scale)
+{
+    RowArgs ra{x, (int64_t)p.hidden, epl::kScaleNone, static_cast<const uint32_t *>(xs), 0, cap,
+               out, static_cast<uint32_t *>(out_scale)};
+    if (scale_format == EPL_SCALE_F32) {
+        ra.scale_mode = epl::kScaleRows;
+        ra.words = p.scale_cols;
+    } else if (scale_format == EPL_SCALE_UE8M0) {
+        ra.scale_mode = epl::kScaleCols;
+        ra.words = (p.scale_cols + 3) / 4;
+    }
+    return ra;
+}
+
+// Pointer checks shared by the scatter entry points.
+bool rows_args_ok(const epl_problem &p, const RowArgs &ra, const int64_t *topk, int64_t cap,
+                  int32_t *m_idx, int32_t *oi)
 {
     const bool any_tokens = p.num_tokens > 0;
-    if (cap < 0)
+    if (cap < 0 || ra.row_bytes % 16 != 0)
         return false;
-    if (any_tokens && (!topk || !aligned(topk, 8) || !oi || !aligned(oi, 4) || !x ||
-                       !aligned(x, 16)))
+    if (any_tokens && (!topk || !aligned(topk, 8) || !oi || !aligned(oi, 4) || !ra.x ||
+                       !aligned(ra.x, 16)))
         return false;
-    if (cap > 0 && (!out || !aligned(out, 16) || !m_idx || !aligned(m_idx, 4)))
+    if (cap > 0 && (!ra.out || !aligned(ra.out, 16) || !m_idx || !aligned(m_idx, 4)))
         return false;
-    if (p.scale_cols > 0) {
-        if (any_tokens && (!xs || !aligned(xs, 4)))
+    if (ra.scale_mode != epl::kScaleNone) {
+        if (ra.words < 1)
             return false;
-        if (cap > 0 && (!out_scale || !aligned(out_scale, 4)))
+        if (any_tokens && (!ra.x_scale || !aligned(ra.x_scale, 4)))
+            return false;
+        if (cap > 0 && (!ra.out_scale || !aligned(ra.out_scale, 4)))
             return false;
     }
     return true;
@@ -305,12 +358,58 @@ int epl_scatter(const epl_problem *p, const uint16_t *x, const float *x_scale,
     if (!workspace || !aligned(workspace, kWsAlign) || !expert_start_loc ||
         !aligned(expert_start_loc, 4))
         return EPL_EINVAL;
-    if (!scatter_args_ok(*p, x, x_scale, topk_idx, capacity_rows, out, out_scale, m_indices,
-                         output_index))
+    const RowArgs ra = bf16_rows(*p, x, x_scale, out, out_scale);
+    if (!rows_args_ok(*p, ra, topk_idx, capacity_rows, m_indices, output_index))
         return EPL_EINVAL;
     const WsLayout w = ws_layout(*p);
-    return enqueue_scatter(*p, w, x, x_scale, topk_idx, expert_start_loc, workspace, capacity_rows,
-                           out, out_scale, m_indices, output_index, static_cast<hipStream_t>(stream));
+    return enqueue_scatter(*p, w, ra, topk_idx, expert_start_loc, workspace, capacity_rows,
+                           m_indices, output_index, static_cast<hipStream_t>(stream));
+}
+
+int epl_scatter_fp8(const epl_problem *p, const uint8_t *x, const void *x_scale, int scale_format,
+                    const int64_t *topk_idx, const int32_t *expert_start_loc, void *workspace,
+                    int64_t capacity_rows, uint8_t *out, void *out_scale, int32_t *m_indices,
+                    int32_t *output_index, void *stream)
+{
+    if (!fp8_problem_ok(p, scale_format))
+        return EPL_EINVAL;
+    if (!workspace || !aligned(workspace, kWsAlign) || !expert_start_loc ||
+        !aligned(expert_start_loc, 4))
+        return EPL_EINVAL;
+    const RowArgs ra = fp8_rows(*p, x, x_scale, scale_format, capacity_rows, out, out_scale);
+    if (!rows_args_ok(*p, ra, topk_idx, capacity_rows, m_indices, output_index))
+        return EPL_EINVAL;
+    const WsLayout w = ws_layout(*p);
+    return enqueue_scatter(*p, w, ra, topk_idx, expert_start_loc, workspace, capacity_rows,
+                           m_indices, output_index, static_cast<hipStream_t>(stream));
+}
+
+// layout + scan + scatter on one stream, shared by both payload types
+static int dispatch_rows(const epl_problem *p, const int64_t *topk_idx, const RowArgs &ra,
+                         int64_t capacity_rows, int32_t *num_tokens_per_expert,
+                         int32_t *num_tokens_per_rank, uint8_t *is_token_in_rank,
+                         int32_t *expert_start_loc, int32_t *total_host, int32_t *m_indices,
+                         int32_t *output_index, void *workspace, void *stream)
+{
+    if (!workspace || !aligned(workspace, kWsAlign) || !num_tokens_per_expert ||
+        !aligned(num_tokens_per_expert, 4) || !num_tokens_per_rank ||
+        !aligned(num_tokens_per_rank, 4) || !expert_start_loc || !aligned(expert_start_loc, 4) ||
+        (total_host && !aligned(total_host, 4)))
+        return EPL_EINVAL;
+    if (p->num_tokens > 0 && !is_token_in_rank)
+        return EPL_EINVAL;
+    if (!rows_args_ok(*p, ra, topk_idx, capacity_rows, m_indices, output_index))
+        return EPL_EINVAL;
+    const WsLayout w = ws_layout(*p);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int rc = enqueue_layout(*p, w, topk_idx, is_token_in_rank, workspace, s);
+    if (rc == EPL_OK)
+        rc = enqueue_scan(*p, w, epl::kScanReduce | epl::kScanPrefix, num_tokens_per_expert,
+                          num_tokens_per_rank, expert_start_loc, total_host, workspace, s);
+    if (rc == EPL_OK)
+        rc = enqueue_scatter(*p, w, ra, topk_idx, expert_start_loc, workspace, capacity_rows,
+                             m_indices, output_index, s);
+    return rc;
 }
 
 int epl_dispatch(const epl_problem *p, const int64_t *topk_idx, const uint16_t *x,
@@ -321,26 +420,25 @@ int epl_dispatch(const epl_problem *p, const int64_t *topk_idx, const uint16_t *
 {
     if (!problem_ok(p))
         return EPL_EINVAL;
-    if (!workspace || !aligned(workspace, kWsAlign) || !num_tokens_per_expert ||
-        !aligned(num_tokens_per_expert, 4) || !num_tokens_per_rank ||
-        !aligned(num_tokens_per_rank, 4) || !expert_start_loc || !aligned(expert_start_loc, 4) ||
-        (total_host && !aligned(total_host, 4)))
+    return dispatch_rows(p, topk_idx, bf16_rows(*p, x, x_scale, out, out_scale), capacity_rows,
+                         num_tokens_per_expert, num_tokens_per_rank, is_token_in_rank,
+                         expert_start_loc, total_host, m_indices, output_index, workspace, stream);
+}
+
+int epl_dispatch_fp8(const epl_problem *p, const int64_t *topk_idx, const uint8_t *x,
+                     const void *x_scale, int scale_format, int64_t capacity_rows,
+                     int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,
+                     uint8_t *is_token_in_rank, int32_t *expert_start_loc, int32_t *total_host,
+                     uint8_t *out, void *out_scale, int32_t *m_indices, int32_t *output_index,
+                     void *workspace, void *stream)
+{
+    if (!fp8_problem_ok(p, scale_format))
         return EPL_EINVAL;
-    if (p->num_tokens > 0 && !is_token_in_rank)
-        return EPL_EINVAL;
-    if (!scatter_args_ok(*p, x, x_scale, topk_idx, capacity_rows, out, out_scale, m_indices,
-                         output_index))
-        return EPL_EINVAL;
-    const WsLayout w = ws_layout(*p);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    int rc = enqueue_layout(*p, w, topk_idx, is_token_in_rank, workspace, s);
-    if (rc == EPL_OK)
-        rc = enqueue_scan(*p, w, epl::kScanReduce | epl::kScanPrefix, num_tokens_per_expert,
-                          num_tokens_per_rank, expert_start_loc, total_host, workspace, s);
-    if (rc == EPL_OK)
-        rc = enqueue_scatter(*p, w, x, x_scale, topk_idx, expert_start_loc, workspace,
-                             capacity_rows, out, out_scale, m_indices, output_index, s);
-    return rc;
+    return dispatch_rows(p, topk_idx,
+                         fp8_rows(*p, x, x_scale, scale_format, capacity_rows, out, out_scale),
+                         capacity_rows, num_tokens_per_expert, num_tokens_per_rank,
+                         is_token_in_rank, expert_start_loc, total_host, m_indices, output_index,
+                         workspace, stream);
 }
 
 int epl_combine(const epl_problem *p, const uint16_t *expert_out, int64_t expert_rows,

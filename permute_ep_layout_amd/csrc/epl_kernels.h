@@ -529,11 +529,19 @@ __device__ __forceinline__ void store_scale(V *dst, const V &v)
         *dst = v;
 }
 
-// One workgroup per token row, grid-stride over tokens. The row is read once
-// (16-byte vectors, VPT per thread per pass) and stored to each of the
-// token's K destination rows with non-temporal stores: the buffer is written
-// once and read much later, so the stores should not displace cached data.
-// The scale row is fetched together with the row and follows it.
+// Scale layouts of the scatter.
+constexpr int kScaleNone = 0;
+constexpr int kScaleRows = 1;   // W words per row, row-major ([rows, W])
+constexpr int kScaleCols = 2;   // W words per row, column-major: word j of row p at j * ld + p
+
+// One workgroup per token row, grid-stride over tokens. A row is row_bytes
+// of opaque payload (bf16: 2H bytes, FP8: H bytes), read once as 16-byte
+// vectors (VPT per thread per pass) and stored to each of the token's K
+// destination rows with non-temporal stores: the buffer is written once and
+// read much later, so the stores should not displace cached data. The
+// token's W scale words are fetched together with the row and follow it,
+// row-major (fp32 scales) or column-major (the transposed packed-UE8M0
+// layout of the FP8 grouped GEMM).
 //
 // Destination rows come from two dependent lookups per slot (expert id and
 // slot rank, then expert offset and block offset). The first K threads run
@@ -545,17 +553,17 @@ __device__ __forceinline__ void store_scale(V *dst, const V &v)
 // i.e. has finished reading that buffer.
 template <int VPT>
 __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
-    const uint16_t *__restrict__ x, const float *__restrict__ x_scale,
+    const uint8_t *__restrict__ x, int64_t row_bytes, int scale_mode,
+    const uint32_t *__restrict__ x_scale, int W, bool scale_vec16, int64_t scale_ld,
     const int64_t *__restrict__ topk, const int32_t *__restrict__ start,
     const int32_t *__restrict__ block_base, const int32_t *__restrict__ slot_rank, int64_t T,
-    int K, int E, int H, int S, bool scale_vec16, int B, int alignment,
-    const int32_t *__restrict__ counts, int64_t capacity, uint16_t *__restrict__ out,
-    float *__restrict__ out_scale, int32_t *__restrict__ m_indices,
+    int K, int E, int B, int alignment, const int32_t *__restrict__ counts, int64_t capacity,
+    uint8_t *__restrict__ out, uint32_t *__restrict__ out_scale, int32_t *__restrict__ m_indices,
     int32_t *__restrict__ output_index, uint32_t *__restrict__ status)
 {
     __shared__ int64_t s_row[2][kMaxTopk];
     const int tid = threadIdx.x;
-    const int nvec = H >> 3;
+    const int nvec = (int)(row_bytes >> 4);
 
     // Padding rows of the aligned blocks: between an expert's last row and
     // the end of its block, marked -1 (workgroup w takes experts w, w + G, ...).
@@ -572,7 +580,10 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
             }
         }
     }
-    const int nq = scale_vec16 ? (S >> 2) : 0;
+    // scale words prefetched with the row: 16-byte pieces (row-major, W % 4 == 0)
+    // or single words (column-major)
+    const int nq = scale_mode == kScaleRows && scale_vec16 ? (W >> 2) : 0;
+    const int nw = scale_mode == kScaleCols ? W : 0;
     const TokenRange tr = token_range(T);
     const int64_t step = tr.stride, t_end = tr.end;
     const bool lead = tid < K;
@@ -602,7 +613,7 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
     int it = 0;
     for (int64_t t = tr.first; t < t_end; t += step, ++it) {
         int64_t *rows = s_row[it & 1];
-        const u32x4 *xrow = reinterpret_cast<const u32x4 *>(x + t * H);
+        const u32x4 *xrow = reinterpret_cast<const u32x4 *>(x + t * row_bytes);
         u32x4 v[VPT];
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
@@ -610,9 +621,12 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
             if (idx < nvec)
                 v[i] = xrow[idx];
         }
-        f32x4 sv = {0.0f, 0.0f, 0.0f, 0.0f};
+        u32x4 sv = {0u, 0u, 0u, 0u};
+        uint32_t sw = 0u;
         if (tid < nq)
-            sv = reinterpret_cast<const f32x4 *>(x_scale + t * S)[tid];
+            sv = reinterpret_cast<const u32x4 *>(x_scale + t * W)[tid];
+        if (tid < nw)
+            sw = x_scale[t * W + tid];
 
         if (lead) {
             int pos = -1;
@@ -653,7 +667,7 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
                     for (int k = 0; k < K; ++k) {
                         const int64_t row = rows[k];
                         if (row >= 0) {
-                            u32x4 *dst = reinterpret_cast<u32x4 *>(out + row * H) + idx;
+                            u32x4 *dst = reinterpret_cast<u32x4 *>(out + row * row_bytes) + idx;
                             if (EPL_ROW_NT)
                                 __builtin_nontemporal_store(v[i], dst);
                             else
@@ -672,24 +686,35 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
                     v[i] = xrow[idx];
             }
         }
-        if (scale_vec16) {
-            // 16-byte pieces of the scale row (S % 4 == 0 and 16-byte aligned bases);
-            // threads beyond the first kScatterThreads pieces (S > 512) take the rest.
+        if (nq > 0) {
+            // 16-byte pieces of the scale row (W % 4 == 0 and 16-byte aligned
+            // bases); threads past the first kScatterThreads pieces take the rest.
             for (int j = tid; j < nq; j += kScatterThreads) {
-                const f32x4 f = j == tid ? sv : reinterpret_cast<const f32x4 *>(x_scale + t * S)[j];
+                const u32x4 f = j == tid ? sv : reinterpret_cast<const u32x4 *>(x_scale + t * W)[j];
                 for (int k = 0; k < K; ++k) {
                     const int64_t row = rows[k];
                     if (row >= 0)
-                        store_scale(reinterpret_cast<f32x4 *>(out_scale + row * S) + j, f);
+                        store_scale(reinterpret_cast<u32x4 *>(out_scale + row * W) + j, f);
                 }
             }
-        } else {
-            for (int j = tid; j < S; j += kScatterThreads) {
-                const float f = x_scale[t * S + j];
+        } else if (scale_mode == kScaleRows) {
+            for (int j = tid; j < W; j += kScatterThreads) {
+                const uint32_t f = x_scale[t * W + j];
                 for (int k = 0; k < K; ++k) {
                     const int64_t row = rows[k];
                     if (row >= 0)
-                        store_scale(out_scale + row * S + j, f);
+                        store_scale(out_scale + row * W + j, f);
+                }
+            }
+        } else if (scale_mode == kScaleCols) {
+            // word j of every destination row lands in column j of the
+            // transposed buffer; rows of one expert are neighbours there
+            for (int j = tid; j < W; j += kScatterThreads) {
+                const uint32_t f = j == tid ? sw : x_scale[t * W + j];
+                for (int k = 0; k < K; ++k) {
+                    const int64_t row = rows[k];
+                    if (row >= 0)
+                        store_scale(out_scale + (int64_t)j * scale_ld + row, f);
                 }
             }
         }

@@ -150,6 +150,24 @@ def test_entry_points_reject_bad_arguments_without_a_gpu(lib):
     assert lib.epl_total(odd, None) == epl.EPL_EINVAL
 
 
+def test_fp8_entry_points_check_their_arguments(lib):
+    fake = 1 << 20
+    ok = P()                                     # H = 7168, S = 56
+    bad_h = P(hidden=136, scale_cols=0)          # 136 % 16 != 0
+    no_s = P(scale_cols=0)
+
+    def scat(p, fmt, xs=fake, outs=fake):
+        return lib.epl_scatter_fp8(ctypes.byref(p), fake, xs, fmt, fake, fake, fake, 10, fake,
+                                   outs, fake, fake, None)
+    assert scat(bad_h, epl.EPL_SCALE_NONE) == epl.EPL_EINVAL
+    assert scat(ok, 7) == epl.EPL_EINVAL                          # unknown format
+    assert scat(no_s, epl.EPL_SCALE_UE8M0) == epl.EPL_EINVAL      # scales without scale_cols
+    assert scat(ok, epl.EPL_SCALE_F32, xs=None) == epl.EPL_EINVAL
+    assert scat(ok, epl.EPL_SCALE_UE8M0, outs=fake + 2) == epl.EPL_EINVAL
+    assert lib.epl_dispatch_fp8(ctypes.byref(bad_h), fake, fake, None, 0, 10, fake, fake, fake,
+                                fake, None, fake, None, fake, fake, fake, None) == epl.EPL_EINVAL
+
+
 def test_strerror(lib):
     for code in (0, -1, -2, -3, -4):
         assert epl.epl_strerror(code)

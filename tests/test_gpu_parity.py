@@ -275,6 +275,91 @@ def test_aligned_capacity_overflow_in_padding_is_flagged():
     np.testing.assert_array_equal(r["m"].cpu().numpy(), ref["m_indices"][:N - 1])
 
 
+# ------------------------------------------------------------- FP8 payload --
+
+def fp8_parity(w, fmt, alignment=0, extra_cap=0, split=False):
+    """FP8 rows and scale words through epl_dispatch_fp8 / epl_scatter_fp8
+    against the oracle's byte-row scatter."""
+    inp = workloads.make_inputs(w)
+    topk, x, xs = inp["topk_idx"], inp["x"], inp["x_scale"]
+    T, K = topk.shape
+    E, R, H, S = w.num_experts, w.num_ranks, w.hidden, w.scale_cols
+    if fmt == epl.EPL_SCALE_NONE:
+        S, xs = 0, None
+    p = epl.Problem.make(T, K, E, R, H, S, alignment)
+    cap = epl.epl_capacity_rows(p) + extra_cap
+    orc_ = orc()
+    cnt, per_rank, in_rank = orc_.layout(topk, E, R)
+    start, N = orc_.scan(cnt, alignment)
+    words = None if xs is None else xs.view(np.uint32)
+    ofmt = {epl.EPL_SCALE_NONE: orc_.SCALE_NONE, epl.EPL_SCALE_F32: orc_.SCALE_ROWS,
+            epl.EPL_SCALE_UE8M0: orc_.SCALE_COLS}[fmt]
+    out_ref, sc_ref, m_ref, oi_ref = orc_.scatter_rows(x, words, ofmt, topk, start, N, scale_ld=cap)
+    W = 0 if xs is None else xs.shape[1]
+    ws = poisoned(epl.epl_workspace_bytes(p), torch.uint8)
+    cnt_d, per_d = poisoned(E, torch.int32), poisoned(R, torch.int32)
+    in_d, start_d = poisoned((T, R), torch.uint8), poisoned(E, torch.int32)
+    out = poisoned((cap, H), torch.uint8)
+    if fmt == epl.EPL_SCALE_F32:
+        out_s = poisoned((cap, S), torch.float32)
+        xs_d = torch.from_numpy(xs).to(DEV)
+    elif fmt == epl.EPL_SCALE_UE8M0:
+        out_s = poisoned((W, cap), torch.int32)
+        xs_d = torch.from_numpy(xs.view(np.int32)).to(DEV)
+    else:
+        out_s, xs_d = None, None
+    m = poisoned(cap, torch.int32)
+    oi = poisoned((T, K), torch.int32)
+    tot = torch.full((1,), -7, dtype=torch.int32).pin_memory()
+    tk = torch.from_numpy(topk).to(DEV)
+    xd = torch.from_numpy(x).to(DEV)
+    if split:
+        epl.epl_layout(p, tk, cnt_d, per_d, in_d, ws)
+        epl.epl_scan(p, cnt_d, start_d, tot, ws)
+        epl.epl_scatter_fp8(p, xd, xs_d, fmt, tk, start_d, ws, cap, out, out_s, m, oi)
+    else:
+        epl.epl_dispatch_fp8(p, tk, xd, xs_d, fmt, cap, cnt_d, per_d, in_d, start_d, tot, out,
+                             out_s, m, oi, ws)
+    assert epl.epl_status(ws) == epl.EPL_OK
+    assert int(tot[0]) == N
+    np.testing.assert_array_equal(cnt_d.cpu().numpy(), cnt)
+    np.testing.assert_array_equal(in_d.cpu().numpy(), in_rank)
+    np.testing.assert_array_equal(start_d.cpu().numpy(), start)
+    np.testing.assert_array_equal(oi.cpu().numpy(), oi_ref)
+    np.testing.assert_array_equal(m[:N].cpu().numpy(), m_ref)
+    real = m_ref >= 0
+    np.testing.assert_array_equal(out[:N].cpu().numpy()[real], out_ref[real])
+    if fmt == epl.EPL_SCALE_F32:
+        np.testing.assert_array_equal(out_s[:N].cpu().numpy().view(np.uint32)[real], sc_ref[real])
+    elif fmt == epl.EPL_SCALE_UE8M0:
+        got = out_s.cpu().numpy().view(np.uint32)[:, :N]
+        want = sc_ref.reshape(W, cap)[:, :N]
+        np.testing.assert_array_equal(got[:, real], want[:, real])
+
+
+def test_fp8_dsv3_ue8m0_parity():
+    print("[parity] workload=dsv3_fp8 ue8m0", flush=True)
+    fp8_parity(workloads.get("dsv3_fp8"), epl.EPL_SCALE_UE8M0)
+
+
+@pytest.mark.parametrize("case", [
+    # name, T, H, E, K, R, fmt, alignment, extra capacity, split
+    ("f32_scales", 700, 1024, 32, 4, 8, epl.EPL_SCALE_F32, 0, 0, False),
+    ("no_scales_ragged_h", 555, 144, 16, 3, 4, epl.EPL_SCALE_NONE, 0, 0, False),
+    ("ue8m0_s5_aligned", 900, 640, 24, 5, 6, epl.EPL_SCALE_UE8M0, 32, 0, False),
+    ("ue8m0_spare_capacity", 400, 512, 16, 2, 4, epl.EPL_SCALE_UE8M0, 0, 77, True),
+    ("ue8m0_large_t", 9000, 256, 64, 6, 8, epl.EPL_SCALE_UE8M0, 16, 0, False),
+], ids=lambda c: c[0])
+def test_fp8_shapes(case):
+    name, T, H, E, K, R, fmt, a, extra, split = case
+    print(f"[parity] fp8 case={name}", flush=True)
+    w = workloads.Workload(name, seed=91, num_tokens=T, hidden=H, num_experts=E, num_topk=K,
+                           num_ranks=R, scales=True, routing="uniform", drop_rate=0.1,
+                           payload="fp8",
+                           scale_format="f32" if fmt == epl.EPL_SCALE_F32 else "ue8m0")
+    fp8_parity(w, fmt, alignment=a, extra_cap=extra, split=split)
+
+
 # ----------------------------------------------------------- ragged shapes --
 
 RAGGED = [

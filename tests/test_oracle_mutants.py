@@ -250,14 +250,28 @@ def test_unmutated_oracle_passes_the_battery():
     assert json.loads(proc.stdout.strip().splitlines()[-1]) == []
 
 
+@pytest.fixture(scope="module")
+def mutant_results(tmp_path_factory):
+    """Build every mutant and run its battery, a few processes at a time."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    d = tmp_path_factory.mktemp("mutants")
+
+    def one(name):
+        find, repl = MUTANTS[name]
+        proc = _run_battery_in_subprocess(_build_mutant(d, name, find, repl))
+        if proc.returncode != 0:
+            return name, "crashed"          # the mutant crashed inside a pin: caught
+        return name, json.loads(proc.stdout.strip().splitlines()[-1])
+
+    workers = max(1, min(6, (os.cpu_count() or 2) - 1))
+    with ThreadPoolExecutor(workers) as pool:
+        return dict(pool.map(one, sorted(MUTANTS)))
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_planted_mistake_is_caught(tmp_path, name):
-    find, repl = MUTANTS[name]
-    lib = _build_mutant(tmp_path, name, find, repl)
-    proc = _run_battery_in_subprocess(lib)
-    if proc.returncode != 0:
-        return          # the mutant crashed inside a pin: caught
-    failed = json.loads(proc.stdout.strip().splitlines()[-1])
+def test_planted_mistake_is_caught(mutant_results, name):
+    failed = mutant_results[name]
     assert failed, f"planted mistake {name!r} passed every pin"
 
 
