@@ -37,14 +37,16 @@ def log(msg):
 
 def algorithmic_bytes(w, N, T_any, out_dtype_bytes=4, pad_rows=0):
     """Bytes each kernel must move (reads + writes), by its definition;
-    alignment padding rows only get their m_indices entry."""
-    T, K, E, R, H, S = (w.num_tokens, w.num_topk, w.num_experts, w.num_ranks, w.hidden,
-                        w.scale_cols)
+    alignment padding rows only get their m_indices entry. A row is 2H bytes
+    (bf16) or H bytes (FP8); a scale row is W 4-byte words."""
+    T, K, E, R, H = w.num_tokens, w.num_topk, w.num_experts, w.num_ranks, w.hidden
+    B = H if w.payload == "fp8" else 2 * H
+    S = w.scale_words
     return {
         "layout": 8 * T * K + 4 * E + 4 * R + T * R,
         "scan": 4 * E + 4 * E + 4,
-        "scatter": (2 * H * T_any + 4 * S * T_any + 8 * T * K + 4 * E) +
-                   (2 * H * N + 4 * S * N + 4 * N + 4 * T * K + 4 * pad_rows),
+        "scatter": (B * T_any + 4 * S * T_any + 8 * T * K + 4 * E) +
+                   (B * N + 4 * S * N + 4 * N + 4 * T * K + 4 * pad_rows),
         "expert": 2 * H * N + 4 * N + 2 * H * N,
         "combine": 2 * H * N + 4 * T * K + 4 * T * K + out_dtype_bytes * T * H,
     }
@@ -76,24 +78,45 @@ def copy_calibration(nbytes):
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
 
 
-def cpu_baseline(w, inp, seconds):
+def cpu_baseline(w, inp, seconds, alignment=0):
     """The CPU oracle as it stands, single-threaded, over full passes of the
     same workload until about `seconds` of work."""
+    import numpy as np
+
     import oracle
+    from permute_ep_layout_amd import workloads
 
     orc = oracle.default()
+    E, R = w.num_experts, w.num_ranks
+    topk, wt = inp["topk_idx"], inp["topk_weights"]
+    if w.payload == "fp8":
+        # FP8 rows out; the combine reads the bf16 expert output, stood in for
+        # (outside the timed passes) by the bf16 rows of the same tokens
+        cnt, _, _ = orc.layout(topk, E, R)
+        start, total = orc.scan(cnt, alignment)
+        eo = orc.scatter(workloads.make_x(w), None, topk, start, total)[0]
+        fmt = orc.SCALE_COLS if w.scale_format == "ue8m0" else orc.SCALE_ROWS
+        xs = None if inp["x_scale"] is None else inp["x_scale"].view(np.uint32)
+        what = "layout, scan, FP8 row and scale-word scatter, fp64 combine of bf16 rows"
+    else:
+        what = "layout, scan, scatter with row copies, fp64 combine"
     passes, rows, t0 = 0, 0, time.perf_counter()
     while True:
-        r = orc.run_all(inp["x"], inp["x_scale"], inp["topk_idx"], inp["topk_weights"],
-                        w.num_experts, w.num_ranks, expert_fn=w.expert_fn)
+        if w.payload == "fp8":
+            cnt, _, _ = orc.layout(topk, E, R)
+            start, total = orc.scan(cnt, alignment)
+            _, _, _, oi = orc.scatter_rows(inp["x"], xs, fmt, topk, start, total)
+            orc.combine(eo, oi, wt)
+        else:
+            total = orc.run_all(inp["x"], inp["x_scale"], topk, wt, E, R,
+                                expert_fn=w.expert_fn, alignment=alignment)["total"]
         passes += 1
-        rows += r["total"]
+        rows += int((topk >= 0).sum())
         el = time.perf_counter() - t0
         if el >= seconds or passes >= 50:
             break
     return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} full pass(es) of the {w.name} workload "
-                      f"(layout, scan, scatter with row copies, fp64 combine), {el:.1f} s"}
+            "sample": f"{passes} full pass(es) of the {w.name} workload ({what}), {el:.1f} s"}
 
 
 def main():
@@ -142,9 +165,18 @@ def main():
     N = int((inp["topk_idx"] >= 0).sum())
     T_any = int((inp["topk_idx"] >= 0).any(axis=1).sum())
 
+    fp8 = w.payload == "fp8"
+    W = w.scale_words
+    fmt = (epl.EPL_SCALE_NONE if not S else
+           epl.EPL_SCALE_UE8M0 if w.scale_format == "ue8m0" else epl.EPL_SCALE_F32)
     topk = torch.from_numpy(inp["topk_idx"]).to(dev)
-    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
-    xs = torch.from_numpy(inp["x_scale"]).to(dev) if S else None
+    if fp8:
+        x = torch.from_numpy(inp["x"]).to(dev)
+        xs = None if not S else torch.from_numpy(
+            inp["x_scale"].view(np.int32) if fmt == epl.EPL_SCALE_UE8M0 else inp["x_scale"]).to(dev)
+    else:
+        x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+        xs = torch.from_numpy(inp["x_scale"]).to(dev) if S else None
     wt = torch.from_numpy(inp["topk_weights"]).to(dev)
     p = epl.Problem.make(T, K, E, R, H, S, args.alignment)
     cap = epl.epl_capacity_rows(p)
@@ -155,12 +187,31 @@ def main():
     in_rank = torch.empty((T, R), dtype=torch.uint8, device=dev)
     start = torch.empty(E, dtype=i32, device=dev)
     total_host = torch.zeros(1, dtype=i32).pin_memory()
-    out = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
-    out_scale = torch.empty((cap, S), dtype=torch.float32, device=dev) if S else None
+    def row_buffers(rows):
+        """Output rows and scale buffer for `rows` rows in the workload's format."""
+        if not fp8:
+            return (torch.empty((rows, H), dtype=torch.bfloat16, device=dev),
+                    torch.empty((rows, S), dtype=torch.float32, device=dev) if S else None)
+        o = torch.empty((rows, H), dtype=torch.uint8, device=dev)
+        if fmt == epl.EPL_SCALE_UE8M0:
+            return o, torch.empty((W, rows), dtype=i32, device=dev)    # column-major words
+        return o, (torch.empty((rows, S), dtype=torch.float32, device=dev) if S else None)
+
+    out, out_scale = row_buffers(cap)
     m_idx = torch.empty(cap, dtype=i32, device=dev)
     oi = torch.empty((T, K), dtype=i32, device=dev)
     scaled = w.expert_fn == "scale"
-    eo = torch.empty_like(out) if scaled else out
+    if fp8:
+        # The combine consumes the grouped GEMM's bf16 output. Stand-in: the
+        # bf16 rows of the same tokens scattered once to the same rows.
+        xb = torch.from_numpy(workloads.make_x(w).view(np.int16)).to(dev).view(torch.bfloat16)
+        eo = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+        pb = epl.Problem.make(T, K, E, R, H, 0, args.alignment)
+        epl.epl_dispatch(pb, topk, xb, None, cap, cnt, per_rank, in_rank, start, total_host, eo,
+                         None, m_idx, oi, ws)
+        del xb
+    else:
+        eo = torch.empty_like(out) if scaled else out
     out_code = epl.EPL_OUT_F32 if args.out_dtype == "f32" else epl.EPL_OUT_BF16
     y = torch.empty((T, H), dtype=torch.float32 if out_code == epl.EPL_OUT_F32 else torch.bfloat16,
                     device=dev)
@@ -172,22 +223,36 @@ def main():
     # timed loop calls the C entry points directly with the same arguments.
     epl.epl_layout(p, topk, cnt, per_rank, in_rank, ws)
     epl.epl_scan(p, cnt, start, total_host, ws)
-    epl.epl_scatter(p, x, xs, topk, start, ws, cap, out, out_scale, m_idx, oi)
+    if fp8:
+        epl.epl_scatter_fp8(p, x, xs, fmt, topk, start, ws, cap, out, out_scale, m_idx, oi)
+    else:
+        epl.epl_scatter(p, x, xs, topk, start, ws, cap, out, out_scale, m_idx, oi)
     if scaled:
         epl.epl_expert_scale(p, out, m_idx, cap, eo, ws)
     epl.epl_combine(p, eo, cap, oi, wt, out_code, y, ws)
-    epl.epl_dispatch(p, topk, x, xs, cap, cnt, per_rank, in_rank, start, total_host, out,
-                     out_scale, m_idx, oi, ws)
+    if fp8:
+        epl.epl_dispatch_fp8(p, topk, x, xs, fmt, cap, cnt, per_rank, in_rank, start, total_host,
+                             out, out_scale, m_idx, oi, ws)
+        scatter_call = epl.prepare("epl_scatter_fp8", p, x, xs, fmt, topk, start, ws, cap, out,
+                                   out_scale, m_idx, oi)
+        dispatch_call = epl.prepare("epl_dispatch_fp8", p, topk, x, xs, fmt, cap, cnt, per_rank,
+                                    in_rank, start, total_host, out, out_scale, m_idx, oi, ws)
+    else:
+        epl.epl_dispatch(p, topk, x, xs, cap, cnt, per_rank, in_rank, start, total_host, out,
+                         out_scale, m_idx, oi, ws)
+        scatter_call = epl.prepare("epl_scatter", p, x, xs, topk, start, ws, cap, out, out_scale,
+                                   m_idx, oi)
+        dispatch_call = epl.prepare("epl_dispatch", p, topk, x, xs, cap, cnt, per_rank, in_rank,
+                                    start, total_host, out, out_scale, m_idx, oi, ws)
     calls = [
         epl.prepare("epl_layout", p, topk, cnt, per_rank, in_rank, ws),
         epl.prepare("epl_scan", p, cnt, start, total_host, ws),
-        epl.prepare("epl_scatter", p, x, xs, topk, start, ws, cap, out, out_scale, m_idx, oi),
+        scatter_call,
     ]
     if scaled:
         calls.append(epl.prepare("epl_expert_scale", p, out, m_idx, cap, eo, ws))
     calls.append(epl.prepare("epl_combine", p, eo, cap, oi, wt, out_code, y, ws))
-    fused_calls = [epl.prepare("epl_dispatch", p, topk, x, xs, cap, cnt, per_rank, in_rank, start,
-                               total_host, out, out_scale, m_idx, oi, ws)] + calls[3:]
+    fused_calls = [dispatch_call] + calls[3:]
 
     def step_split(events=None):
         for i, call in enumerate(calls):
@@ -276,11 +341,13 @@ def main():
                 if mode == "exact":
                     stream.synchronize()
                     n_ex = int(total_host[0])
-                    o = torch.empty((n_ex, H), dtype=torch.bfloat16, device=dev)
-                    o_s = torch.empty((n_ex, S), dtype=torch.float32, device=dev) if S else None
+                    o, o_s = row_buffers(n_ex)
                     m_i = torch.empty(n_ex, dtype=i32, device=dev)
                     ev_b.record(stream)
-                    epl.epl_scatter(p, x, xs, topk, start, ws, n_ex, o, o_s, m_i, oi)
+                    if fp8:
+                        epl.epl_scatter_fp8(p, x, xs, fmt, topk, start, ws, n_ex, o, o_s, m_i, oi)
+                    else:
+                        epl.epl_scatter(p, x, xs, topk, start, ws, n_ex, o, o_s, m_i, oi)
                 else:
                     ev_b.record(stream)
                     calls[2]()
@@ -334,7 +401,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s, 1 thread)")
-        cpu = cpu_baseline(w, inp, args.cpu_seconds)
+        cpu = cpu_baseline(w, inp, args.cpu_seconds, args.alignment)
 
     result = {
         "metric": "routed token-rows/s (dispatch+combine)",
@@ -347,12 +414,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": w.name,
             "num_tokens": T, "hidden": H, "num_experts": E, "num_topk": K,
             "num_virtual_ranks": R, "scale_cols": S, "routing": w.routing,
+            "payload": w.payload, "scale_format": w.scale_format if S else None,
             "drop_rate": w.drop_rate, "expert_fn": w.expert_fn, "routed_rows": N,
             "expert_alignment": args.alignment, "buffer_rows": n_rows,
             "combine_out": args.out_dtype, "capacity_rows": cap,

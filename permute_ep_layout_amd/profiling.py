@@ -52,6 +52,21 @@ def short_name(kernel_name: str) -> str:
     return kernel_name.split("(")[0][:60]
 
 
+def unique_short(counts: dict) -> dict:
+    """{full name: short name} for {full name: launches}. Where instances of
+    one template share a short name, the most-launched keeps it and the
+    others get their template arguments appended (``scatter<7>``)."""
+    out, taken = {}, set()
+    for name in sorted(counts, key=lambda n: -counts[n]):
+        short = short_name(name)
+        if short in taken:
+            head = name.split("(")[0]
+            short += head[head.find("<"):] if "<" in head else f"#{len(taken)}"
+        taken.add(short)
+        out[name] = short
+    return out
+
+
 def _one(pattern: str, d: str) -> str:
     hits = sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
     if not hits:
@@ -61,9 +76,10 @@ def _one(pattern: str, d: str) -> str:
 
 def kernel_stats(d: str):
     rows = list(csv.DictReader(open(_one("*kernel_stats.csv", d))))
+    names = unique_short({r["Name"]: int(r["Calls"]) for r in rows})
     out = []
     for r in rows:
-        out.append(dict(name=r["Name"], short=short_name(r["Name"]), calls=int(r["Calls"]),
+        out.append(dict(name=r["Name"], short=names[r["Name"]], calls=int(r["Calls"]),
                         avg_us=float(r["AverageNs"]) / 1e3, min_us=float(r["MinNs"]) / 1e3,
                         max_us=float(r["MaxNs"]) / 1e3))
     return out
@@ -123,9 +139,10 @@ def write_traffic(fetch: str, write: str, copy_fetch: str, copy_write: str, copy
         lines += [f"- {k}: `{c}`"]
     lines += ["", "| kernel | dispatches | FETCH (MB) | WRITE (MB) | HBM bytes (MB, scaled) |",
               "|---|---|---|---|---|"]
-    for name in sorted(set(f_k) | set(w_k)):
-        short = short_name(name)
-        if short not in dict(SHORT).values():
+    names = unique_short({n: len(f_k.get(n, w_k.get(n, []))) for n in set(f_k) | set(w_k)})
+    for name in sorted(names, key=lambda n: names[n]):
+        short = names[name]
+        if short_name(name) not in dict(SHORT).values():
             continue
         fk = statistics.median(f_k.get(name, [0.0]))
         wk = statistics.median(w_k.get(name, [0.0]))
@@ -148,16 +165,20 @@ def write_counters(d: str, cmd: str, out: str, title: str):
     for r in csv.DictReader(open(path)):
         key = (r["Kernel_Name"], r.get("Dispatch_Id", r.get("Correlation_Id")), r["Counter_Name"])
         per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    launches = {}
+    for (name, disp, _) in per:
+        launches.setdefault(name, set()).add(disp)
+    names = unique_short({n: len(d) for n, d in launches.items()})
     table = {}
     for (name, _, counter), v in per.items():
-        table.setdefault(short_name(name), {}).setdefault(counter, []).append(v)
+        table.setdefault(names[name], {}).setdefault(counter, []).append(v)
     counters = sorted({c for k in table.values() for c in k})
     lines = [f"# {title}", "", "Command:", "", "```", cmd, "```", "",
              "Median per dispatch (summed over the device's counter instances).", "",
              "| kernel | " + " | ".join(counters) + " |",
              "|---|" + "---|" * len(counters)]
     for k in sorted(table):
-        if k not in dict(SHORT).values():
+        if k.split("<")[0] not in dict(SHORT).values():
             continue
         vals = [statistics.median(table[k][c]) if c in table[k] else float("nan") for c in counters]
         lines.append(f"| `{k}` | " + " | ".join(f"{v:.0f}" for v in vals) + " |")
