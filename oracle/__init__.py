@@ -59,6 +59,8 @@ class Oracle:
         lib.epl_oracle_bf16_from_double.restype = ctypes.c_uint16
         lib.epl_oracle_layout.argtypes = [_c_i64, _c_i32, _c_i32, _c_i32, _ptr, _ptr, _ptr, _ptr]
         lib.epl_oracle_layout.restype = ctypes.c_int
+        lib.epl_oracle_rdma_counts.argtypes = [_c_i64, _c_i32, _c_i32, _ptr, _ptr]
+        lib.epl_oracle_rdma_counts.restype = ctypes.c_int
         lib.epl_oracle_scan.argtypes = [_c_i32, _ptr, _c_i32, _ptr, _ptr]
         lib.epl_oracle_scan.restype = ctypes.c_int
         lib.epl_oracle_scatter.argtypes = [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
@@ -98,6 +100,18 @@ class Oracle:
         _check(self.lib.epl_oracle_layout(T, K, num_experts, num_ranks, _p(topk), _p(cnt),
                                           _p(per_rank), _p(in_rank)), "layout")
         return cnt, per_rank, in_rank
+
+    def rdma_counts(self, is_token_in_rank: np.ndarray, ranks_per_node: int):
+        """num_tokens_per_rdma_rank [R / G] i32 for G = ranks_per_node GPUs
+        per node, or None when all R ranks fit on one node (R <= G)."""
+        in_rank = _c(is_token_in_rank, np.uint8)
+        T, R = in_rank.shape
+        G = int(ranks_per_node)
+        if G <= 0 or G >= R:
+            return None
+        out = np.empty(R // G, np.int32)
+        _check(self.lib.epl_oracle_rdma_counts(T, R, G, _p(in_rank), _p(out)), "rdma_counts")
+        return out
 
     def scan(self, num_tokens_per_expert: np.ndarray, alignment: int = 0):
         """Returns (expert_start_loc [E] i32, total int); with alignment a > 1
@@ -224,6 +238,6 @@ def lib_path() -> str:
 def __getattr__(name):
     # module-level shorthands: oracle.layout(...), oracle.scan(...), ...
     if name in ("bf16_to_double", "bf16_from_double", "bf16_from_double_array", "layout",
-                "scan", "scatter", "expert_scale", "combine", "run_all"):
+                "rdma_counts", "scan", "scatter", "expert_scale", "combine", "run_all"):
         return getattr(default(), name)
     raise AttributeError(name)

@@ -143,6 +143,33 @@ int epl_oracle_layout(int64_t T, int32_t K, int32_t E, int32_t R,
     return ORACLE_OK;
 }
 
+/* [DEEPEP] Dispatch, get_dispatch_layout: with ranks spread over nodes of
+ * G GPUs each, the tokens bound for each RDMA rank, i.e. for each node
+ * (rank r sits on node r / G; a token reaches another node through the peer
+ * with the same GPU index there). A token counts once for a node if it goes
+ * to any rank of that node. The page gives no value for the single-node
+ * case; callers take it as "not produced". */
+int epl_oracle_rdma_counts(int64_t T, int32_t R, int32_t G,
+                           const uint8_t *is_token_in_rank,
+                           int32_t *num_tokens_per_rdma_rank)
+{
+    if (T < 0 || R < 1 || G < 1 || R % G != 0)
+        return ORACLE_EINVAL;
+    int32_t nodes = R / G;
+    for (int32_t n = 0; n < nodes; ++n) {
+        int32_t tokens = 0;
+        for (int64_t t = 0; t < T; ++t) {
+            int any = 0;
+            for (int32_t r = n * G; r < (n + 1) * G; ++r)
+                if (is_token_in_rank[t * R + r])
+                    any = 1;
+            tokens += any;
+        }
+        num_tokens_per_rdma_rank[n] = tokens;
+    }
+    return ORACLE_OK;
+}
+
 /* ---------------------------------------------------------------- scan -- */
 
 /* [ANATOMY] subsection 5 / [SGLANG] section 2.2: each expert's block starts

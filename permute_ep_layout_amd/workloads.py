@@ -57,6 +57,15 @@ class Workload:
     expert_fn: str = "identity"   # "identity" or "scale" (row * (1 + e/256), bf16)
     payload: str = "bf16"         # "bf16" or "fp8" (e4m3, one byte per element)
     scale_format: str = "f32"     # "f32" (fp32 per 128 columns) or "ue8m0" (packed exponents)
+    ranks_per_node: int = 0       # G for num_tokens_per_rdma_rank (0: not asked for)
+    # Receive side ("recv" routing): the batch one rank holds after the
+    # dispatch. Tokens are drawn with uniform top-K routing over
+    # recv_global_experts experts spread over recv_src_ranks ranks and kept
+    # when they pick at least one expert of rank recv_rank; ids are local
+    # (0 .. num_experts-1) with -1 for experts of other ranks.
+    recv_global_experts: int = 0
+    recv_src_ranks: int = 0
+    recv_rank: int = 0
 
     @property
     def scale_cols(self) -> int:
@@ -73,22 +82,31 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads. "dsv3" borrows only the public DeepSeek-V3 MoE dimensions
+# The five workloads, plus the FP8 and receive-side variants of "dsv3". "dsv3" borrows only the public DeepSeek-V3 MoE dimensions
 # (hidden 7168, 256 routed experts, top-8); no weights or data are involved.
 WORKLOADS = {
     "tiny": Workload("tiny", seed=1, num_tokens=64, hidden=128, num_experts=16,
-                     num_topk=2, num_ranks=8, scales=False, routing="uniform"),
+                     num_topk=2, num_ranks=8, scales=False, routing="uniform",
+                     ranks_per_node=2),
     "small": Workload("small", seed=2, num_tokens=2048, hidden=4096, num_experts=64,
                       num_topk=6, num_ranks=8, scales=False, routing="uniform",
                       drop_rate=0.05),
     "dsv3": Workload("dsv3", seed=3, num_tokens=4096, hidden=7168, num_experts=256,
-                     num_topk=8, num_ranks=32, scales=True, routing="uniform"),
+                     num_topk=8, num_ranks=32, scales=True, routing="uniform",
+                     ranks_per_node=8),
     "skew": Workload("skew", seed=4, num_tokens=16384, hidden=7168, num_experts=256,
                      num_topk=8, num_ranks=32, scales=True, routing="zipf",
-                     zipf_s=1.2, cold_experts=8),
+                     zipf_s=1.2, cold_experts=8, ranks_per_node=8),
     "large": Workload("large", seed=5, num_tokens=65536, hidden=7168, num_experts=256,
                       num_topk=8, num_ranks=64, scales=False, routing="uniform",
-                      expert_fn="scale"),
+                      expert_fn="scale", ranks_per_node=8),
+    # what one of the 32 ranks of the DeepSeek-V3-shaped setup receives:
+    # 32 x 4096 source tokens, each kept with probability
+    # 1 - C(248,8)/C(256,8) = 0.2271 (at least one of the rank's 8 experts),
+    # i.e. 29765 tokens and, on average, 32768 local slots
+    "dsv3_recv": Workload("dsv3_recv", seed=6, num_tokens=29765, hidden=7168, num_experts=8,
+                          num_topk=8, num_ranks=1, scales=True, routing="recv",
+                          recv_global_experts=256, recv_src_ranks=32, recv_rank=0),
     # the DeepSeek-V3-shaped batch as DeepEP dispatches it for an FP8 grouped
     # GEMM: e4m3 rows and power-of-two (UE8M0) scales packed 4 per int32
     "dsv3_fp8": Workload("dsv3_fp8", seed=3, num_tokens=4096, hidden=7168, num_experts=256,
@@ -164,8 +182,28 @@ def cold_experts(w: Workload) -> np.ndarray:
     return np.sort(perm[w.num_experts - w.cold_experts:])
 
 
+def _received_global(w: Workload) -> np.ndarray:
+    """Global top-K rows [T, K] of the tokens rank recv_rank receives: uniform
+    routing over recv_global_experts experts, keeping the rows that pick at
+    least one of the rank's experts, in draw order, until T are kept."""
+    El, lo = w.num_experts, w.recv_rank * w.num_experts
+    rng = _rng(w.seed, STREAM_TOPK)
+    kept, have = [], 0
+    while have < w.num_tokens:
+        g = _uniform_distinct(rng, 1 << 14, w.recv_global_experts, w.num_topk)
+        g = g[((g >= lo) & (g < lo + El)).any(axis=1)]
+        kept.append(g)
+        have += len(g)
+    return np.concatenate(kept)[:w.num_tokens]
+
+
 def make_topk(w: Workload) -> np.ndarray:
     """topk_idx [T, K] int64, -1 = no selection."""
+    if w.routing == "recv":
+        g = _received_global(w)
+        lo = w.recv_rank * w.num_experts
+        mine = (g >= lo) & (g < lo + w.num_experts)
+        return np.ascontiguousarray(np.where(mine, g - lo, -1))
     if w.routing == "uniform":
         topk = _uniform_distinct(_rng(w.seed, STREAM_TOPK), w.num_tokens,
                                  w.num_experts, w.num_topk)
@@ -183,6 +221,12 @@ def make_weights(w: Workload, topk: np.ndarray) -> np.ndarray:
     """topk_weights [T, K] fp32: softmax of N(0,1) logits over the token's
     valid slots, 0 on -1 slots, so the valid weights of a token sum to 1."""
     logits = _rng(w.seed, STREAM_LOGITS).standard_normal(topk.shape)
+    if w.routing == "recv":
+        # the sender's weights: softmax over all K slots of the global row
+        # (every slot is valid there); slots of other ranks arrive as 0
+        ex = np.exp(logits - logits.max(axis=1, keepdims=True))
+        wt = ex / ex.sum(axis=1, keepdims=True)
+        return np.ascontiguousarray(np.where(topk >= 0, wt, 0.0).astype(np.float32))
     valid = topk >= 0
     masked = np.where(valid, logits, -np.inf)
     mx = masked.max(axis=1, keepdims=True)

@@ -59,6 +59,9 @@ MUTANTS = {
     "expert_factor_255": ("1.0 + (double)m_indices[p] / 256.0", "1.0 + (double)m_indices[p] / 255.0"),
     "slots_in_reverse_k": ("for (int32_t k = 0; k < K; ++k) {\n            int64_t e = topk_idx[t * K + k];\n            if (e < -1",
                            "for (int32_t k = K - 1; k >= 0; --k) {\n            int64_t e = topk_idx[t * K + k];\n            if (e < -1"),
+    "rdma_nodes_strided": ("for (int32_t r = n * G; r < (n + 1) * G; ++r)",
+                           "for (int32_t r = n; r < R; r += nodes)"),
+    "rdma_counts_ranks_not_tokens": ("                    any = 1;", "                    ++tokens;"),
     "scale_row_of_wrong_token": ("x_scale + t * (int64_t)S", "x_scale + (T - 1 - t) * (int64_t)S"),
 }
 
@@ -224,7 +227,13 @@ def _battery(orc: Oracle):
         m = np.array([255, 128, 1, 1], np.int32)
         return orc.expert_scale(rows, m)[:, 0].tolist() == [0x4000, 0x3FC0, 0x3F82, 0x3F80]
 
-    for name, fn in [("golden_scan", golden_scan), ("golden_hand", golden_hand), ("brute", brute),
+    def golden_rdma():
+        g = load_golden("rdma_counts_example.txt")
+        topk = np.array(g["topk_idx"], np.int64)
+        _, _, in_rank = orc.layout(topk, g["num_experts"][0], g["num_ranks"][0])
+        return all(orc.rdma_counts(in_rank, G).tolist() == g[f"rdma_g{G}"] for G in (1, 2, 4))
+
+    for name, fn in [("golden_scan", golden_scan), ("golden_rdma", golden_rdma), ("golden_hand", golden_hand), ("brute", brute),
                      ("golden_alignment", golden_alignment), ("brute_aligned", brute_aligned),
                      ("scale_cols_layout", scale_cols_layout),
                      ("rows_aligned_padding", rows_aligned_padding), ("brute_rows", brute_rows),

@@ -94,6 +94,46 @@ def test_golden_route_token_3_7():
     assert in_rank[0].tolist() == g["is_token_in_rank"]
 
 
+def brute_rdma(topk, E, R, G):
+    """Tokens per node straight from topk_idx: node of a slot = its owner
+    rank // G; a token counts once per node it reaches."""
+    T, K = topk.shape
+    epr = E // R
+    return np.array([sum(1 for t in range(T)
+                         if any(topk[t, k] >= 0 and (topk[t, k] // epr) // G == n
+                                for k in range(K)))
+                     for n in range(R // G)])
+
+
+def test_golden_rdma_counts_example():
+    g = load_golden("rdma_counts_example.txt")
+    E, R = g["num_experts"][0], g["num_ranks"][0]
+    topk = np.array(g["topk_idx"], dtype=np.int64)
+    _, _, in_rank = oracle.layout(topk, E, R)
+    for G in (1, 2, 4):
+        assert oracle.rdma_counts(in_rank, G).tolist() == g[f"rdma_g{G}"], G
+    assert oracle.rdma_counts(in_rank, 8) is None          # one node
+    assert oracle.rdma_counts(in_rank, 0) is None          # not asked for
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_rdma_counts_against_brute_force(seed):
+    rng = np.random.default_rng(300 + seed)
+    R = int(rng.choice([2, 4, 6, 8, 12]))
+    E = R * int(rng.integers(1, 4))
+    T, K = int(rng.integers(0, 40)), int(rng.integers(1, 6))
+    topk = rng.integers(-1, E, size=(T, K)).astype(np.int64)
+    _, per_rank, in_rank = oracle.layout(topk, E, R)
+    for G in [g for g in range(1, R) if R % g == 0]:
+        got = oracle.rdma_counts(in_rank, G)
+        np.testing.assert_array_equal(got, brute_rdma(topk, E, R, G))
+        nodes = per_rank.reshape(R // G, G)
+        # a node gets at least as many tokens as its busiest rank and at
+        # most the sum over its ranks
+        assert (got >= nodes.max(axis=1)).all() and (got <= nodes.sum(axis=1)).all()
+    np.testing.assert_array_equal(oracle.rdma_counts(in_rank, 1), per_rank)
+
+
 def test_golden_scatter_hand_example():
     g = load_golden("scatter_hand_example.txt")
     E, R = g["num_experts"][0], g["num_ranks"][0]
@@ -457,3 +497,67 @@ def test_expert_scale_hand_checked_values():
     m = np.array([c[1] for c in cases], np.int32)
     got = oracle.expert_scale(rows, m)[:, 0]
     assert [hex(v) for v in got] == [hex(c[2]) for c in cases]
+
+
+# ------------------------------------------------- receive side (local ids) --
+
+def _to_local(topk, r, El):
+    """The batch rank r holds after the dispatch: tokens that pick one of its
+    experts [r*El, (r+1)*El), ids made local, -1 for other ranks' experts."""
+    mine = (topk >= r * El) & (topk < (r + 1) * El)
+    keep = np.nonzero(mine.any(axis=1))[0]
+    return keep, np.where(mine[keep], topk[keep] - r * El, -1)
+
+
+@pytest.mark.parametrize("seed,a", [(0, 0), (1, 0), (2, 4), (3, 3)])
+def test_local_mode_is_the_global_buffer_restricted(seed, a):
+    """With contiguous ownership, rank r's experts form one stretch of the
+    global expert-contiguous buffer. Run on the rank's received batch with
+    local ids, the path must produce exactly that stretch: the same rows in
+    the same order, m_indices shifted by r*El, output_index shifted by the
+    stretch's start."""
+    rng = np.random.default_rng(500 + seed)
+    T, K, R, El, H = 150, 4, 6, 4, 8
+    E = R * El
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    topk[rng.random(topk.shape) < 0.15] = -1
+    x = rng.integers(0, 1 << 15, size=(T, H), dtype=np.uint16)
+    xs = rng.uniform(0.01, 1, size=(T, 1)).astype(np.float32)
+    g = run_oracle(topk, E, R, x=x, x_scale=xs, alignment=a)
+    for r in range(R):
+        keep, lt = _to_local(topk, r, El)
+        loc = run_oracle(lt, El, 1, x=x[keep], x_scale=xs[keep], alignment=a)
+        lo = g["start"][r * El]
+        hi = g["start"][(r + 1) * El] if r + 1 < R else g["total"]
+        assert loc["total"] == hi - lo
+        np.testing.assert_array_equal(loc["cnt"], g["cnt"][r * El:(r + 1) * El])
+        m = g["m"][lo:hi]
+        np.testing.assert_array_equal(loc["m"], np.where(m >= 0, m - r * El, -1))
+        real = m >= 0
+        np.testing.assert_array_equal(loc["out"][real], g["out"][lo:hi][real])
+        np.testing.assert_array_equal(loc["out_scale"][real], g["out_scale"][lo:hi][real])
+        want_oi = np.where(lt >= 0, g["oi"][keep] - lo, -1)
+        np.testing.assert_array_equal(loc["oi"], want_oi)
+        assert loc["per_rank"].tolist() == [len(keep)]
+
+
+def test_local_partial_combines_sum_to_the_global_combine():
+    """Each rank combines only its own slots; adding the partial sums of all
+    ranks per source token gives the global combine (fp64, up to rounding)."""
+    rng = np.random.default_rng(77)
+    T, K, R, El, H = 120, 5, 4, 6, 16
+    E = R * El
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    topk[rng.random(topk.shape) < 0.1] = -1
+    x = rng.integers(0, 1 << 15, size=(T, H), dtype=np.uint16) & np.uint16(0xBFFF)  # finite
+    w = rng.uniform(0.05, 1, size=(T, K)).astype(np.float32)
+    g = run_oracle(topk, E, R, x=x)
+    y = oracle.combine(g["out"], g["oi"], w)
+    acc = np.zeros((T, H))
+    for r in range(R):
+        keep, lt = _to_local(topk, r, El)
+        loc = run_oracle(lt, El, 1, x=x[keep])
+        acc[keep] += oracle.combine(loc["out"], loc["oi"], w[keep])
+    xv = np.array([[oracle.bf16_to_double(int(v)) for v in row] for row in x])
+    bound = np.abs(w.astype(np.float64)).sum(axis=1, keepdims=True) * np.abs(xv)
+    assert np.all(np.abs(acc - y) <= 1e-12 * bound + 1e-300)

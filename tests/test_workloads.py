@@ -98,3 +98,27 @@ def test_scales():
     assert s.shape == (300, 56) and s.dtype == np.float32
     assert s.min() >= 0.01 and s.max() <= 1.0
     assert workloads.make_scales(workloads.get("small")) is None
+
+
+def test_receive_side_batch():
+    """dsv3_recv: every kept token picks at least one of the rank's experts;
+    ids are local or -1; local slots average K*El/Eg / P(hit) per token."""
+    w = workloads.get("dsv3_recv")
+    topk = workloads.make_topk(w)
+    assert topk.shape == (29765, 8) and topk.dtype == np.int64
+    valid = topk >= 0
+    assert valid.any(axis=1).all()
+    assert (topk[valid] < 8).all() and (topk[~valid] == -1).all()
+    srt = np.sort(np.where(valid, topk, -np.arange(1, 9)), axis=1)
+    assert (np.diff(srt, axis=1) != 0).all()
+    p_hit = 1.0 - np.prod([(248 - i) / (256 - i) for i in range(8)])
+    assert abs(valid.sum(axis=1).mean() - 8 * 8 / 256 / p_hit) < 0.01
+    cnt = np.bincount(topk[valid], minlength=8)
+    assert cnt.min() > 0.95 * cnt.mean() and cnt.max() < 1.05 * cnt.mean()
+    # the sender's weights: positive on local slots, 0 elsewhere, sum <= 1
+    wt = workloads.make_weights(w, topk)
+    assert (wt[~valid] == 0).all() and (wt[valid] > 0).all()
+    assert wt.astype(np.float64).sum(axis=1).max() <= 1.0 + 1e-6
+    # the same draws as the send side: a global row with all K experts valid
+    g = workloads._received_global(w)
+    np.testing.assert_array_equal(np.where(valid, topk, -1), np.where(g < 8, g, -1))
