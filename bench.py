@@ -42,8 +42,10 @@ def algorithmic_bytes(w, N, T_any, out_dtype_bytes=4, pad_rows=0):
     T, K, E, R, H = w.num_tokens, w.num_topk, w.num_experts, w.num_ranks, w.hidden
     B = H if w.payload == "fp8" else 2 * H
     S = w.scale_words
+    G = w.ranks_per_node
+    nodes = R // G if 0 < G < R else 0
     return {
-        "layout": 8 * T * K + 4 * E + 4 * R + T * R,
+        "layout": 8 * T * K + 4 * E + 4 * R + 4 * nodes + T * R,
         "scan": 4 * E + 4 * E + 4,
         "scatter": (B * T_any + 4 * S * T_any + 8 * T * K + 4 * E) +
                    (B * N + 4 * S * N + 4 * N + 4 * T * K + 4 * pad_rows),
@@ -178,12 +180,13 @@ def main():
         x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
         xs = torch.from_numpy(inp["x_scale"]).to(dev) if S else None
     wt = torch.from_numpy(inp["topk_weights"]).to(dev)
-    p = epl.Problem.make(T, K, E, R, H, S, args.alignment)
+    p = epl.Problem.make(T, K, E, R, H, S, args.alignment, w.ranks_per_node)
     cap = epl.epl_capacity_rows(p)
     i32 = torch.int32
     ws = torch.empty(epl.epl_workspace_bytes(p), dtype=torch.uint8, device=dev)
     cnt = torch.empty(E, dtype=i32, device=dev)
     per_rank = torch.empty(R, dtype=i32, device=dev)
+    per_node = torch.empty(p.num_nodes, dtype=i32, device=dev) if p.num_nodes else None
     in_rank = torch.empty((T, R), dtype=torch.uint8, device=dev)
     start = torch.empty(E, dtype=i32, device=dev)
     total_host = torch.zeros(1, dtype=i32).pin_memory()
@@ -206,9 +209,9 @@ def main():
         # bf16 rows of the same tokens scattered once to the same rows.
         xb = torch.from_numpy(workloads.make_x(w).view(np.int16)).to(dev).view(torch.bfloat16)
         eo = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
-        pb = epl.Problem.make(T, K, E, R, H, 0, args.alignment)
-        epl.epl_dispatch(pb, topk, xb, None, cap, cnt, per_rank, in_rank, start, total_host, eo,
-                         None, m_idx, oi, ws)
+        pb = epl.Problem.make(T, K, E, R, H, 0, args.alignment, w.ranks_per_node)
+        epl.epl_dispatch(pb, topk, xb, None, cap, cnt, per_rank, per_node, in_rank, start,
+                         total_host, eo, None, m_idx, oi, ws)
         del xb
     else:
         eo = torch.empty_like(out) if scaled else out
@@ -221,7 +224,7 @@ def main():
 
     # One checked pass through the argument-validating wrappers, then the
     # timed loop calls the C entry points directly with the same arguments.
-    epl.epl_layout(p, topk, cnt, per_rank, in_rank, ws)
+    epl.epl_layout(p, topk, cnt, per_rank, per_node, in_rank, ws)
     epl.epl_scan(p, cnt, start, total_host, ws)
     if fp8:
         epl.epl_scatter_fp8(p, x, xs, fmt, topk, start, ws, cap, out, out_scale, m_idx, oi)
@@ -231,21 +234,22 @@ def main():
         epl.epl_expert_scale(p, out, m_idx, cap, eo, ws)
     epl.epl_combine(p, eo, cap, oi, wt, out_code, y, ws)
     if fp8:
-        epl.epl_dispatch_fp8(p, topk, x, xs, fmt, cap, cnt, per_rank, in_rank, start, total_host,
-                             out, out_scale, m_idx, oi, ws)
+        epl.epl_dispatch_fp8(p, topk, x, xs, fmt, cap, cnt, per_rank, per_node, in_rank, start,
+                             total_host, out, out_scale, m_idx, oi, ws)
         scatter_call = epl.prepare("epl_scatter_fp8", p, x, xs, fmt, topk, start, ws, cap, out,
                                    out_scale, m_idx, oi)
         dispatch_call = epl.prepare("epl_dispatch_fp8", p, topk, x, xs, fmt, cap, cnt, per_rank,
-                                    in_rank, start, total_host, out, out_scale, m_idx, oi, ws)
+                                    per_node, in_rank, start, total_host, out, out_scale, m_idx,
+                                    oi, ws)
     else:
-        epl.epl_dispatch(p, topk, x, xs, cap, cnt, per_rank, in_rank, start, total_host, out,
-                         out_scale, m_idx, oi, ws)
+        epl.epl_dispatch(p, topk, x, xs, cap, cnt, per_rank, per_node, in_rank, start,
+                         total_host, out, out_scale, m_idx, oi, ws)
         scatter_call = epl.prepare("epl_scatter", p, x, xs, topk, start, ws, cap, out, out_scale,
                                    m_idx, oi)
-        dispatch_call = epl.prepare("epl_dispatch", p, topk, x, xs, cap, cnt, per_rank, in_rank,
-                                    start, total_host, out, out_scale, m_idx, oi, ws)
+        dispatch_call = epl.prepare("epl_dispatch", p, topk, x, xs, cap, cnt, per_rank, per_node,
+                                    in_rank, start, total_host, out, out_scale, m_idx, oi, ws)
     calls = [
-        epl.prepare("epl_layout", p, topk, cnt, per_rank, in_rank, ws),
+        epl.prepare("epl_layout", p, topk, cnt, per_rank, per_node, in_rank, ws),
         epl.prepare("epl_scan", p, cnt, start, total_host, ws),
         scatter_call,
     ]
@@ -419,7 +423,8 @@ def main():
         "config": {
             "workload": w.name,
             "num_tokens": T, "hidden": H, "num_experts": E, "num_topk": K,
-            "num_virtual_ranks": R, "scale_cols": S, "routing": w.routing,
+            "num_virtual_ranks": R, "ranks_per_node": w.ranks_per_node, "scale_cols": S,
+            "routing": w.routing,
             "payload": w.payload, "scale_format": w.scale_format if S else None,
             "drop_rate": w.drop_rate, "expert_fn": w.expert_fn, "routed_rows": N,
             "expert_alignment": args.alignment, "buffer_rows": n_rows,

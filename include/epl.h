@@ -42,6 +42,17 @@
  *   experts [r*E/R, (r+1)*E/R); E must be a multiple of R.
  * - Row order inside an expert's block: by token, then by top-k slot. The
  *   result is therefore deterministic (bit-identical from run to run).
+ * - Send side and receive side. On the send side topk_idx holds global
+ *   expert ids and the layout's per-rank outputs say where tokens go. On
+ *   the receive side (the batch a rank holds after the dispatch) topk_idx
+ *   holds the rank's local expert ids, 0 .. E/R - 1, with -1 for the slots
+ *   whose experts live on other ranks; the same calls then run with
+ *   num_experts = the local expert count and num_ranks = 1, and scatter
+ *   and combine touch only the local experts' rows, with no id remapping
+ *   (the direct local-id path of "参考sglang代码，重构vllm021中EP高吞吐代码，
+ *   消除空泡问题", section 7; DeepEP's received top-k ids, section Dispatch
+ *   of "[MoE] Deepseek的All-to-all通信: DeepEP代码解读"). The combine then
+ *   yields each received token's partial sum over the rank's experts.
  */
 #ifndef EPL_H
 #define EPL_H
@@ -90,6 +101,12 @@ typedef struct epl_problem {
                              (the grouped GEMM's block_m; DeepEP's
                              expert_alignment). Padding rows get m_indices = -1
                              and are otherwise not written.               */
+    int32_t ranks_per_node; /* G: GPUs per node, for num_tokens_per_rdma_rank.
+                             0 or G >= R: one node, that output is not
+                             produced; 1 <= G < R: R % G == 0, rank r sits on
+                             node r / G and the layout counts the tokens
+                             bound for each of the R / G nodes.            */
+    int32_t reserved;     /* must be 0                                        */
 } epl_problem;
 /* Also required: T * K + E * (a - 1) <= INT32_MAX (row indices are int32). */
 
@@ -113,14 +130,20 @@ int64_t epl_capacity_rows(const epl_problem *p);
 /* Step 1 -- layout. Reads topk_idx [T, K] int64 (-1 = no selection).
  * Writes num_tokens_per_expert [E] int32 (routed slots per expert),
  * num_tokens_per_rank [R] int32 (tokens sent to each rank, a token counted
- * once per rank however many of its experts live there) and
- * is_token_in_rank [T, R] uint8 (1 if any valid slot of the token goes to
- * the rank, else 0). Also fills the workspace for epl_scatter and resets
- * the status word (bit for out-of-range ids set if any was seen; such an
- * id counts as -1). */
+ * once per rank however many of its experts live there),
+ * num_tokens_per_rdma_rank [R / G] int32 when the problem spans several
+ * nodes (1 <= ranks_per_node = G < R): tokens sent to each node's RDMA
+ * rank, a token counted once per node however many of the node's ranks it
+ * goes to ("[MoE] Deepseek的All-to-all通信: DeepEP代码解读", section Dispatch,
+ * get_dispatch_layout's second output; NULL is accepted, and the pointer
+ * ignored, when the problem fits one node), and is_token_in_rank [T, R]
+ * uint8 (1 if any valid slot of the token goes to the rank, else 0). Also
+ * fills the workspace for epl_scatter and resets the status word (bit for
+ * out-of-range ids set if any was seen; such an id counts as -1). */
 int epl_layout(const epl_problem *p, const int64_t *topk_idx,
                int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,
-               uint8_t *is_token_in_rank, void *workspace, void *stream);
+               int32_t *num_tokens_per_rdma_rank, uint8_t *is_token_in_rank,
+               void *workspace, void *stream);
 
 /* Step 2 -- scan. expert_start_loc[e] = sum of block sizes of experts e' < e
  * (exclusive, expert_start_loc[0] = 0), where an expert's block size is its
@@ -163,6 +186,7 @@ int epl_scatter(const epl_problem *p, const uint16_t *x, const float *x_scale,
 int epl_dispatch(const epl_problem *p, const int64_t *topk_idx,
                  const uint16_t *x, const float *x_scale, int64_t capacity_rows,
                  int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,
+                 int32_t *num_tokens_per_rdma_rank,
                  uint8_t *is_token_in_rank, int32_t *expert_start_loc,
                  int32_t *total_host, uint16_t *out, float *out_scale,
                  int32_t *m_indices, int32_t *output_index,
@@ -184,6 +208,7 @@ int epl_scatter_fp8(const epl_problem *p, const uint8_t *x, const void *x_scale,
 int epl_dispatch_fp8(const epl_problem *p, const int64_t *topk_idx, const uint8_t *x,
                      const void *x_scale, int scale_format, int64_t capacity_rows,
                      int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,
+                     int32_t *num_tokens_per_rdma_rank,
                      uint8_t *is_token_in_rank, int32_t *expert_start_loc,
                      int32_t *total_host, uint8_t *out, void *out_scale,
                      int32_t *m_indices, int32_t *output_index, void *workspace,

@@ -57,7 +57,7 @@ class EplError(RuntimeError):
 
 
 class Problem(ctypes.Structure):
-    """epl_problem: T, K, E, R, H, S (see include/epl.h)."""
+    """epl_problem: T, K, E, R, H, S, a, G (see include/epl.h)."""
 
     _fields_ = [
         ("num_tokens", ctypes.c_int64),
@@ -67,18 +67,26 @@ class Problem(ctypes.Structure):
         ("hidden", ctypes.c_int32),
         ("scale_cols", ctypes.c_int32),
         ("expert_alignment", ctypes.c_int32),
+        ("ranks_per_node", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
     @classmethod
     def make(cls, num_tokens, num_topk, num_experts, num_ranks, hidden, scale_cols=0,
-             expert_alignment=0):
+             expert_alignment=0, ranks_per_node=0):
         return cls(int(num_tokens), int(num_topk), int(num_experts), int(num_ranks), int(hidden),
-                   int(scale_cols), int(expert_alignment))
+                   int(scale_cols), int(expert_alignment), int(ranks_per_node), 0)
+
+    @property
+    def num_nodes(self) -> int:
+        """Entries of num_tokens_per_rdma_rank (0 when it is not produced)."""
+        G, R = self.ranks_per_node, self.num_ranks
+        return R // G if 0 < G < R else 0
 
     def __repr__(self):
         return (f"Problem(T={self.num_tokens}, K={self.num_topk}, E={self.num_experts}, "
                 f"R={self.num_ranks}, H={self.hidden}, S={self.scale_cols}, "
-                f"a={self.expert_alignment})")
+                f"a={self.expert_alignment}, G={self.ranks_per_node})")
 
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -123,18 +131,19 @@ def load() -> ctypes.CDLL:
     lib.epl_workspace_bytes.restype = ctypes.c_size_t
     lib.epl_capacity_rows.argtypes = [_PP]
     lib.epl_capacity_rows.restype = i64
-    lib.epl_layout.argtypes = [_PP, _P, _P, _P, _P, _P, _P]
+    lib.epl_layout.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P]
     lib.epl_layout.restype = i32
     lib.epl_scan.argtypes = [_PP, _P, _P, _P, _P, _P]
     lib.epl_scan.restype = i32
     lib.epl_scatter.argtypes = [_PP, _P, _P, _P, _P, _P, i64, _P, _P, _P, _P, _P]
     lib.epl_scatter.restype = i32
-    lib.epl_dispatch.argtypes = [_PP, _P, _P, _P, i64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.epl_dispatch.argtypes = [_PP, _P, _P, _P, i64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                 _P]
     lib.epl_dispatch.restype = i32
     lib.epl_scatter_fp8.argtypes = [_PP, _P, _P, i32, _P, _P, _P, i64, _P, _P, _P, _P, _P]
     lib.epl_scatter_fp8.restype = i32
     lib.epl_dispatch_fp8.argtypes = [_PP, _P, _P, _P, i32, i64, _P, _P, _P, _P, _P, _P, _P, _P,
-                                     _P, _P, _P]
+                                     _P, _P, _P, _P]
     lib.epl_dispatch_fp8.restype = i32
     lib.epl_combine.argtypes = [_PP, _P, i64, _P, _P, i32, _P, _P, _P]
     lib.epl_combine.restype = i32
@@ -223,19 +232,28 @@ def epl_capacity_rows(p: Problem) -> int:
     return int(load().epl_capacity_rows(_prob(p)))
 
 
+def _need_per_node(p: Problem, t, dev):
+    """num_tokens_per_rdma_rank: [R / G] int32 when the problem spans several
+    nodes; otherwise None (ignored by the library)."""
+    if p.num_nodes:
+        _need(t, "num_tokens_per_rdma_rank", _torch().int32, (p.num_nodes,), dev)
+
+
 def epl_layout(p: Problem, topk_idx, num_tokens_per_expert, num_tokens_per_rank,
-               is_token_in_rank, workspace, stream=None):
+               num_tokens_per_rdma_rank, is_token_in_rank, workspace, stream=None):
     torch = _torch()
     T, K, E, R = p.num_tokens, p.num_topk, p.num_experts, p.num_ranks
     _need(topk_idx, "topk_idx", torch.int64, (T, K))
     dev = topk_idx.device
     _need(num_tokens_per_expert, "num_tokens_per_expert", torch.int32, (E,), dev)
     _need(num_tokens_per_rank, "num_tokens_per_rank", torch.int32, (R,), dev)
+    _need_per_node(p, num_tokens_per_rdma_rank, dev)
     _need(is_token_in_rank, "is_token_in_rank", torch.uint8, (T, R), dev)
     _need(workspace, "workspace", torch.uint8, None, dev)
     _check(load().epl_layout(_prob(p), _ptr(topk_idx), _ptr(num_tokens_per_expert),
-                             _ptr(num_tokens_per_rank), _ptr(is_token_in_rank), _ptr(workspace),
-                             _stream(stream, dev)), "epl_layout")
+                             _ptr(num_tokens_per_rank), _ptr(num_tokens_per_rdma_rank),
+                             _ptr(is_token_in_rank), _ptr(workspace), _stream(stream, dev)),
+           "epl_layout")
 
 
 def epl_scan(p: Problem, num_tokens_per_expert, expert_start_loc, total_host, workspace,
@@ -286,14 +304,16 @@ def epl_scatter(p: Problem, x, x_scale, topk_idx, expert_start_loc, workspace, c
 
 
 def epl_dispatch(p: Problem, topk_idx, x, x_scale, capacity_rows, num_tokens_per_expert,
-                 num_tokens_per_rank, is_token_in_rank, expert_start_loc, total_host, out,
-                 out_scale, m_indices, output_index, workspace, stream=None):
+                 num_tokens_per_rank, num_tokens_per_rdma_rank, is_token_in_rank,
+                 expert_start_loc, total_host, out, out_scale, m_indices, output_index, workspace,
+                 stream=None):
     torch = _torch()
     dev = _check_scatter_args(p, x, x_scale, topk_idx, capacity_rows, out, out_scale, m_indices,
                               output_index)
     E, R, T = p.num_experts, p.num_ranks, p.num_tokens
     _need(num_tokens_per_expert, "num_tokens_per_expert", torch.int32, (E,), dev)
     _need(num_tokens_per_rank, "num_tokens_per_rank", torch.int32, (R,), dev)
+    _need_per_node(p, num_tokens_per_rdma_rank, dev)
     _need(is_token_in_rank, "is_token_in_rank", torch.uint8, (T, R), dev)
     _need(expert_start_loc, "expert_start_loc", torch.int32, (E,), dev)
     _need(workspace, "workspace", torch.uint8, None, dev)
@@ -302,7 +322,8 @@ def epl_dispatch(p: Problem, topk_idx, x, x_scale, capacity_rows, num_tokens_per
         raise ValueError("total_host must be a pinned CPU int32 tensor")
     _check(load().epl_dispatch(_prob(p), _ptr(topk_idx), _ptr(x), _ptr(x_scale),
                                int(capacity_rows), _ptr(num_tokens_per_expert),
-                               _ptr(num_tokens_per_rank), _ptr(is_token_in_rank),
+                               _ptr(num_tokens_per_rank), _ptr(num_tokens_per_rdma_rank),
+                               _ptr(is_token_in_rank),
                                _ptr(expert_start_loc), _ptr(total_host), _ptr(out),
                                _ptr(out_scale), _ptr(m_indices), _ptr(output_index),
                                _ptr(workspace), _stream(stream, dev)), "epl_dispatch")
@@ -348,15 +369,16 @@ def epl_scatter_fp8(p: Problem, x, x_scale, scale_format, topk_idx, expert_start
 
 
 def epl_dispatch_fp8(p: Problem, topk_idx, x, x_scale, scale_format, capacity_rows,
-                     num_tokens_per_expert, num_tokens_per_rank, is_token_in_rank,
-                     expert_start_loc, total_host, out, out_scale, m_indices, output_index,
-                     workspace, stream=None):
+                     num_tokens_per_expert, num_tokens_per_rank, num_tokens_per_rdma_rank,
+                     is_token_in_rank, expert_start_loc, total_host, out, out_scale, m_indices,
+                     output_index, workspace, stream=None):
     torch = _torch()
     dev = _check_fp8_args(p, x, x_scale, scale_format, topk_idx, capacity_rows, out, out_scale,
                           m_indices, output_index)
     E, R, T = p.num_experts, p.num_ranks, p.num_tokens
     _need(num_tokens_per_expert, "num_tokens_per_expert", torch.int32, (E,), dev)
     _need(num_tokens_per_rank, "num_tokens_per_rank", torch.int32, (R,), dev)
+    _need_per_node(p, num_tokens_per_rdma_rank, dev)
     _need(is_token_in_rank, "is_token_in_rank", torch.uint8, (T, R), dev)
     _need(expert_start_loc, "expert_start_loc", torch.int32, (E,), dev)
     _need(workspace, "workspace", torch.uint8, None, dev)
@@ -366,7 +388,8 @@ def epl_dispatch_fp8(p: Problem, topk_idx, x, x_scale, scale_format, capacity_ro
     _check(load().epl_dispatch_fp8(_prob(p), _ptr(topk_idx), _ptr(x), _ptr(x_scale),
                                    int(scale_format), int(capacity_rows),
                                    _ptr(num_tokens_per_expert), _ptr(num_tokens_per_rank),
-                                   _ptr(is_token_in_rank), _ptr(expert_start_loc),
+                                   _ptr(num_tokens_per_rdma_rank), _ptr(is_token_in_rank),
+                                   _ptr(expert_start_loc),
                                    _ptr(total_host), _ptr(out), _ptr(out_scale), _ptr(m_indices),
                                    _ptr(output_index), _ptr(workspace), _stream(stream, dev)),
            "epl_dispatch_fp8")
@@ -449,6 +472,7 @@ class DispatchResult(NamedTuple):
     expert_start_loc: "torch.Tensor"     # [E] i32
     num_tokens_per_expert: "torch.Tensor"
     num_tokens_per_rank: "torch.Tensor"
+    num_tokens_per_rdma_rank: Optional["torch.Tensor"]   # [R / G] i32, None on one node
     is_token_in_rank: "torch.Tensor"     # [T, R] u8 (0/1)
     total_host: "torch.Tensor"           # pinned [1] i32, valid after the stream syncs
     workspace: "torch.Tensor"
@@ -470,25 +494,29 @@ def workspace_for(p: Problem, device):
 
 def dispatch(x, topk_idx, num_experts: int, num_ranks: int, x_scale=None,
              capacity: Optional[int] = None, mode: str = "capacity", workspace=None,
-             stream=None, expert_alignment: int = 0) -> DispatchResult:
+             stream=None, expert_alignment: int = 0, ranks_per_node: int = 0) -> DispatchResult:
     """Layout + scan + scatter.
 
     mode="capacity" (default): one epl_dispatch call; the output buffers have
     `capacity` rows (default epl_capacity_rows, which always suffices) and no
     host wait happens. mode="exact": epl_layout + epl_scan, then the host waits for the
     total N, allocates exactly N rows and calls epl_scatter.
+
+    Receive side: pass the rank's local expert ids (-1 for other ranks'
+    experts) with num_experts = the local expert count and num_ranks = 1.
     """
     torch = _torch()
     T, H = x.shape
     K = topk_idx.shape[1]
     S = 0 if x_scale is None else x_scale.shape[1]
-    p = Problem.make(T, K, num_experts, num_ranks, H, S, expert_alignment)
+    p = Problem.make(T, K, num_experts, num_ranks, H, S, expert_alignment, ranks_per_node)
     _check(epl_validate(p), "epl_validate")
     dev = x.device
     ws = workspace if workspace is not None else workspace_for(p, dev)
     i32 = torch.int32
     cnt = torch.empty(num_experts, dtype=i32, device=dev)
     per_rank = torch.empty(num_ranks, dtype=i32, device=dev)
+    per_node = torch.empty(p.num_nodes, dtype=i32, device=dev) if p.num_nodes else None
     in_rank = torch.empty((T, num_ranks), dtype=torch.uint8, device=dev)
     start = torch.empty(num_experts, dtype=i32, device=dev)
     oi = torch.empty((T, K), dtype=i32, device=dev)
@@ -498,10 +526,10 @@ def dispatch(x, topk_idx, num_experts: int, num_ranks: int, x_scale=None,
         out = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
         out_scale = torch.empty((cap, S), dtype=torch.float32, device=dev) if S else None
         m_idx = torch.empty(cap, dtype=i32, device=dev)
-        epl_dispatch(p, topk_idx, x, x_scale, cap, cnt, per_rank, in_rank, start, total_host, out,
-                     out_scale, m_idx, oi, ws, stream)
+        epl_dispatch(p, topk_idx, x, x_scale, cap, cnt, per_rank, per_node, in_rank, start,
+                     total_host, out, out_scale, m_idx, oi, ws, stream)
     elif mode == "exact":
-        epl_layout(p, topk_idx, cnt, per_rank, in_rank, ws, stream)
+        epl_layout(p, topk_idx, cnt, per_rank, per_node, in_rank, ws, stream)
         epl_scan(p, cnt, start, total_host, ws, stream)
         torch.cuda.current_stream(dev).synchronize() if stream is None else stream.synchronize()
         cap = int(total_host[0])
@@ -511,8 +539,8 @@ def dispatch(x, topk_idx, num_experts: int, num_ranks: int, x_scale=None,
         epl_scatter(p, x, x_scale, topk_idx, start, ws, cap, out, out_scale, m_idx, oi, stream)
     else:
         raise ValueError(f"unknown mode {mode!r}")
-    return DispatchResult(out, out_scale, m_idx, oi, start, cnt, per_rank, in_rank, total_host,
-                          ws, p)
+    return DispatchResult(out, out_scale, m_idx, oi, start, cnt, per_rank, per_node, in_rank,
+                          total_host, ws, p)
 
 
 def combine(expert_out, output_index, topk_weights, out_dtype=None, workspace=None,

@@ -24,6 +24,14 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 int alignment_of(const epl_problem &p) { return p.expert_alignment > 1 ? p.expert_alignment : 1; }
 
+// Nodes whose token counts the layout produces: R / G when the ranks span
+// several nodes of G, else 0 (one node: not produced).
+int nodes_of(const epl_problem &p)
+{
+    const int G = p.ranks_per_node;
+    return (G > 0 && G < p.num_ranks) ? p.num_ranks / G : 0;
+}
+
 // Rows that always suffice: T*K, or round_up(T*K + E*(a-1), a) with padding.
 int64_t capacity_bound(const epl_problem &p)
 {
@@ -48,6 +56,11 @@ bool problem_ok(const epl_problem *p)
         return false;
     if (p->expert_alignment < 0 || p->expert_alignment > epl::kMaxAlignment)
         return false;
+    if (p->ranks_per_node < 0 || p->reserved != 0)
+        return false;
+    if (p->ranks_per_node > 0 && p->ranks_per_node < p->num_ranks &&
+        p->num_ranks % p->ranks_per_node != 0)
+        return false;
     if (capacity_bound(*p) > (int64_t)INT32_MAX)
         return false;
     return true;
@@ -71,7 +84,8 @@ int layout_block_tokens(const epl_problem &p)
 {
     int64_t cap = std::min<int64_t>(epl::kLayoutThreads, epl::kMaxSlotsPerBlock / p.num_topk);
     // the LDS bound: keys and ranks take 8 bytes per slot
-    const size_t fixed = epl::layout_lds_bytes(0, p.num_topk, p.num_experts, p.num_ranks);
+    const size_t fixed =
+        epl::layout_lds_bytes(0, p.num_topk, p.num_experts, p.num_ranks + nodes_of(p));
     cap = std::min<int64_t>(cap, (int64_t)((epl::kLayoutLdsBytes - fixed) / (8 * (size_t)p.num_topk)));
     int64_t want = (p.num_tokens + 63) / 64;
     want = std::max<int64_t>(16, want);
@@ -95,7 +109,7 @@ WsLayout ws_layout(const epl_problem &p)
     w.block_count = off;
     off += round_up((size_t)w.num_blocks * (size_t)p.num_experts * 4, kWsAlign);
     w.block_rank = off;
-    off += round_up((size_t)w.num_blocks * (size_t)p.num_ranks * 4, kWsAlign);
+    off += round_up((size_t)w.num_blocks * (size_t)(p.num_ranks + nodes_of(p)) * 4, kWsAlign);
     w.block_err = off;
     off += round_up((size_t)w.num_blocks * 4, kWsAlign);
     w.slot_rank = off;
@@ -126,10 +140,12 @@ int enqueue_layout(const epl_problem &p, const WsLayout &w, const int64_t *topk,
     if (w.num_blocks == 0)
         return EPL_OK;
     const bool vec16 = (p.num_ranks % 16 == 0) && aligned(in_rank, 16);
+    const int Rn = nodes_of(p);
     hipLaunchKernelGGL(epl::ep_layout_kernel, dim3((unsigned)w.num_blocks), dim3(epl::kLayoutThreads),
-                       epl::layout_lds_bytes(w.block_tokens, p.num_topk, p.num_experts, p.num_ranks),
-                       s, topk, p.num_tokens, p.num_topk,
-                       p.num_experts, p.num_ranks, p.num_experts / p.num_ranks, w.block_tokens,
+                       epl::layout_lds_bytes(w.block_tokens, p.num_topk, p.num_experts,
+                                             p.num_ranks + Rn),
+                       s, topk, p.num_tokens, p.num_topk, p.num_experts, p.num_ranks,
+                       p.num_experts / p.num_ranks, p.ranks_per_node, Rn, w.block_tokens,
                        in_rank, vec16, at<int32_t>(ws, w.block_count), at<int32_t>(ws, w.block_rank),
                        at<uint32_t>(ws, w.block_err), at<int32_t>(ws, w.slot_rank));
     return launch_status();
@@ -151,13 +167,13 @@ int32_t *mapped_host_word(int32_t *host)
 }
 
 int enqueue_scan(const epl_problem &p, const WsLayout &w, int mode, int32_t *cnt, int32_t *per_rank,
-                 int32_t *start, int32_t *total_host, void *ws, hipStream_t s)
+                 int32_t *per_node, int32_t *start, int32_t *total_host, void *ws, hipStream_t s)
 {
     int32_t *mapped = (mode & epl::kScanPrefix) ? mapped_host_word(total_host) : nullptr;
     hipLaunchKernelGGL(epl::ep_scan_kernel, dim3(1), dim3(epl::kScanThreads), 0, s, mode,
-                       w.num_blocks, p.num_experts, p.num_ranks, alignment_of(p),
+                       w.num_blocks, p.num_experts, p.num_ranks, nodes_of(p), alignment_of(p),
                        at<int32_t>(ws, w.block_count), at<int32_t>(ws, w.block_rank),
-                       at<uint32_t>(ws, w.block_err), cnt, per_rank, start,
+                       at<uint32_t>(ws, w.block_err), cnt, per_rank, per_node, start,
                        at<int32_t>(ws, w.counts), at<WsHeader>(ws, 0), mapped);
     int rc = launch_status();
     if (rc != EPL_OK)
@@ -278,11 +294,18 @@ bool rows_args_ok(const epl_problem &p, const RowArgs &ra, const int64_t *topk, 
     return true;
 }
 
+// The per-node output is required (and 4-byte aligned) exactly when the
+// problem spans several nodes.
+bool per_node_ok(const epl_problem &p, const int32_t *per_node)
+{
+    return nodes_of(p) == 0 || (per_node && aligned(per_node, 4));
+}
+
 }  // namespace
 
 extern "C" {
 
-int epl_version(void) { return 0x000200; }
+int epl_version(void) { return 0x000300; }
 
 int epl_validate(const epl_problem *p) { return problem_ok(p) ? EPL_OK : EPL_EINVAL; }
 
@@ -314,13 +337,15 @@ const char *epl_strerror(int code)
 }
 
 int epl_layout(const epl_problem *p, const int64_t *topk_idx, int32_t *num_tokens_per_expert,
-               int32_t *num_tokens_per_rank, uint8_t *is_token_in_rank, void *workspace,
-               void *stream)
+               int32_t *num_tokens_per_rank, int32_t *num_tokens_per_rdma_rank,
+               uint8_t *is_token_in_rank, void *workspace, void *stream)
 {
     if (!problem_ok(p))
         return EPL_EINVAL;
     if (!workspace || !aligned(workspace, kWsAlign) || !num_tokens_per_expert ||
         !aligned(num_tokens_per_expert, 4) || !num_tokens_per_rank || !aligned(num_tokens_per_rank, 4))
+        return EPL_EINVAL;
+    if (!per_node_ok(*p, num_tokens_per_rdma_rank))
         return EPL_EINVAL;
     if (p->num_tokens > 0 && (!topk_idx || !aligned(topk_idx, 8) || !is_token_in_rank))
         return EPL_EINVAL;
@@ -330,7 +355,8 @@ int epl_layout(const epl_problem *p, const int64_t *topk_idx, int32_t *num_token
     if (rc != EPL_OK)
         return rc;
     return enqueue_scan(*p, w, epl::kScanReduce, num_tokens_per_expert, num_tokens_per_rank,
-                        nullptr, nullptr, workspace, s);
+                        nodes_of(*p) ? num_tokens_per_rdma_rank : nullptr, nullptr, nullptr,
+                        workspace, s);
 }
 
 int epl_scan(const epl_problem *p, const int32_t *num_tokens_per_expert, int32_t *expert_start_loc,
@@ -344,7 +370,7 @@ int epl_scan(const epl_problem *p, const int32_t *num_tokens_per_expert, int32_t
         return EPL_EINVAL;
     const WsLayout w = ws_layout(*p);
     return enqueue_scan(*p, w, epl::kScanPrefix, const_cast<int32_t *>(num_tokens_per_expert),
-                        nullptr, expert_start_loc, total_host, workspace,
+                        nullptr, nullptr, expert_start_loc, total_host, workspace,
                         static_cast<hipStream_t>(stream));
 }
 
@@ -387,9 +413,10 @@ int epl_scatter_fp8(const epl_problem *p, const uint8_t *x, const void *x_scale,
 // layout + scan + scatter on one stream, shared by both payload types
 static int dispatch_rows(const epl_problem *p, const int64_t *topk_idx, const RowArgs &ra,
                          int64_t capacity_rows, int32_t *num_tokens_per_expert,
-                         int32_t *num_tokens_per_rank, uint8_t *is_token_in_rank,
-                         int32_t *expert_start_loc, int32_t *total_host, int32_t *m_indices,
-                         int32_t *output_index, void *workspace, void *stream)
+                         int32_t *num_tokens_per_rank, int32_t *num_tokens_per_rdma_rank,
+                         uint8_t *is_token_in_rank, int32_t *expert_start_loc,
+                         int32_t *total_host, int32_t *m_indices, int32_t *output_index,
+                         void *workspace, void *stream)
 {
     if (!workspace || !aligned(workspace, kWsAlign) || !num_tokens_per_expert ||
         !aligned(num_tokens_per_expert, 4) || !num_tokens_per_rank ||
@@ -398,6 +425,8 @@ static int dispatch_rows(const epl_problem *p, const int64_t *topk_idx, const Ro
         return EPL_EINVAL;
     if (p->num_tokens > 0 && !is_token_in_rank)
         return EPL_EINVAL;
+    if (!per_node_ok(*p, num_tokens_per_rdma_rank))
+        return EPL_EINVAL;
     if (!rows_args_ok(*p, ra, topk_idx, capacity_rows, m_indices, output_index))
         return EPL_EINVAL;
     const WsLayout w = ws_layout(*p);
@@ -405,7 +434,8 @@ static int dispatch_rows(const epl_problem *p, const int64_t *topk_idx, const Ro
     int rc = enqueue_layout(*p, w, topk_idx, is_token_in_rank, workspace, s);
     if (rc == EPL_OK)
         rc = enqueue_scan(*p, w, epl::kScanReduce | epl::kScanPrefix, num_tokens_per_expert,
-                          num_tokens_per_rank, expert_start_loc, total_host, workspace, s);
+                          num_tokens_per_rank, nodes_of(*p) ? num_tokens_per_rdma_rank : nullptr,
+                          expert_start_loc, total_host, workspace, s);
     if (rc == EPL_OK)
         rc = enqueue_scatter(*p, w, ra, topk_idx, expert_start_loc, workspace, capacity_rows,
                              m_indices, output_index, s);
@@ -414,22 +444,25 @@ static int dispatch_rows(const epl_problem *p, const int64_t *topk_idx, const Ro
 
 int epl_dispatch(const epl_problem *p, const int64_t *topk_idx, const uint16_t *x,
                  const float *x_scale, int64_t capacity_rows, int32_t *num_tokens_per_expert,
-                 int32_t *num_tokens_per_rank, uint8_t *is_token_in_rank,
-                 int32_t *expert_start_loc, int32_t *total_host, uint16_t *out, float *out_scale,
+                 int32_t *num_tokens_per_rank, int32_t *num_tokens_per_rdma_rank,
+                 uint8_t *is_token_in_rank, int32_t *expert_start_loc, int32_t *total_host,
+                 uint16_t *out, float *out_scale,
                  int32_t *m_indices, int32_t *output_index, void *workspace, void *stream)
 {
     if (!problem_ok(p))
         return EPL_EINVAL;
     return dispatch_rows(p, topk_idx, bf16_rows(*p, x, x_scale, out, out_scale), capacity_rows,
-                         num_tokens_per_expert, num_tokens_per_rank, is_token_in_rank,
-                         expert_start_loc, total_host, m_indices, output_index, workspace, stream);
+                         num_tokens_per_expert, num_tokens_per_rank, num_tokens_per_rdma_rank,
+                         is_token_in_rank, expert_start_loc, total_host, m_indices, output_index,
+                         workspace, stream);
 }
 
 int epl_dispatch_fp8(const epl_problem *p, const int64_t *topk_idx, const uint8_t *x,
                      const void *x_scale, int scale_format, int64_t capacity_rows,
                      int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,
-                     uint8_t *is_token_in_rank, int32_t *expert_start_loc, int32_t *total_host,
-                     uint8_t *out, void *out_scale, int32_t *m_indices, int32_t *output_index,
+                     int32_t *num_tokens_per_rdma_rank, uint8_t *is_token_in_rank,
+                     int32_t *expert_start_loc, int32_t *total_host, uint8_t *out,
+                     void *out_scale, int32_t *m_indices, int32_t *output_index,
                      void *workspace, void *stream)
 {
     if (!fp8_problem_ok(p, scale_format))
@@ -437,8 +470,8 @@ int epl_dispatch_fp8(const epl_problem *p, const int64_t *topk_idx, const uint8_
     return dispatch_rows(p, topk_idx,
                          fp8_rows(*p, x, x_scale, scale_format, capacity_rows, out, out_scale),
                          capacity_rows, num_tokens_per_expert, num_tokens_per_rank,
-                         is_token_in_rank, expert_start_loc, total_host, m_indices, output_index,
-                         workspace, stream);
+                         num_tokens_per_rdma_rank, is_token_in_rank, expert_start_loc, total_host,
+                         m_indices, output_index, workspace, stream);
 }
 
 int epl_combine(const epl_problem *p, const uint16_t *expert_out, int64_t expert_rows,

@@ -109,26 +109,28 @@ __device__ __forceinline__ void store_mask_bytes(uint8_t *dst, uint64_t mask, in
     }
 }
 
-// Dynamic LDS of the layout kernel for E experts, R ranks, B tokens of K
-// slots. Kept <= kLayoutLdsBytes by the host's choice of B.
+// Dynamic LDS of the layout kernel for E experts, RC token-count columns
+// (R ranks, then the nodes if asked for), B tokens of K slots. Kept <=
+// kLayoutLdsBytes by the host's choice of B.
 constexpr size_t kLayoutLdsBytes = 65536;
-__host__ __device__ constexpr size_t layout_lds_bytes(int B, int K, int E, int R)
+__host__ __device__ constexpr size_t layout_lds_bytes(int B, int K, int E, int RC)
 {
     return sizeof(int32_t) * ((size_t)2 * B * K              // keys, ranks
                               + (size_t)kLayoutWaves * E      // running count per wave and expert
                               + (size_t)kLayoutWaves * ((E + 3) / 4)   // per-chunk byte counters
-                              + (size_t)R + 1);               // tokens per rank, error flag
+                              + (size_t)RC + 1);              // tokens per rank / node, error flag
 }
 
 // One workgroup per block of B tokens (B <= kLayoutThreads, B * K <=
 // kMaxSlotsPerBlock). Outputs: in_rank rows of the block's tokens;
-// block_count[b][e] (slots of expert e in block b); block_rank[b][r] (tokens
-// of block b sent to rank r); block_err[b]; slot_rank[t*K+k] = rank of slot
-// (t,k) among the block's earlier slots of the same expert, or -1 for an
-// invalid slot.
+// block_count[b][e] (slots of expert e in block b); block_rank[b][c] (tokens
+// of block b sent to rank c for c < R, to node c - R for R <= c < R + Rn,
+// a node being G consecutive ranks); block_err[b]; slot_rank[t*K+k] = rank
+// of slot (t,k) among the block's earlier slots of the same expert, or -1
+// for an invalid slot.
 __global__ __launch_bounds__(kLayoutThreads) void ep_layout_kernel(
     const int64_t *__restrict__ topk, int64_t T, int K, int E, int R, int experts_per_rank,
-    int B, uint8_t *__restrict__ in_rank, bool in_rank_vec16,
+    int G, int Rn, int B, uint8_t *__restrict__ in_rank, bool in_rank_vec16,
     int32_t *__restrict__ block_count, int32_t *__restrict__ block_rank,
     uint32_t *__restrict__ block_err, int32_t *__restrict__ slot_rank)
 {
@@ -139,8 +141,9 @@ __global__ __launch_bounds__(kLayoutThreads) void ep_layout_kernel(
     int32_t *lrank = keys + max_slots;                     // [B*K] rank within the owning wave
     int32_t *wave_cnt = lrank + max_slots;                 // [waves][E]
     uint32_t *chunk_cnt = reinterpret_cast<uint32_t *>(wave_cnt + kLayoutWaves * E);  // [waves][E/4]
-    int32_t *rank_cnt = reinterpret_cast<int32_t *>(chunk_cnt + kLayoutWaves * cwords); // [R]
-    int32_t *s_err = rank_cnt + R;                         // [1]
+    int32_t *rank_cnt = reinterpret_cast<int32_t *>(chunk_cnt + kLayoutWaves * cwords); // [R+Rn]
+    const int RC = R + Rn;
+    int32_t *s_err = rank_cnt + RC;                        // [1]
 
     const int64_t b = blockIdx.x;
     const int64_t t0 = b * B;
@@ -154,7 +157,7 @@ __global__ __launch_bounds__(kLayoutThreads) void ep_layout_kernel(
         wave_cnt[i] = 0;
     for (int i = tid; i < kLayoutWaves * cwords; i += kLayoutThreads)
         chunk_cnt[i] = 0;
-    for (int i = tid; i < R; i += kLayoutThreads)
+    for (int i = tid; i < RC; i += kLayoutThreads)
         rank_cnt[i] = 0;
     if (tid == 0)
         *s_err = 0;
@@ -245,6 +248,27 @@ __global__ __launch_bounds__(kLayoutThreads) void ep_layout_kernel(
                     atomicAdd(&rank_cnt[w0 + r], __popcll(has));
             }
         }
+        // Tokens per node (G consecutive ranks), the same way: a token
+        // counts once for a node whichever of its ranks it reaches.
+        for (int n0 = 0; n0 < Rn; n0 += 64) {
+            const int wn = min(64, Rn - n0);
+            uint64_t mask = 0;
+            if (tok) {
+                for (int k = 0; k < K; ++k) {
+                    const int packed = keys[tid * K + k];
+                    if (packed >= 0) {
+                        const int n = (packed >> 16) / G - n0;
+                        if (n >= 0 && n < wn)
+                            mask |= 1ull << n;
+                    }
+                }
+            }
+            for (int n = 0; n < wn; ++n) {
+                const uint64_t has = wave_ballot((mask >> n) & 1u);
+                if (lane == 0 && has)
+                    atomicAdd(&rank_cnt[R + n0 + n], __popcll(has));
+            }
+        }
     }
     __syncthreads();
 
@@ -258,8 +282,8 @@ __global__ __launch_bounds__(kLayoutThreads) void ep_layout_kernel(
         }
         block_count[b * E + e] = run;
     }
-    for (int r = tid; r < R; r += kLayoutThreads)
-        block_rank[b * R + r] = rank_cnt[r];
+    for (int r = tid; r < RC; r += kLayoutThreads)
+        block_rank[b * RC + r] = rank_cnt[r];
     __syncthreads();
     if (tid == 0)
         block_err[b] = (uint32_t)*s_err;
@@ -320,7 +344,8 @@ __device__ __forceinline__ int segment_sum(const int32_t *m, int ncols, int col,
 }
 
 // Single workgroup. kScanReduce: column sums of block_count / block_rank
-// give num_tokens_per_expert / num_tokens_per_rank, block_count is replaced
+// give num_tokens_per_expert / num_tokens_per_rank (and, for the Rn node
+// columns after the R rank columns, num_tokens_per_rdma_rank), block_count is replaced
 // by its exclusive prefix over blocks, and the status word is reset to the
 // layout's error bits. kScanPrefix: exclusive prefix of the per-expert block
 // sizes (the counts, read from `cnt` unless kScanReduce produced them,
@@ -334,14 +359,15 @@ __device__ __forceinline__ int segment_sum(const int32_t *m, int ncols, int col,
 // per-column scan over the P segment sums gives each segment's offset, and
 // the thread then rewrites its segment as a running prefix.
 __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
-    int mode, int64_t nb, int E, int R, int alignment, int32_t *__restrict__ block_count,
+    int mode, int64_t nb, int E, int R, int Rn, int alignment, int32_t *__restrict__ block_count,
     const int32_t *__restrict__ block_rank, const uint32_t *__restrict__ block_err,
-    int32_t *__restrict__ cnt, int32_t *__restrict__ per_rank, int32_t *__restrict__ start,
+    int32_t *__restrict__ cnt, int32_t *__restrict__ per_rank, int32_t *__restrict__ per_node,
+    int32_t *__restrict__ start,
     int32_t *__restrict__ ws_counts, WsHeader *__restrict__ hdr, int32_t *__restrict__ total_out)
 {
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_seg[kMaxExperts];
-    __shared__ int s_rseg[kMaxExperts];
+    __shared__ int s_rseg[2 * kMaxExperts];
     __shared__ int s_wave[kScanThreads / kWave];
     __shared__ uint32_t s_err;
     const int tid = threadIdx.x;
@@ -351,7 +377,8 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
             s_err = 0;
         const int P = E <= kScanThreads ? kScanThreads / E : 1;
         const int64_t L = (nb + P - 1) / P;
-        const int PR = R <= kScanThreads ? kScanThreads / R : 1;
+        const int RC = R + Rn;      // rank columns, then node columns
+        const int PR = RC <= kScanThreads ? kScanThreads / RC : 1;
         const int64_t LR = (nb + PR - 1) / PR;
         // When every thread owns at most one segment of at most 16 blocks,
         // the segment stays in registers between the sum and the rewrite.
@@ -372,10 +399,10 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
                 s_seg[q * E + e] = segment_sum(block_count, E, e, b0, b1);
             }
         }
-        for (int col = tid; col < R * PR; col += kScanThreads) {
-            const int r = col % R, q = col / R;
+        for (int col = tid; col < RC * PR; col += kScanThreads) {
+            const int r = col % RC, q = col / RC;
             const int64_t b0 = q * LR;
-            s_rseg[q * R + r] = segment_sum(block_rank, R, r, b0, min(nb, b0 + LR));
+            s_rseg[q * RC + r] = segment_sum(block_rank, RC, r, b0, min(nb, b0 + LR));
         }
         uint32_t err = 0;
         for (int64_t bb = tid; bb < nb; bb += kScanThreads)
@@ -394,11 +421,14 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
             cnt[e] = run;
             ws_counts[e] = run;
         }
-        for (int r = tid; r < R; r += kScanThreads) {
+        for (int r = tid; r < RC; r += kScanThreads) {
             int run = 0;
             for (int q = 0; q < PR; ++q)
-                run += s_rseg[q * R + r];
-            per_rank[r] = run;
+                run += s_rseg[q * RC + r];
+            if (r < R)
+                per_rank[r] = run;
+            else
+                per_node[r - R] = run;
         }
         __syncthreads();
         // Rewrite block_count as the exclusive prefix over blocks.

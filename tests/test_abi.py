@@ -49,8 +49,9 @@ def test_no_oracle_in_the_product_path():
 
 
 def test_problem_struct_layout():
-    assert ctypes.sizeof(epl.Problem) == 32
+    assert ctypes.sizeof(epl.Problem) == 40
     assert epl.Problem.num_topk.offset == 8 and epl.Problem.expert_alignment.offset == 28
+    assert epl.Problem.ranks_per_node.offset == 32 and epl.Problem.reserved.offset == 36
 
 
 def P(**kw):
@@ -92,6 +93,26 @@ def test_expert_alignment_range(lib, a, ok):
     assert (epl.epl_validate(p) == epl.EPL_OK) == ok
 
 
+@pytest.mark.parametrize("G,ok,nodes", [(0, True, 0), (1, True, 32), (8, True, 4), (32, True, 0),
+                                        (64, True, 0), (3, False, 0), (-1, False, 0)])
+def test_ranks_per_node(lib, G, ok, nodes):
+    """R = 32: G divides R for a multi-node problem; G >= R is one node."""
+    p = P(ranks_per_node=G)
+    assert (epl.epl_validate(p) == epl.EPL_OK) == ok
+    if ok:
+        assert p.num_nodes == nodes
+
+
+def test_reserved_must_be_zero(lib):
+    p = P()
+    p.reserved = 1
+    assert epl.epl_validate(p) == epl.EPL_EINVAL
+
+
+def test_workspace_grows_with_node_columns(lib):
+    assert epl.epl_workspace_bytes(P(ranks_per_node=1)) >= epl.epl_workspace_bytes(P())
+
+
 @pytest.mark.parametrize("T,K,E,a,want", [
     (4096, 8, 256, 0, 4096 * 8),
     (4096, 8, 256, 1, 4096 * 8),
@@ -128,8 +149,13 @@ def test_entry_points_reject_bad_arguments_without_a_gpu(lib):
     pp = ctypes.byref(p)
     fake = 1 << 20            # an aligned, never dereferenced address
     odd = fake + 2            # misaligned
-    assert lib.epl_layout(pp, None, None, None, None, None, None) == epl.EPL_EINVAL
-    assert lib.epl_layout(pp, fake, fake, fake, fake, odd, None) == epl.EPL_EINVAL   # workspace
+    assert lib.epl_layout(pp, None, None, None, None, None, None, None) == epl.EPL_EINVAL
+    assert lib.epl_layout(pp, fake, fake, fake, None, fake, odd, None) == epl.EPL_EINVAL  # ws
+    multi = P(ranks_per_node=8)                  # 4 nodes: the per-node output is required
+    assert lib.epl_layout(ctypes.byref(multi), fake, fake, fake, None, fake, fake,
+                          None) == epl.EPL_EINVAL
+    assert lib.epl_layout(ctypes.byref(multi), fake, fake, fake, odd, fake, fake,
+                          None) == epl.EPL_EINVAL
     assert lib.epl_scan(pp, fake, fake, None, None, None) == epl.EPL_EINVAL
     assert lib.epl_scan(pp, odd, fake, None, fake, None) == epl.EPL_EINVAL
     assert lib.epl_scatter(pp, fake, fake, fake, fake, fake, -1, fake, fake, fake, fake,
@@ -138,14 +164,17 @@ def test_entry_points_reject_bad_arguments_without_a_gpu(lib):
                            None) == epl.EPL_EINVAL                                  # x misaligned
     assert lib.epl_scatter(pp, fake, None, fake, fake, fake, 10, fake, fake, fake, fake,
                            None) == epl.EPL_EINVAL                                  # scales missing
-    assert lib.epl_dispatch(pp, fake, fake, fake, 10, fake, fake, None, fake, None, fake, fake,
-                            fake, fake, fake, None) == epl.EPL_EINVAL               # in_rank null
+    assert lib.epl_dispatch(pp, fake, fake, fake, 10, fake, fake, None, None, fake, None, fake,
+                            fake, fake, fake, fake, None) == epl.EPL_EINVAL         # in_rank null
+    assert lib.epl_dispatch(ctypes.byref(multi), fake, fake, fake, 10, fake, fake, None, fake,
+                            fake, None, fake, fake, fake, fake, fake,
+                            None) == epl.EPL_EINVAL                                 # per-node null
     assert lib.epl_combine(pp, fake, 10, fake, fake, 7, fake, None, None) == epl.EPL_EINVAL
     assert lib.epl_combine(pp, fake, 10, fake, fake, 0, odd, None, None) == epl.EPL_EINVAL
     assert lib.epl_expert_scale(pp, fake, fake, 10, fake, None, None) == epl.EPL_EINVAL
     bad = P(num_ranks=3)
-    assert lib.epl_dispatch(ctypes.byref(bad), fake, fake, fake, 10, fake, fake, fake, fake, None,
-                            fake, fake, fake, fake, fake, None) == epl.EPL_EINVAL
+    assert lib.epl_dispatch(ctypes.byref(bad), fake, fake, fake, 10, fake, fake, None, fake, fake,
+                            None, fake, fake, fake, fake, fake, None) == epl.EPL_EINVAL
     assert lib.epl_status(None, None) == epl.EPL_EINVAL
     assert lib.epl_total(odd, None) == epl.EPL_EINVAL
 
@@ -164,8 +193,9 @@ def test_fp8_entry_points_check_their_arguments(lib):
     assert scat(no_s, epl.EPL_SCALE_UE8M0) == epl.EPL_EINVAL      # scales without scale_cols
     assert scat(ok, epl.EPL_SCALE_F32, xs=None) == epl.EPL_EINVAL
     assert scat(ok, epl.EPL_SCALE_UE8M0, outs=fake + 2) == epl.EPL_EINVAL
-    assert lib.epl_dispatch_fp8(ctypes.byref(bad_h), fake, fake, None, 0, 10, fake, fake, fake,
-                                fake, None, fake, None, fake, fake, fake, None) == epl.EPL_EINVAL
+    assert lib.epl_dispatch_fp8(ctypes.byref(bad_h), fake, fake, None, 0, 10, fake, fake, None,
+                                fake, fake, None, fake, None, fake, fake, fake,
+                                None) == epl.EPL_EINVAL
 
 
 def test_strerror(lib):
@@ -179,7 +209,7 @@ def test_python_binding_rejects_cpu_tensors(lib):
     p = epl.Problem.make(4, 2, 8, 2, 16, 0)
     with pytest.raises(ValueError, match="GPU tensor"):
         epl.epl_layout(p, torch.zeros((4, 2), dtype=torch.int64), torch.zeros(8, dtype=torch.int32),
-                       torch.zeros(2, dtype=torch.int32), torch.zeros((4, 2), dtype=torch.uint8),
-                       torch.zeros(256, dtype=torch.uint8))
+                       torch.zeros(2, dtype=torch.int32), None,
+                       torch.zeros((4, 2), dtype=torch.uint8), torch.zeros(256, dtype=torch.uint8))
     with pytest.raises(TypeError, match="int64"):
-        epl.epl_layout(p, torch.zeros((4, 2), dtype=torch.int32), None, None, None, None)
+        epl.epl_layout(p, torch.zeros((4, 2), dtype=torch.int32), None, None, None, None, None)

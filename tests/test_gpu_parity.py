@@ -57,16 +57,17 @@ def poisoned(shape, dtype, byte=POISON):
 
 
 def gpu_dispatch(topk, x, xs, E, R, cap=None, byte=POISON, stream=None, split=False,
-                 alignment=0):
+                 alignment=0, G=0):
     """Run dispatch through the C ABI on poisoned buffers; returns tensors."""
     T, K = topk.shape
     H = x.shape[1]
     S = 0 if xs is None else xs.shape[1]
-    p = epl.Problem.make(T, K, E, R, H, S, alignment)
+    p = epl.Problem.make(T, K, E, R, H, S, alignment, G)
     cap = epl.epl_capacity_rows(p) if cap is None else cap
     ws = poisoned(epl.epl_workspace_bytes(p), torch.uint8, byte)
     r = dict(
         cnt=poisoned(E, torch.int32, byte), per_rank=poisoned(R, torch.int32, byte),
+        per_node=poisoned(p.num_nodes, torch.int32, byte) if p.num_nodes else None, G=G,
         in_rank=poisoned((T, R), torch.uint8, byte), start=poisoned(E, torch.int32, byte),
         out=poisoned((cap, H), torch.bfloat16, byte),
         out_scale=poisoned((cap, S), torch.float32, byte) if S else None,
@@ -76,13 +77,14 @@ def gpu_dispatch(topk, x, xs, E, R, cap=None, byte=POISON, stream=None, split=Fa
     xd = to_bf16(x)
     xsd = None if xs is None else torch.from_numpy(xs).to(DEV)
     if split:
-        epl.epl_layout(p, tk, r["cnt"], r["per_rank"], r["in_rank"], ws, stream)
+        epl.epl_layout(p, tk, r["cnt"], r["per_rank"], r["per_node"], r["in_rank"], ws, stream)
         epl.epl_scan(p, r["cnt"], r["start"], r["total_host"], ws, stream)
         epl.epl_scatter(p, xd, xsd, tk, r["start"], ws, cap, r["out"], r["out_scale"], r["m"],
                         r["oi"], stream)
     else:
-        epl.epl_dispatch(p, tk, xd, xsd, cap, r["cnt"], r["per_rank"], r["in_rank"], r["start"],
-                         r["total_host"], r["out"], r["out_scale"], r["m"], r["oi"], ws, stream)
+        epl.epl_dispatch(p, tk, xd, xsd, cap, r["cnt"], r["per_rank"], r["per_node"], r["in_rank"],
+                         r["start"], r["total_host"], r["out"], r["out_scale"], r["m"], r["oi"],
+                         ws, stream)
     r["x"], r["topk"] = xd, tk
     return r
 
@@ -105,6 +107,11 @@ def check_layout_and_scatter(r, ref, x, xs):
     np.testing.assert_array_equal(r["cnt"].cpu().numpy(), ref["num_tokens_per_expert"])
     np.testing.assert_array_equal(r["per_rank"].cpu().numpy(), ref["num_tokens_per_rank"])
     np.testing.assert_array_equal(r["in_rank"].cpu().numpy(), ref["is_token_in_rank"])
+    want_nodes = orc().rdma_counts(ref["is_token_in_rank"], r["G"])
+    if want_nodes is None:
+        assert r["per_node"] is None
+    else:
+        np.testing.assert_array_equal(r["per_node"].cpu().numpy(), want_nodes)
     np.testing.assert_array_equal(r["start"].cpu().numpy(), ref["expert_start_loc"])
     np.testing.assert_array_equal(r["oi"].cpu().numpy(), ref["output_index"])
     np.testing.assert_array_equal(r["m"][:N].cpu().numpy(), ref["m_indices"])
@@ -141,7 +148,7 @@ def full_parity(w: workloads.Workload, inp=None, split=False, alignment=0):
     topk, x, xs, wt = inp["topk_idx"], inp["x"], inp["x_scale"], inp["topk_weights"]
     E, R = w.num_experts, w.num_ranks
     ref = orc().run_all(x, xs, topk, wt, E, R, expert_fn=w.expert_fn, alignment=alignment)
-    r = gpu_dispatch(topk, x, xs, E, R, split=split, alignment=alignment)
+    r = gpu_dispatch(topk, x, xs, E, R, split=split, alignment=alignment, G=w.ranks_per_node)
     assert epl.epl_status(r["ws"]) == epl.EPL_OK
     check_layout_and_scatter(r, ref, x, xs)
     N = ref["total"]
@@ -163,7 +170,7 @@ def full_parity(w: workloads.Workload, inp=None, split=False, alignment=0):
 
 # ------------------------------------------------------------ workloads --
 
-@pytest.mark.parametrize("name", ["tiny", "small", "dsv3", "skew"])
+@pytest.mark.parametrize("name", ["tiny", "small", "dsv3", "skew", "dsv3_recv"])
 def test_workload_full_parity(name):
     print(f"[parity] workload={name}", flush=True)
     full_parity(workloads.get(name))
@@ -207,7 +214,7 @@ def test_large_batch_sampled_parity():
     _, _, m_ref, oi_ref = orc().scatter(None, None, topk, start, N, copy_rows=False)
     ref = dict(num_tokens_per_expert=cnt, num_tokens_per_rank=per_rank, is_token_in_rank=in_rank,
                expert_start_loc=start, total=N, m_indices=m_ref, output_index=oi_ref)
-    r = gpu_dispatch(topk, x, None, E, R)
+    r = gpu_dispatch(topk, x, None, E, R, G=w.ranks_per_node)
     eo = torch.empty_like(r["out"])
     epl.epl_expert_scale(r["p"], r["out"], r["m"], r["cap"], eo, r["ws"])
     y = gpu_combine(r, eo, wt, epl.EPL_OUT_F32)
@@ -314,12 +321,12 @@ def fp8_parity(w, fmt, alignment=0, extra_cap=0, split=False):
     tk = torch.from_numpy(topk).to(DEV)
     xd = torch.from_numpy(x).to(DEV)
     if split:
-        epl.epl_layout(p, tk, cnt_d, per_d, in_d, ws)
+        epl.epl_layout(p, tk, cnt_d, per_d, None, in_d, ws)
         epl.epl_scan(p, cnt_d, start_d, tot, ws)
         epl.epl_scatter_fp8(p, xd, xs_d, fmt, tk, start_d, ws, cap, out, out_s, m, oi)
     else:
-        epl.epl_dispatch_fp8(p, tk, xd, xs_d, fmt, cap, cnt_d, per_d, in_d, start_d, tot, out,
-                             out_s, m, oi, ws)
+        epl.epl_dispatch_fp8(p, tk, xd, xs_d, fmt, cap, cnt_d, per_d, None, in_d, start_d, tot,
+                             out, out_s, m, oi, ws)
     assert epl.epl_status(ws) == epl.EPL_OK
     assert int(tot[0]) == N
     np.testing.assert_array_equal(cnt_d.cpu().numpy(), cnt)
@@ -384,6 +391,58 @@ def test_ragged_shapes(case):
     w = workloads.Workload(name, seed=77, num_tokens=T, hidden=H, num_experts=E, num_topk=K,
                            num_ranks=R, scales=scales, routing="uniform", drop_rate=drop)
     full_parity(w)
+
+
+# ------------------------------------------------- tokens per node (RDMA) --
+
+# (name, E, R, G, T, K): one node (not produced), one rank per node (equals
+# the per-rank counts), more than 64 nodes (two mask windows), and the
+# largest column count the scan handles (2048 ranks + 2048 nodes).
+NODES = [
+    ("g1", 16, 8, 1, 500, 3),
+    ("dsv3_like_g4", 256, 32, 4, 4096, 8),
+    ("nodes128", 256, 256, 2, 5000, 8),
+    ("r2048_g1", 2048, 2048, 1, 3000, 8),
+    ("r2048_g8", 2048, 2048, 8, 3000, 8),
+    ("one_node", 64, 64, 64, 100, 4),
+    ("g_above_r", 64, 16, 32, 100, 4),
+]
+
+
+@pytest.mark.parametrize("case", NODES, ids=[c[0] for c in NODES])
+def test_tokens_per_node(case):
+    name, E, R, G, T, K = case
+    print(f"[parity] nodes case={name}", flush=True)
+    w = workloads.Workload(name, seed=91, num_tokens=T, hidden=64, num_experts=E, num_topk=K,
+                           num_ranks=R, scales=False, routing="uniform", drop_rate=0.1,
+                           ranks_per_node=G)
+    r, _ = full_parity(w)
+    if G == 1:
+        assert torch.equal(r["per_node"], r["per_rank"])
+
+
+def test_receive_side_is_the_global_buffer_restricted():
+    """The batch of rank 3 with local ids, dispatched on the GPU, reproduces
+    the stretch of rank 3's experts in the GPU's global buffer."""
+    w = workloads.get("dsv3").with_(num_tokens=3000, drop_rate=0.05)
+    inp = workloads.make_inputs(w)
+    topk, x, xs = inp["topk_idx"], inp["x"], inp["x_scale"]
+    El, r = w.num_experts // w.num_ranks, 3
+    g = gpu_dispatch(topk, x, xs, w.num_experts, w.num_ranks, G=w.ranks_per_node)
+    mine = (topk >= r * El) & (topk < (r + 1) * El)
+    keep = np.nonzero(mine.any(axis=1))[0]
+    lt = np.ascontiguousarray(np.where(mine[keep], topk[keep] - r * El, -1))
+    loc = gpu_dispatch(lt, x[keep], xs[keep], El, 1)
+    torch.cuda.synchronize()
+    assert epl.epl_status(g["ws"]) == epl.EPL_OK and epl.epl_status(loc["ws"]) == epl.EPL_OK
+    lo = int(g["start"][r * El])
+    n = int(loc["total_host"][0])
+    assert n == int(g["start"][(r + 1) * El]) - lo
+    assert torch.equal(loc["out"][:n].view(torch.int16), g["out"][lo:lo + n].view(torch.int16))
+    assert torch.equal(loc["out_scale"][:n], g["out_scale"][lo:lo + n])
+    assert torch.equal(loc["m"][:n] + r * El, g["m"][lo:lo + n])
+    want_oi = np.where(lt >= 0, g["oi"].cpu().numpy()[keep] - lo, -1)
+    np.testing.assert_array_equal(loc["oi"].cpu().numpy(), want_oi)
 
 
 # ------------------------------------------------------------- edge cases --
@@ -475,7 +534,7 @@ def test_capacity_overflow_flagged_without_out_of_bounds_writes():
     in_rank, start = poisoned((T, R), torch.uint8), poisoned(E, torch.int32)
     oi = poisoned((T, K), torch.int32)
     epl.epl_dispatch(p, torch.from_numpy(topk).to(DEV), to_bf16(x), None, cap, cnt, per_rank,
-                     in_rank, start, None, out, None, m, oi, ws)
+                     None, in_rank, start, None, out, None, m, oi, ws)
     assert epl.epl_status(ws) == epl.EPL_ECAPACITY
     np.testing.assert_array_equal(oi.cpu().numpy(), ref["output_index"])
     np.testing.assert_array_equal(u16(out), ref["out"][:cap])
@@ -496,7 +555,7 @@ def test_combine_flags_row_beyond_expert_output():
     # a clean layout resets the status word
     epl.epl_layout(p, torch.zeros((T, K), dtype=torch.int64, device=DEV),
                    torch.empty(4, dtype=torch.int32, device=DEV),
-                   torch.empty(2, dtype=torch.int32, device=DEV),
+                   torch.empty(2, dtype=torch.int32, device=DEV), None,
                    torch.empty((T, 2), dtype=torch.uint8, device=DEV), ws)
     y = poisoned((T, H), torch.float32)
     epl.epl_combine(p, to_bf16(eo), 20, torch.from_numpy(oi).to(DEV),
