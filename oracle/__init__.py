@@ -59,6 +59,14 @@ class Oracle:
         lib.epl_oracle_bf16_from_double.restype = ctypes.c_uint16
         lib.epl_oracle_layout.argtypes = [_c_i64, _c_i32, _c_i32, _c_i32, _ptr, _ptr, _ptr, _ptr]
         lib.epl_oracle_layout.restype = ctypes.c_int
+        lib.epl_oracle_e4m3_from_double.argtypes = [ctypes.c_double]
+        lib.epl_oracle_e4m3_from_double.restype = ctypes.c_uint8
+        lib.epl_oracle_quantize_e4m3.argtypes = [_c_i64, _c_i32, _ptr, _ptr, _ptr]
+        lib.epl_oracle_quantize_e4m3.restype = ctypes.c_int
+        lib.epl_oracle_ll_dispatch.argtypes = [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
+                                               _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
+                                               _ptr]
+        lib.epl_oracle_ll_dispatch.restype = ctypes.c_int
         lib.epl_oracle_rdma_counts.argtypes = [_c_i64, _c_i32, _c_i32, _ptr, _ptr]
         lib.epl_oracle_rdma_counts.restype = ctypes.c_int
         lib.epl_oracle_scan.argtypes = [_c_i32, _ptr, _c_i32, _ptr, _ptr]
@@ -88,6 +96,46 @@ class Oracle:
         f = self.lib.epl_oracle_bf16_from_double
         flat = np.asarray(v, dtype=np.float64).ravel()
         return np.array([f(float(a)) for a in flat], dtype=np.uint16).reshape(np.shape(v))
+
+    def e4m3_from_double_array(self, v: np.ndarray) -> np.ndarray:
+        f = self.lib.epl_oracle_e4m3_from_double
+        flat = np.asarray(v, dtype=np.float64).ravel()
+        return np.array([f(float(a)) for a in flat], dtype=np.uint8).reshape(np.shape(v))
+
+    def quantize_e4m3(self, x: np.ndarray):
+        """bf16 x [T, H] (uint16 bits) -> (e4m3 bytes [T, H], fp32 scales [T, H/128])."""
+        xb = _c(x, np.uint16)
+        T, H = xb.shape
+        q = np.empty((T, H), np.uint8)
+        sc = np.empty((T, H // 128), np.float32)
+        _check(self.lib.epl_oracle_quantize_e4m3(T, H, _p(xb), _p(q), _p(sc)), "quantize_e4m3")
+        return q, sc
+
+    def ll_dispatch(self, x: Optional[np.ndarray], topk_idx: np.ndarray, num_experts: int,
+                    tokens_per_segment: int, cap: int, hidden: Optional[int] = None):
+        """Fixed-rectangle (low-latency) layout. Returns a dict with out
+        [E, cap, H] u8 (rows past recv_count zero), out_scale [E, S, cap] f32,
+        recv_count [E], src_info [E, cap] (-1 past recv_count), layout_range
+        [E, T/M, 2] (begin, count), output_index [T, K] and overflow (bool).
+        With x None only the indices are produced."""
+        topk = _c(topk_idx, np.int64)
+        T, K = topk.shape
+        E, M = int(num_experts), int(tokens_per_segment)
+        xb = None if x is None else _c(x, np.uint16)
+        H = int(hidden) if xb is None else xb.shape[1]
+        S = H // 128
+        out = None if xb is None else np.zeros((E, cap, H), np.uint8)
+        out_scale = None if xb is None else np.zeros((E, S, cap), np.float32)
+        recv = np.empty(E, np.int32)
+        src = np.full((E, cap), -1, np.int32)
+        rng = np.empty((E, T // M if M else 0, 2), np.int32)
+        oi = np.empty((T, K), np.int32)
+        ovf = np.zeros(1, np.int32)
+        _check(self.lib.epl_oracle_ll_dispatch(T, K, E, H, M, int(cap), _p(xb), _p(topk),
+                                               _p(out), _p(out_scale), _p(recv), _p(src),
+                                               _p(rng), _p(oi), _p(ovf)), "ll_dispatch")
+        return dict(out=out, out_scale=out_scale, recv_count=recv, src_info=src,
+                    layout_range=rng, output_index=oi, overflow=bool(ovf[0]))
 
     def layout(self, topk_idx: np.ndarray, num_experts: int, num_ranks: int):
         """Returns (num_tokens_per_expert [E] i32, num_tokens_per_rank [R] i32,
@@ -238,6 +286,7 @@ def lib_path() -> str:
 def __getattr__(name):
     # module-level shorthands: oracle.layout(...), oracle.scan(...), ...
     if name in ("bf16_to_double", "bf16_from_double", "bf16_from_double_array", "layout",
-                "rdma_counts", "scan", "scatter", "expert_scale", "combine", "run_all"):
+                "rdma_counts", "scan", "scatter", "expert_scale", "combine", "run_all",
+                "e4m3_from_double_array", "quantize_e4m3", "ll_dispatch"):
         return getattr(default(), name)
     raise AttributeError(name)

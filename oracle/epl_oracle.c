@@ -41,7 +41,10 @@
  * Parity pins (tests/test_oracle_pins.py): worked examples from the pages,
  * an O((TK)^2) brute force of the placement definition, numpy's stable
  * argsort, closed forms for combine on exactly representable values,
- * torch's float->bf16 rounding for the bf16 encoder, and invariants.
+ * torch's float->bf16 and float->float8_e4m3fn rounding for the two
+ * encoders, the quantiser redone with numpy binary32 arithmetic, the
+ * fixed-rectangle layout against the (pinned) prefix-sum layout, and
+ * invariants.
  */
 #include <math.h>
 #include <stdint.h>
@@ -312,6 +315,172 @@ int epl_oracle_scatter_rows(int64_t T, int32_t K, int32_t E, int64_t row_bytes,
         }
     }
     free(next);
+    return rc;
+}
+
+/* ------------------------------------------------ FP8 e4m3 quantisation -- */
+
+/* Round a double to the nearest FP8 e4m3 value (the OCP "fn" encoding: 1 sign
+ * bit, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, largest
+ * finite value 448), ties to even, and return its byte. Written from the
+ * number format like the bf16 encoder: a value in [2^(e-1), 2^e) is a
+ * multiple of 2^(e-4); below the smallest normal 2^-6 the spacing is 2^-9.
+ * Magnitudes that round above 448 saturate to 448 (the quantiser below never
+ * produces them). NaN gives 0x7F. */
+uint8_t epl_oracle_e4m3_from_double(double v)
+{
+    if (isnan(v))
+        return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs(v);
+    if (a == 0.0)
+        return sign;
+    int e2;
+    (void)frexp(a, &e2);              /* a = m * 2^e2, 0.5 <= m < 1 */
+    int quantum = e2 - 4;
+    if (quantum < -9)
+        quantum = -9;                 /* subnormal spacing */
+    double r = ldexp(nearbyint(ldexp(a, -quantum)), quantum);
+    if (r > 448.0)
+        r = 448.0;
+    if (r < ldexp(1.0, -6))           /* subnormal (or zero): r = m * 2^-9 */
+        return (uint8_t)(sign | (uint8_t)ldexp(r, 9));
+    int e;
+    double m = frexp(r, &e);          /* r = m * 2^e, 0.5 <= m < 1 */
+    int exp_field = e + 6;            /* (e - 1) + bias 7 */
+    int mant = (int)ldexp(m * 2.0 - 1.0, 3);
+    return (uint8_t)(sign | (uint8_t)(exp_field << 3) | (uint8_t)mant);
+}
+
+/* The low-latency dispatch sends FP8 rows with one fp32 scale per 128
+ * hidden columns ([DEEPEP] low_latency mode: the dispatch casts to FP8 on
+ * the way, and returns scales of shape [..., hidden / 128]). The pages do
+ * not give the cast; reading: per 128-column group of a token,
+ *   amax = max |x|, scale = amax / 448, inv = 448 / amax (0 if amax = 0),
+ *   q = e4m3(x * inv),
+ * every operation in binary32 with round to nearest (the product x * inv
+ * is rounded to binary32 before the e4m3 rounding; this file is built with
+ * -ffp-contract=off for x86-64, where float arithmetic is binary32), so that the group's
+ * largest magnitude lands on 448 and q * scale approximates x. x is bf16
+ * [T, H], H a multiple of 128; q is [T, H] bytes, scale [T, H / 128]. */
+int epl_oracle_quantize_e4m3(int64_t T, int32_t H, const uint16_t *x, uint8_t *q, float *scale)
+{
+    if (T < 0 || H < 0 || H % 128 != 0)
+        return ORACLE_EINVAL;
+    int32_t S = H / 128;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t g = 0; g < S; ++g) {
+            const uint16_t *xg = x + t * (int64_t)H + (int64_t)g * 128;
+            float amax = 0.0f;
+            for (int32_t i = 0; i < 128; ++i) {
+                float v = fabsf((float)epl_oracle_bf16_to_double(xg[i]));
+                if (v > amax)
+                    amax = v;
+            }
+            float s = amax / 448.0f;
+            float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+            scale[t * (int64_t)S + g] = s;
+            for (int32_t i = 0; i < 128; ++i) {
+                float p = (float)epl_oracle_bf16_to_double(xg[i]) * inv;
+                q[t * (int64_t)H + (int64_t)g * 128 + i] = epl_oracle_e4m3_from_double((double)p);
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------- low-latency rectangle -- */
+
+/* Strategy A of [ANATOMY] high-throughput part, subsection 3 (a fixed
+ * rectangle sized for the worst case, no count exchange), in the shape of
+ * DeepEP's low-latency receive buffers ([DEEPEP] low_latency mode): every
+ * expert e owns rows [e * cap, (e + 1) * cap) of a [E * cap, H] FP8 buffer,
+ * with cap = (source segments) x (tokens per segment) in the worst case. The
+ * T tokens arrive as T / M source segments of M tokens each (segment s =
+ * tokens [s * M, (s + 1) * M), padding tokens carry only -1 slots). An
+ * expert's slots fill its rows from the first one in (token, k) order, so
+ * the valid rows of e are its first recv_count[e] rows, grouped by source
+ * segment; the row holds the token's quantised row (epl_oracle_quantize_e4m3)
+ * and its scales go to out_scale[(e * S + g) * cap + j], column-major in the
+ * last two dimensions as DeepEP returns them. src_info of the row is the
+ * token's index within its segment; layout_range[e][s] = (rows of e from
+ * segments before s, rows of e from segment s), i.e. where segment s's rows
+ * start within e's block and how many there are; output_index[t, k] is the
+ * row (e * cap + j) or -1. A slot beyond cap rows is not placed
+ * (output_index -1, not counted in recv_count) and *overflow is set to 1.
+ * Rows of an expert past its recv_count are left untouched. With x NULL
+ * only the indices are produced. */
+int epl_oracle_ll_dispatch(int64_t T, int32_t K, int32_t E, int32_t H, int32_t M, int64_t cap,
+                           const uint16_t *x, const int64_t *topk_idx, uint8_t *out,
+                           float *out_scale, int32_t *recv_count, int32_t *src_info,
+                           int32_t *layout_range, int32_t *output_index, int32_t *overflow)
+{
+    if (T < 0 || K < 1 || E < 1 || H < 0 || H % 128 != 0 || M < 1 || T % M != 0 || cap < 0)
+        return ORACLE_EINVAL;
+    int32_t S = H / 128;
+    int64_t nseg = T / M;
+    uint8_t *qrow = (uint8_t *)malloc((size_t)H + 1);
+    float *srow = (float *)malloc(sizeof(float) * ((size_t)S + 1));
+    if (!qrow || !srow) {
+        free(qrow);
+        free(srow);
+        return ORACLE_EINVAL;
+    }
+    *overflow = 0;
+    for (int32_t e = 0; e < E; ++e) {
+        recv_count[e] = 0;
+        for (int64_t s = 0; s < nseg; ++s) {
+            layout_range[(e * nseg + s) * 2 + 0] = 0;
+            layout_range[(e * nseg + s) * 2 + 1] = 0;
+        }
+    }
+    int rc = ORACLE_OK;
+    for (int64_t t = 0; t < T && rc == ORACLE_OK; ++t) {
+        int64_t seg = t / M;
+        int quantised = 0;
+        for (int32_t k = 0; k < K; ++k) {      /* slots in k order */
+            int64_t e = topk_idx[t * K + k];
+            if (e < -1 || e >= E) {
+                rc = ORACLE_ERANGE;
+                break;
+            }
+            if (e == -1) {
+                output_index[t * K + k] = -1;  /* not selected */
+                continue;
+            }
+            int64_t j = recv_count[e];
+            if (j >= cap) {                    /* the rectangle is full */
+                *overflow = 1;
+                output_index[t * K + k] = -1;  /* dropped */
+                continue;
+            }
+            recv_count[e] += 1;
+            layout_range[(e * nseg + seg) * 2 + 1] += 1;
+            int64_t row = e * cap + j;
+            output_index[t * K + k] = (int32_t)row;
+            src_info[row] = (int32_t)(t - seg * M);
+            if (!x)
+                continue;                      /* indices only */
+            if (!quantised) {
+                epl_oracle_quantize_e4m3(1, H, x + t * (int64_t)H, qrow, srow);
+                quantised = 1;
+            }
+            if (out)
+                memcpy(out + row * (int64_t)H, qrow, (size_t)H);
+            if (out_scale)
+                for (int32_t g = 0; g < S; ++g)
+                    out_scale[(e * (int64_t)S + g) * cap + j] = srow[g];
+        }
+    }
+    for (int32_t e = 0; e < E; ++e) {
+        int32_t before = 0;                    /* rows of e from earlier segments */
+        for (int64_t s = 0; s < nseg; ++s) {
+            layout_range[(e * nseg + s) * 2 + 0] = before;
+            before += layout_range[(e * nseg + s) * 2 + 1];
+        }
+    }
+    free(qrow);
+    free(srow);
     return rc;
 }
 

@@ -62,6 +62,20 @@ MUTANTS = {
     "rdma_nodes_strided": ("for (int32_t r = n * G; r < (n + 1) * G; ++r)",
                            "for (int32_t r = n; r < R; r += nodes)"),
     "rdma_counts_ranks_not_tokens": ("                    any = 1;", "                    ++tokens;"),
+    "e4m3_truncates": ("double r = ldexp(nearbyint(ldexp(a, -quantum)), quantum);",
+                       "double r = ldexp(floor(ldexp(a, -quantum)), quantum);"),
+    "e4m3_four_mantissa_bits": ("int quantum = e2 - 4;", "int quantum = e2 - 5;"),
+    "quant_amax_signed": ("float v = fabsf((float)epl_oracle_bf16_to_double(xg[i]));",
+                          "float v = (float)epl_oracle_bf16_to_double(xg[i]);"),
+    "quant_stores_inverse_scale": ("scale[t * (int64_t)S + g] = s;",
+                                   "scale[t * (int64_t)S + g] = inv;"),
+    "ll_rows_without_expert_stride": ("int64_t row = e * cap + j;", "int64_t row = e + j;"),
+    "ll_src_info_global_token": ("src_info[row] = (int32_t)(t - seg * M);",
+                                 "src_info[row] = (int32_t)t;"),
+    "ll_range_begin_inclusive": ("            layout_range[(e * nseg + s) * 2 + 0] = before;\n            before += layout_range[(e * nseg + s) * 2 + 1];",
+                                 "            before += layout_range[(e * nseg + s) * 2 + 1];\n            layout_range[(e * nseg + s) * 2 + 0] = before;"),
+    "ll_overflow_ignored": ("            if (j >= cap) {                    /* the rectangle is full */",
+                            "            if (j >= cap + 1) {                    /* the rectangle is full */"),
     "scale_row_of_wrong_token": ("x_scale + t * (int64_t)S", "x_scale + (T - 1 - t) * (int64_t)S"),
 }
 
@@ -233,7 +247,44 @@ def _battery(orc: Oracle):
         _, _, in_rank = orc.layout(topk, g["num_experts"][0], g["num_ranks"][0])
         return all(orc.rdma_counts(in_rank, G).tolist() == g[f"rdma_g{G}"] for G in (1, 2, 4))
 
-    for name, fn in [("golden_scan", golden_scan), ("golden_rdma", golden_rdma), ("golden_hand", golden_hand), ("brute", brute),
+    def golden_ll():
+        g = load_golden("ll_rectangle_example.txt")
+        topk = np.array(g["topk_idx"], np.int64)
+        E, M = g["num_experts"][0], g["tokens_per_segment"][0]
+        r = orc.ll_dispatch(None, topk, E, M, 4, hidden=128)
+        ok = (r["output_index"].tolist() == g["cap4_output_index"]
+              and r["recv_count"].tolist() == g["cap4_recv_count"])
+        ok = ok and all(r["layout_range"][e].ravel().tolist() == g[f"cap4_range_e{e}"]
+                        for e in (1, 3, 7))
+        ok = ok and (r["src_info"][[3, 3, 7, 7, 1], [0, 1, 0, 1, 0]] == 0).all()
+        r1 = orc.ll_dispatch(None, topk, E, M, 1, hidden=128)
+        return ok and r1["output_index"].tolist() == g["cap1_output_index"] and r1["overflow"]
+
+    def ll_src_segments():
+        rng = np.random.default_rng(8)
+        T, K, E, M = 24, 2, 4, 6
+        topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+        r = orc.ll_dispatch(None, topk, E, M, T, hidden=128)
+        tt, kk = np.nonzero(topk >= 0)
+        return np.array_equal(r["src_info"].reshape(-1)[r["output_index"][tt, kk]], tt % M)
+
+    def quant_ref():
+        import torch
+        rng = np.random.default_rng(23)
+        f = rng.standard_normal((6, 256)).astype(np.float32)
+        f[2, :128] *= -1e-3
+        x = (torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+        q, sc = orc.quantize_e4m3(x)
+        xf = (x.astype(np.uint32) << 16).view(np.float32).reshape(6, 2, 128)
+        amax = np.abs(xf).max(axis=2)
+        inv = (np.float32(448) / amax).astype(np.float32)
+        p = (xf * inv[:, :, None]).astype(np.float32).reshape(6, 256)
+        want = torch.from_numpy(p).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        return np.array_equal(q, want) and np.array_equal(sc, (amax / np.float32(448)).astype(np.float32))
+
+    for name, fn in [("golden_scan", golden_scan), ("golden_rdma", golden_rdma),
+                     ("golden_ll", golden_ll), ("ll_src_segments", ll_src_segments),
+                     ("quant_ref", quant_ref), ("golden_hand", golden_hand), ("brute", brute),
                      ("golden_alignment", golden_alignment), ("brute_aligned", brute_aligned),
                      ("scale_cols_layout", scale_cols_layout),
                      ("rows_aligned_padding", rows_aligned_padding), ("brute_rows", brute_rows),

@@ -561,3 +561,165 @@ def test_local_partial_combines_sum_to_the_global_combine():
     xv = np.array([[oracle.bf16_to_double(int(v)) for v in row] for row in x])
     bound = np.abs(w.astype(np.float64)).sum(axis=1, keepdims=True) * np.abs(xv)
     assert np.all(np.abs(acc - y) <= 1e-12 * bound + 1e-300)
+
+
+# ------------------------------------------------------ FP8 e4m3 encoding --
+
+def _e4m3_values():
+    """Every finite e4m3 value, decoded by torch (the encoding's own
+    decoder), sorted."""
+    torch = pytest.importorskip("torch")
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    return codes, vals
+
+
+def test_e4m3_encoder_matches_torch():
+    """Every finite code round-trips; midpoints between neighbours (ties)
+    and random values in range round as torch's float8_e4m3fn conversion
+    does (round to nearest even)."""
+    torch = pytest.importorskip("torch")
+    codes, vals = _e4m3_values()
+    np.testing.assert_array_equal(oracle.e4m3_from_double_array(vals), codes)
+    pos = np.unique(vals[vals >= 0])
+    mids = (pos[1:] + pos[:-1]) / 2                      # exact in binary32
+    rng = np.random.default_rng(12)
+    rnd = rng.standard_normal(4000) * np.exp2(rng.integers(-12, 9, 4000))
+    v = np.concatenate([mids, -mids, rnd[np.abs(rnd) < 464]]).astype(np.float32)
+    want = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(oracle.e4m3_from_double_array(v.astype(np.float64)), want)
+
+
+def _bf16(a):
+    import torch
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).view(torch.int16) \
+        .numpy().view(np.uint16)
+
+
+def test_quantize_matches_float32_reference():
+    """The quantiser against the same steps done with numpy binary32
+    arithmetic and torch's e4m3 conversion: bit-exact codes and scales."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(21)
+    T, H = 40, 512
+    f = rng.standard_normal((T, H)).astype(np.float32) * np.exp2(
+        rng.integers(-20, 20, (T, H // 128, 1)).astype(np.float32)).repeat(128, axis=2).reshape(T, H)
+    f[3, :128] = 0.0                                  # an all-zero group
+    f[4, 128:256] = 0.0
+    f[4, 200] = -3.0                                  # one negative value carries the max
+    x = _bf16(f)
+    q, sc = oracle.quantize_e4m3(x)
+    xf = (x.astype(np.uint32) << 16).view(np.float32).reshape(T, H // 128, 128)
+    amax = np.abs(xf).max(axis=2)
+    s_ref = (amax / np.float32(448)).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        inv = np.where(amax > 0, np.float32(448) / amax, np.float32(0)).astype(np.float32)
+    p = (xf * inv[:, :, None]).astype(np.float32).reshape(T, H)
+    q_ref = torch.from_numpy(p).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(sc, s_ref)
+    np.testing.assert_array_equal(q, q_ref)
+
+
+def test_quantize_properties():
+    """The largest magnitude of each group encodes to +-448; q * scale is
+    within e4m3's half-spacing of x (relative 2^-4 for normal codes); an
+    all-zero group gives zero codes and scale 0."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(22)
+    f = rng.standard_normal((16, 256)).astype(np.float32)
+    f[5, 128:] = 0.0
+    x = _bf16(f)
+    q, sc = oracle.quantize_e4m3(x)
+    xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    deq = torch.from_numpy(q).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    deq = deq * np.repeat(sc.astype(np.float64), 128, axis=1)
+    for t in range(16):
+        for g in range(2):
+            blk = slice(128 * g, 128 * (g + 1))
+            i = np.argmax(np.abs(xf[t, blk]))
+            if sc[t, g] == 0:
+                assert (q[t, blk] == 0).all()
+                continue
+            assert q[t, blk][i] in (0x7E, 0xFE)
+            err = np.abs(deq[t, blk] - xf[t, blk])
+            tol = np.maximum(np.abs(xf[t, blk]) * 2.0 ** -4, 2.0 ** -10 * sc[t, g]) * (1 + 1e-6)
+            assert (err <= tol).all()
+    assert sc[5, 1] == 0
+
+
+# ------------------------------------------- low-latency fixed rectangle --
+
+def test_golden_ll_rectangle_example():
+    g = load_golden("ll_rectangle_example.txt")
+    topk = np.array(g["topk_idx"], np.int64)
+    E, M = g["num_experts"][0], g["tokens_per_segment"][0]
+    r = oracle.ll_dispatch(None, topk, E, M, 4, hidden=128)
+    assert r["output_index"].tolist() == g["cap4_output_index"]
+    assert r["recv_count"].tolist() == g["cap4_recv_count"] and not r["overflow"]
+    for e in (1, 3, 7):
+        assert r["layout_range"][e].ravel().tolist() == g[f"cap4_range_e{e}"]
+    assert (r["src_info"][[3, 3, 7, 7, 1], [0, 1, 0, 1, 0]] == 0).all()
+    r1 = oracle.ll_dispatch(None, topk, E, M, 1, hidden=128)
+    assert r1["output_index"].tolist() == g["cap1_output_index"]
+    assert r1["recv_count"].tolist() == g["cap1_recv_count"] and r1["overflow"]
+
+
+@pytest.mark.parametrize("seed,M", [(0, 16), (1, 7), (2, 1), (3, 50)])
+def test_ll_rectangle_against_exact_layout(seed, M):
+    """Within each expert the rectangle holds the same rows in the same order
+    as the exact (prefix-sum) layout: row - e*cap == exact row - start[e].
+    Rows are the quantised token rows, scales column-major per expert;
+    src_info and layout_range follow from the token's segment."""
+    rng = np.random.default_rng(600 + seed)
+    nseg, K, E, H = 6, 4, 12, 256
+    T = nseg * M
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    topk[rng.random(topk.shape) < 0.2] = -1
+    x = _bf16(rng.standard_normal((T, H)).astype(np.float32))
+    cap = T                                   # the worst case: every token at one expert
+    r = oracle.ll_dispatch(x, topk, E, M, cap)
+    assert not r["overflow"]
+    cnt, _, _ = oracle.layout(topk, E, 1)
+    start, total = oracle.scan(cnt)
+    _, _, m, oi = oracle.scatter(None, None, topk, start, total)
+    np.testing.assert_array_equal(r["recv_count"], cnt)
+    valid = topk >= 0
+    e_of = np.where(valid, topk, 0)
+    want = np.where(valid, oi - start[e_of] + e_of * cap, -1)
+    np.testing.assert_array_equal(r["output_index"], want)
+    q, sc = oracle.quantize_e4m3(x)
+    out = r["out"].reshape(E * cap, -1)
+    tt, kk = np.nonzero(valid)
+    rows = r["output_index"][tt, kk]
+    np.testing.assert_array_equal(out[rows], q[tt])
+    ee, jj = rows // cap, rows % cap
+    np.testing.assert_array_equal(r["out_scale"][ee, :, jj], sc[tt])
+    np.testing.assert_array_equal(r["src_info"].reshape(-1)[rows], tt % M)
+    seg_counts = np.zeros((E, nseg), np.int64)
+    np.add.at(seg_counts, (e_of[valid], tt // M), 1)
+    np.testing.assert_array_equal(r["layout_range"][:, :, 1], seg_counts)
+    np.testing.assert_array_equal(r["layout_range"][:, :, 0],
+                                  np.cumsum(seg_counts, axis=1) - seg_counts)
+    # the rows of segment s within expert e are exactly its layout_range
+    for e in range(E):
+        for s in range(nseg):
+            b, c = r["layout_range"][e, s]
+            assert (r["src_info"][e, b:b + c] >= 0).all()
+            seg_rows = rows[(ee == e) & (tt // M == s)] % cap
+            assert sorted(seg_rows.tolist()) == list(range(b, b + c))
+
+
+def test_ll_rectangle_overflow_keeps_the_first_rows():
+    rng = np.random.default_rng(44)
+    T, K, E, M, cap = 64, 3, 4, 8, 20
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    r = oracle.ll_dispatch(None, topk, E, M, cap, hidden=128)
+    big = oracle.ll_dispatch(None, topk, E, M, T, hidden=128)
+    assert r["overflow"] and not big["overflow"]
+    np.testing.assert_array_equal(r["recv_count"], np.minimum(big["recv_count"], cap))
+    # slots within capacity keep their rows (re-based to the smaller stride)
+    b = big["output_index"]
+    j = np.where(b >= 0, b % T, -1)
+    e = np.where(b >= 0, b // T, 0)
+    want = np.where((b >= 0) & (j < cap), e * cap + j, -1)
+    np.testing.assert_array_equal(r["output_index"], want)
