@@ -54,6 +54,188 @@ def algorithmic_bytes(w, N, T_any, out_dtype_bytes=4, pad_rows=0):
     }
 
 
+def ll_algorithmic_bytes(w, N, T_any, out_dtype_bytes=4):
+    """Low-latency dispatch (layout + reduction + cast-and-place, one call):
+    reads the token rows once (bf16), topk and the per-slot offsets; writes
+    the FP8 rows, their fp32 scales, src_info, output_index, recv_count and
+    layout_range. Combine as in the prefix-sum path."""
+    T, K, E, H = w.num_tokens, w.num_topk, w.num_experts, w.hidden
+    S, nseg = H // 128, T // w.ll_segment
+    return {
+        "ll_dispatch": (2 * H * T_any + 8 * T * K + 4 * T * K) +
+                       (H * N + 4 * S * N + 4 * N + 4 * T * K + 4 * E + 8 * E * nseg),
+        "combine": 2 * H * N + 4 * T * K + 4 * T * K + out_dtype_bytes * T * H,
+    }
+
+
+def ll_cpu_baseline(w, inp, seconds):
+    """The oracle's low-latency dispatch (quantise + place) and fp64 combine,
+    single-threaded, over full passes of the workload."""
+    import numpy as np
+
+    import oracle
+
+    orc = oracle.default()
+    topk, x, wt = inp["topk_idx"], inp["x"], inp["topk_weights"]
+    T, K = topk.shape
+    cap = T
+    passes, rows, t0 = 0, 0, time.perf_counter()
+    while True:
+        r = orc.ll_dispatch(x, topk, w.num_experts, w.ll_segment, cap)
+        # combine over the bf16 expert rows, gathered compactly (same sums)
+        oi = r["output_index"]
+        valid = oi >= 0
+        compact = np.full(oi.shape, -1, np.int32)
+        compact[valid] = np.arange(int(valid.sum()), dtype=np.int32)
+        eo = np.repeat(x, K, axis=0)[valid.ravel()]
+        orc.combine(eo, compact, wt)
+        passes += 1
+        rows += int(valid.sum())
+        el = time.perf_counter() - t0
+        if el >= seconds or passes >= 50:
+            break
+    return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} full pass(es) of the {w.name} workload (fixed-rectangle "
+                      f"layout, FP8 cast, fp64 combine), {el:.1f} s"}
+
+
+def run_ll(args, w, inp):
+    """The low-latency step: epl_ll_dispatch (layout, per-block reduction,
+    FP8 cast into the fixed rectangle) then epl_combine over the experts' bf16
+    output rectangle, on one stream."""
+    import numpy as np
+    import torch
+
+    import permute_ep_layout_amd as epl
+
+    dev = torch.device("cuda:0")
+    T, K, E, H = w.num_tokens, w.num_topk, w.num_experts, w.hidden
+    M, S = w.ll_segment, H // 128
+    cap = M * (T // M)                 # the worst case: every segment's tokens at one expert
+    topk_h = inp["topk_idx"]
+    N = int((topk_h >= 0).sum())
+    T_any = int((topk_h >= 0).any(axis=1).sum())
+    topk = torch.from_numpy(topk_h).to(dev)
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    wt = torch.from_numpy(inp["topk_weights"]).to(dev)
+    p = epl.Problem.make(T, K, E, 1, H, S)
+    i32 = torch.int32
+    ws = torch.empty(epl.epl_ll_workspace_bytes(p, M), dtype=torch.uint8, device=dev)
+    out = torch.empty((E, cap, H), dtype=torch.uint8, device=dev)
+    out_scale = torch.empty((E, S, cap), dtype=torch.float32, device=dev)
+    recv = torch.empty(E, dtype=i32, device=dev)
+    src = torch.empty((E, cap), dtype=i32, device=dev)
+    lrange = torch.empty((E, T // M, 2), dtype=i32, device=dev)
+    oi = torch.empty((T, K), dtype=i32, device=dev)
+    epl.epl_ll_dispatch(p, M, cap, topk, x, out, out_scale, recv, src, lrange, oi, ws)
+    # the experts' bf16 output rectangle, stood in for by the bf16 rows of
+    # the tokens placed there
+    eo = torch.empty((E * cap, H), dtype=torch.bfloat16, device=dev)
+    flat = oi.view(-1).long()
+    sel = flat >= 0
+    tok = torch.arange(T, device=dev).repeat_interleave(K)[sel]
+    eo[flat[sel]] = x[tok]
+    del flat, sel, tok
+    out_code = epl.EPL_OUT_F32 if args.out_dtype == "f32" else epl.EPL_OUT_BF16
+    y = torch.empty((T, H), dtype=torch.float32 if out_code == epl.EPL_OUT_F32 else torch.bfloat16,
+                    device=dev)
+    pc = epl.Problem.make(T, K, E, 1, H, 0)
+    epl.epl_combine(pc, eo, E * cap, oi, wt, out_code, y, ws)
+    stream = torch.cuda.current_stream(dev)
+    dispatch_call = epl.prepare("epl_ll_dispatch", p, M, cap, topk, x, out, out_scale, recv, src,
+                                lrange, oi, ws)
+    combine_call = epl.prepare("epl_combine", pc, eo, E * cap, oi, wt, out_code, y, ws)
+
+    log(f"low-latency step: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        dispatch_call()
+        combine_call()
+    torch.cuda.synchronize()
+    if epl.epl_status(ws) != epl.EPL_OK or int(recv.sum()) != N:
+        raise RuntimeError(f"low-latency dispatch failed: status {epl.epl_status(ws)}")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        dispatch_call()
+        evs[i][0].record(stream)
+        combine_call()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    prev = [ev0] + [e[1] for e in evs[:-1]]
+    timed_ms = {"ll_dispatch": float(np.mean([a.elapsed_time(m) for a, (m, _) in zip(prev, evs)])),
+                "combine": float(np.mean([m.elapsed_time(e) for m, e in evs]))}
+    assert epl.epl_status(ws) == epl.EPL_OK
+
+    cold_ms = {}
+    if not args.timed_only:
+        flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        runs = []
+        for i in range(args.warmup + 10):
+            evc = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            flush_buf.sum()
+            evc[0].record(stream)
+            dispatch_call()
+            evc[1].record(stream)
+            flush_buf.sum()
+            evc[2].record(stream)
+            combine_call()
+            evc[3].record(stream)
+            if i >= args.warmup:
+                runs.append(evc)
+        torch.cuda.synchronize()
+        cold_ms = {"ll_dispatch": float(np.median([e[0].elapsed_time(e[1]) for e in runs])),
+                   "combine": float(np.median([e[2].elapsed_time(e[3]) for e in runs]))}
+        del flush_buf
+
+    nbytes = ll_algorithmic_bytes(w, N, T_any, 4 if out_code == epl.EPL_OUT_F32 else 2)
+    dominant = max(timed_ms, key=lambda n: timed_ms[n])
+    dom_gbps = nbytes[dominant] / (timed_ms[dominant] * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s, 1 thread)")
+        cpu = ll_cpu_baseline(w, inp, args.cpu_seconds)
+    result = {
+        "metric": "routed token-rows/s (dispatch+combine)",
+        "value": N / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16->fp8-e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "mode": "low-latency fixed rectangle",
+            "num_tokens": T, "hidden": H, "num_experts": E, "num_topk": K,
+            "tokens_per_segment": M, "segments": T // M, "rows_per_expert": cap,
+            "routing": w.routing, "routed_rows": N, "combine_out": args.out_dtype,
+        },
+        "timed_region_ms": timed_ms,
+        "algorithmic_bytes": nbytes,
+        "gbps": {k: nbytes[k] / (v * 1e-3) / 1e9 for k, v in timed_ms.items()},
+        "cold_cache": None if not cold_ms else {
+            "ms": cold_ms, "gbps": {k: nbytes[k] / (v * 1e-3) / 1e9 for k, v in cold_ms.items()}},
+        "roofline": {
+            "kernel": dominant, "bound": "hbm", "achieved": dom_gbps, "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": dom_gbps / HBM_PEAK_GBPS,
+            "algorithmic_bytes": nbytes[dominant], "avg_launch_ms": timed_ms[dominant],
+            "traffic": measured_traffic(w.name, "ll_scatter" if dominant == "ll_dispatch"
+                                        else dominant),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def measured_traffic(workload, kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary,
     only if it was taken on the current kernel sources."""
@@ -164,6 +346,9 @@ def main():
                         w.scale_cols)
     log(f"workload {w.name}: T={T} K={K} E={E} R={R} H={H} S={S}; generating inputs")
     inp = workloads.make_inputs(w)
+    if w.ll_segment:
+        run_ll(args, w, inp)
+        return
     N = int((inp["topk_idx"] >= 0).sum())
     T_any = int((inp["topk_idx"] >= 0).any(axis=1).sum())
 

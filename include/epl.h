@@ -214,6 +214,43 @@ int epl_dispatch_fp8(const epl_problem *p, const int64_t *topk_idx, const uint8_
                      int32_t *m_indices, int32_t *output_index, void *workspace,
                      void *stream);
 
+/* Low-latency dispatch into a fixed rectangle (strategy A of "高性能专家并行
+ * （EP）内核解剖学解读", high-throughput part, subsection 3: room for the
+ * worst case, no count exchange; laid out like the low-latency receive
+ * buffers of "[MoE] Deepseek的All-to-all通信: DeepEP代码解读", section
+ * low_latency, with the FP8 cast the low-latency dispatch does on the way).
+ * The T tokens arrive as T / M source segments of M = tokens_per_segment
+ * tokens (segment s = tokens [s*M, (s+1)*M); T % M == 0; tokens of a short
+ * segment are padded with all -1 slots). Expert e owns rows
+ * [e*cap, (e+1)*cap) of `out`, cap = rows_per_expert (the worst case is M
+ * times the number of segments); its slots fill them from the first one in
+ * (token, k) order, so the valid rows of e are its first recv_count[e]
+ * rows, grouped by segment. Each placed row holds the token's row cast to
+ * FP8 e4m3 per 128-column group: scale = amax / 448, codes = e4m3(x *
+ * (448 / amax)) rounded to nearest even (binary32 steps; an all-zero group
+ * has scale 0 and zero codes). Outputs, all device memory:
+ *   out           uint8 [E, cap, H]   e4m3 codes (rows past recv_count untouched)
+ *   out_scale     float [E, S, cap]   scale of group g of row j at (e*S + g)*cap + j
+ *                                     (column-major per expert), S = H / 128
+ *   recv_count    int32 [E]           rows placed for each expert
+ *   src_info      int32 [E, cap]      token index within its segment, per placed row
+ *   layout_range  int32 [E, T/M, 2]   (begin, count) of segment s's rows in e's block
+ *   output_index  int32 [T, K]        e*cap + j, or -1 (no selection, or no room)
+ * A slot that finds its expert's rectangle full is not placed and sets
+ * EPL_ECAPACITY in the status word. Requires H % 128 == 0, scale_cols ==
+ * H / 128, no expert alignment, E * cap <= INT32_MAX; num_ranks and
+ * ranks_per_node are not used. x: bf16 [T, H], 16-byte aligned; out 16-byte
+ * aligned. The workspace must have epl_ll_workspace_bytes(p, M) bytes
+ * (256-byte aligned); the call runs the layout, the per-block reduction and
+ * the cast-and-place kernel on `stream`. Receive side: pass local expert
+ * ids (-1 for other ranks' experts) and E = the local expert count. */
+size_t epl_ll_workspace_bytes(const epl_problem *p, int32_t tokens_per_segment);
+int epl_ll_dispatch(const epl_problem *p, int32_t tokens_per_segment, int64_t rows_per_expert,
+                    const int64_t *topk_idx, const uint16_t *x, uint8_t *out,
+                    float *out_scale, int32_t *recv_count, int32_t *src_info,
+                    int32_t *layout_range, int32_t *output_index, void *workspace,
+                    void *stream);
+
 /* Step 4 -- combine. For every token t:
  *   y[t, :] = sum over k ascending with output_index[t, k] >= 0 of
  *             topk_weights[t, k] * expert_out[output_index[t, k], :]
@@ -250,7 +287,7 @@ int64_t epl_total(const void *workspace, void *stream);
 /* Static text for a status code. */
 const char *epl_strerror(int code);
 
-/* Library version, e.g. 0x000200 for 0.2.0. */
+/* Library version, e.g. 0x000300 for 0.3.0. */
 int epl_version(void);
 
 #ifdef __cplusplus

@@ -44,6 +44,7 @@ C_ENTRY_POINTS = (
     "epl_validate", "epl_workspace_bytes", "epl_capacity_rows", "epl_layout", "epl_scan",
     "epl_scatter", "epl_dispatch", "epl_scatter_fp8", "epl_dispatch_fp8", "epl_combine",
     "epl_expert_scale", "epl_status", "epl_total", "epl_strerror", "epl_version",
+    "epl_ll_workspace_bytes", "epl_ll_dispatch",
 )
 
 
@@ -145,6 +146,10 @@ def load() -> ctypes.CDLL:
     lib.epl_dispatch_fp8.argtypes = [_PP, _P, _P, _P, i32, i64, _P, _P, _P, _P, _P, _P, _P, _P,
                                      _P, _P, _P, _P]
     lib.epl_dispatch_fp8.restype = i32
+    lib.epl_ll_workspace_bytes.argtypes = [_PP, i32]
+    lib.epl_ll_workspace_bytes.restype = ctypes.c_size_t
+    lib.epl_ll_dispatch.argtypes = [_PP, i32, i64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.epl_ll_dispatch.restype = i32
     lib.epl_combine.argtypes = [_PP, _P, i64, _P, _P, i32, _P, _P, _P]
     lib.epl_combine.restype = i32
     lib.epl_expert_scale.argtypes = [_PP, _P, _P, i64, _P, _P, _P]
@@ -393,6 +398,39 @@ def epl_dispatch_fp8(p: Problem, topk_idx, x, x_scale, scale_format, capacity_ro
                                    _ptr(total_host), _ptr(out), _ptr(out_scale), _ptr(m_indices),
                                    _ptr(output_index), _ptr(workspace), _stream(stream, dev)),
            "epl_dispatch_fp8")
+
+
+def epl_ll_workspace_bytes(p: Problem, tokens_per_segment: int) -> int:
+    return int(load().epl_ll_workspace_bytes(_prob(p), int(tokens_per_segment)))
+
+
+def epl_ll_dispatch(p: Problem, tokens_per_segment, rows_per_expert, topk_idx, x, out, out_scale,
+                    recv_count, src_info, layout_range, output_index, workspace, stream=None):
+    """Fixed-rectangle (low-latency) dispatch; shapes as in include/epl.h:
+    out uint8 [E, cap, H], out_scale f32 [E, S, cap], recv_count i32 [E],
+    src_info i32 [E, cap], layout_range i32 [E, T/M, 2], output_index i32
+    [T, K]; x bf16 [T, H]."""
+    torch = _torch()
+    T, K, E, H = p.num_tokens, p.num_topk, p.num_experts, p.hidden
+    M, cap = int(tokens_per_segment), int(rows_per_expert)
+    if M < 1 or T % M:
+        raise ValueError("num_tokens must be a multiple of tokens_per_segment")
+    _need(topk_idx, "topk_idx", torch.int64, (T, K))
+    dev = topk_idx.device
+    _need(x, "x", torch.bfloat16, (T, H), dev)
+    _need(out, "out", torch.uint8, (E, cap, H), dev)
+    _need(out_scale, "out_scale", torch.float32, (E, H // 128, cap), dev)
+    _need(recv_count, "recv_count", torch.int32, (E,), dev)
+    _need(src_info, "src_info", torch.int32, (E, cap), dev)
+    _need(layout_range, "layout_range", torch.int32, (E, T // M, 2), dev)
+    _need(output_index, "output_index", torch.int32, (T, K), dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
+    if workspace.numel() < epl_ll_workspace_bytes(p, M):
+        raise ValueError("workspace smaller than epl_ll_workspace_bytes")
+    _check(load().epl_ll_dispatch(_prob(p), M, cap, _ptr(topk_idx), _ptr(x), _ptr(out),
+                                  _ptr(out_scale), _ptr(recv_count), _ptr(src_info),
+                                  _ptr(layout_range), _ptr(output_index), _ptr(workspace),
+                                  _stream(stream, dev)), "epl_ll_dispatch")
 
 
 def epl_combine(p: Problem, expert_out, expert_rows, output_index, topk_weights, out_dtype, y,

@@ -92,16 +92,27 @@ int layout_block_tokens(const epl_problem &p)
     return (int)std::max<int64_t>(1, std::min<int64_t>(want, cap));
 }
 
+// The low-latency layout reads per-segment offsets off the per-block ones,
+// so its blocks must tile the source segments of M tokens: the largest
+// divisor of M not above the usual block size.
+int ll_block_tokens(const epl_problem &p, int32_t M)
+{
+    int b = std::min<int64_t>(layout_block_tokens(p), M);
+    while (b > 1 && M % b != 0)
+        --b;
+    return std::max(b, 1);
+}
+
 struct WsLayout {
     int block_tokens;
     int64_t num_blocks;
     size_t counts, block_count, block_rank, block_err, slot_rank, bytes;
 };
 
-WsLayout ws_layout(const epl_problem &p)
+WsLayout ws_layout(const epl_problem &p, int block_tokens)
 {
     WsLayout w{};
-    w.block_tokens = layout_block_tokens(p);
+    w.block_tokens = block_tokens;
     w.num_blocks = (p.num_tokens + w.block_tokens - 1) / w.block_tokens;
     size_t off = round_up(sizeof(WsHeader), kWsAlign);
     w.counts = off;
@@ -117,6 +128,8 @@ WsLayout ws_layout(const epl_problem &p)
     w.bytes = off;
     return w;
 }
+
+WsLayout ws_layout(const epl_problem &p) { return ws_layout(p, layout_block_tokens(p)); }
 
 template <typename T>
 T *at(void *ws, size_t off)
@@ -301,6 +314,36 @@ bool per_node_ok(const epl_problem &p, const int32_t *per_node)
     return nodes_of(p) == 0 || (per_node && aligned(per_node, 4));
 }
 
+// Low-latency problems: scales are produced (H % 128 == 0, S = H / 128), no
+// alignment, T a whole number of segments of M tokens, row ids int32.
+bool ll_ok(const epl_problem *p, int32_t M, int64_t cap)
+{
+    if (!problem_ok(p) || p->hidden % 128 != 0 || p->scale_cols != p->hidden / 128)
+        return false;
+    if (p->expert_alignment > 1 || M < 1 || p->num_tokens % M != 0 || cap < 0)
+        return false;
+    return (int64_t)p->num_experts * cap <= (int64_t)INT32_MAX;
+}
+
+template <int VPT>
+void launch_ll_scatter(const epl_problem &p, const WsLayout &w, int32_t M, int64_t cap,
+                       const uint16_t *x, const int64_t *topk, void *ws, uint8_t *out,
+                       float *out_scale, int32_t *recv_count, int32_t *src_info,
+                       int32_t *layout_range, int32_t *output_index, hipStream_t s)
+{
+    // one workgroup per token, and at least enough for the recv_count /
+    // layout_range entries (also when there are no tokens)
+    const int64_t entries = (int64_t)p.num_experts * std::max<int64_t>(1, p.num_tokens / M);
+    const int64_t need = (entries + epl::kScatterThreads - 1) / epl::kScatterThreads;
+    const unsigned grid = row_grid(std::max<int64_t>(p.num_tokens, need), epl::kCombineGrid);
+    hipLaunchKernelGGL(epl::ep_ll_scatter_kernel<VPT>, dim3(grid), dim3(epl::kScatterThreads), 0, s,
+                       x, p.hidden, topk, at<const int32_t>(ws, w.block_count),
+                       at<const int32_t>(ws, w.slot_rank), at<const int32_t>(ws, w.counts),
+                       p.num_tokens, p.num_topk, p.num_experts, w.block_tokens, M, cap, out,
+                       out_scale, recv_count, src_info, layout_range, output_index,
+                       &at<WsHeader>(ws, 0)->status);
+}
+
 }  // namespace
 
 extern "C" {
@@ -472,6 +515,62 @@ int epl_dispatch_fp8(const epl_problem *p, const int64_t *topk_idx, const uint8_
                          capacity_rows, num_tokens_per_expert, num_tokens_per_rank,
                          num_tokens_per_rdma_rank, is_token_in_rank, expert_start_loc, total_host,
                          m_indices, output_index, workspace, stream);
+}
+
+size_t epl_ll_workspace_bytes(const epl_problem *p, int32_t tokens_per_segment)
+{
+    if (!ll_ok(p, tokens_per_segment, 0))
+        return 0;
+    return ws_layout(*p, ll_block_tokens(*p, tokens_per_segment)).bytes;
+}
+
+int epl_ll_dispatch(const epl_problem *p, int32_t tokens_per_segment, int64_t rows_per_expert,
+                    const int64_t *topk_idx, const uint16_t *x, uint8_t *out, float *out_scale,
+                    int32_t *recv_count, int32_t *src_info, int32_t *layout_range,
+                    int32_t *output_index, void *workspace, void *stream)
+{
+    const int32_t M = tokens_per_segment;
+    const int64_t cap = rows_per_expert;
+    if (!ll_ok(p, M, cap))
+        return EPL_EINVAL;
+    if (!workspace || !aligned(workspace, kWsAlign) || !recv_count || !aligned(recv_count, 4))
+        return EPL_EINVAL;
+    if (p->num_tokens > 0 && (!topk_idx || !aligned(topk_idx, 8) || !x || !aligned(x, 16) ||
+                              !output_index || !aligned(output_index, 4) || !layout_range ||
+                              !aligned(layout_range, 4)))
+        return EPL_EINVAL;
+    if (cap > 0 && (!out || !aligned(out, 16) || !out_scale || !aligned(out_scale, 4) ||
+                    !src_info || !aligned(src_info, 4)))
+        return EPL_EINVAL;
+    const WsLayout w = ws_layout(*p, ll_block_tokens(*p, M));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int rc = enqueue_layout(*p, w, topk_idx, nullptr, workspace, s);
+    if (rc == EPL_OK)
+        rc = enqueue_scan(*p, w, epl::kScanReduce, nullptr, nullptr, nullptr, nullptr, nullptr,
+                          workspace, s);
+    if (rc != EPL_OK)
+        return rc;
+    const int64_t nvec = p->hidden / 8;
+    const int vpt = (int)std::min<int64_t>(8, (nvec + epl::kScatterThreads - 1) / epl::kScatterThreads);
+    switch (std::max(vpt, 1)) {
+#define EPL_LL_CASE(V)                                                                             \
+    case V:                                                                                        \
+        launch_ll_scatter<V>(*p, w, M, cap, x, topk_idx, workspace, out, out_scale, recv_count,    \
+                             src_info, layout_range, output_index, s);                             \
+        break;
+        EPL_LL_CASE(1)
+        EPL_LL_CASE(2)
+        EPL_LL_CASE(3)
+        EPL_LL_CASE(4)
+        EPL_LL_CASE(5)
+        EPL_LL_CASE(6)
+        EPL_LL_CASE(7)
+        EPL_LL_CASE(8)
+#undef EPL_LL_CASE
+    default:
+        return EPL_EINVAL;
+    }
+    return launch_status();
 }
 
 int epl_combine(const epl_problem *p, const uint16_t *expert_out, int64_t expert_rows,

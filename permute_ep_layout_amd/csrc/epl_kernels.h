@@ -240,7 +240,8 @@ __global__ __launch_bounds__(kLayoutThreads) void ep_layout_kernel(
                             mask |= 1ull << r;
                     }
                 }
-                store_mask_bytes(in_rank + (t0 + tid) * R + w0, mask, wr, in_rank_vec16);
+                if (in_rank)
+                    store_mask_bytes(in_rank + (t0 + tid) * R + w0, mask, wr, in_rank_vec16);
             }
             for (int r = 0; r < wr; ++r) {
                 const uint64_t has = wave_ballot((mask >> r) & 1u);
@@ -418,17 +419,20 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
                 run += v;
             }
             s_cnt[e] = run;
-            cnt[e] = run;
+            if (cnt)
+                cnt[e] = run;
             ws_counts[e] = run;
         }
         for (int r = tid; r < RC; r += kScanThreads) {
             int run = 0;
             for (int q = 0; q < PR; ++q)
                 run += s_rseg[q * RC + r];
-            if (r < R)
-                per_rank[r] = run;
-            else
+            if (r < R) {
+                if (per_rank)
+                    per_rank[r] = run;
+            } else if (per_node) {
                 per_node[r - R] = run;
+            }
         }
         __syncthreads();
         // Rewrite block_count as the exclusive prefix over blocks.
@@ -494,6 +498,7 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Workgroup counts of the row kernels. Combine: one workgroup per token (the
 // dispatcher starts a new workgroup as soon as one retires, which balances
@@ -745,6 +750,165 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
                     const int64_t row = rows[k];
                     if (row >= 0)
                         store_scale(out_scale + (int64_t)j * scale_ld + row, f);
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------- low-latency fixed rectangle --
+
+// e4m3 (OCP "fn": bias 7, max 448, no infinities) of a binary32 value, round
+// to nearest even; magnitudes that round above 448 give 448. Normal results
+// (|p| >= 2^-6) round the 23-bit mantissa to 3 bits on the bit pattern (a
+// carry moves into the exponent as it should), then rebias the exponent
+// from 127 to 7; smaller magnitudes are multiples of 2^-9, rounded with
+// rint (which may give 8 = 2^-6, the smallest normal code).
+__device__ __forceinline__ uint32_t e4m3_rne(float p)
+{
+    const uint32_t u = __float_as_uint(p);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t code;
+    if (a >= 0x3C800000u) {                       // 2^-6
+        const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+        code = (r >> 20) - (120u << 3);           // exponent 127 -> 7
+        code = code > 0x7Eu ? 0x7Eu : code;
+    } else {
+        code = (uint32_t)rintf(__uint_as_float(a) * 512.0f);
+    }
+    return sign | code;
+}
+
+// Strategy A (a fixed rectangle, no count exchange) in the shape of the
+// low-latency receive buffers: expert e owns rows [e * cap, (e + 1) * cap)
+// of the FP8 buffer; its slots fill them from the first in (token, k)
+// order, j = block offset + in-block rank (the same per-expert position as
+// the prefix-sum layout, without the prefix over experts). One workgroup per
+// token (grid-stride): the first K threads place the token's slots
+// (output_index = e * cap + j, src_info[row] = t mod M, or -1 past the
+// rectangle, with the capacity bit in the status word), then, if any slot
+// was placed, all threads cast the bf16 row to e4m3 one 128-column group at
+// a time: the group's 16 vectors of 8 values sit on 16 neighbouring lanes,
+// which reduce |x| to amax with xor shuffles; scale = amax / 448 and
+// codes = e4m3(x * (448 / amax)) (zero codes for an all-zero group). The
+// 8-byte code vectors are stored to every placed row with non-temporal
+// stores and each group's scale to out_scale[(e * S + g) * cap + j]
+// (column-major per expert). Before its tokens every workgroup also writes
+// a share of recv_count and layout_range (begin, count per expert and
+// source segment of M tokens), read off the per-block offsets: blocks of B
+// tokens with B dividing M, so segment s starts at block s * M / B.
+template <int VPT>
+__global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
+    const uint16_t *__restrict__ x, int H, const int64_t *__restrict__ topk,
+    const int32_t *__restrict__ block_base, const int32_t *__restrict__ slot_rank,
+    const int32_t *__restrict__ counts, int64_t T, int K, int E, int B, int M, int64_t cap,
+    uint8_t *__restrict__ out, float *__restrict__ out_scale, int32_t *__restrict__ recv_count,
+    int32_t *__restrict__ src_info, int32_t *__restrict__ layout_range,
+    int32_t *__restrict__ output_index, uint32_t *__restrict__ status)
+{
+    __shared__ int32_t s_e[2][kMaxTopk];      // expert of each placed slot, -1 if none
+    __shared__ int32_t s_j[2][kMaxTopk];      // row within the expert's block
+    const int tid = threadIdx.x;
+    const int S = H / 128;
+    const int nvec = H / 8;                   // 16-byte vectors of 8 bf16 values
+
+    // recv_count and layout_range
+    {
+        const int64_t nseg = T / M;
+        const int64_t bps = M / B;
+        const int64_t n = (int64_t)E * nseg;
+        const int64_t g0 = (int64_t)blockIdx.x * kScatterThreads + tid;
+        const int64_t gs = (int64_t)gridDim.x * kScatterThreads;
+        for (int64_t e = g0; e < E; e += gs)
+            recv_count[e] = (int32_t)min((int64_t)counts[e], cap);
+        for (int64_t i = g0; i < n; i += gs) {
+            const int e = (int)(i / nseg);
+            const int64_t sg = i % nseg;
+            const int64_t b0 = min((int64_t)block_base[(sg * bps) * E + e], cap);
+            const int64_t b1 = sg + 1 < nseg ? min((int64_t)block_base[((sg + 1) * bps) * E + e], cap)
+                                             : min((int64_t)counts[e], cap);
+            layout_range[2 * i] = (int32_t)b0;
+            layout_range[2 * i + 1] = (int32_t)(b1 - b0);
+        }
+    }
+
+    const TokenRange tr = token_range(T);
+    int it = 0;
+    for (int64_t t = tr.first; t < tr.end; t += tr.stride, ++it) {
+        int32_t *se = s_e[it & 1], *sj = s_j[it & 1];
+        if (tid < K) {
+            const int64_t e = topk[t * K + tid];
+            int32_t pe = -1, pj = 0, oi = -1;
+            if (e >= 0 && e < E) {
+                const int64_t j = (int64_t)block_base[(t / B) * E + e] + slot_rank[t * K + tid];
+                if (j < cap) {
+                    const int64_t row = e * cap + j;
+                    pe = (int32_t)e;
+                    pj = (int32_t)j;
+                    oi = (int32_t)row;
+                    src_info[row] = (int32_t)(t % M);
+                } else {
+                    atomicOr(status, kStatusCapacity);
+                }
+            }
+            output_index[t * K + tid] = oi;
+            se[tid] = pe;
+            sj[tid] = pj;
+        }
+        lds_barrier();
+        bool any = false;
+        for (int k = 0; k < K; ++k)
+            any |= se[k] >= 0;
+        if (!any)
+            continue;
+
+        const u32x4 *xrow = reinterpret_cast<const u32x4 *>(x + t * (int64_t)H);
+        for (int base = 0; base < nvec; base += kScatterThreads * VPT) {
+            u32x4 v[VPT];
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int idx = base + i * kScatterThreads + tid;
+                if (idx < nvec)
+                    v[i] = __builtin_nontemporal_load(xrow + idx);
+            }
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int idx = base + i * kScatterThreads + tid;
+                if (idx >= nvec)      // whole 16-lane groups drop out together (nvec % 16 == 0)
+                    continue;
+                float f[8];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    f[2 * q] = __uint_as_float(v[i][q] << 16);
+                    f[2 * q + 1] = __uint_as_float(v[i][q] & 0xFFFF0000u);
+                }
+                float amax = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    amax = fmaxf(amax, fabsf(f[q]));
+#pragma unroll
+                for (int d = 1; d < 16; d <<= 1)
+                    amax = fmaxf(amax, __shfl_xor(amax, d, kWave));
+                const float scale = amax / 448.0f;
+                const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+                uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    w0 |= e4m3_rne(f[q] * inv) << (8 * q);
+                    w1 |= e4m3_rne(f[4 + q] * inv) << (8 * q);
+                }
+                const u32x2 codes = {w0, w1};
+                const int g = idx / 16;
+                for (int k = 0; k < K; ++k) {
+                    const int e = se[k];
+                    if (e < 0)
+                        continue;
+                    const int64_t j = sj[k];
+                    const int64_t row = (int64_t)e * cap + j;
+                    __builtin_nontemporal_store(codes, reinterpret_cast<u32x2 *>(out + row * H) + idx);
+                    if ((tid & 15) == 0)
+                        out_scale[((int64_t)e * S + g) * cap + j] = scale;
                 }
             }
         }

@@ -33,6 +33,7 @@ TRAFFIC_MARK = "traffic-json:"
 
 # short names of the library's kernels, matched against demangled names
 SHORT = (("ep_layout_kernel", "layout"), ("ep_scan_kernel", "scan"),
+         ("ep_ll_scatter_kernel", "ll_scatter"),
          ("ep_scatter_kernel", "scatter"), ("ep_combine_kernel", "combine"),
          ("ep_expert_scale_kernel", "expert"))
 

@@ -66,6 +66,9 @@ class Workload:
     recv_global_experts: int = 0
     recv_src_ranks: int = 0
     recv_rank: int = 0
+    # Low-latency (fixed-rectangle) dispatch: tokens arrive as segments of
+    # ll_segment tokens (one per source rank); 0 = not a low-latency workload.
+    ll_segment: int = 0
 
     @property
     def scale_cols(self) -> int:
@@ -104,6 +107,12 @@ WORKLOADS = {
     # 32 x 4096 source tokens, each kept with probability
     # 1 - C(248,8)/C(256,8) = 0.2271 (at least one of the rank's 8 experts),
     # i.e. 29765 tokens and, on average, 32768 local slots
+    # the same batch dispatched the low-latency way: 32 source ranks of 128
+    # decode tokens, every expert's rectangle sized for the worst case
+    # (32 x 128 = 4096 rows), FP8 cast on the way
+    "dsv3_ll": Workload("dsv3_ll", seed=3, num_tokens=4096, hidden=7168, num_experts=256,
+                        num_topk=8, num_ranks=32, scales=False, routing="uniform",
+                        ll_segment=128),
     "dsv3_recv": Workload("dsv3_recv", seed=6, num_tokens=29765, hidden=7168, num_experts=8,
                           num_topk=8, num_ranks=1, scales=True, routing="recv",
                           recv_global_experts=256, recv_src_ranks=32, recv_rank=0),

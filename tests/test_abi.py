@@ -213,3 +213,25 @@ def test_python_binding_rejects_cpu_tensors(lib):
                        torch.zeros((4, 2), dtype=torch.uint8), torch.zeros(256, dtype=torch.uint8))
     with pytest.raises(TypeError, match="int64"):
         epl.epl_layout(p, torch.zeros((4, 2), dtype=torch.int32), None, None, None, None, None)
+
+
+def test_ll_workspace_and_argument_checks(lib):
+    fake = 1 << 20
+    ok = P(num_tokens=4096)                       # H = 7168, S = 56
+    assert epl.epl_ll_workspace_bytes(ok, 128) >= epl.epl_workspace_bytes(ok)
+    assert epl.epl_ll_workspace_bytes(ok, 100) == 0          # 4096 % 100 != 0
+    assert epl.epl_ll_workspace_bytes(ok, 0) == 0
+    assert epl.epl_ll_workspace_bytes(P(scale_cols=0), 128) == 0    # scales are produced
+    assert epl.epl_ll_workspace_bytes(P(expert_alignment=64), 128) == 0
+    # a prime segment length still tiles: blocks of one token
+    assert epl.epl_ll_workspace_bytes(P(num_tokens=127 * 3), 127) > 0
+
+    def call(p, M=128, cap=4096, ws=fake, out=fake):
+        return lib.epl_ll_dispatch(ctypes.byref(p), M, cap, fake, fake, out, fake, fake, fake,
+                                   fake, fake, ws, None)
+    assert call(ok, M=100) == epl.EPL_EINVAL
+    assert call(ok, cap=-1) == epl.EPL_EINVAL
+    assert call(ok, cap=(1 << 31) // 256) == epl.EPL_EINVAL     # E * cap > INT32_MAX
+    assert call(ok, ws=fake + 64) == epl.EPL_EINVAL
+    assert call(ok, out=fake + 8) == epl.EPL_EINVAL
+    assert call(P(hidden=7168 + 64, scale_cols=0)) == epl.EPL_EINVAL

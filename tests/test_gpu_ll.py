@@ -1,0 +1,179 @@
+"""GPU parity of the low-latency (fixed-rectangle) dispatch against the CPU
+oracle, through the C ABI: recv_count, layout_range, output_index and
+src_info bit-exact; the FP8 codes and fp32 scales of every placed row
+bit-exact (the quantisation decision is taken in binary32 on both sides);
+rows past an expert's recv_count untouched (poisoned buffers)."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import permute_ep_layout_amd as epl  # noqa: E402
+from permute_ep_layout_amd import workloads  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+POISON = 0x5A
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    epl.load()
+
+
+def poisoned(shape, dtype):
+    t = torch.empty(shape, dtype=dtype, device=DEV)
+    t.view(torch.uint8).fill_(POISON)
+    return t
+
+
+def gpu_ll(topk, x, E, M, cap, stream=None):
+    T, K = topk.shape
+    H = x.shape[1]
+    p = epl.Problem.make(T, K, E, 1, H, H // 128)
+    ws = poisoned(epl.epl_ll_workspace_bytes(p, M), torch.uint8)
+    r = dict(out=poisoned((E, cap, H), torch.uint8),
+             out_scale=poisoned((E, H // 128, cap), torch.float32),
+             recv_count=poisoned(E, torch.int32), src_info=poisoned((E, cap), torch.int32),
+             layout_range=poisoned((E, T // M, 2), torch.int32),
+             output_index=poisoned((T, K), torch.int32), ws=ws)
+    xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(DEV).view(torch.bfloat16)
+    epl.epl_ll_dispatch(p, M, cap, torch.from_numpy(topk).to(DEV), xd, r["out"], r["out_scale"],
+                        r["recv_count"], r["src_info"], r["layout_range"], r["output_index"], ws,
+                        stream)
+    return r
+
+
+def check_ll(topk, x, E, M, cap, expect_overflow=False, untouched_sample=64):
+    print(f"[ll] T={topk.shape[0]} K={topk.shape[1]} E={E} M={M} cap={cap} H={x.shape[1]}",
+          flush=True)
+    orc = oracle.default()
+    ref = orc.ll_dispatch(None, topk, E, M, cap, hidden=x.shape[1])
+    q, sc = orc.quantize_e4m3(x)
+    r = gpu_ll(topk, x, E, M, cap)
+    torch.cuda.synchronize()
+    st = epl.epl_status(r["ws"])
+    assert st == (epl.EPL_ECAPACITY if expect_overflow else epl.EPL_OK)
+    assert ref["overflow"] == expect_overflow
+    np.testing.assert_array_equal(r["recv_count"].cpu().numpy(), ref["recv_count"])
+    np.testing.assert_array_equal(r["layout_range"].cpu().numpy(), ref["layout_range"])
+    oi = r["output_index"].cpu().numpy()
+    np.testing.assert_array_equal(oi, ref["output_index"])
+    tt, kk = np.nonzero(oi >= 0)
+    rows = oi[tt, kk].astype(np.int64)
+    ee, jj = rows // cap, rows % cap
+    np.testing.assert_array_equal(r["src_info"].view(-1).cpu().numpy()[rows], tt % M)
+    rows_d = torch.from_numpy(rows).to(DEV)
+    got = r["out"].view(E * cap, -1)[rows_d].cpu().numpy()
+    np.testing.assert_array_equal(got, q[tt])
+    got_s = r["out_scale"][torch.from_numpy(ee).to(DEV), :, torch.from_numpy(jj).to(DEV)]
+    np.testing.assert_array_equal(got_s.cpu().numpy().view(np.uint32), sc[tt].view(np.uint32))
+    # rows past recv_count stay untouched
+    rc = ref["recv_count"]
+    rng = np.random.default_rng(0)
+    free = [(e, j) for e in rng.permutation(E)[:untouched_sample] for j in (rc[e], cap - 1)
+            if j < cap and j >= rc[e]]
+    for e, j in free:
+        assert (r["out"][e, j] == POISON).all()
+        assert (r["src_info"][e, j:j + 1].view(torch.uint8) == POISON).all()
+    return r, ref
+
+
+def _topk(rng, T, K, E, drop=0.0):
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    if drop:
+        topk[rng.random(topk.shape) < drop] = -1
+    return topk
+
+
+def _x(rng, T, H, spread=True):
+    f = rng.standard_normal((T, H)).astype(np.float32)
+    if spread:   # groups of very different magnitude, and tiny values next to big ones
+        f *= np.exp2(rng.integers(-30, 30, (T, H // 128, 1))).repeat(128, axis=2).reshape(T, H)
+        f[:, ::37] *= 1e-4
+    return workloads.fp32_to_bf16_bits(f)
+
+
+def test_dsv3_ll_full_size():
+    """The DeepSeek-V3-shaped batch as 32 segments of 128 tokens, every
+    expert's rectangle sized for the worst case (4096 rows)."""
+    w = workloads.get("dsv3_ll")
+    inp = workloads.make_inputs(w)
+    M = w.ll_segment
+    check_ll(inp["topk_idx"], inp["x"], w.num_experts, M, w.num_tokens)
+
+
+LL_CASES = [
+    # (name, segments, M, K, E, H, cap, drop)
+    ("ragged_m7", 6, 7, 4, 12, 256, 42, 0.2),
+    ("h128", 5, 32, 3, 16, 128, 160, 0.0),
+    ("h9216_two_passes", 4, 16, 2, 8, 9216, 64, 0.1),
+    ("k1", 8, 64, 1, 32, 512, 512, 0.0),
+    ("prime_m", 3, 127, 8, 64, 256, 381, 0.05),
+    ("e1_all_one_expert", 4, 50, 2, 1, 256, 400, 0.3),
+]
+
+
+@pytest.mark.parametrize("case", LL_CASES, ids=[c[0] for c in LL_CASES])
+def test_ll_shapes(case):
+    name, nseg, M, K, E, H, cap, drop = case
+    rng = np.random.default_rng(hash(name) % (1 << 31))
+    T = nseg * M
+    topk = _topk(rng, T, K, E, drop) if K <= E else rng.integers(-1, E, (T, K)).astype(np.int64)
+    check_ll(topk, _x(rng, T, H), E, M, cap)
+
+
+def test_ll_receive_side_local_ids():
+    """One receiver's rectangle: local ids (8 experts), -1 elsewhere."""
+    w = workloads.get("dsv3_ll")
+    inp = workloads.make_inputs(w)
+    El, r = 8, 5
+    topk = inp["topk_idx"]
+    mine = (topk >= r * El) & (topk < (r + 1) * El)
+    local = np.ascontiguousarray(np.where(mine, topk - r * El, -1))
+    check_ll(local, inp["x"], El, w.ll_segment, w.num_tokens)
+
+
+def test_ll_overflow_is_flagged_and_keeps_the_first_rows():
+    rng = np.random.default_rng(3)
+    topk = _topk(rng, 256, 4, 8)
+    check_ll(topk, _x(rng, 256, 256), 8, 64, 100, expect_overflow=True)
+
+
+def test_ll_zero_tokens_and_all_invalid():
+    rng = np.random.default_rng(4)
+    check_ll(np.zeros((0, 4), np.int64), np.zeros((0, 256), np.uint16), 8, 16, 32)
+    check_ll(-np.ones((64, 4), np.int64), _x(rng, 64, 256), 8, 16, 32)
+
+
+def test_ll_zero_groups_and_exact_powers():
+    """All-zero groups (scale 0, codes 0), groups whose values are exact
+    powers of two (codes hit exact binary32 products), and a negative
+    group maximum."""
+    rng = np.random.default_rng(5)
+    T, H = 64, 512
+    f = rng.standard_normal((T, H)).astype(np.float32)
+    f[::3, :128] = 0.0
+    f[1::3, 128:256] = np.exp2(rng.integers(-10, 10, (len(range(1, T, 3)), 128))).astype(np.float32)
+    f[2::3, 256:384] = -np.abs(f[2::3, 256:384]) * 1000
+    x = workloads.fp32_to_bf16_bits(f)
+    check_ll(_topk(rng, T, 4, 16), x, 16, 16, 64)
+
+
+def test_ll_side_stream_and_repeat_is_deterministic():
+    rng = np.random.default_rng(6)
+    topk, x = _topk(rng, 512, 6, 32, 0.1), _x(rng, 512, 1024)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        a = gpu_ll(topk, x, 32, 128, 512, stream=s)
+        b = gpu_ll(topk, x, 32, 128, 512, stream=s)
+    s.synchronize()
+    for key in ("recv_count", "layout_range", "output_index"):
+        assert torch.equal(a[key], b[key]), key
+    oi = a["output_index"].view(-1)
+    rows = oi[oi >= 0].long()
+    assert torch.equal(a["out"].view(32 * 512, -1)[rows], b["out"].view(32 * 512, -1)[rows])
