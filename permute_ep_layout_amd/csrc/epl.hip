@@ -331,11 +331,13 @@ void launch_ll_scatter(const epl_problem &p, const WsLayout &w, int32_t M, int64
                        float *out_scale, int32_t *recv_count, int32_t *src_info,
                        int32_t *layout_range, int32_t *output_index, hipStream_t s)
 {
-    // one workgroup per token, and at least enough for the recv_count /
-    // layout_range entries (also when there are no tokens)
+    // kLLGrid workgroups striding over the tokens (fewer with fewer tokens),
+    // and at least enough for the recv_count / layout_range entries (also
+    // when there are no tokens)
     const int64_t entries = (int64_t)p.num_experts * std::max<int64_t>(1, p.num_tokens / M);
     const int64_t need = (entries + epl::kScatterThreads - 1) / epl::kScatterThreads;
-    const unsigned grid = row_grid(std::max<int64_t>(p.num_tokens, need), epl::kCombineGrid);
+    const unsigned grid =
+        row_grid(std::max<int64_t>(std::min<int64_t>(p.num_tokens, epl::kLLGrid), need), 1 << 30);
     hipLaunchKernelGGL(epl::ep_ll_scatter_kernel<VPT>, dim3(grid), dim3(epl::kScatterThreads), 0, s,
                        x, p.hidden, topk, at<const int32_t>(ws, w.block_count),
                        at<const int32_t>(ws, w.slot_rank), at<const int32_t>(ws, w.counts),
@@ -550,8 +552,8 @@ int epl_ll_dispatch(const epl_problem *p, int32_t tokens_per_segment, int64_t ro
                           workspace, s);
     if (rc != EPL_OK)
         return rc;
-    const int64_t nvec = p->hidden / 8;
-    const int vpt = (int)std::min<int64_t>(8, (nvec + epl::kScatterThreads - 1) / epl::kScatterThreads);
+    const int64_t npair = p->hidden / 16;     // 16 bf16 values per thread and step
+    const int vpt = (int)std::min<int64_t>(8, (npair + epl::kScatterThreads - 1) / epl::kScatterThreads);
     switch (std::max(vpt, 1)) {
 #define EPL_LL_CASE(V)                                                                             \
     case V:                                                                                        \

@@ -376,10 +376,12 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
     if (mode & kScanReduce) {
         if (tid == 0)
             s_err = 0;
-        const int P = E <= kScanThreads ? kScanThreads / E : 1;
+        // segments per column: enough to occupy the threads, but never more
+        // than there are blocks (each segment sum is later added serially)
+        const int P = (int)max((int64_t)1, min((int64_t)(E <= kScanThreads ? kScanThreads / E : 1), nb));
         const int64_t L = (nb + P - 1) / P;
         const int RC = R + Rn;      // rank columns, then node columns
-        const int PR = RC <= kScanThreads ? kScanThreads / RC : 1;
+        const int PR = (int)max((int64_t)1, min((int64_t)(RC <= kScanThreads ? kScanThreads / RC : 1), nb));
         const int64_t LR = (nb + PR - 1) / PR;
         // When every thread owns at most one segment of at most 16 blocks,
         // the segment stays in registers between the sum and the rewrite.
@@ -759,45 +761,68 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
 // ------------------------------------------- low-latency fixed rectangle --
 
 // e4m3 (OCP "fn": bias 7, max 448, no infinities) of a binary32 value, round
-// to nearest even; magnitudes that round above 448 give 448. Normal results
-// (|p| >= 2^-6) round the 23-bit mantissa to 3 bits on the bit pattern (a
-// carry moves into the exponent as it should), then rebias the exponent
-// from 127 to 7; smaller magnitudes are multiples of 2^-9, rounded with
-// rint (which may give 8 = 2^-6, the smallest normal code).
+// to nearest even; magnitudes that round above 448 give 448. Both cases are
+// computed and one is selected (no divergent branch per element): normal
+// results (|p| >= 2^-6) round the 23-bit mantissa to 3 bits on the bit
+// pattern (a carry moves into the exponent as it should) and rebias the
+// exponent from 127 to 7; smaller magnitudes are multiples of 2^-9, rounded
+// with rint (which may give 8 = 2^-6, the smallest normal code).
 __device__ __forceinline__ uint32_t e4m3_rne(float p)
 {
     const uint32_t u = __float_as_uint(p);
-    const uint32_t sign = (u >> 24) & 0x80u;
     const uint32_t a = u & 0x7FFFFFFFu;
-    uint32_t code;
-    if (a >= 0x3C800000u) {                       // 2^-6
-        const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-        code = (r >> 20) - (120u << 3);           // exponent 127 -> 7
-        code = code > 0x7Eu ? 0x7Eu : code;
-    } else {
-        code = (uint32_t)rintf(__uint_as_float(a) * 512.0f);
-    }
-    return sign | code;
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    const uint32_t normal = min((r >> 20) - (120u << 3), 0x7Eu);      // exponent 127 -> 7
+    const uint32_t sub = (uint32_t)rintf(__uint_as_float(a) * 512.0f); // multiples of 2^-9
+    return ((u >> 24) & 0x80u) | (a >= 0x3C800000u ? normal : sub);    // 2^-6
 }
+
+// Maximum over the 8 lanes of a half DPP row (lanes 8m .. 8m+7), returned
+// to every one of them: mirror within the half row (lane i meets lane 7-i,
+// so each quad then holds all four pair maxima), then two quad permutes.
+__device__ __forceinline__ float half_row_max(float v)
+{
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    return v;
+}
+
+// e4m3 codes of 4 binary32 values packed little-endian into a word.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d)
+{
+    return e4m3_rne(a) | (e4m3_rne(b) << 8) | (e4m3_rne(c) << 16) | (e4m3_rne(d) << 24);
+}
+
+#ifndef EPL_LL_GRID
+#define EPL_LL_GRID 2048
+#endif
+constexpr int kLLGrid = EPL_LL_GRID;
 
 // Strategy A (a fixed rectangle, no count exchange) in the shape of the
 // low-latency receive buffers: expert e owns rows [e * cap, (e + 1) * cap)
 // of the FP8 buffer; its slots fill them from the first in (token, k)
 // order, j = block offset + in-block rank (the same per-expert position as
-// the prefix-sum layout, without the prefix over experts). One workgroup per
-// token (grid-stride): the first K threads place the token's slots
-// (output_index = e * cap + j, src_info[row] = t mod M, or -1 past the
-// rectangle, with the capacity bit in the status word), then, if any slot
-// was placed, all threads cast the bf16 row to e4m3 one 128-column group at
-// a time: the group's 16 vectors of 8 values sit on 16 neighbouring lanes,
-// which reduce |x| to amax with xor shuffles; scale = amax / 448 and
-// codes = e4m3(x * (448 / amax)) (zero codes for an all-zero group). The
-// 8-byte code vectors are stored to every placed row with non-temporal
-// stores and each group's scale to out_scale[(e * S + g) * cap + j]
-// (column-major per expert). Before its tokens every workgroup also writes
-// a share of recv_count and layout_range (begin, count per expert and
-// source segment of M tokens), read off the per-block offsets: blocks of B
-// tokens with B dividing M, so segment s starts at block s * M / B.
+// the prefix-sum layout, without the prefix over experts).
+//
+// Workgroups stride over the tokens (XCD-aware ranges), one token ahead:
+// while a token is cast and stored, its workgroup already loads the next
+// token's row (if that token selects any expert) and the first K threads
+// place the next token's slots (output_index = e * cap + j, src_info[row] =
+// t mod M, or -1 past the rectangle with the capacity bit in the status
+// word); the placements reach the other threads through a double-buffered
+// LDS table and one LDS-only barrier per token. A thread owns 16
+// consecutive values of the row (two 16-byte loads) per step, so a
+// 128-column group spans the 8 lanes of a half DPP row, which reduce |x|
+// to amax with lane permutes; scale = amax / 448 and codes = e4m3(x *
+// (448 / amax)) (zero codes for an all-zero group). Each thread's 16 codes
+// go to every placed row as one 16-byte non-temporal store, and each
+// group's scale to out_scale[(e * S + g) * cap + j] (column-major per
+// expert). Before its tokens every workgroup also writes a share of
+// recv_count and layout_range (begin, count per expert and source segment
+// of M tokens), read off the per-block offsets: blocks of B tokens with B
+// dividing M, so segment s starts at block s * M / B. VPT = steps of 16
+// values per thread per pass over the row.
 template <int VPT>
 __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
     const uint16_t *__restrict__ x, int H, const int64_t *__restrict__ topk,
@@ -811,7 +836,7 @@ __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
     __shared__ int32_t s_j[2][kMaxTopk];      // row within the expert's block
     const int tid = threadIdx.x;
     const int S = H / 128;
-    const int nvec = H / 8;                   // 16-byte vectors of 8 bf16 values
+    const int npair = H / 16;                 // pairs of 16-byte vectors: 16 bf16 values
 
     // recv_count and layout_range
     {
@@ -833,85 +858,124 @@ __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
         }
     }
 
+    // slot `tid` of token t: place it and publish (expert, row) in the table
+    auto place = [&](int64_t t, int32_t *se, int32_t *sj) {
+        const int64_t e = topk[t * K + tid];
+        int32_t pe = -1, pj = 0, oi = -1;
+        if (e >= 0 && e < E) {
+            const uint32_t tu = (uint32_t)t;   // T * K <= INT32_MAX
+            const int64_t j = (int64_t)block_base[(int64_t)(tu / (uint32_t)B) * E + e] +
+                              slot_rank[t * K + tid];
+            if (j < cap) {
+                const int64_t row = e * cap + j;
+                pe = (int32_t)e;
+                pj = (int32_t)j;
+                oi = (int32_t)row;
+                src_info[row] = (int32_t)(tu % (uint32_t)M);
+            } else {
+                atomicOr(status, kStatusCapacity);
+            }
+        }
+        output_index[t * K + tid] = oi;
+        se[tid] = pe;
+        sj[tid] = pj;
+    };
+    // whether token t has a slot at all (uniform: every wave reads the ids)
+    auto has_slot = [&](int64_t t) {
+        bool any = false;
+        for (int k = 0; k < K; ++k) {
+            const int64_t e = topk[t * K + k];
+            any |= e >= 0 && e < E;
+        }
+        return any;
+    };
+    // pass `base` (in pairs) of token t's row
+    auto load_row = [&](int64_t t, int base, u32x4 (*v)[2]) {
+        const u32x4 *xrow = reinterpret_cast<const u32x4 *>(x + t * (int64_t)H);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int pi = base + i * kScatterThreads + tid;
+            if (pi < npair) {
+                v[i][0] = __builtin_nontemporal_load(xrow + 2 * pi);
+                v[i][1] = __builtin_nontemporal_load(xrow + 2 * pi + 1);
+            }
+        }
+    };
+
     const TokenRange tr = token_range(T);
+    const bool lead = tid < K;
+    u32x4 v[VPT][2], vn[VPT][2];
+    bool any = false;
+    if (tr.first < tr.end) {
+        if (lead)
+            place(tr.first, s_e[0], s_j[0]);
+        any = has_slot(tr.first);
+        if (any)
+            load_row(tr.first, 0, v);
+    }
     int it = 0;
     for (int64_t t = tr.first; t < tr.end; t += tr.stride, ++it) {
-        int32_t *se = s_e[it & 1], *sj = s_j[it & 1];
-        if (tid < K) {
-            const int64_t e = topk[t * K + tid];
-            int32_t pe = -1, pj = 0, oi = -1;
-            if (e >= 0 && e < E) {
-                const int64_t j = (int64_t)block_base[(t / B) * E + e] + slot_rank[t * K + tid];
-                if (j < cap) {
-                    const int64_t row = e * cap + j;
-                    pe = (int32_t)e;
-                    pj = (int32_t)j;
-                    oi = (int32_t)row;
-                    src_info[row] = (int32_t)(t % M);
-                } else {
-                    atomicOr(status, kStatusCapacity);
-                }
-            }
-            output_index[t * K + tid] = oi;
-            se[tid] = pe;
-            sj[tid] = pj;
-        }
         lds_barrier();
-        bool any = false;
-        for (int k = 0; k < K; ++k)
-            any |= se[k] >= 0;
-        if (!any)
-            continue;
+        const int32_t *se = s_e[it & 1], *sj = s_j[it & 1];
+        // the next token: its row loads and its placements overlap this
+        // token's cast and stores
+        const int64_t tn = t + tr.stride;
+        const bool any_next = tn < tr.end && has_slot(tn);
+        if (any_next)
+            load_row(tn, 0, vn);
+        if (lead && tn < tr.end)
+            place(tn, s_e[(it + 1) & 1], s_j[(it + 1) & 1]);
 
-        const u32x4 *xrow = reinterpret_cast<const u32x4 *>(x + t * (int64_t)H);
-        for (int base = 0; base < nvec; base += kScatterThreads * VPT) {
-            u32x4 v[VPT];
+        for (int base = 0; any;) {
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
-                const int idx = base + i * kScatterThreads + tid;
-                if (idx < nvec)
-                    v[i] = __builtin_nontemporal_load(xrow + idx);
-            }
-#pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                const int idx = base + i * kScatterThreads + tid;
-                if (idx >= nvec)      // whole 16-lane groups drop out together (nvec % 16 == 0)
+                const int pi = base + i * kScatterThreads + tid;
+                if (pi >= npair)      // whole 8-lane groups drop out together (npair % 8 == 0)
                     continue;
-                float f[8];
+                float f[16];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    f[2 * q] = __uint_as_float(v[i][q] << 16);
-                    f[2 * q + 1] = __uint_as_float(v[i][q] & 0xFFFF0000u);
+                for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        f[8 * h + 2 * q] = __uint_as_float(v[i][h][q] << 16);
+                        f[8 * h + 2 * q + 1] = __uint_as_float(v[i][h][q] & 0xFFFF0000u);
+                    }
                 }
                 float amax = 0.0f;
 #pragma unroll
-                for (int q = 0; q < 8; ++q)
+                for (int q = 0; q < 16; ++q)
                     amax = fmaxf(amax, fabsf(f[q]));
-#pragma unroll
-                for (int d = 1; d < 16; d <<= 1)
-                    amax = fmaxf(amax, __shfl_xor(amax, d, kWave));
+                amax = half_row_max(amax);
                 const float scale = amax / 448.0f;
                 const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
-                uint32_t w0 = 0, w1 = 0;
+                u32x4 codes;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    w0 |= e4m3_rne(f[q] * inv) << (8 * q);
-                    w1 |= e4m3_rne(f[4 + q] * inv) << (8 * q);
-                }
-                const u32x2 codes = {w0, w1};
-                const int g = idx / 16;
+                for (int q = 0; q < 4; ++q)
+                    codes[q] = e4m3x4(f[4 * q] * inv, f[4 * q + 1] * inv, f[4 * q + 2] * inv,
+                                      f[4 * q + 3] * inv);
+                const int g = pi / 8;
                 for (int k = 0; k < K; ++k) {
                     const int e = se[k];
                     if (e < 0)
                         continue;
                     const int64_t j = sj[k];
                     const int64_t row = (int64_t)e * cap + j;
-                    __builtin_nontemporal_store(codes, reinterpret_cast<u32x2 *>(out + row * H) + idx);
-                    if ((tid & 15) == 0)
+                    __builtin_nontemporal_store(codes, reinterpret_cast<u32x4 *>(out + row * H) + pi);
+                    if ((tid & 7) == 0)
                         out_scale[((int64_t)e * S + g) * cap + j] = scale;
                 }
             }
+            base += kScatterThreads * VPT;
+            if (base >= npair)
+                break;
+            load_row(t, base, v);
         }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            v[i][0] = vn[i][0];
+            v[i][1] = vn[i][1];
+        }
+        any = any_next;
     }
 }
 

@@ -111,7 +111,8 @@ LL_CASES = [
     # (name, segments, M, K, E, H, cap, drop)
     ("ragged_m7", 6, 7, 4, 12, 256, 42, 0.2),
     ("h128", 5, 32, 3, 16, 128, 160, 0.0),
-    ("h9216_two_passes", 4, 16, 2, 8, 9216, 64, 0.1),
+    ("h9216", 4, 16, 2, 8, 9216, 64, 0.1),
+    ("h16512_two_passes", 4, 16, 2, 8, 16512, 64, 0.1),
     ("k1", 8, 64, 1, 32, 512, 512, 0.0),
     ("prime_m", 3, 127, 8, 64, 256, 381, 0.05),
     ("e1_all_one_expert", 4, 50, 2, 1, 256, 400, 0.3),
