@@ -77,6 +77,13 @@ bool fp8_problem_ok(const epl_problem *p, int scale_format)
     return (scale_format == EPL_SCALE_F32 || scale_format == EPL_SCALE_UE8M0) && p->scale_cols > 0;
 }
 
+#ifndef EPL_LAYOUT_BLOCKS
+#define EPL_LAYOUT_BLOCKS 64       // blocks the layout aims for
+#endif
+#ifndef EPL_LAYOUT_MIN_TOKENS
+#define EPL_LAYOUT_MIN_TOKENS 16   // smallest block
+#endif
+
 // Tokens per layout block: enough blocks to spread the work (about 64), but
 // at most 256 tokens (one per thread) and at most 2048 slots (the LDS key
 // buffer), and at least 16 tokens so the per-block count matrix stays small.
@@ -87,8 +94,8 @@ int layout_block_tokens(const epl_problem &p)
     const size_t fixed =
         epl::layout_lds_bytes(0, p.num_topk, p.num_experts, p.num_ranks + nodes_of(p));
     cap = std::min<int64_t>(cap, (int64_t)((epl::kLayoutLdsBytes - fixed) / (8 * (size_t)p.num_topk)));
-    int64_t want = (p.num_tokens + 63) / 64;
-    want = std::max<int64_t>(16, want);
+    int64_t want = (p.num_tokens + EPL_LAYOUT_BLOCKS - 1) / EPL_LAYOUT_BLOCKS;
+    want = std::max<int64_t>(EPL_LAYOUT_MIN_TOKENS, want);
     return (int)std::max<int64_t>(1, std::min<int64_t>(want, cap));
 }
 
@@ -593,14 +600,17 @@ int epl_combine(const epl_problem *p, const uint16_t *expert_out, int64_t expert
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint32_t *status = workspace ? &at<WsHeader>(workspace, 0)->status : nullptr;
     const dim3 grid(row_grid(p->num_tokens, epl::kCombineGrid));
+    const int64_t y_bytes = p->num_tokens * (int64_t)p->hidden * (out_dtype == EPL_OUT_BF16 ? 2 : 4);
+    const bool y_nt = y_bytes > epl::kYNtBytes;
+    auto launch = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(epl::kCombineThreads), 0, s, expert_out, expert_rows,
+                           output_index, topk_weights, p->num_tokens, p->num_topk, p->hidden, y,
+                           status);
+    };
     if (out_dtype == EPL_OUT_BF16)
-        hipLaunchKernelGGL(epl::ep_combine_kernel<true>, grid, dim3(epl::kCombineThreads), 0, s,
-                           expert_out, expert_rows, output_index, topk_weights, p->num_tokens,
-                           p->num_topk, p->hidden, y, status);
+        y_nt ? launch(epl::ep_combine_kernel<true, true>) : launch(epl::ep_combine_kernel<true, false>);
     else
-        hipLaunchKernelGGL(epl::ep_combine_kernel<false>, grid, dim3(epl::kCombineThreads), 0, s,
-                           expert_out, expert_rows, output_index, topk_weights, p->num_tokens,
-                           p->num_topk, p->hidden, y, status);
+        y_nt ? launch(epl::ep_combine_kernel<false, true>) : launch(epl::ep_combine_kernel<false, false>);
     return launch_status();
 }
 

@@ -511,6 +511,13 @@ constexpr int kScatterGrid = EPL_SCATTER_GRID;
 constexpr int64_t kScatterGridFrom = EPL_SCATTER_GRID_FROM;
 constexpr int kCombineGrid = EPL_COMBINE_GRID;
 
+// Combine outputs above this size (half of MI355X's 256 MB Infinity Cache)
+// are written with non-temporal stores.
+#ifndef EPL_Y_NT_BYTES
+#define EPL_Y_NT_BYTES (128ll << 20)
+#endif
+constexpr int64_t kYNtBytes = EPL_Y_NT_BYTES;
+
 #ifndef EPL_XCD_MAP
 #define EPL_XCD_MAP 1
 #endif
@@ -1012,6 +1019,21 @@ __device__ __forceinline__ void fma_bf16x8(float *acc, float w, const u32x4 &v)
 
 constexpr int kCombineUnroll = EPL_COMBINE_UNROLL;   // column vectors per thread per pass
 
+// The combine's output rows: write-back stores while y fits comfortably in
+// the Infinity Cache (the host decides, see kYNtBytes), so the step that
+// follows finds them there; non-temporal stores for a larger y, which would
+// only be evicted again and drain during the next kernels.
+// (A template parameter, not a run-time flag: the compiler would merge the
+// two stores of a run-time branch into one plain store.)
+template <bool NT, typename V>
+__device__ __forceinline__ void store_y(V *dst, const V &v)
+{
+    if (NT)
+        __builtin_nontemporal_store(v, dst);
+    else
+        *dst = v;
+}
+
 // One workgroup per token (grid-stride over tokens): y[t] = sum over valid k
 // (ascending) of w[t,k] * expert_out[output_index[t,k]], fp32 accumulation.
 // Each thread owns kCombineUnroll 8-column vectors per pass and issues the
@@ -1020,7 +1042,7 @@ constexpr int kCombineUnroll = EPL_COMBINE_UNROLL;   // column vectors per threa
 // are read once, so the loads are non-temporal. The first wave fetches the
 // next token's output_index / weights while the current token streams; the
 // compacted slot table is double-buffered in LDS (see ep_scatter_kernel).
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool Y_NT>
 __global__ __launch_bounds__(kCombineThreads) void ep_combine_kernel(
     const uint16_t *__restrict__ expert_out, int64_t rows, const int32_t *__restrict__ oi,
     const float *__restrict__ w, int64_t T, int K, int H, void *__restrict__ y,
@@ -1108,11 +1130,11 @@ __global__ __launch_bounds__(kCombineThreads) void ep_combine_kernel(
                 if (OUT_BF16) {
                     u32x4 o = {pack_bf16x2(acc[u][0], acc[u][1]), pack_bf16x2(acc[u][2], acc[u][3]),
                                pack_bf16x2(acc[u][4], acc[u][5]), pack_bf16x2(acc[u][6], acc[u][7])};
-                    reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(y) + t * H)[idx] = o;
+                    store_y<Y_NT>(reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(y) + t * H) + idx, o);
                 } else {
                     f32x4 *yr = reinterpret_cast<f32x4 *>(static_cast<float *>(y) + t * H) + 2 * idx;
-                    yr[0] = f32x4{acc[u][0], acc[u][1], acc[u][2], acc[u][3]};
-                    yr[1] = f32x4{acc[u][4], acc[u][5], acc[u][6], acc[u][7]};
+                    store_y<Y_NT>(yr, f32x4{acc[u][0], acc[u][1], acc[u][2], acc[u][3]});
+                    store_y<Y_NT>(yr + 1, f32x4{acc[u][4], acc[u][5], acc[u][6], acc[u][7]});
                 }
             }
         }
