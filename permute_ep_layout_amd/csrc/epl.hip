@@ -601,16 +601,27 @@ int epl_combine(const epl_problem *p, const uint16_t *expert_out, int64_t expert
     uint32_t *status = workspace ? &at<WsHeader>(workspace, 0)->status : nullptr;
     const dim3 grid(row_grid(p->num_tokens, epl::kCombineGrid));
     const int64_t y_bytes = p->num_tokens * (int64_t)p->hidden * (out_dtype == EPL_OUT_BF16 ? 2 : 4);
+    // A y that stays in the caches (a batch of a few thousand tokens) goes
+    // faster with 256 threads per token; a large y streamed past the caches
+    // (large or sparse batches) with 128.
     const bool y_nt = y_bytes > epl::kYNtBytes;
-    auto launch = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, grid, dim3(epl::kCombineThreads), 0, s, expert_out, expert_rows,
+    auto launch = [&](auto kernel, int threads) {
+        hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, s, expert_out, expert_rows,
                            output_index, topk_weights, p->num_tokens, p->num_topk, p->hidden, y,
                            status);
     };
-    if (out_dtype == EPL_OUT_BF16)
-        y_nt ? launch(epl::ep_combine_kernel<true, true>) : launch(epl::ep_combine_kernel<true, false>);
-    else
-        y_nt ? launch(epl::ep_combine_kernel<false, true>) : launch(epl::ep_combine_kernel<false, false>);
+    constexpr int tn = epl::kCombineThreads, tc = epl::kCombineThreadsCached;
+    if (out_dtype == EPL_OUT_BF16) {
+        if (y_nt)
+            launch(epl::ep_combine_kernel<true, true, tn>, tn);
+        else
+            launch(epl::ep_combine_kernel<true, false, tc>, tc);
+    } else {
+        if (y_nt)
+            launch(epl::ep_combine_kernel<false, true, tn>, tn);
+        else
+            launch(epl::ep_combine_kernel<false, false, tc>, tc);
+    }
     return launch_status();
 }
 

@@ -45,7 +45,10 @@ constexpr int kRowThreads = 128;          // expert-scale workgroup
 #define EPL_SCATTER_THREADS 128
 #endif
 #ifndef EPL_COMBINE_THREADS
-#define EPL_COMBINE_THREADS 128
+#define EPL_COMBINE_THREADS 128      // when y is written past the caches
+#endif
+#ifndef EPL_COMBINE_THREADS_CACHED
+#define EPL_COMBINE_THREADS_CACHED 256   // when y stays in the caches
 #endif
 #ifndef EPL_COMBINE_UNROLL
 #define EPL_COMBINE_UNROLL 2
@@ -61,6 +64,7 @@ constexpr int kRowThreads = 128;          // expert-scale workgroup
 #endif
 constexpr int kScatterThreads = EPL_SCATTER_THREADS;
 constexpr int kCombineThreads = EPL_COMBINE_THREADS;
+constexpr int kCombineThreadsCached = EPL_COMBINE_THREADS_CACHED;
 
 // Status word bits (workspace header).
 constexpr uint32_t kStatusBadExpert = 1u;      // topk id outside [-1, E)
@@ -1019,6 +1023,17 @@ __device__ __forceinline__ void fma_bf16x8(float *acc, float w, const u32x4 &v)
 
 constexpr int kCombineUnroll = EPL_COMBINE_UNROLL;   // column vectors per thread per pass
 
+#ifndef EPL_COMBINE_LOAD_NT
+#define EPL_COMBINE_LOAD_NT 1
+#endif
+// The gathered expert-output rows are read once: non-temporal loads.
+__device__ __forceinline__ u32x4 load_row_vec(const u32x4 *p)
+{
+    if (EPL_COMBINE_LOAD_NT)
+        return __builtin_nontemporal_load(p);
+    return *p;
+}
+
 // The combine's output rows: write-back stores while y fits comfortably in
 // the Infinity Cache (the host decides, see kYNtBytes), so the step that
 // follows finds them there; non-temporal stores for a larger y, which would
@@ -1042,8 +1057,8 @@ __device__ __forceinline__ void store_y(V *dst, const V &v)
 // are read once, so the loads are non-temporal. The first wave fetches the
 // next token's output_index / weights while the current token streams; the
 // compacted slot table is double-buffered in LDS (see ep_scatter_kernel).
-template <bool OUT_BF16, bool Y_NT>
-__global__ __launch_bounds__(kCombineThreads) void ep_combine_kernel(
+template <bool OUT_BF16, bool Y_NT, int THREADS>
+__global__ __launch_bounds__(THREADS) void ep_combine_kernel(
     const uint16_t *__restrict__ expert_out, int64_t rows, const int32_t *__restrict__ oi,
     const float *__restrict__ w, int64_t T, int K, int H, void *__restrict__ y,
     uint32_t *__restrict__ status)
@@ -1097,7 +1112,7 @@ __global__ __launch_bounds__(kCombineThreads) void ep_combine_kernel(
         const int64_t *srow = s_row[buf];
         const float *sw = s_w[buf];
 
-        for (int base = tid; base < nvec; base += kCombineThreads * U) {
+        for (int base = tid; base < nvec; base += THREADS * U) {
             float acc[U][8];
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -1108,11 +1123,11 @@ __global__ __launch_bounds__(kCombineThreads) void ep_combine_kernel(
                 u32x4 v[U][8];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int idx = base + u * kCombineThreads;
+                    const int idx = base + u * THREADS;
 #pragma unroll
                     for (int j = 0; j < 8; ++j)
                         if (g + j < n && idx < nvec)
-                            v[u][j] = __builtin_nontemporal_load(
+                            v[u][j] = load_row_vec(
                                 reinterpret_cast<const u32x4 *>(expert_out + srow[g + j] * H) + idx);
                 }
 #pragma unroll
@@ -1124,7 +1139,7 @@ __global__ __launch_bounds__(kCombineThreads) void ep_combine_kernel(
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int idx = base + u * kCombineThreads;
+                const int idx = base + u * THREADS;
                 if (idx >= nvec)
                     continue;
                 if (OUT_BF16) {
