@@ -26,6 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace epl {
 
 constexpr int kWave = 64;
@@ -1009,25 +1011,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
-__device__ __forceinline__ void fma_bf16x8(float *acc, float w, const u32x4 &v)
-{
-    acc[0] = fmaf(w, bf16_lo(v.x), acc[0]);
-    acc[1] = fmaf(w, bf16_hi(v.x), acc[1]);
-    acc[2] = fmaf(w, bf16_lo(v.y), acc[2]);
-    acc[3] = fmaf(w, bf16_hi(v.y), acc[3]);
-    acc[4] = fmaf(w, bf16_lo(v.z), acc[4]);
-    acc[5] = fmaf(w, bf16_hi(v.z), acc[5]);
-    acc[6] = fmaf(w, bf16_lo(v.w), acc[6]);
-    acc[7] = fmaf(w, bf16_hi(v.w), acc[7]);
-}
-
 constexpr int kCombineUnroll = EPL_COMBINE_UNROLL;   // column vectors per thread per pass
 
 #ifndef EPL_COMBINE_LOAD_NT
 #define EPL_COMBINE_LOAD_NT 1
 #endif
 // The gathered expert-output rows are read once: non-temporal loads.
-__device__ __forceinline__ u32x4 load_row_vec(const u32x4 *p)
+template <typename V>
+__device__ __forceinline__ V load_row_vec(const V *p)
 {
     if (EPL_COMBINE_LOAD_NT)
         return __builtin_nontemporal_load(p);
@@ -1067,7 +1058,6 @@ __global__ __launch_bounds__(THREADS) void ep_combine_kernel(
     __shared__ float s_w[2][kMaxTopk];
     __shared__ int s_n[2];
     const int tid = threadIdx.x;
-    const int nvec = H >> 3;
     const TokenRange tr = token_range(T);
     const int64_t step = tr.stride, t_end = tr.end;
     constexpr int U = kCombineUnroll;
@@ -1112,44 +1102,60 @@ __global__ __launch_bounds__(THREADS) void ep_combine_kernel(
         const int64_t *srow = s_row[buf];
         const float *sw = s_w[buf];
 
-        for (int base = tid; base < nvec; base += THREADS * U) {
-            float acc[U][8];
+        // Column units: 8 columns (16-byte loads) for a bf16 y, whose 8
+        // outputs are again 16 bytes; 4 columns (8-byte loads) for an fp32 y,
+        // so that each 16-byte store of 4 outputs sits next to its
+        // neighbour lane's and a store instruction covers one contiguous
+        // span (8 columns per lane would leave every other 16 bytes of a
+        // span to a second instruction, which non-temporal stores write to
+        // memory as partial lines).
+        constexpr int CW = OUT_BF16 ? 8 : 4;
+        constexpr int UU = OUT_BF16 ? U : 2 * U;
+        using In = typename std::conditional<CW == 8, u32x4, u32x2>::type;
+        const int nunit = H / CW;
+        for (int base = tid; base < nunit; base += THREADS * UU) {
+            float acc[UU][CW];
 #pragma unroll
-            for (int u = 0; u < U; ++u)
+            for (int u = 0; u < UU; ++u)
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
+                for (int j = 0; j < CW; ++j)
                     acc[u][j] = 0.0f;
             for (int g = 0; g < n; g += 8) {
-                u32x4 v[U][8];
+                In v[UU][8];
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
+                for (int u = 0; u < UU; ++u) {
                     const int idx = base + u * THREADS;
 #pragma unroll
                     for (int j = 0; j < 8; ++j)
-                        if (g + j < n && idx < nvec)
+                        if (g + j < n && idx < nunit)
                             v[u][j] = load_row_vec(
-                                reinterpret_cast<const u32x4 *>(expert_out + srow[g + j] * H) + idx);
+                                reinterpret_cast<const In *>(expert_out + srow[g + j] * H) + idx);
                 }
 #pragma unroll
-                for (int u = 0; u < U; ++u)
+                for (int u = 0; u < UU; ++u)
 #pragma unroll
                     for (int j = 0; j < 8; ++j)
-                        if (g + j < n)
-                            fma_bf16x8(acc[u], sw[g + j], v[u][j]);
+                        if (g + j < n) {
+                            const float wj = sw[g + j];
+#pragma unroll
+                            for (int q = 0; q < CW / 2; ++q) {
+                                acc[u][2 * q] = fmaf(wj, bf16_lo(v[u][j][q]), acc[u][2 * q]);
+                                acc[u][2 * q + 1] = fmaf(wj, bf16_hi(v[u][j][q]), acc[u][2 * q + 1]);
+                            }
+                        }
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+            for (int u = 0; u < UU; ++u) {
                 const int idx = base + u * THREADS;
-                if (idx >= nvec)
+                if (idx >= nunit)
                     continue;
                 if (OUT_BF16) {
                     u32x4 o = {pack_bf16x2(acc[u][0], acc[u][1]), pack_bf16x2(acc[u][2], acc[u][3]),
                                pack_bf16x2(acc[u][4], acc[u][5]), pack_bf16x2(acc[u][6], acc[u][7])};
                     store_y<Y_NT>(reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(y) + t * H) + idx, o);
                 } else {
-                    f32x4 *yr = reinterpret_cast<f32x4 *>(static_cast<float *>(y) + t * H) + 2 * idx;
-                    store_y<Y_NT>(yr, f32x4{acc[u][0], acc[u][1], acc[u][2], acc[u][3]});
-                    store_y<Y_NT>(yr + 1, f32x4{acc[u][4], acc[u][5], acc[u][6], acc[u][7]});
+                    store_y<Y_NT>(reinterpret_cast<f32x4 *>(static_cast<float *>(y) + t * H) + idx,
+                                  f32x4{acc[u][0], acc[u][1], acc[u][2], acc[u][3]});
                 }
             }
         }
