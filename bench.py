@@ -35,6 +35,71 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# ---------------------------------------------------------------- timing --
+#
+# Timing markers are HIP events created with hipEventDisableSystemFence. A
+# default event record ends with a system-scope release, which writes back and
+# invalidates the GPU's caches: on MI355X that stalled the next kernel by
+# about 5.6 us after each big kernel, an artefact of the measurement (a
+# dispatch -> combine chain on one stream needs no system-scope fence).
+
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+_HIP = None
+
+
+def hip_runtime():
+    """The HIP runtime library that torch (and libepl.so) already use."""
+    global _HIP
+    if _HIP is None:
+        import ctypes
+
+        import torch  # noqa: F401  (loads the runtime)
+
+        path = next(line.split()[-1] for line in open("/proc/self/maps")
+                    if "libamdhip64" in line)
+        lib = ctypes.CDLL(path)
+        vp = ctypes.c_void_p
+        lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+        lib.hipEventRecord.argtypes = [vp, vp]
+        lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        lib.hipEventDestroy.argtypes = [vp]
+        _HIP = lib
+    return _HIP
+
+
+class Event:
+    """A timing event (the subset of torch.cuda.Event used here)."""
+
+    def __init__(self):
+        import ctypes
+
+        self._h = ctypes.c_void_p()
+        rc = hip_runtime().hipEventCreateWithFlags(ctypes.byref(self._h),
+                                                   HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream=None):
+        import torch
+
+        s = stream if stream is not None else torch.cuda.current_stream()
+        if hip_runtime().hipEventRecord(self._h, s.cuda_stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to `end` (both must have completed)."""
+        import ctypes
+
+        ms = ctypes.c_float()
+        if hip_runtime().hipEventElapsedTime(ctypes.byref(ms), self._h, end._h) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def __del__(self):
+        if _HIP is not None and self._h:
+            _HIP.hipEventDestroy(self._h)
+
+
 def algorithmic_bytes(w, N, T_any, out_dtype_bytes=4, pad_rows=0):
     """Bytes each kernel must move (reads + writes), by its definition;
     alignment padding rows only get their m_indices entry. A row is 2H bytes
@@ -153,8 +218,8 @@ def run_ll(args, w, inp):
     torch.cuda.synchronize()
     if epl.epl_status(ws) != epl.EPL_OK or int(recv.sum()) != N:
         raise RuntimeError(f"low-latency dispatch failed: status {epl.epl_status(ws)}")
-    ev0 = torch.cuda.Event(enable_timing=True)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ev0 = Event()
+    evs = [(Event(), Event())
            for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
@@ -177,7 +242,7 @@ def run_ll(args, w, inp):
         flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         runs = []
         for i in range(args.warmup + 10):
-            evc = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            evc = [Event() for _ in range(4)]
             flush_buf.sum()
             evc[0].record(stream)
             dispatch_call()
@@ -478,8 +543,8 @@ def main():
     # stream the kernels run on (before combine, after combine): combine's
     # duration is measured exactly, and the interval from the previous step's
     # end to this step's combine is the dispatch (+ expert) part.
-    ev0 = torch.cuda.Event(enable_timing=True)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ev0 = Event()
+    evs = [(Event(), Event())
            for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
@@ -504,7 +569,7 @@ def main():
         # points (layout, scan, scatter, ...), an event around every launch.
         for _ in range(args.warmup):
             step_split()
-        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        sev = [[Event() for _ in range(len(names) + 1)]
                for _ in range(args.steps)]
         torch.cuda.synchronize()
         for i in range(args.steps):
@@ -522,8 +587,8 @@ def main():
         for mode in ("capacity", "exact"):
             gaps = []
             for _ in range(args.warmup + 10):
-                ev_a = torch.cuda.Event(enable_timing=True)
-                ev_b = torch.cuda.Event(enable_timing=True)
+                ev_a = Event()
+                ev_b = Event()
                 calls[0]()
                 calls[1]()
                 ev_a.record(stream)
@@ -551,7 +616,7 @@ def main():
         flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         cold = {"scatter": [], "combine": []}
         for i in range(args.warmup + 10):
-            evc = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            evc = [Event() for _ in range(4)]
             calls[0]()
             calls[1]()
             flush_buf.sum()
