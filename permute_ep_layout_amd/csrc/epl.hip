@@ -165,7 +165,9 @@ int enqueue_layout(const epl_problem &p, const WsLayout &w, const int64_t *topk,
                        epl::layout_lds_bytes(w.block_tokens, p.num_topk, p.num_experts,
                                              p.num_ranks + Rn),
                        s, topk, p.num_tokens, p.num_topk, p.num_experts, p.num_ranks,
-                       p.num_experts / p.num_ranks, p.ranks_per_node, Rn, w.block_tokens,
+                       p.num_experts / p.num_ranks, epl::div_magic(p.num_experts / p.num_ranks),
+                       p.ranks_per_node, epl::div_magic(std::max(p.ranks_per_node, 1)), Rn,
+                       w.block_tokens,
                        in_rank, vec16, at<int32_t>(ws, w.block_count), at<int32_t>(ws, w.block_rank),
                        at<uint32_t>(ws, w.block_err), at<int32_t>(ws, w.slot_rank));
     return launch_status();

@@ -93,7 +93,34 @@ __device__ __forceinline__ int lane_id()
     return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 }
 
+// Workgroup barrier that orders LDS accesses only. __syncthreads() also
+// orders global memory, which on CDNA makes every wave wait for all of its
+// outstanding global stores (they share the vmcnt counter with loads) before
+// the barrier. No kernel here hands data between its threads through global
+// memory (the outputs are read by later kernels), so every barrier is this
+// one: the row kernels keep their stores streaming across tokens, and the
+// layout and scan kernels do not wait for their own output stores (in the
+// layout, waiting for the token->rank mask stores had cost ~5 us).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // --------------------------------------------------------------- layout --
+
+// n / d for n, d < 2^16 without a division: the high word of n * magic with
+// magic = ceil(2^32 / d) (the error n * (magic - 2^32/d) / 2^32 < 2^-16 stays
+// below the 1/d distance to the next integer); d = 1 is the identity.
+__host__ __device__ inline uint32_t div_magic(uint32_t d)
+{
+    return d > 1 ? (uint32_t)((((uint64_t)1 << 32) + d - 1) / d) : 0u;
+}
+__device__ __forceinline__ int div_small(uint32_t n, int d, uint32_t magic)
+{
+    return d > 1 ? (int)__umulhi(n, magic) : (int)n;
+}
 
 // Writes the 0/1 bytes of `n` (<= 64) mask bits to dst; `vec16` says that
 // dst is 16-byte aligned and n is a multiple of 16.
@@ -136,7 +163,8 @@ __host__ __device__ constexpr size_t layout_lds_bytes(int B, int K, int E, int R
 // for an invalid slot.
 __global__ __launch_bounds__(kLayoutThreads) void ep_layout_kernel(
     const int64_t *__restrict__ topk, int64_t T, int K, int E, int R, int experts_per_rank,
-    int G, int Rn, int B, uint8_t *__restrict__ in_rank, bool in_rank_vec16,
+    uint32_t epr_magic, int G, uint32_t node_magic, int Rn, int B, uint8_t *__restrict__ in_rank,
+    bool in_rank_vec16,
     int32_t *__restrict__ block_count, int32_t *__restrict__ block_rank,
     uint32_t *__restrict__ block_err, int32_t *__restrict__ slot_rank)
 {
@@ -176,12 +204,12 @@ __global__ __launch_bounds__(kLayoutThreads) void ep_layout_kernel(
         const int64_t e = src[s];
         int packed = -1;
         if (e >= 0 && e < E)
-            packed = (int)e | (((int)e / experts_per_rank) << 16);
+            packed = (int)e | (div_small((uint32_t)e, experts_per_rank, epr_magic) << 16);
         else if (e != -1)
             bad = true;
         keys[s] = packed;
     }
-    __syncthreads();
+    lds_barrier();
     if (bad)
         atomicOr(reinterpret_cast<uint32_t *>(s_err), 1u);
 
@@ -230,54 +258,45 @@ __global__ __launch_bounds__(kLayoutThreads) void ep_layout_kernel(
         }
     }
 
-    // Token -> rank mask (one thread per token) and tokens per rank, one
-    // 64-rank window at a time; rank counts are summed with ballots.
-    {
-        const bool tok = tid < nt;
+    // Token -> rank mask (one thread per token), tokens per rank and tokens
+    // per node, one 64-wide window at a time. A token adds one to the count
+    // of each rank (node) in its mask: at most K LDS atomics per token (a
+    // ballot per rank had cost ~3.4 us at 32 ranks).
+    if (tid < nt) {
         for (int w0 = 0; w0 < R; w0 += 64) {
             const int wr = min(64, R - w0);
             uint64_t mask = 0;
-            if (tok) {
-                for (int k = 0; k < K; ++k) {
-                    const int packed = keys[tid * K + k];
-                    if (packed >= 0) {
-                        const int r = (packed >> 16) - w0;
-                        if (r >= 0 && r < wr)
-                            mask |= 1ull << r;
-                    }
+            for (int k = 0; k < K; ++k) {
+                const int packed = keys[tid * K + k];
+                if (packed >= 0) {
+                    const int r = (packed >> 16) - w0;
+                    if (r >= 0 && r < wr)
+                        mask |= 1ull << r;
                 }
-                if (in_rank)
-                    store_mask_bytes(in_rank + (t0 + tid) * R + w0, mask, wr, in_rank_vec16);
             }
-            for (int r = 0; r < wr; ++r) {
-                const uint64_t has = wave_ballot((mask >> r) & 1u);
-                if (lane == 0 && has)
-                    atomicAdd(&rank_cnt[w0 + r], __popcll(has));
-            }
+            if (in_rank)
+                store_mask_bytes(in_rank + (t0 + tid) * R + w0, mask, wr, in_rank_vec16);
+            for (uint64_t m = mask; m; m &= m - 1)
+                atomicAdd(&rank_cnt[w0 + __builtin_ctzll(m)], 1);
         }
-        // Tokens per node (G consecutive ranks), the same way: a token
-        // counts once for a node whichever of its ranks it reaches.
+        // a token counts once for a node (G consecutive ranks) whichever of
+        // its ranks it reaches; node = rank / G
         for (int n0 = 0; n0 < Rn; n0 += 64) {
             const int wn = min(64, Rn - n0);
             uint64_t mask = 0;
-            if (tok) {
-                for (int k = 0; k < K; ++k) {
-                    const int packed = keys[tid * K + k];
-                    if (packed >= 0) {
-                        const int n = (packed >> 16) / G - n0;
-                        if (n >= 0 && n < wn)
-                            mask |= 1ull << n;
-                    }
+            for (int k = 0; k < K; ++k) {
+                const int packed = keys[tid * K + k];
+                if (packed >= 0) {
+                    const int n = div_small((uint32_t)packed >> 16, G, node_magic) - n0;
+                    if (n >= 0 && n < wn)
+                        mask |= 1ull << n;
                 }
             }
-            for (int n = 0; n < wn; ++n) {
-                const uint64_t has = wave_ballot((mask >> n) & 1u);
-                if (lane == 0 && has)
-                    atomicAdd(&rank_cnt[R + n0 + n], __popcll(has));
-            }
+            for (uint64_t m = mask; m; m &= m - 1)
+                atomicAdd(&rank_cnt[R + n0 + __builtin_ctzll(m)], 1);
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // Per expert: exclusive prefix over the waves (in place) and block total.
     for (int e = tid; e < E; e += kLayoutThreads) {
@@ -291,7 +310,7 @@ __global__ __launch_bounds__(kLayoutThreads) void ep_layout_kernel(
     }
     for (int r = tid; r < RC; r += kLayoutThreads)
         block_rank[b * RC + r] = rank_cnt[r];
-    __syncthreads();
+    lds_barrier();
     if (tid == 0)
         block_err[b] = (uint32_t)*s_err;
 
@@ -316,7 +335,7 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int *s_wave)
     }
     if (lane == kWave - 1)
         s_wave[wave] = v;
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {
         constexpr int nw = kScanThreads / kWave;
         int x = lane < nw ? s_wave[lane] : 0;
@@ -328,7 +347,7 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int *s_wave)
         if (lane < nw)
             s_wave[lane] = x;
     }
-    __syncthreads();
+    lds_barrier();
     return v + (wave > 0 ? s_wave[wave - 1] : 0);
 }
 
@@ -416,7 +435,7 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
         uint32_t err = 0;
         for (int64_t bb = tid; bb < nb; bb += kScanThreads)
             err |= block_err[bb];
-        __syncthreads();
+        lds_barrier();
         if (err)
             atomicOr(&s_err, err);
         for (int e = tid; e < E; e += kScanThreads) {
@@ -442,7 +461,7 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
                 per_node[r - R] = run;
             }
         }
-        __syncthreads();
+        lds_barrier();
         // Rewrite block_count as the exclusive prefix over blocks.
         for (int col = tid; col < E * P; col += kScanThreads) {
             const int e = col % E, q = col / E;
@@ -479,7 +498,7 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
             s_cnt[e] = cnt[e];
             ws_counts[e] = s_cnt[e];
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     if (mode & kScanPrefix) {
@@ -554,18 +573,6 @@ __device__ __forceinline__ TokenRange token_range(int64_t T)
         return {xcd * per + w / kNumXcd, G / kNumXcd, min(T, (xcd + 1) * per)};
     }
     return {w, G, T};
-}
-
-// Workgroup barrier that orders LDS accesses only. __syncthreads() also
-// orders global memory, which on CDNA makes every wave wait for all of its
-// outstanding global stores (they share the vmcnt counter with loads) before
-// the barrier; the row kernels below only publish small LDS tables through
-// their barriers and must keep their row stores streaming across tokens.
-__device__ __forceinline__ void lds_barrier()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Scale rows are small (S floats): written back through L2 by default so that

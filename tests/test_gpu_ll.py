@@ -178,3 +178,39 @@ def test_ll_side_stream_and_repeat_is_deterministic():
     oi = a["output_index"].view(-1)
     rows = oi[oi >= 0].long()
     assert torch.equal(a["out"].view(32 * 512, -1)[rows], b["out"].view(32 * 512, -1)[rows])
+
+
+def test_ll_rows_feed_the_combine():
+    """The rectangle's output_index drives epl_combine over a bf16 [E*cap, H]
+    expert-output buffer (rows of the rectangle); the sums match the fp64
+    oracle within 1e-5 of sum |w v|."""
+    rng = np.random.default_rng(8)
+    nseg, M, K, E, H = 4, 64, 6, 16, 512
+    T, cap = nseg * M, nseg * M
+    topk = _topk(rng, T, K, E, 0.15)
+    x = _x(rng, T, H, spread=False)
+    wt = rng.uniform(0.05, 1.0, (T, K)).astype(np.float32)
+    r = gpu_ll(topk, x, E, M, cap)
+    oi = r["output_index"]
+    # expert output = the token's own bf16 row, placed at its rectangle row
+    eo = torch.zeros((E * cap, H), dtype=torch.bfloat16, device=DEV)
+    flat = oi.view(-1).long()
+    sel = flat >= 0
+    tok = torch.arange(T, device=DEV).repeat_interleave(K)[sel]
+    xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(DEV).view(torch.bfloat16)
+    eo[flat[sel]] = xd[tok]
+    p = epl.Problem.make(T, K, E, 1, H, 0)
+    y = poisoned((T, H), torch.float32)
+    epl.epl_combine(p, eo, E * cap, oi, torch.from_numpy(wt).to(DEV), epl.EPL_OUT_F32, y, r["ws"])
+    torch.cuda.synchronize()
+    assert epl.epl_status(r["ws"]) == epl.EPL_OK
+    orc = oracle.default()
+    oi_h = oi.cpu().numpy()
+    valid = oi_h >= 0
+    compact = np.full(oi_h.shape, -1, np.int32)
+    compact[valid] = np.arange(int(valid.sum()), dtype=np.int32)
+    rows = np.repeat(x, K, axis=0)[valid.ravel()]
+    y_ref = orc.combine(rows, compact, wt)
+    bound = orc.combine(rows & np.uint16(0x7FFF), compact, np.abs(wt))
+    d = np.abs(y.cpu().numpy().astype(np.float64) - y_ref)
+    assert (d <= 1e-5 * bound).all()
