@@ -393,7 +393,7 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
 {
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_seg[kMaxExperts];
-    __shared__ int s_rseg[2 * kMaxExperts];
+    __shared__ int s_rseg[2 * kMaxExperts];   // rank and node column totals
     __shared__ int s_wave[kScanThreads / kWave];
     __shared__ uint32_t s_err;
     const int tid = threadIdx.x;
@@ -406,8 +406,9 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
         const int P = (int)max((int64_t)1, min((int64_t)(E <= kScanThreads ? kScanThreads / E : 1), nb));
         const int64_t L = (nb + P - 1) / P;
         const int RC = R + Rn;      // rank columns, then node columns
-        const int PR = (int)max((int64_t)1, min((int64_t)(RC <= kScanThreads ? kScanThreads / RC : 1), nb));
-        const int64_t LR = (nb + PR - 1) / PR;
+        for (int r = tid; r < RC; r += kScanThreads)
+            s_rseg[r] = 0;
+        lds_barrier();
         // When every thread owns at most one segment of at most 16 blocks,
         // the segment stays in registers between the sum and the rewrite.
         const bool held = E * P <= kScanThreads && L <= 16;
@@ -427,10 +428,23 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
                 s_seg[q * E + e] = segment_sum(block_count, E, e, b0, b1);
             }
         }
-        for (int col = tid; col < RC * PR; col += kScanThreads) {
-            const int r = col % RC, q = col / RC;
-            const int64_t b0 = q * LR;
-            s_rseg[q * RC + r] = segment_sum(block_rank, RC, r, b0, min(nb, b0 + LR));
+        // Rank and node columns only need their totals: every element of
+        // the [nb, RC] matrix is added into its column in LDS (integer adds,
+        // exact in any order), four loads in flight per thread.
+        const int64_t nrc = nb * RC;
+        for (int64_t i0 = tid; i0 < nrc; i0 += 4 * kScanThreads) {
+            int v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t i = i0 + (int64_t)j * kScanThreads;
+                v[j] = i < nrc ? block_rank[i] : 0;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t i = i0 + (int64_t)j * kScanThreads;
+                if (v[j])
+                    atomicAdd(&s_rseg[i % RC], v[j]);
+            }
         }
         uint32_t err = 0;
         for (int64_t bb = tid; bb < nb; bb += kScanThreads)
@@ -451,9 +465,7 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
             ws_counts[e] = run;
         }
         for (int r = tid; r < RC; r += kScanThreads) {
-            int run = 0;
-            for (int q = 0; q < PR; ++q)
-                run += s_rseg[q * RC + r];
+            const int run = s_rseg[r];
             if (r < R) {
                 if (per_rank)
                     per_rank[r] = run;

@@ -235,3 +235,14 @@ def test_ll_workspace_and_argument_checks(lib):
     assert call(ok, ws=fake + 64) == epl.EPL_EINVAL
     assert call(ok, out=fake + 8) == epl.EPL_EINVAL
     assert call(P(hidden=7168 + 64, scale_cols=0)) == epl.EPL_EINVAL
+
+
+def test_small_division_by_multiply_high_is_exact():
+    """The layout divides owner and node ids (< 2^16) by multiplying with
+    ceil(2^32 / d) and keeping the high word; that equals n // d for every
+    n, d < 2^16 used (d up to the 2048 experts per rank)."""
+    import numpy as np
+    n = np.arange(1 << 16, dtype=np.uint64)
+    for d in range(2, 2049):
+        magic = np.uint64(((1 << 32) + d - 1) // d)
+        assert np.array_equal((n * magic) >> np.uint64(32), n // np.uint64(d)), d
