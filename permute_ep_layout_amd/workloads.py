@@ -120,7 +120,7 @@ WORKLOADS = {
     # GEMM: e4m3 rows and power-of-two (UE8M0) scales packed 4 per int32
     "dsv3_fp8": Workload("dsv3_fp8", seed=3, num_tokens=4096, hidden=7168, num_experts=256,
                          num_topk=8, num_ranks=32, scales=True, routing="uniform",
-                         payload="fp8", scale_format="ue8m0"),
+                         payload="fp8", scale_format="ue8m0", ranks_per_node=8),
 }
 
 

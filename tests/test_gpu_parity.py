@@ -293,7 +293,7 @@ def fp8_parity(w, fmt, alignment=0, extra_cap=0, split=False):
     E, R, H, S = w.num_experts, w.num_ranks, w.hidden, w.scale_cols
     if fmt == epl.EPL_SCALE_NONE:
         S, xs = 0, None
-    p = epl.Problem.make(T, K, E, R, H, S, alignment)
+    p = epl.Problem.make(T, K, E, R, H, S, alignment, w.ranks_per_node)
     cap = epl.epl_capacity_rows(p) + extra_cap
     orc_ = orc()
     cnt, per_rank, in_rank = orc_.layout(topk, E, R)
@@ -305,6 +305,7 @@ def fp8_parity(w, fmt, alignment=0, extra_cap=0, split=False):
     W = 0 if xs is None else xs.shape[1]
     ws = poisoned(epl.epl_workspace_bytes(p), torch.uint8)
     cnt_d, per_d = poisoned(E, torch.int32), poisoned(R, torch.int32)
+    node_d = poisoned(p.num_nodes, torch.int32) if p.num_nodes else None
     in_d, start_d = poisoned((T, R), torch.uint8), poisoned(E, torch.int32)
     out = poisoned((cap, H), torch.uint8)
     if fmt == epl.EPL_SCALE_F32:
@@ -321,16 +322,19 @@ def fp8_parity(w, fmt, alignment=0, extra_cap=0, split=False):
     tk = torch.from_numpy(topk).to(DEV)
     xd = torch.from_numpy(x).to(DEV)
     if split:
-        epl.epl_layout(p, tk, cnt_d, per_d, None, in_d, ws)
+        epl.epl_layout(p, tk, cnt_d, per_d, node_d, in_d, ws)
         epl.epl_scan(p, cnt_d, start_d, tot, ws)
         epl.epl_scatter_fp8(p, xd, xs_d, fmt, tk, start_d, ws, cap, out, out_s, m, oi)
     else:
-        epl.epl_dispatch_fp8(p, tk, xd, xs_d, fmt, cap, cnt_d, per_d, None, in_d, start_d, tot,
+        epl.epl_dispatch_fp8(p, tk, xd, xs_d, fmt, cap, cnt_d, per_d, node_d, in_d, start_d, tot,
                              out, out_s, m, oi, ws)
     assert epl.epl_status(ws) == epl.EPL_OK
     assert int(tot[0]) == N
     np.testing.assert_array_equal(cnt_d.cpu().numpy(), cnt)
     np.testing.assert_array_equal(in_d.cpu().numpy(), in_rank)
+    np.testing.assert_array_equal(per_d.cpu().numpy(), per_rank)
+    if node_d is not None:
+        np.testing.assert_array_equal(node_d.cpu().numpy(), orc_.rdma_counts(in_rank, w.ranks_per_node))
     np.testing.assert_array_equal(start_d.cpu().numpy(), start)
     np.testing.assert_array_equal(oi.cpu().numpy(), oi_ref)
     np.testing.assert_array_equal(m[:N].cpu().numpy(), m_ref)
@@ -363,7 +367,8 @@ def test_fp8_shapes(case):
     w = workloads.Workload(name, seed=91, num_tokens=T, hidden=H, num_experts=E, num_topk=K,
                            num_ranks=R, scales=True, routing="uniform", drop_rate=0.1,
                            payload="fp8",
-                           scale_format="f32" if fmt == epl.EPL_SCALE_F32 else "ue8m0")
+                           scale_format="f32" if fmt == epl.EPL_SCALE_F32 else "ue8m0",
+                           ranks_per_node=2)
     fp8_parity(w, fmt, alignment=a, extra_cap=extra, split=split)
 
 
