@@ -1,0 +1,103 @@
+"""The dispatch + combine chain captured in a HIP graph (torch.cuda.CUDAGraph
+over the C ABI calls): every replay, with eager work on other buffers in
+between, reproduces the eager results bit for bit. The chain records no
+memset node; the scan writes N through a mapped host word."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import permute_ep_layout_amd as epl  # noqa: E402
+from permute_ep_layout_amd import workloads  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    epl.load()
+
+
+class Chain:
+    """Buffers and pre-marshalled calls for one dispatch + combine."""
+
+    def __init__(self, w, stream):
+        inp = workloads.make_inputs(w)
+        T, K, E, R, H, S = (w.num_tokens, w.num_topk, w.num_experts, w.num_ranks, w.hidden,
+                            w.scale_cols)
+        self.topk = torch.from_numpy(inp["topk_idx"]).to(DEV)
+        self.x = torch.from_numpy(inp["x"].view(np.int16)).to(DEV).view(torch.bfloat16)
+        self.xs = torch.from_numpy(inp["x_scale"]).to(DEV) if S else None
+        self.wt = torch.from_numpy(inp["topk_weights"]).to(DEV)
+        p = epl.Problem.make(T, K, E, R, H, S, 0, w.ranks_per_node)
+        self.cap = cap = epl.epl_capacity_rows(p)
+        i32 = torch.int32
+        self.ws = torch.empty(epl.epl_workspace_bytes(p), dtype=torch.uint8, device=DEV)
+        self.cnt = torch.empty(E, dtype=i32, device=DEV)
+        self.per = torch.empty(R, dtype=i32, device=DEV)
+        self.node = torch.empty(p.num_nodes, dtype=i32, device=DEV) if p.num_nodes else None
+        self.inr = torch.empty((T, R), dtype=torch.uint8, device=DEV)
+        self.start = torch.empty(E, dtype=i32, device=DEV)
+        self.total = torch.zeros(1, dtype=i32).pin_memory()
+        self.out = torch.empty((cap, H), dtype=torch.bfloat16, device=DEV)
+        self.osc = torch.empty((cap, S), dtype=torch.float32, device=DEV) if S else None
+        self.m = torch.empty(cap, dtype=i32, device=DEV)
+        self.oi = torch.empty((T, K), dtype=i32, device=DEV)
+        self.y = torch.empty((T, H), dtype=torch.float32, device=DEV)
+        # checked once through the validating wrappers, then pre-marshalled
+        epl.epl_dispatch(p, self.topk, self.x, self.xs, cap, self.cnt, self.per, self.node,
+                         self.inr, self.start, self.total, self.out, self.osc, self.m, self.oi,
+                         self.ws, stream)
+        epl.epl_combine(p, self.out, cap, self.oi, self.wt, epl.EPL_OUT_F32, self.y, self.ws,
+                        stream)
+        self.calls = [
+            epl.prepare("epl_dispatch", p, self.topk, self.x, self.xs, cap, self.cnt, self.per,
+                        self.node, self.inr, self.start, self.total, self.out, self.osc, self.m,
+                        self.oi, self.ws, stream=stream),
+            epl.prepare("epl_combine", p, self.out, cap, self.oi, self.wt, epl.EPL_OUT_F32, self.y,
+                        self.ws, stream=stream),
+        ]
+
+    def run(self):
+        for c in self.calls:
+            c()
+
+    def snapshot(self):
+        n = int(self.total[0])
+        return dict(n=n, y=self.y.clone(), oi=self.oi.clone(), m=self.m[:n].clone(),
+                    out=self.out[:n].clone(), start=self.start.clone(), cnt=self.cnt.clone())
+
+    def poison(self):
+        for t in (self.y, self.oi, self.m, self.out, self.start, self.cnt):
+            t.view(torch.uint8).fill_(0x5A)
+        self.total.fill_(-1)
+
+
+def test_graph_replays_match_eager():
+    s = torch.cuda.Stream()
+    w = workloads.get("dsv3").with_(num_tokens=1536)
+    other = workloads.get("small").with_(num_tokens=700)
+    with torch.cuda.stream(s):
+        a = Chain(w, s)
+        b = Chain(other, s)
+        a.run()
+        s.synchronize()
+        ref = a.snapshot()
+        assert epl.epl_status(a.ws, s.cuda_stream) == epl.EPL_OK
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            a.run()
+        for i in range(4):
+            a.poison()
+            b.run()                       # eager work on other buffers in between
+            g.replay()
+            s.synchronize()
+            got = a.snapshot()
+            assert got["n"] == ref["n"], i
+            for key in ("y", "oi", "m", "out", "start", "cnt"):
+                assert torch.equal(got[key].view(torch.uint8), ref[key].view(torch.uint8)), (i, key)
+            assert epl.epl_status(a.ws, s.cuda_stream) == epl.EPL_OK
