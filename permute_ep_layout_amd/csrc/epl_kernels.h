@@ -13,6 +13,10 @@
 //              scales, m_indices, output_index), section 3.3 (-1 markers);
 //   combine -- the way back to token order, weighted by topk_weights
 //              ("高性能专家并行（EP）内核解剖学解读", 任务设定与数据流).
+// The low-latency variant (ep_ll_scatter_kernel) places rows into a fixed
+// rectangle per expert instead (strategy A of the EP anatomy page, high-
+// throughput part subsection 3; the receive buffers of the DeepEP page's
+// low_latency section) and casts them to FP8 on the way.
 //
 // Determinism. Counts are integer sums, so atomics would already give exact
 // counts; row positions are another matter. Here nothing about positions
