@@ -38,11 +38,35 @@ SHORT = (("ep_layout_kernel", "layout"), ("ep_scan_kernel", "scan"),
          ("ep_expert_scale_kernel", "expert"))
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without comments and with whitespace runs collapsed, so
+    that editing a comment does not make the counters look stale."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif text[i] == '"':                       # string literal, kept whole
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(text[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest(root: str = ROOT) -> str:
+    """Digest of the kernel sources' code (comments and layout ignored)."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(root, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(root, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
