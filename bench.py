@@ -28,6 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+METRIC = "routed token-rows/s and achieved HBM GB/s (% peak) for dispatch+combine"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.md")
 
 
@@ -266,7 +267,7 @@ def run_ll(args, w, inp):
         log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s, 1 thread)")
         cpu = ll_cpu_baseline(w, inp, args.cpu_seconds)
     result = {
-        "metric": "routed token-rows/s (dispatch+combine)",
+        "metric": METRIC,
         "value": N / (ms_per_step * 1e-3),
         "unit": "rows/s",
         "n_gpus": 1,
@@ -658,7 +659,7 @@ def main():
         cpu = cpu_baseline(w, inp, args.cpu_seconds, args.alignment)
 
     result = {
-        "metric": "routed token-rows/s (dispatch+combine)",
+        "metric": METRIC,
         "value": N / (ms_per_step * 1e-3),
         "unit": "rows/s",
         "n_gpus": 1,
