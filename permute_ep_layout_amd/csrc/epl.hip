@@ -601,28 +601,32 @@ int epl_combine(const epl_problem *p, const uint16_t *expert_out, int64_t expert
         return EPL_EINVAL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint32_t *status = workspace ? &at<WsHeader>(workspace, 0)->status : nullptr;
-    const dim3 grid(row_grid(p->num_tokens, epl::kCombineGrid));
-    const int64_t y_bytes = p->num_tokens * (int64_t)p->hidden * (out_dtype == EPL_OUT_BF16 ? 2 : 4);
-    // A y that stays in the caches (a batch of a few thousand tokens) goes
-    // faster with 256 threads per token; a large y streamed past the caches
-    // (large or sparse batches) with 128.
+    const bool bf16 = out_dtype == EPL_OUT_BF16;
+    const int64_t y_bytes = p->num_tokens * (int64_t)p->hidden * (bf16 ? 2 : 4);
     const bool y_nt = y_bytes > epl::kYNtBytes;
+    constexpr int th = epl::kCombineThreads;
+    // Column parts per token: as many as make one pass of the workgroup's
+    // threads cover a part.
+    const int64_t units = p->hidden / epl::combine_unit_cols(bf16);
+    const int64_t per_pass = (int64_t)th * epl::combine_units_per_thread(bf16);
+    const int parts =
+        (int)std::max<int64_t>(1, std::min<int64_t>(epl::kCombineMaxParts, (units + per_pass - 1) / per_pass));
+    const dim3 grid(row_grid(p->num_tokens * parts, epl::kCombineGrid));
     auto launch = [&](auto kernel, int threads) {
         hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, s, expert_out, expert_rows,
-                           output_index, topk_weights, p->num_tokens, p->num_topk, p->hidden, y,
-                           status);
+                           output_index, topk_weights, p->num_tokens, p->num_topk, p->hidden,
+                           parts, y, status);
     };
-    constexpr int tn = epl::kCombineThreads, tc = epl::kCombineThreadsCached;
-    if (out_dtype == EPL_OUT_BF16) {
+    if (bf16) {
         if (y_nt)
-            launch(epl::ep_combine_kernel<true, true, tn>, tn);
+            launch(epl::ep_combine_kernel<true, true, th>, th);
         else
-            launch(epl::ep_combine_kernel<true, false, tc>, tc);
+            launch(epl::ep_combine_kernel<true, false, th>, th);
     } else {
         if (y_nt)
-            launch(epl::ep_combine_kernel<false, true, tn>, tn);
+            launch(epl::ep_combine_kernel<false, true, th>, th);
         else
-            launch(epl::ep_combine_kernel<false, false, tc>, tc);
+            launch(epl::ep_combine_kernel<false, false, th>, th);
     }
     return launch_status();
 }

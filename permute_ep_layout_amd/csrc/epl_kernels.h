@@ -51,10 +51,7 @@ constexpr int kRowThreads = 128;          // expert-scale workgroup
 #define EPL_SCATTER_THREADS 128
 #endif
 #ifndef EPL_COMBINE_THREADS
-#define EPL_COMBINE_THREADS 128      // when y is written past the caches
-#endif
-#ifndef EPL_COMBINE_THREADS_CACHED
-#define EPL_COMBINE_THREADS_CACHED 256   // when y stays in the caches
+#define EPL_COMBINE_THREADS 256
 #endif
 #ifndef EPL_COMBINE_UNROLL
 #define EPL_COMBINE_UNROLL 2
@@ -70,7 +67,6 @@ constexpr int kRowThreads = 128;          // expert-scale workgroup
 #endif
 constexpr int kScatterThreads = EPL_SCATTER_THREADS;
 constexpr int kCombineThreads = EPL_COMBINE_THREADS;
-constexpr int kCombineThreadsCached = EPL_COMBINE_THREADS_CACHED;
 
 // Status word bits (workspace header).
 constexpr uint32_t kStatusBadExpert = 1u;      // topk id outside [-1, E)
@@ -1035,6 +1031,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 }
 
 constexpr int kCombineUnroll = EPL_COMBINE_UNROLL;   // column vectors per thread per pass
+constexpr int kCombineMaxParts = 64;                  // column parts per token, at most
 
 #ifndef EPL_COMBINE_LOAD_NT
 #define EPL_COMBINE_LOAD_NT 1
@@ -1063,46 +1060,68 @@ __device__ __forceinline__ void store_y(V *dst, const V &v)
         *dst = v;
 }
 
-// One workgroup per token (grid-stride over tokens): y[t] = sum over valid k
-// (ascending) of w[t,k] * expert_out[output_index[t,k]], fp32 accumulation.
-// Each thread owns kCombineUnroll 8-column vectors per pass and issues the
-// loads of up to 8 gathered rows for all of them before accumulating, so
-// 8 * kCombineUnroll row loads per thread are in flight. The gathered rows
+// Column units of the combine: 8 columns (16-byte loads) for a bf16 y, whose
+// 8 outputs are again 16 bytes; 4 columns (8-byte loads) for an fp32 y, so
+// that each 16-byte store of 4 outputs sits next to its neighbour lane's and
+// a store instruction covers one contiguous span (8 columns per lane would
+// leave every other 16 bytes of a span to a second instruction, which
+// non-temporal stores write to memory as partial lines).
+__host__ __device__ constexpr int combine_unit_cols(bool out_bf16) { return out_bf16 ? 8 : 4; }
+// Units a thread covers in one pass.
+__host__ __device__ constexpr int combine_units_per_thread(bool out_bf16)
+{
+    return out_bf16 ? kCombineUnroll : 2 * kCombineUnroll;
+}
+
+// One work item per (token, column part), grid-stride over the items:
+// y[t] = sum over valid k (ascending) of w[t,k] * expert_out[output_index[t,k]],
+// fp32 accumulation, item t * parts + q covering the q-th of `parts` equal
+// column ranges of row t. The host picks parts so that a workgroup covers
+// its range in one pass: the work per workgroup shrinks and the last
+// workgroups of a launch finish sooner. Each thread issues the loads of up to
+// 8 gathered rows for all of its units before accumulating. The gathered rows
 // are read once, so the loads are non-temporal. The first wave fetches the
-// next token's output_index / weights while the current token streams; the
+// next item's output_index / weights while the current one streams; the
 // compacted slot table is double-buffered in LDS (see ep_scatter_kernel).
 template <bool OUT_BF16, bool Y_NT, int THREADS>
 __global__ __launch_bounds__(THREADS) void ep_combine_kernel(
     const uint16_t *__restrict__ expert_out, int64_t rows, const int32_t *__restrict__ oi,
-    const float *__restrict__ w, int64_t T, int K, int H, void *__restrict__ y,
+    const float *__restrict__ w, int64_t T, int K, int H, int parts, void *__restrict__ y,
     uint32_t *__restrict__ status)
 {
     __shared__ int64_t s_row[2][kMaxTopk];
     __shared__ float s_w[2][kMaxTopk];
     __shared__ int s_n[2];
     const int tid = threadIdx.x;
-    const TokenRange tr = token_range(T);
-    const int64_t step = tr.stride, t_end = tr.end;
-    constexpr int U = kCombineUnroll;
+    const TokenRange tr = token_range(T * parts);
+    const int64_t step = tr.stride, i_end = tr.end;
 
     int64_t p_next = -1;
     float w_next = 0.0f;
-    if (tid < K && tr.first < t_end) {
-        p_next = oi[tr.first * K + tid];
-        w_next = w[tr.first * K + tid];
+    if (tid < K && tr.first < i_end) {
+        p_next = oi[(tr.first / parts) * K + tid];
+        w_next = w[(tr.first / parts) * K + tid];
     }
 
+    constexpr int CW = combine_unit_cols(OUT_BF16);
+    constexpr int UU = combine_units_per_thread(OUT_BF16);
+    using In = typename std::conditional<CW == 8, u32x4, u32x2>::type;
+    const int nunit_row = H / CW;
+    const int part_units = (nunit_row + parts - 1) / parts;
+
     int it = 0;
-    for (int64_t t = tr.first; t < t_end; t += step, ++it) {
+    for (int64_t item = tr.first; item < i_end; item += step, ++it) {
+        const int64_t t = item / parts;
+        const int q = (int)(item - t * parts);
         const int buf = it & 1;
         if (tid < kWave) {
             // Compact the valid slots, keeping ascending k: lane k finds its
             // place among the lower valid lanes with one ballot (K <= 64).
             int64_t p = p_next;
             const float wt = w_next;
-            if (tid < K && t + step < t_end) {
-                p_next = oi[(t + step) * K + tid];
-                w_next = w[(t + step) * K + tid];
+            if (tid < K && item + step < i_end) {
+                p_next = oi[((item + step) / parts) * K + tid];
+                w_next = w[((item + step) / parts) * K + tid];
             }
             if (p >= rows) {
                 if (status)
@@ -1125,18 +1144,9 @@ __global__ __launch_bounds__(THREADS) void ep_combine_kernel(
         const int64_t *srow = s_row[buf];
         const float *sw = s_w[buf];
 
-        // Column units: 8 columns (16-byte loads) for a bf16 y, whose 8
-        // outputs are again 16 bytes; 4 columns (8-byte loads) for an fp32 y,
-        // so that each 16-byte store of 4 outputs sits next to its
-        // neighbour lane's and a store instruction covers one contiguous
-        // span (8 columns per lane would leave every other 16 bytes of a
-        // span to a second instruction, which non-temporal stores write to
-        // memory as partial lines).
-        constexpr int CW = OUT_BF16 ? 8 : 4;
-        constexpr int UU = OUT_BF16 ? U : 2 * U;
-        using In = typename std::conditional<CW == 8, u32x4, u32x2>::type;
-        const int nunit = H / CW;
-        for (int base = tid; base < nunit; base += THREADS * UU) {
+        // this item's units: [q * part_units, nunit)
+        const int nunit = min(nunit_row, (q + 1) * part_units);
+        for (int base = q * part_units + tid; base < nunit; base += THREADS * UU) {
             float acc[UU][CW];
 #pragma unroll
             for (int u = 0; u < UU; ++u)
