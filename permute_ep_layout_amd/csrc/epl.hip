@@ -146,12 +146,14 @@ T *at(void *ws, size_t off)
 
 int launch_status() { return hipGetLastError() == hipSuccess ? EPL_OK : EPL_EHIP; }
 
-// Workgroups for a row kernel: min(tokens, limit), and never more than 2^24
-// (the dispatch packet counts work-items in 32 bits); the kernels stride over
-// any tokens beyond the grid.
-unsigned row_grid(int64_t tokens, int64_t limit)
+// Workgroups for a row kernel: min(items, limit), and never more than 2^22:
+// the dispatch packet counts work-items in 32 bits, and 2^22 workgroups of
+// up to 1024 threads stay below 2^32. The kernels stride over any items
+// beyond the grid.
+constexpr int64_t kMaxRowGrid = int64_t(1) << 22;
+unsigned row_grid(int64_t items, int64_t limit)
 {
-    return (unsigned)std::min<int64_t>(tokens, std::min<int64_t>(limit, int64_t(1) << 24));
+    return (unsigned)std::min<int64_t>(items, std::min<int64_t>(limit, kMaxRowGrid));
 }
 
 int enqueue_layout(const epl_problem &p, const WsLayout &w, const int64_t *topk, uint8_t *in_rank,

@@ -398,6 +398,17 @@ def test_ragged_shapes(case):
     full_parity(w)
 
 
+def test_more_tokens_than_the_largest_grid():
+    """2^22 + 777 tokens: the row kernels' grids stop at 2^22 workgroups and
+    the scatter and combine stride over the rest; the layout has 16 K blocks,
+    so the scan sums columns longer than a thread holds."""
+    print("[parity] 2^22 + 777 tokens, hidden 8", flush=True)
+    w = workloads.Workload("grid_stride", seed=91, num_tokens=(1 << 22) + 777, hidden=8,
+                           num_experts=16, num_topk=2, num_ranks=4, scales=False,
+                           routing="uniform", drop_rate=0.1)
+    full_parity(w)
+
+
 # ------------------------------------------------- tokens per node (RDMA) --
 
 # (name, E, R, G, T, K): one node (not produced), one rank per node (equals
