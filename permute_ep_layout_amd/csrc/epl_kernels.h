@@ -850,7 +850,7 @@ constexpr int kLLGrid = EPL_LL_GRID;
 // (448 / amax)) (zero codes for an all-zero group). Each thread's 16 codes
 // go to every placed row as one 16-byte non-temporal store, and each
 // group's scale to out_scale[(e * S + g) * cap + j] (column-major per
-// expert). Before its tokens every workgroup also writes a share of
+// expert), the 8 lanes of the group sharing the slots. Before its tokens every workgroup also writes a share of
 // recv_count and layout_range (begin, count per expert and source segment
 // of M tokens), read off the per-block offsets: blocks of B tokens with B
 // dividing M, so segment s starts at block s * M / B. VPT = steps of 16
@@ -993,8 +993,14 @@ __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
                     const int64_t j = sj[k];
                     const int64_t row = (int64_t)e * cap + j;
                     __builtin_nontemporal_store(codes, reinterpret_cast<u32x4 *>(out + row * H) + pi);
-                    if ((tid & 7) == 0)
-                        out_scale[((int64_t)e * S + g) * cap + j] = scale;
+                }
+                // every lane of the group holds the scale: lane q stores it
+                // for slots q, q + 8, ... (one store instruction for 8 slots)
+                for (int k = tid & 7; k < K; k += 8) {
+                    const int e = se[k];
+                    if (e < 0)
+                        continue;
+                    out_scale[((int64_t)e * S + g) * cap + sj[k]] = scale;
                 }
             }
             base += kScatterThreads * VPT;
