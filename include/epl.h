@@ -259,7 +259,8 @@ int epl_ll_dispatch(const epl_problem *p, int32_t tokens_per_segment, int64_t ro
  * topk_weights is fp32 [T, K]; y is fp32 or bf16 [T, H] per `out_dtype`.
  * An output_index >= expert_rows is skipped and, if `workspace` is not
  * NULL, recorded as EPL_ERANGE in its status word. expert_out / y: 16-byte
- * aligned. */
+ * aligned; output_index / topk_weights: 4-byte aligned; y must not overlap
+ * any input. */
 int epl_combine(const epl_problem *p, const uint16_t *expert_out,
                 int64_t expert_rows, const int32_t *output_index,
                 const float *topk_weights, int out_dtype, void *y,
