@@ -1,0 +1,108 @@
+"""Host-side checks of bench.py (no GPU): the algorithmic byte counts behind
+the roofline figures, the counter-summary lookup and the one-GPU guard.
+
+The expected byte totals are the per-workload figures stated with the
+workload definitions (DeepSeek-V3-shaped, skewed and large batches), in MB
+of 10^6 bytes rounded to 0.1 MB; the test recomputes nothing from bench.py's
+own formulas."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from permute_ep_layout_amd import profiling, workloads  # noqa: E402
+
+
+def mb(x):
+    return round(x / 1e6, 1)
+
+
+# (workload, routed rows N, tokens with a slot, layout MB, scatter MB,
+#  combine MB with fp32 y, combine MB with bf16 y, scatter + combine MB)
+STATED = [
+    ("dsv3", 32768, 4096, 0.39, 537.3, 587.5, 528.7, 1124.7),
+    ("skew", 131072, 16384, 1.57, 2149.1, 2349.9, 2115.0, 4498.9),
+    ("large", 524288, 65536, 8.39, 8464.1, 9399.4, 8459.9, 17863.5),
+]
+
+
+@pytest.mark.parametrize("case", STATED, ids=[c[0] for c in STATED])
+def test_algorithmic_bytes_match_the_stated_totals(case):
+    name, N, T_any, layout, scatter, comb32, comb16, both = case
+    w = workloads.get(name)
+    b32 = bench.algorithmic_bytes(w, N, T_any, 4)
+    b16 = bench.algorithmic_bytes(w, N, T_any, 2)
+    # the stated layout figure has no per-node column; those add 4 bytes each
+    assert abs(b32["layout"] / 1e6 - layout) < 0.01
+    assert mb(b32["scatter"]) == scatter
+    assert mb(b32["combine"]) == comb32
+    assert mb(b16["combine"]) == comb16
+    assert mb(b32["scatter"] + b32["combine"]) == both
+
+
+def test_fp8_scatter_bytes_halve_the_rows():
+    """FP8 rows are H bytes and the UE8M0 scales ceil(S/4) = 14 words:
+    at DeepSeek-V3 shape 29.4 + 0.2 + 0.3 MB read (rows, scales, ids) and
+    234.9 + 1.8 + 0.3 MB written (rows, scales, m_indices + output_index),
+    266.8 MB against 537.3 MB for bf16 rows with fp32 scales."""
+    w = workloads.get("dsv3_fp8")
+    assert w.scale_words == 14
+    assert mb(bench.algorithmic_bytes(w, 32768, 4096)["scatter"]) == 266.8
+
+
+def test_low_latency_bytes():
+    """Low-latency dispatch at DeepSeek-V3 shape: bf16 rows in, FP8 rows and
+    fp32 scales out for 32768 routed rows, plus the small per-slot arrays."""
+    w = workloads.get("dsv3_ll")
+    b = bench.ll_algorithmic_bytes(w, 32768, 4096)
+    assert mb(b["ll_dispatch"]) == 301.7
+    assert mb(b["combine"]) == 587.5
+
+
+def test_padding_rows_cost_one_index_each():
+    w = workloads.get("dsv3")
+    a = bench.algorithmic_bytes(w, 32768, 4096, 4, pad_rows=0)
+    b = bench.algorithmic_bytes(w, 32768, 4096, 4, pad_rows=1000)
+    assert b["scatter"] - a["scatter"] == 4000
+    assert b["combine"] == a["combine"]
+
+
+def test_traffic_lookup_requires_the_profiled_sources(monkeypatch):
+    """roofline.traffic comes from the committed counter summary only while
+    the kernel sources match the digest it was taken on."""
+    path = bench.TRAFFIC_FILE.format(workload="dsv3")
+    data = profiling.read_traffic(path)
+    assert data and "combine" in data["kernels"]
+    if data["source_digest"] == profiling.source_digest():
+        got = bench.measured_traffic("dsv3", "combine")
+        assert got == data["kernels"]["combine"]["bytes_per_launch"]
+    monkeypatch.setattr(profiling, "source_digest", lambda root=None: "0" * 16)
+    assert bench.measured_traffic("dsv3", "combine") is None
+    assert bench.measured_traffic("no_such_workload", "combine") is None
+
+
+def test_digest_ignores_comments_only():
+    a = "int f(int x) { return x + 1; } // add one\n/* block */"
+    b = "int f(int x)\n{\n    return x + 1;   /* other words */\n}\n"
+    c = "int f(int x) { return x + 2; }"
+    assert profiling._code_only(a) == profiling._code_only(b)
+    assert profiling._code_only(a) != profiling._code_only(c)
+    # string literals keep their comment-like text
+    assert "//" in profiling._code_only('const char *s = "a // b";')
+
+
+def test_more_than_one_gpu_is_refused():
+    proc = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                          capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert proc.returncode == 2
+    assert "one GPU" in proc.stdout + proc.stderr
+    # nothing that looks like a result line
+    for line in proc.stdout.splitlines():
+        with pytest.raises(ValueError):
+            json.loads(line)
