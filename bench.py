@@ -314,6 +314,61 @@ def measured_traffic(workload, kernel):
     return None if entry is None else entry.get("bytes_per_launch")
 
 
+def stream_ceilings(mib):
+    """Rates of plain streaming kernels (libepl_probe.so) for fixed read:write
+    mixes of 16-byte words, each stream `mib` MiB: the practical ceiling that
+    a kernel with the same mix can be compared with. Prints one JSON line."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    from permute_ep_layout_amd import build as B
+
+    if not os.path.exists(B.PROBE_LIB):
+        raise RuntimeError(f"{B.PROBE_LIB} is not built (run python __graft_entry__.py build)")
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    for f in (lib.epl_probe_mix, lib.epl_probe_fan):
+        f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                      ctypes.c_int, ctypes.c_int, ctypes.c_uint, ctypes.c_void_p]
+    n = (mib << 20) // 16
+    pad = 656     # words (41 x 256 B) between streams beyond n: line-aligned, not at powers of two
+    src = torch.full((8 * (n + pad) * 4,), 3, dtype=torch.int32, device="cuda")
+    dst = torch.zeros((8 * (n + pad) * 4,), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    grid = 8192
+
+    def rate(fn, nbytes, reps=10):
+        for _ in range(2):
+            if fn() != 0:
+                raise RuntimeError("probe launch failed")
+        torch.cuda.synchronize()
+        evs = [(Event(), Event()) for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return nbytes / (float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e-3) / 1e9
+
+    out = {}
+    for ld, spacing in ((n + pad, "offset"), (n, "aligned")):
+        for nt in (0, 1):
+            kind = "nt" if nt else "wb"
+            for r in (1, 2, 4, 8):
+                out[f"{spacing}_read{r}_write1_{kind}"] = rate(
+                    lambda: lib.epl_probe_mix(src.data_ptr(), dst.data_ptr(), n, ld, r, nt, grid,
+                                              stream.cuda_stream), (r + 1) * n * 16)
+            for f in (1, 4, 8):
+                out[f"{spacing}_read1_write{f}_{kind}"] = rate(
+                    lambda: lib.epl_probe_fan(src.data_ptr(), dst.data_ptr(), n, ld, f, nt, grid,
+                                              stream.cuda_stream), (f + 1) * n * 16)
+    print(json.dumps({"stream_ceilings_gbps": {k: round(v, 1) for k, v in out.items()},
+                      "mib_per_stream": mib, "word_bytes": 16, "pad_words": pad,
+                      "workgroups": grid, "threads": 256, "peak_gbps": HBM_PEAK_GBPS}),
+          flush=True)
+
+
 def copy_calibration(nbytes):
     """A plain copy kernel of known size (fp32 elementwise: read once, write
     once) for scaling the HBM byte counters."""
@@ -385,6 +440,8 @@ def main():
                          "the timed region alone)")
     ap.add_argument("--copy-calibration", type=int, metavar="BYTES", default=0,
                     help="only run a plain copy kernel of BYTES bytes (counter calibration)")
+    ap.add_argument("--ceilings", type=int, metavar="MIB", default=0,
+                    help="only run the streaming read:write mix probes, MIB MiB per stream")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -394,6 +451,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.ceilings:
+        stream_ceilings(args.ceilings)
         return
 
     import numpy as np

@@ -16,6 +16,9 @@ CSRC = os.path.join(PKG, "csrc")
 SOURCES = [os.path.join(CSRC, "epl.hip")]
 DEPENDS = SOURCES + [os.path.join(CSRC, "epl_kernels.h"), os.path.join(INCLUDE, "epl.h")]
 LIB = os.path.join(PKG, "libepl.so")
+# streaming-bandwidth probes for bench.py --ceilings (not on the dispatch path)
+PROBE_SOURCES = [os.path.join(CSRC, "stream_probe.hip")]
+PROBE_LIB = os.path.join(PKG, "libepl_probe.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -44,8 +47,9 @@ def needs_build(lib: str = LIB) -> bool:
     return any(os.path.getmtime(d) > t for d in DEPENDS)
 
 
-def build(out: str = LIB, extra_flags=(), verbose: bool = False) -> str:
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, *SOURCES, "-o", out + ".tmp"]
+def build(out: str = LIB, extra_flags=(), verbose: bool = False, sources=None) -> str:
+    sources = SOURCES if sources is None else sources
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, *sources, "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
@@ -57,6 +61,10 @@ def build(out: str = LIB, extra_flags=(), verbose: bool = False) -> str:
         print("\n".join(msgs))
     os.replace(out + ".tmp", out)
     return out
+
+
+def build_probe(verbose: bool = False) -> str:
+    return build(PROBE_LIB, verbose=verbose, sources=PROBE_SOURCES)
 
 
 if __name__ == "__main__":

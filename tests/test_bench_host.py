@@ -106,3 +106,25 @@ def test_more_than_one_gpu_is_refused():
     for line in proc.stdout.splitlines():
         with pytest.raises(ValueError):
             json.loads(line)
+
+
+def test_probe_library_exports_and_checks_arguments():
+    """The streaming probes behind bench.py --ceilings: both entry points
+    exist and reject bad arguments on the host (no GPU call is made)."""
+    import ctypes
+
+    from permute_ep_layout_amd import build as B
+
+    if not os.path.exists(B.PROBE_LIB):
+        pytest.skip("probe library not built")
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    for name in ("epl_probe_mix", "epl_probe_fan"):
+        f = getattr(lib, name)
+        f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                      ctypes.c_int, ctypes.c_int, ctypes.c_uint, ctypes.c_void_p]
+        assert f(None, None, 16, 16, 1, 0, 64, None) == -1      # null buffers
+        assert f(16, 32, 0, 0, 1, 0, 64, None) == -1            # no words
+        assert f(16, 32, 16, 8, 1, 0, 64, None) == -1           # streams overlap
+        assert f(16, 32, 16, 16, 3, 0, 64, None) == -1          # unsupported mix
+        assert f(8, 32, 16, 16, 1, 0, 64, None) == -1           # misaligned
+        assert f(16, 32, 16, 16, 1, 0, 0, None) == -1           # empty grid
