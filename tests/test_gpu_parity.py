@@ -494,6 +494,37 @@ def test_all_slots_invalid():
     topk = -np.ones((300, 4), np.int64)
     r, ref, y = _edge(topk, 16, 4)
     assert (r["oi"] == -1).all() and (y == 0).all()
+    # the sum starts from +0: every bit of y is clear, also in bf16
+    assert (y.view(torch.int32) == 0).all()
+    yb = gpu_combine(r, r["out"], np.ones((300, 4), np.float32), epl.EPL_OUT_BF16)
+    assert (u16(yb) == 0).all()
+
+
+def test_non_finite_rows_propagate_like_the_oracle():
+    """NaN and +-Inf in expert rows are summed like any value: y is NaN, +Inf
+    or -Inf exactly where the oracle's fp64 sum is (0 * Inf gives NaN on both
+    sides), and the finite elements stay within the tolerance."""
+    rng = np.random.default_rng(12)
+    T, K, E, R, H = 400, 4, 16, 4, 64
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    x, _, wt = _mk(topk, H, seed=12)
+    wt[rng.random(wt.shape) < 0.05] = 0.0               # some zero weights meet an Inf
+    specials = np.array([0x7FC0, 0x7F80, 0xFF80], np.uint16)   # NaN, +Inf, -Inf
+    hit = rng.random(x.shape) < 0.01
+    x[hit] = specials[rng.integers(0, 3, int(hit.sum()))]
+    ref = orc().run_all(x, None, topk, wt, E, R)
+    r = gpu_dispatch(topk, x, None, E, R)
+    assert epl.epl_status(r["ws"]) == epl.EPL_OK
+    check_layout_and_scatter(r, ref, x, None)
+    y = gpu_combine(r, r["out"], wt, epl.EPL_OUT_F32).cpu().numpy().astype(np.float64)
+    yr = ref["y"]
+    assert np.isnan(yr).any() and np.isinf(yr).any()
+    np.testing.assert_array_equal(np.isnan(y), np.isnan(yr))
+    np.testing.assert_array_equal(np.isposinf(y), np.isposinf(yr))
+    np.testing.assert_array_equal(np.isneginf(y), np.isneginf(yr))
+    fin = np.isfinite(yr)
+    bound = combine_bound(ref["expert_out"], ref["output_index"], wt)
+    assert (np.abs(y[fin] - yr[fin]) <= 1e-5 * bound[fin]).all()
 
 
 def test_duplicate_experts_within_a_token():
