@@ -793,12 +793,13 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
 // ------------------------------------------- low-latency fixed rectangle --
 
 // e4m3 (OCP "fn": bias 7, max 448, no infinities) of a binary32 value, round
-// to nearest even; magnitudes that round above 448 give 448. Both cases are
-// computed and one is selected (no divergent branch per element): normal
-// results (|p| >= 2^-6) round the 23-bit mantissa to 3 bits on the bit
-// pattern (a carry moves into the exponent as it should) and rebias the
-// exponent from 127 to 7; smaller magnitudes are multiples of 2^-9, rounded
-// with rint (which may give 8 = 2^-6, the smallest normal code).
+// to nearest even; magnitudes that round above 448 (infinities too) give 448,
+// and a NaN of either sign gives the code 0x7F. Both cases are computed and
+// one is selected (no divergent branch per element): normal results
+// (|p| >= 2^-6) round the 23-bit mantissa to 3 bits on the bit pattern (a
+// carry moves into the exponent as it should) and rebias the exponent from
+// 127 to 7; smaller magnitudes are multiples of 2^-9, rounded with rint
+// (which may give 8 = 2^-6, the smallest normal code).
 __device__ __forceinline__ uint32_t e4m3_rne(float p)
 {
     const uint32_t u = __float_as_uint(p);
@@ -806,7 +807,8 @@ __device__ __forceinline__ uint32_t e4m3_rne(float p)
     const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
     const uint32_t normal = min((r >> 20) - (120u << 3), 0x7Eu);      // exponent 127 -> 7
     const uint32_t sub = (uint32_t)rintf(__uint_as_float(a) * 512.0f); // multiples of 2^-9
-    return ((u >> 24) & 0x80u) | (a >= 0x3C800000u ? normal : sub);    // 2^-6
+    const uint32_t code = ((u >> 24) & 0x80u) | (a >= 0x3C800000u ? normal : sub);  // 2^-6
+    return a > 0x7F800000u ? 0x7Fu : code;
 }
 
 // Maximum over the 8 lanes of a half DPP row (lanes 8m .. 8m+7), returned

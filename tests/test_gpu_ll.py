@@ -167,6 +167,27 @@ def test_ll_zero_groups_and_exact_powers():
     check_ll(_topk(rng, T, 4, 16), x, 16, 16, 64)
 
 
+def test_ll_non_finite_values_encode_like_the_oracle():
+    """NaN and +-Inf in the token rows: a group's amax skips NaN (a group of
+    NaNs only gets scale 0), an Inf makes the scale Inf and the factor 0, and
+    every NaN that reaches the encoder (a NaN value, or Inf * 0) is the code
+    0x7F; codes and scales bit-exact against the oracle."""
+    rng = np.random.default_rng(31)
+    nseg, M, K, E, H = 4, 32, 4, 16, 512
+    T = nseg * M
+    topk = _topk(rng, T, K, E)
+    x = _x(rng, T, H, spread=False)
+    specials = np.array([0x7FC0, 0xFFC0, 0x7F80, 0xFF80], np.uint16)   # +-NaN, +-Inf
+    hit = rng.random(x.shape) < 0.004
+    x[hit] = specials[rng.integers(0, 4, int(hit.sum()))]
+    x[5, 128:256] = 0x7FC0          # a group of NaNs only
+    x[9, 0:128] = 0x0000            # an all-zero group
+    x[9, 7] = 0xFF80                # ... but for one -Inf
+    q, sc = oracle.default().quantize_e4m3(x)
+    assert (q == 0x7F).any() and np.isinf(sc).any() and sc[5, 1] == 0.0
+    check_ll(topk, x, E, M, T)
+
+
 def test_ll_side_stream_and_repeat_is_deterministic():
     rng = np.random.default_rng(6)
     topk, x = _topk(rng, 512, 6, 32, 0.1), _x(rng, 512, 1024)
