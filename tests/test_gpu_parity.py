@@ -525,6 +525,12 @@ def test_non_finite_rows_propagate_like_the_oracle():
     fin = np.isfinite(yr)
     bound = combine_bound(ref["expert_out"], ref["output_index"], wt)
     assert (np.abs(y[fin] - yr[fin]) <= 1e-5 * bound[fin]).all()
+    # bf16 output: NaN stays NaN, infinities stay infinite with their sign
+    yb = u16(gpu_combine(r, r["out"], wt, epl.EPL_OUT_BF16))
+    ybf = (yb.astype(np.uint32) << 16).view(np.float32)
+    np.testing.assert_array_equal(np.isnan(ybf), np.isnan(yr))
+    np.testing.assert_array_equal(np.isposinf(ybf), np.isposinf(yr))
+    np.testing.assert_array_equal(np.isneginf(ybf), np.isneginf(yr))
 
 
 def test_duplicate_experts_within_a_token():
