@@ -269,11 +269,14 @@ _DEFAULT = None
 
 
 def default() -> Oracle:
-    """The oracle built from ``epl_oracle.c`` (rebuilt when the source is newer)."""
+    """The oracle built from ``epl_oracle.c`` (rebuilt when the source is newer),
+    or the build named by EPL_ORACLE_LIB (the test suite's sanitizer run)."""
     global _DEFAULT
     if _DEFAULT is None:
         path, src = _build.LIB, _build.SRC
-        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(src):
+        if os.environ.get("EPL_ORACLE_LIB"):
+            path = os.environ["EPL_ORACLE_LIB"]
+        elif not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(src):
             _build.build()
         _DEFAULT = Oracle(path)
     return _DEFAULT

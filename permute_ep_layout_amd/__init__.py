@@ -111,11 +111,12 @@ def ensure_built(verbose: bool = False) -> str:
 
 
 def load() -> ctypes.CDLL:
-    """Load libepl.so; raises if it has not been built."""
+    """Load libepl.so (or the build named by EPL_LIB, e.g. the test suite's
+    host-sanitizer build); raises if it has not been built."""
     global _LIB
     if _LIB is not None:
         return _LIB
-    path = _build.LIB
+    path = os.environ.get("EPL_LIB") or _build.LIB
     if not os.path.exists(path):
         raise ImportError(
             f"libepl.so is not built ({path}); run `python -m permute_ep_layout_amd.build` "
