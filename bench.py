@@ -134,6 +134,21 @@ def ll_algorithmic_bytes(w, N, T_any, out_dtype_bytes=4):
     }
 
 
+def host_cpu():
+    """Model name of the host CPU the oracle baseline ran on, and the logical
+    CPUs this process may use."""
+    name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": name, "logical_cpus": len(os.sched_getaffinity(0))}
+
+
 def ll_cpu_baseline(w, inp, seconds):
     """The oracle's low-latency dispatch (quantise + place) and fp64 combine,
     single-threaded, over full passes of the workload."""
@@ -162,7 +177,7 @@ def ll_cpu_baseline(w, inp, seconds):
             break
     return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
             "sample": f"{passes} full pass(es) of the {w.name} workload (fixed-rectangle "
-                      f"layout, FP8 cast, fp64 combine), {el:.1f} s"}
+                      f"layout, FP8 cast, fp64 combine), {el:.1f} s", "host": host_cpu()}
 
 
 def run_ll(args, w, inp):
@@ -421,7 +436,8 @@ def cpu_baseline(w, inp, seconds, alignment=0):
         if el >= seconds or passes >= 50:
             break
     return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} full pass(es) of the {w.name} workload ({what}), {el:.1f} s"}
+            "sample": f"{passes} full pass(es) of the {w.name} workload ({what}), {el:.1f} s",
+            "host": host_cpu()}
 
 
 def main():

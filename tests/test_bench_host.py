@@ -128,3 +128,9 @@ def test_probe_library_exports_and_checks_arguments():
         assert f(16, 32, 16, 16, 3, 0, 64, None) == -1          # unsupported mix
         assert f(8, 32, 16, 16, 1, 0, 64, None) == -1           # misaligned
         assert f(16, 32, 16, 16, 1, 0, 0, None) == -1           # empty grid
+
+
+def test_host_cpu_description():
+    h = bench.host_cpu()
+    assert isinstance(h["model"], str) and h["model"]
+    assert h["logical_cpus"] >= 1
