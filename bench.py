@@ -378,7 +378,29 @@ def stream_ceilings(mib):
                 out[f"{spacing}_read1_write{f}_{kind}"] = rate(
                     lambda: lib.epl_probe_fan(src.data_ptr(), dst.data_ptr(), n, ld, f, nt, grid,
                                               stream.cuda_stream), (f + 1) * n * 16)
+    # Write-only pieces over 1 GiB (HBM-only): how much one workgroup writes
+    # and which XCD writes it. (piece words, threads): 4 KB with one store per
+    # thread; 14 KB (a bf16 row of 7168) as 128 threads x 7 stores, as the
+    # scatter writes a row, and as 896 threads x 1.
+    lib.epl_probe_pieces.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.epl_probe_fill32.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32,
+                                     ctypes.c_void_p]
+    wn = min(dst.numel() // 4, (1 << 30) // 16)
+    pieces = {}
+    for words, threads in ((256, 256), (896, 128), (896, 896)):
+        for xcd in (0, 1):
+            for nt in (0, 1):
+                key = (f"piece{words * 16}B_t{threads}_{'xcd' if xcd else 'inorder'}_"
+                       f"{'nt' if nt else 'wb'}")
+                pieces[key] = rate(
+                    lambda: lib.epl_probe_pieces(dst.data_ptr(), wn, words, threads, nt, xcd,
+                                                 stream.cuda_stream), wn * 16)
+    pieces["runtime_fill32"] = rate(
+        lambda: lib.epl_probe_fill32(dst.data_ptr(), wn * 4, 7, stream.cuda_stream), wn * 16)
     print(json.dumps({"stream_ceilings_gbps": {k: round(v, 1) for k, v in out.items()},
+                      "write_pieces_gbps": {k: round(v, 1) for k, v in pieces.items()},
+                      "write_pieces_bytes": wn * 16,
                       "mib_per_stream": mib, "word_bytes": 16, "pad_words": pad,
                       "workgroups": grid, "threads": 256, "peak_gbps": HBM_PEAK_GBPS}),
           flush=True)

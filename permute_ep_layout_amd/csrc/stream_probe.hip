@@ -11,6 +11,13 @@
 // (which would put their words in the same DRAM banks at the same time).
 // Loads are non-temporal (each word is read once); stores are write-back or
 // non-temporal per the caller's flag. Workgroups of 256 threads stride over i.
+//
+//   pieces: out is cut into pieces of `piece` words, one workgroup per piece
+//           (no striding), its threads storing the piece's words in order;
+//           the pieces go in address order or, with `xcd`, each XCD (workgroup
+//           i runs on XCD i mod 8) takes one contiguous eighth of them. This
+//           measures how the bytes one workgroup writes, and which XCD writes
+//           them, set the HBM write rate.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -73,6 +80,22 @@ __global__ __launch_bounds__(kThreads) void fan_kernel(const u32x4 *__restrict__
         for (int f = 0; f < FAN; ++f)
             put<NT>(out + f * ld + i, v);
     }
+}
+
+template <bool NT, bool XCD>
+__global__ __launch_bounds__(1024) void pieces_kernel(u32x4 *__restrict__ out, int64_t n,
+                                                      int64_t piece, int64_t npieces)
+{
+    int64_t r = blockIdx.x;
+    if (XCD) {
+        const int64_t per = (npieces + 7) / 8;
+        r = (r % 8) * per + r / 8;
+    }
+    if (r >= npieces)
+        return;
+    const int64_t b0 = r * piece, b1 = min(n, b0 + piece);
+    for (int64_t i = b0 + threadIdx.x; i < b1; i += blockDim.x)
+        put<NT>(out + i, u32x4{(uint32_t)i, (uint32_t)r, 1u, 2u});
 }
 
 template <int R>
@@ -141,6 +164,42 @@ int epl_probe_fan(const void *in, void *out, int64_t n, int64_t ld, int fan, int
     case 8: return launch_fan<8>(in, out, n, ld, nt_stores, grid, s);
     default: return -1;
     }
+}
+
+// `out` holds n 16-byte words, cut into pieces of `piece` words, one
+// workgroup of `threads` threads (64 .. 1024, a multiple of 64) per piece.
+// Returns 0, -1 for bad arguments, -4 if the launch failed.
+int epl_probe_pieces(void *out, int64_t n, int64_t piece, int threads, int nt_stores, int xcd,
+                     void *stream)
+{
+    if (!out || n <= 0 || piece <= 0 || threads < 64 || threads > 1024 || threads % 64 != 0 ||
+        reinterpret_cast<uintptr_t>(out) % 16 != 0)
+        return -1;
+    const int64_t npieces = (n + piece - 1) / piece;
+    const int64_t grid = xcd ? (npieces + 7) / 8 * 8 : npieces;
+    if (grid > (int64_t(1) << 22))
+        return -1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    u32x4 *o = static_cast<u32x4 *>(out);
+    const dim3 g((unsigned)grid), b((unsigned)threads);
+    if (nt_stores && xcd)
+        hipLaunchKernelGGL((pieces_kernel<true, true>), g, b, 0, s, o, n, piece, npieces);
+    else if (nt_stores)
+        hipLaunchKernelGGL((pieces_kernel<true, false>), g, b, 0, s, o, n, piece, npieces);
+    else if (xcd)
+        hipLaunchKernelGGL((pieces_kernel<false, true>), g, b, 0, s, o, n, piece, npieces);
+    else
+        hipLaunchKernelGGL((pieces_kernel<false, false>), g, b, 0, s, o, n, piece, npieces);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// The runtime's own fill of n 32-bit words (for comparison with the pieces).
+int epl_probe_fill32(void *out, int64_t n, uint32_t value, void *stream)
+{
+    if (!out || n <= 0 || reinterpret_cast<uintptr_t>(out) % 4 != 0)
+        return -1;
+    return hipMemsetD32Async(reinterpret_cast<hipDeviceptr_t>(out), (int)value, (size_t)n,
+                             static_cast<hipStream_t>(stream)) == hipSuccess ? 0 : -4;
 }
 
 }  // extern "C"

@@ -109,8 +109,8 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_probe_library_exports_and_checks_arguments():
-    """The streaming probes behind bench.py --ceilings: both entry points
-    exist and reject bad arguments on the host (no GPU call is made)."""
+    """The streaming probes behind bench.py --ceilings: every entry point
+    exists and rejects bad arguments on the host (no GPU call is made)."""
     import ctypes
 
     from permute_ep_layout_amd import build as B
@@ -128,6 +128,21 @@ def test_probe_library_exports_and_checks_arguments():
         assert f(16, 32, 16, 16, 3, 0, 64, None) == -1          # unsupported mix
         assert f(8, 32, 16, 16, 1, 0, 64, None) == -1           # misaligned
         assert f(16, 32, 16, 16, 1, 0, 0, None) == -1           # empty grid
+    pieces = lib.epl_probe_pieces
+    pieces.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                       ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert pieces(None, 256, 256, 256, 0, 0, None) == -1        # null buffer
+    assert pieces(16, 0, 256, 256, 0, 0, None) == -1            # no words
+    assert pieces(16, 256, 0, 256, 0, 0, None) == -1            # empty pieces
+    assert pieces(16, 256, 256, 96, 0, 0, None) == -1           # not whole waves
+    assert pieces(16, 256, 256, 2048, 0, 0, None) == -1         # above 1024 threads
+    assert pieces(8, 256, 256, 256, 0, 0, None) == -1           # misaligned
+    assert pieces(16, 1 << 40, 1, 64, 0, 0, None) == -1         # grid above 2^22
+    fill = lib.epl_probe_fill32
+    fill.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p]
+    assert fill(None, 16, 7, None) == -1
+    assert fill(16, 0, 7, None) == -1
+    assert fill(2, 16, 7, None) == -1
 
 
 def test_host_cpu_description():
