@@ -662,7 +662,7 @@ def main():
     }
     assert epl.epl_status(ws) == epl.EPL_OK
 
-    per_kernel_ms, bubble, cold_ms = {}, {}, {}
+    per_kernel_ms, bubble, cold_ms, copy_gbps = {}, {}, {}, None
     if not args.timed_only:
         # Per-kernel breakdown: the same kernels through the individual entry
         # points (layout, scan, scatter, ...), an event around every launch.
@@ -737,6 +737,24 @@ def main():
         del flush_buf
         assert epl.epl_status(ws) == epl.EPL_OK
 
+        # A practical ceiling beside the spec peak: a plain device-to-device
+        # copy of 1 GiB (torch's copy_, i.e. hipMemcpyAsync), HBM-only size;
+        # its rate counts the bytes read and written.
+        copy_src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        copy_dst = torch.empty_like(copy_src)
+        for _ in range(2):
+            copy_dst.copy_(copy_src)
+        cev = [(Event(), Event()) for _ in range(10)]
+        torch.cuda.synchronize()
+        for a, b in cev:
+            a.record(stream)
+            copy_dst.copy_(copy_src)
+            b.record(stream)
+        torch.cuda.synchronize()
+        copy_gbps = 2 * copy_src.numel() * 4 / (
+            float(np.median([a.elapsed_time(b) for a, b in cev])) * 1e-3) / 1e9
+        del copy_src, copy_dst
+
     nbytes = algorithmic_bytes(w, N, T_any, 4 if out_code == epl.EPL_OUT_F32 else 2,
                                n_rows - N)
     gbps = {n: nbytes[n] / (per_kernel_ms[n] * 1e-3) / 1e9 for n in per_kernel_ms}
@@ -782,9 +800,17 @@ def main():
         "timed_region_ms": timed_ms,
         "per_kernel_ms": per_kernel_ms,
         "per_kernel_gbps": gbps,
+        "per_kernel_rows_per_s": {n: N / (v * 1e-3) for n, v in per_kernel_ms.items()},
         "algorithmic_bytes": nbytes,
         "scatter_combine": {"ms": sc_ms, "gbps": sc_gbps, "frac_of_peak": sc_gbps / HBM_PEAK_GBPS},
         "scan_to_scatter_gap_us": bubble,
+        "practical_ceiling": None if copy_gbps is None else {
+            "kind": "device-to-device copy of 1 GiB (hipMemcpyAsync), bytes read + written",
+            "gbps": copy_gbps,
+            "frac_of_peak": copy_gbps / HBM_PEAK_GBPS,
+            "scatter_combine_frac_of_copy": sc_gbps / copy_gbps,
+            "dominant_frac_of_copy": dom_gbps / copy_gbps,
+        },
         "cold_cache": None if not cold_ms else {
             "ms": cold_ms,
             "gbps": {k: nbytes[k] / (v * 1e-3) / 1e9 for k, v in cold_ms.items()},
