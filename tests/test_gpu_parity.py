@@ -162,10 +162,21 @@ def full_parity(w: workloads.Workload, inp=None, split=False, alignment=0):
     y = gpu_combine(r, eo, wt, epl.EPL_OUT_F32)
     yb = gpu_combine(r, eo, wt, epl.EPL_OUT_BF16)
     bound = combine_bound(ref["expert_out"], ref["output_index"], wt)
-    check_combine_f32(y.cpu().numpy(), ref["y"], bound)
+    y_cpu = y.cpu()
+    check_combine_f32(y_cpu.numpy(), ref["y"], bound)
     check_combine_bf16(u16(yb), ref["y"], bound)
+    check_bf16_is_rne_of_f32(u16(yb), y_cpu)
     assert epl.epl_status(r["ws"]) == epl.EPL_OK
     return r, y
+
+
+def check_bf16_is_rne_of_f32(yb_u16, y_f32_cpu):
+    """Both output types come from the same fp32 sums in the same order, so
+    the bf16 output must be exactly their round-to-nearest-even, checked
+    against torch's own float32 -> bfloat16 conversion (finite values)."""
+    assert torch.isfinite(y_f32_cpu).all()
+    want = y_f32_cpu.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(yb_u16, want)
 
 
 # ------------------------------------------------------------ workloads --
