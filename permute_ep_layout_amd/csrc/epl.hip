@@ -607,10 +607,12 @@ int epl_combine(const epl_problem *p, const uint16_t *expert_out, int64_t expert
     const int64_t y_bytes = p->num_tokens * (int64_t)p->hidden * (bf16 ? 2 : 4);
     const bool y_nt = y_bytes > epl::kYNtBytes;
     constexpr int th = epl::kCombineThreads;
+    const bool few = p->num_tokens < epl::kCombineFewBelow;
+    const int unroll = few ? epl::kCombineUnrollFew : epl::kCombineUnroll;
     // Column parts per token: as many as make one pass of the workgroup's
     // threads cover a part.
     const int64_t units = p->hidden / epl::combine_unit_cols(bf16);
-    const int64_t per_pass = (int64_t)th * epl::combine_units_per_thread(bf16);
+    const int64_t per_pass = (int64_t)th * epl::combine_units_per_thread(bf16, unroll);
     const int parts =
         (int)std::max<int64_t>(1, std::min<int64_t>(epl::kCombineMaxParts, (units + per_pass - 1) / per_pass));
     const dim3 grid(row_grid(p->num_tokens * parts, epl::kCombineGrid));
@@ -619,16 +621,21 @@ int epl_combine(const epl_problem *p, const uint16_t *expert_out, int64_t expert
                            output_index, topk_weights, p->num_tokens, p->num_topk, p->hidden,
                            parts, y, status);
     };
+    constexpr int u1 = epl::kCombineUnrollFew, u2 = epl::kCombineUnroll;
     if (bf16) {
         if (y_nt)
-            launch(epl::ep_combine_kernel<true, true, th>, th);
+            few ? launch(epl::ep_combine_kernel<true, true, th, u1>, th)
+                : launch(epl::ep_combine_kernel<true, true, th, u2>, th);
         else
-            launch(epl::ep_combine_kernel<true, false, th>, th);
+            few ? launch(epl::ep_combine_kernel<true, false, th, u1>, th)
+                : launch(epl::ep_combine_kernel<true, false, th, u2>, th);
     } else {
         if (y_nt)
-            launch(epl::ep_combine_kernel<false, true, th>, th);
+            few ? launch(epl::ep_combine_kernel<false, true, th, u1>, th)
+                : launch(epl::ep_combine_kernel<false, true, th, u2>, th);
         else
-            launch(epl::ep_combine_kernel<false, false, th>, th);
+            few ? launch(epl::ep_combine_kernel<false, false, th, u1>, th)
+                : launch(epl::ep_combine_kernel<false, false, th, u2>, th);
     }
     return launch_status();
 }

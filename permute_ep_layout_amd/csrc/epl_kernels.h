@@ -56,6 +56,12 @@ constexpr int kRowThreads = 128;          // expert-scale workgroup
 #ifndef EPL_COMBINE_UNROLL
 #define EPL_COMBINE_UNROLL 2
 #endif
+#ifndef EPL_COMBINE_UNROLL_FEW
+#define EPL_COMBINE_UNROLL_FEW 1
+#endif
+#ifndef EPL_COMBINE_FEW_BELOW
+#define EPL_COMBINE_FEW_BELOW 8192
+#endif
 #ifndef EPL_SCATTER_GRID
 #define EPL_SCATTER_GRID 1024
 #endif
@@ -1041,7 +1047,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
-constexpr int kCombineUnroll = EPL_COMBINE_UNROLL;   // column vectors per thread per pass
+// Column vectors per thread per pass (the combine's unroll): kCombineUnroll
+// from kCombineFewBelow tokens on, kCombineUnrollFew below. With few tokens
+// the smaller unroll cuts each token into more, smaller column parts, so the
+// launch's last workgroups finish sooner (DSV3, 4096 tokens: 104.0 -> 103.3
+// us; 2048 tokens at hidden 4096: 25.5 -> 24.3 us); from 16384 tokens on
+// the extra per-part overhead costs more than the shorter tail saves
+// (16384 tokens: 410 -> 412 us, 65536: 1620 -> 1631 us).
+constexpr int kCombineUnroll = EPL_COMBINE_UNROLL;
+constexpr int kCombineUnrollFew = EPL_COMBINE_UNROLL_FEW;
+constexpr int64_t kCombineFewBelow = EPL_COMBINE_FEW_BELOW;
 constexpr int kCombineMaxParts = 64;                  // column parts per token, at most
 
 #ifndef EPL_COMBINE_LOAD_NT
@@ -1079,9 +1094,9 @@ __device__ __forceinline__ void store_y(V *dst, const V &v)
 // non-temporal stores write to memory as partial lines).
 __host__ __device__ constexpr int combine_unit_cols(bool out_bf16) { return out_bf16 ? 8 : 4; }
 // Units a thread covers in one pass.
-__host__ __device__ constexpr int combine_units_per_thread(bool out_bf16)
+__host__ __device__ constexpr int combine_units_per_thread(bool out_bf16, int unroll)
 {
-    return out_bf16 ? kCombineUnroll : 2 * kCombineUnroll;
+    return out_bf16 ? unroll : 2 * unroll;
 }
 
 // One work item per (token, column part), grid-stride over the items:
@@ -1094,7 +1109,7 @@ __host__ __device__ constexpr int combine_units_per_thread(bool out_bf16)
 // are read once, so the loads are non-temporal. The first wave fetches the
 // next item's output_index / weights while the current one streams; the
 // compacted slot table is double-buffered in LDS (see ep_scatter_kernel).
-template <bool OUT_BF16, bool Y_NT, int THREADS>
+template <bool OUT_BF16, bool Y_NT, int THREADS, int UNROLL>
 __global__ __launch_bounds__(THREADS) void ep_combine_kernel(
     const uint16_t *__restrict__ expert_out, int64_t rows, const int32_t *__restrict__ oi,
     const float *__restrict__ w, int64_t T, int K, int H, int parts, void *__restrict__ y,
@@ -1115,7 +1130,7 @@ __global__ __launch_bounds__(THREADS) void ep_combine_kernel(
     }
 
     constexpr int CW = combine_unit_cols(OUT_BF16);
-    constexpr int UU = combine_units_per_thread(OUT_BF16);
+    constexpr int UU = combine_units_per_thread(OUT_BF16, UNROLL);
     using In = typename std::conditional<CW == 8, u32x4, u32x2>::type;
     const int nunit_row = H / CW;
     const int part_units = (nunit_row + parts - 1) / parts;
