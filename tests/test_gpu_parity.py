@@ -397,6 +397,10 @@ RAGGED = [
     ("k1", 900, 1, 8, 8, 136, False, 0.0),
     ("e1", 64, 1, 1, 1, 8, False, 0.3),
     ("r_not_mult16", 400, 4, 36, 12, 96, False, 0.0),
+    # 8192 tokens and more: the combine's other unit count and the scatter's
+    # one-workgroup-per-token grid, with ragged rows
+    ("many_tokens_h264", 9000, 5, 24, 6, 264, False, 0.1),
+    ("many_tokens_scales_s9", 8500, 4, 32, 8, 1152, True, 0.05),
 ]
 
 
