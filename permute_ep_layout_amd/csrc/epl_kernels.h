@@ -1050,10 +1050,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 // Column vectors per thread per pass (the combine's unroll): kCombineUnroll
 // from kCombineFewBelow tokens on, kCombineUnrollFew below. With few tokens
 // the smaller unroll cuts each token into more, smaller column parts, so the
-// launch's last workgroups finish sooner (DSV3, 4096 tokens: 104.0 -> 103.3
-// us; 2048 tokens at hidden 4096: 25.5 -> 24.3 us); from 16384 tokens on
-// the extra per-part overhead costs more than the shorter tail saves
-// (16384 tokens: 410 -> 412 us, 65536: 1620 -> 1631 us).
+// launch's last workgroups finish sooner (about 1% at 4096 tokens of hidden
+// 7168, 5% at 2048 tokens of hidden 4096); from 16384 tokens on the extra
+// per-part overhead costs more than the shorter tail saves (0.5-0.7%).
 constexpr int kCombineUnroll = EPL_COMBINE_UNROLL;
 constexpr int kCombineUnrollFew = EPL_COMBINE_UNROLL_FEW;
 constexpr int64_t kCombineFewBelow = EPL_COMBINE_FEW_BELOW;
