@@ -442,23 +442,45 @@ def cpu_baseline(w, inp, seconds, alignment=0):
         what = "layout, scan, FP8 row and scale-word scatter, fp64 combine of bf16 rows"
     else:
         what = "layout, scan, scatter with row copies, fp64 combine"
-    passes, rows, t0 = 0, 0, time.perf_counter()
-    while True:
-        if w.payload == "fp8":
-            cnt, _, _ = orc.layout(topk, E, R)
-            start, total = orc.scan(cnt, alignment)
-            _, _, _, oi = orc.scatter_rows(inp["x"], xs, fmt, topk, start, total)
-            orc.combine(eo, oi, wt)
-        else:
-            total = orc.run_all(inp["x"], inp["x_scale"], topk, wt, E, R,
-                                expert_fn=w.expert_fn, alignment=alignment)["total"]
-        passes += 1
-        rows += int((topk >= 0).sum())
-        el = time.perf_counter() - t0
-        if el >= seconds or passes >= 50:
-            break
+    step_s = {}
+
+    def timed(name, fn, *a, **kw):
+        t = time.perf_counter()
+        r = fn(*a, **kw)
+        step_s[name] = step_s.get(name, 0.0) + time.perf_counter() - t
+        return r
+
+    # one core: the oracle is single-threaded C; pin the timing thread to one
+    # of the CPUs it may use, and restore the mask afterwards
+    mask = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else None
+    if mask:
+        os.sched_setaffinity(0, {min(mask)})
+    try:
+        passes, rows, t0 = 0, 0, time.perf_counter()
+        while True:
+            cnt, _, _ = timed("layout", orc.layout, topk, E, R)
+            start, total = timed("scan", orc.scan, cnt, alignment)
+            if w.payload == "fp8":
+                _, _, _, oi = timed("scatter", orc.scatter_rows, inp["x"], xs, fmt, topk, start,
+                                    total)
+            else:
+                out, _, m_idx, oi = timed("scatter", orc.scatter, inp["x"], inp["x_scale"], topk,
+                                          start, total)
+                eo = out if w.expert_fn == "identity" else timed("expert", orc.expert_scale, out,
+                                                                 m_idx)
+            timed("combine", orc.combine, eo, oi, wt)
+            passes += 1
+            rows += int((topk >= 0).sum())
+            el = time.perf_counter() - t0
+            if el >= seconds or passes >= 50:
+                break
+    finally:
+        if mask:
+            os.sched_setaffinity(0, mask)
     return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} full pass(es) of the {w.name} workload ({what}), {el:.1f} s",
+            "sample": f"{passes} full pass(es) of the {w.name} workload ({what}), {el:.1f} s, "
+                      f"pinned to one CPU",
+            "per_step_ms": {k: v * 1e3 / passes for k, v in step_s.items()},
             "host": host_cpu()}
 
 
