@@ -682,6 +682,8 @@ def main():
             [a.elapsed_time(m) for a, (m, _) in zip(prev, evs)])),
         "combine": float(np.mean([m.elapsed_time(e) for m, e in evs])),
     }
+    comb = [m.elapsed_time(e) for m, e in evs]
+    spread = {"timed_combine": {"median_ms": float(np.median(comb)), "min_ms": float(np.min(comb))}}
     assert epl.epl_status(ws) == epl.EPL_OK
 
     per_kernel_ms, bubble, cold_ms, copy_gbps = {}, {}, {}, None
@@ -698,6 +700,9 @@ def main():
         torch.cuda.synchronize()
         per_kernel_ms = {
             n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in sev])) for i, n in enumerate(names)}
+        for i, n in enumerate(names):
+            ts = [e[i].elapsed_time(e[i + 1]) for e in sev]
+            spread[n] = {"median_ms": float(np.median(ts)), "min_ms": float(np.min(ts))}
         assert epl.epl_status(ws) == epl.EPL_OK
 
         # The pages' "bubble": idle GPU time between the scan that yields the row
@@ -823,6 +828,7 @@ def main():
         "per_kernel_ms": per_kernel_ms,
         "per_kernel_gbps": gbps,
         "per_kernel_rows_per_s": {n: N / (v * 1e-3) for n, v in per_kernel_ms.items()},
+        "spread": spread,
         "algorithmic_bytes": nbytes,
         "scatter_combine": {"ms": sc_ms, "gbps": sc_gbps, "frac_of_peak": sc_gbps / HBM_PEAK_GBPS},
         "scan_to_scatter_gap_us": bubble,
