@@ -618,6 +618,10 @@ constexpr int kScaleCols = 2;   // W words per row, column-major: word j of row 
 // row-major (fp32 scales) or column-major (the transposed packed-UE8M0
 // layout of the FP8 grouped GEMM).
 //
+// With PF the workgroup loads the next token's row (first pass) while it
+// stores the current one, so the row loads of a striding workgroup stay in
+// flight across tokens.
+//
 // Destination rows come from two dependent lookups per slot (expert id and
 // slot rank, then expert offset and block offset). The first K threads run
 // them ahead of the data: while token t streams, they already hold the
@@ -626,7 +630,7 @@ constexpr int kScaleCols = 2;   // W words per row, column-major: word j of row 
 // table, so one barrier per token suffices: a thread can only overwrite a
 // buffer after every thread has passed the barrier of the token in between,
 // i.e. has finished reading that buffer.
-template <int VPT>
+template <int VPT, bool PF>
 __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
     const uint8_t *__restrict__ x, int64_t row_bytes, int scale_mode,
     const uint32_t *__restrict__ x_scale, int W, bool scale_vec16, int64_t scale_ld,
@@ -685,16 +689,44 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
         }
     }
 
+    // PF: the first pass of the next token's row is loaded while the
+    // current token is stored (one token ahead).
+    u32x4 vn[VPT];
+    if (PF && tr.first < t_end) {
+        const u32x4 *xrow = reinterpret_cast<const u32x4 *>(x + tr.first * row_bytes);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int idx = i * kScatterThreads + tid;
+            if (idx < nvec)
+                vn[i] = xrow[idx];
+        }
+    }
+
     int it = 0;
     for (int64_t t = tr.first; t < t_end; t += step, ++it) {
         int64_t *rows = s_row[it & 1];
         const u32x4 *xrow = reinterpret_cast<const u32x4 *>(x + t * row_bytes);
         u32x4 v[VPT];
+        if (PF) {
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int idx = i * kScatterThreads + tid;
-            if (idx < nvec)
-                v[i] = xrow[idx];
+            for (int i = 0; i < VPT; ++i)
+                v[i] = vn[i];
+            if (t + step < t_end) {
+                const u32x4 *nrow = reinterpret_cast<const u32x4 *>(x + (t + step) * row_bytes);
+#pragma unroll
+                for (int i = 0; i < VPT; ++i) {
+                    const int idx = i * kScatterThreads + tid;
+                    if (idx < nvec)
+                        vn[i] = nrow[idx];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int idx = i * kScatterThreads + tid;
+                if (idx < nvec)
+                    v[i] = xrow[idx];
+            }
         }
         u32x4 sv = {0u, 0u, 0u, 0u};
         uint32_t sw = 0u;
