@@ -310,18 +310,23 @@ def run_ll(args, w, inp):
             "unit": "GB/s", "frac": dom_gbps / HBM_PEAK_GBPS,
             "algorithmic_bytes": nbytes[dominant], "avg_launch_ms": timed_ms[dominant],
             "traffic": measured_traffic(w.name, "ll_scatter" if dominant == "ll_dispatch"
-                                        else dominant),
+                                        else dominant, args.out_dtype),
         },
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
 
 
-def measured_traffic(workload, kernel):
+def measured_traffic(workload, kernel, out_dtype="f32", alignment=0):
     """HBM bytes per launch from the committed rocprofv3 counter summary,
-    only if it was taken on the current kernel sources."""
+    only if it was taken on the current kernel sources and with the same
+    options: the summaries profile each workload with the default options
+    (fp32 combine output, no expert alignment), whose bytes differ from
+    other settings'."""
     from permute_ep_layout_amd import profiling
 
+    if out_dtype != "f32" or alignment:
+        return None
     data = profiling.read_traffic(TRAFFIC_FILE.format(workload=workload))
     if not data or data.get("source_digest") != profiling.source_digest():
         return None
@@ -794,7 +799,7 @@ def main():
     dom_gbps = nbytes[dominant] / (kernel_ms[dominant] * 1e-3) / 1e9
     sc_ms = kernel_ms["scatter"] + kernel_ms["combine"]
     sc_gbps = (nbytes["scatter"] + nbytes["combine"]) / (sc_ms * 1e-3) / 1e9 if sc_ms else 0.0
-    traffic = measured_traffic(w.name, dominant)
+    traffic = measured_traffic(w.name, dominant, args.out_dtype, args.alignment)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -75,13 +75,17 @@ def test_padding_rows_cost_one_index_each():
 
 def test_traffic_lookup_requires_the_profiled_sources(monkeypatch):
     """roofline.traffic comes from the committed counter summary only while
-    the kernel sources match the digest it was taken on."""
+    the kernel sources match the digest it was taken on, and only for the
+    options it was taken with."""
     path = bench.TRAFFIC_FILE.format(workload="dsv3")
     data = profiling.read_traffic(path)
     assert data and "combine" in data["kernels"]
     if data["source_digest"] == profiling.source_digest():
         got = bench.measured_traffic("dsv3", "combine")
         assert got == data["kernels"]["combine"]["bytes_per_launch"]
+    # the summaries were taken with the default options only
+    assert bench.measured_traffic("dsv3", "combine", out_dtype="bf16") is None
+    assert bench.measured_traffic("dsv3", "combine", alignment=128) is None
     monkeypatch.setattr(profiling, "source_digest", lambda root=None: "0" * 16)
     assert bench.measured_traffic("dsv3", "combine") is None
     assert bench.measured_traffic("no_such_workload", "combine") is None
