@@ -237,10 +237,10 @@ void launch_scatter(const epl_problem &p, const WsLayout &w, const RowArgs &ra,
     const bool vec16 = ra.scale_mode == epl::kScaleRows && ra.words % 4 == 0 &&
                        aligned(ra.x_scale, 16) && aligned(ra.out_scale, 16);
     // A workgroup that strides over at least 4 tokens loads the next one's
-    // row while it stores the current one. At DSV3 (4 tokens per workgroup)
-    // this took the HBM-only scatter from 112-114 to 107-108 us and FP8 rows
-    // from 59.7 to 56.7 us, with the batch in the Infinity Cache no change;
-    // with 2 tokens per workgroup (2048 tokens) it cost ~4%.
+    // row while it stores the current one. At 4096 tokens of hidden 7168 (4
+    // tokens per workgroup) this took the HBM-only scatter from 112-114 to
+    // 107-110 us (FP8 rows: 59.7 to 56.7 us), with the batch in the Infinity
+    // Cache no change; with 2 tokens per workgroup (2048 tokens) it cost ~4%.
     const bool pf = EPL_SCATTER_PF && (int64_t)grid * 4 <= p.num_tokens;
     auto kernel = pf ? epl::ep_scatter_kernel<VPT, true> : epl::ep_scatter_kernel<VPT, false>;
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(epl::kScatterThreads), 0, s,
