@@ -84,12 +84,30 @@ bool fp8_problem_ok(const epl_problem *p, int scale_format)
 #define EPL_LAYOUT_MIN_TOKENS 16   // smallest block
 #endif
 
+#ifndef EPL_LAYOUT_MATRIX_BUDGET
+#define EPL_LAYOUT_MATRIX_BUDGET 65536
+#endif
+
 // Tokens per layout block: enough blocks to spread the work (about 64), but
 // at most 256 tokens (one per thread) and at most 2048 slots (the LDS key
 // buffer), and at least 16 tokens so the per-block count matrix stays small.
+// With many tokens, blocks stay at 64 tokens (else 128) while the matrix the
+// scan reduces, blocks x (experts + rank and node columns), holds at most
+// EPL_LAYOUT_MATRIX_BUDGET entries: smaller blocks rank their slots sooner,
+// but a larger matrix makes the single-workgroup scan longer. Measured on
+// layout + reduce: 29765 tokens with 8 local experts 20.6 -> 14.9 us (64),
+// 16384 tokens with 256 experts 25.2 -> 22.9 us (128), while 65536 tokens
+// with 256 experts keep 256 (128 would take 35.3 -> 42.9 us).
 int layout_block_tokens(const epl_problem &p)
 {
     int64_t cap = std::min<int64_t>(epl::kLayoutThreads, epl::kMaxSlotsPerBlock / p.num_topk);
+    const int64_t cols = (int64_t)p.num_experts + p.num_ranks + nodes_of(p);
+    for (int64_t b : {64, 128}) {
+        if ((p.num_tokens + b - 1) / b * cols <= EPL_LAYOUT_MATRIX_BUDGET) {
+            cap = std::min(cap, b);
+            break;
+        }
+    }
     // the LDS bound: keys and ranks take 8 bytes per slot
     const size_t fixed =
         epl::layout_lds_bytes(0, p.num_topk, p.num_experts, p.num_ranks + nodes_of(p));
