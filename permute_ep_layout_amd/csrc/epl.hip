@@ -241,27 +241,18 @@ struct RowArgs {
     uint32_t *out_scale;
 };
 
-#ifndef EPL_SCATTER_PF
-#define EPL_SCATTER_PF 1
-#endif
 template <int VPT>
 void launch_scatter(const epl_problem &p, const WsLayout &w, const RowArgs &ra,
                     const int64_t *topk, const int32_t *start, void *ws, int64_t cap,
                     int32_t *m_idx, int32_t *oi, hipStream_t s)
 {
-    const unsigned grid = p.num_tokens >= epl::kScatterGridFrom
-                              ? row_grid(p.num_tokens, p.num_tokens)
-                              : row_grid(p.num_tokens, epl::kScatterGrid);
+    const unsigned grid =
+        p.num_tokens >= epl::kScatterGridFrom ? row_grid(p.num_tokens, p.num_tokens)
+        : ra.row_bytes >= epl::kScatterLongRowBytes ? row_grid(p.num_tokens, epl::kScatterGridLong)
+                                                     : row_grid(p.num_tokens, epl::kScatterGrid);
     const bool vec16 = ra.scale_mode == epl::kScaleRows && ra.words % 4 == 0 &&
                        aligned(ra.x_scale, 16) && aligned(ra.out_scale, 16);
-    // A workgroup that strides over at least 4 tokens loads the next one's
-    // row while it stores the current one. At 4096 tokens of hidden 7168 (4
-    // tokens per workgroup) this took the HBM-only scatter from 112-114 to
-    // 107-110 us (FP8 rows: 59.7 to 56.7 us), with the batch in the Infinity
-    // Cache no change; with 2 tokens per workgroup (2048 tokens) it cost ~4%.
-    const bool pf = EPL_SCATTER_PF && (int64_t)grid * 4 <= p.num_tokens;
-    auto kernel = pf ? epl::ep_scatter_kernel<VPT, true> : epl::ep_scatter_kernel<VPT, false>;
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(epl::kScatterThreads), 0, s,
+    hipLaunchKernelGGL(epl::ep_scatter_kernel<VPT>, dim3(grid), dim3(epl::kScatterThreads), 0, s,
                        ra.x, ra.row_bytes, ra.scale_mode, ra.x_scale, ra.words, vec16,
                        ra.scale_ld, topk, start, at<const int32_t>(ws, w.block_count),
                        at<const int32_t>(ws, w.slot_rank), p.num_tokens, p.num_topk,
