@@ -154,7 +154,19 @@ WsLayout ws_layout(const epl_problem &p, int block_tokens)
     return w;
 }
 
-WsLayout ws_layout(const epl_problem &p) { return ws_layout(p, layout_block_tokens(p)); }
+// Batches that one workgroup lays out and scans by itself (see
+// ep_layout_scan_kernel): all their tokens form a single block.
+bool fused_layout(const epl_problem &p)
+{
+    return p.num_tokens >= 1 && p.num_tokens * (int64_t)p.num_topk <= epl::kFusedMaxSlots &&
+           p.num_experts <= epl::kFusedMaxExperts &&
+           p.num_ranks + nodes_of(p) <= epl::kFusedMaxCols;
+}
+
+WsLayout ws_layout(const epl_problem &p)
+{
+    return ws_layout(p, fused_layout(p) ? (int)p.num_tokens : layout_block_tokens(p));
+}
 
 template <typename T>
 T *at(void *ws, size_t off)
@@ -206,6 +218,33 @@ int32_t *mapped_host_word(int32_t *host)
         return nullptr;
     }
     return static_cast<int32_t *>(dev);
+}
+
+// Layout and scan of a small batch in one launch (fused_layout(p)). With
+// `start` null only the layout's outputs are produced (epl_layout); with it,
+// also expert_start_loc and N, copied to *total_host if that is not null.
+int enqueue_fused(const epl_problem &p, const WsLayout &w, const int64_t *topk, uint8_t *in_rank,
+                  int32_t *cnt, int32_t *per_rank, int32_t *per_node, int32_t *start,
+                  int32_t *total_host, void *ws, hipStream_t s)
+{
+    const bool vec16 = (p.num_ranks % 16 == 0) && aligned(in_rank, 16);
+    int32_t *mapped = start ? mapped_host_word(total_host) : nullptr;
+    hipLaunchKernelGGL(epl::ep_layout_scan_kernel, dim3(1), dim3(epl::kFusedThreads), 0, s, topk,
+                       p.num_tokens, p.num_topk, p.num_experts, p.num_ranks,
+                       p.num_experts / p.num_ranks, epl::div_magic(p.num_experts / p.num_ranks),
+                       p.ranks_per_node, epl::div_magic(std::max(p.ranks_per_node, 1)), nodes_of(p),
+                       alignment_of(p), in_rank, vec16, cnt, per_rank, per_node, start,
+                       at<int32_t>(ws, w.block_count), at<int32_t>(ws, w.slot_rank),
+                       at<int32_t>(ws, w.counts), at<WsHeader>(ws, 0), mapped);
+    int rc = launch_status();
+    if (rc != EPL_OK)
+        return rc;
+    if (start && total_host && !mapped) {
+        if (hipMemcpyAsync(total_host, &at<WsHeader>(ws, 0)->total, sizeof(int32_t),
+                           hipMemcpyDeviceToHost, s) != hipSuccess)
+            return EPL_EHIP;
+    }
+    return EPL_OK;
 }
 
 int enqueue_scan(const epl_problem &p, const WsLayout &w, int mode, int32_t *cnt, int32_t *per_rank,
@@ -426,6 +465,10 @@ int epl_layout(const epl_problem *p, const int64_t *topk_idx, int32_t *num_token
         return EPL_EINVAL;
     const WsLayout w = ws_layout(*p);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (fused_layout(*p))
+        return enqueue_fused(*p, w, topk_idx, is_token_in_rank, num_tokens_per_expert,
+                             num_tokens_per_rank, nodes_of(*p) ? num_tokens_per_rdma_rank : nullptr,
+                             nullptr, nullptr, workspace, s);
     int rc = enqueue_layout(*p, w, topk_idx, is_token_in_rank, workspace, s);
     if (rc != EPL_OK)
         return rc;
@@ -506,11 +549,19 @@ static int dispatch_rows(const epl_problem *p, const int64_t *topk_idx, const Ro
         return EPL_EINVAL;
     const WsLayout w = ws_layout(*p);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    int rc = enqueue_layout(*p, w, topk_idx, is_token_in_rank, workspace, s);
-    if (rc == EPL_OK)
-        rc = enqueue_scan(*p, w, epl::kScanReduce | epl::kScanPrefix, num_tokens_per_expert,
-                          num_tokens_per_rank, nodes_of(*p) ? num_tokens_per_rdma_rank : nullptr,
-                          expert_start_loc, total_host, workspace, s);
+    int rc;
+    if (fused_layout(*p)) {
+        rc = enqueue_fused(*p, w, topk_idx, is_token_in_rank, num_tokens_per_expert,
+                           num_tokens_per_rank, nodes_of(*p) ? num_tokens_per_rdma_rank : nullptr,
+                           expert_start_loc, total_host, workspace, s);
+    } else {
+        rc = enqueue_layout(*p, w, topk_idx, is_token_in_rank, workspace, s);
+        if (rc == EPL_OK)
+            rc = enqueue_scan(*p, w, epl::kScanReduce | epl::kScanPrefix, num_tokens_per_expert,
+                              num_tokens_per_rank,
+                              nodes_of(*p) ? num_tokens_per_rdma_rank : nullptr,
+                              expert_start_loc, total_host, workspace, s);
+    }
     if (rc == EPL_OK)
         rc = enqueue_scatter(*p, w, ra, topk_idx, expert_start_loc, workspace, capacity_rows,
                              m_indices, output_index, s);

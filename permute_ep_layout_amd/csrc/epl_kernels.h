@@ -545,6 +545,204 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
     }
 }
 
+// ------------------------------------------------- layout + scan, fused --
+
+// Decode-sized batches (at most kFusedMaxSlots slots, kFusedMaxExperts experts
+// and kFusedMaxCols rank + node columns) run layout and scan in one workgroup:
+// the slots need no per-block offsets, so the per-block count matrix and the
+// second launch that reduces it go away. The results are those of
+// ep_layout_kernel + ep_scan_kernel with a single block of all T tokens:
+// block_count (one row of E zeros), slot_rank = rank of slot (t, k) among
+// all earlier slots of its expert, per-expert / per-rank / per-node counts,
+// the token -> rank mask, the counts copy for the padding rows, the status
+// word, and, if `start` is not null, expert_start_loc and N (header, and the
+// caller's host-mapped word if `total_out` is not null).
+//
+// Ranking: wave w owns a contiguous run of 64-slot chunks and walks it in
+// order, as in ep_layout_kernel; each lane keeps its chunks' keys and
+// in-wave ranks in registers (at most kFusedChunksPerWave per lane), a
+// prefix over the 16 waves per expert then turns them into global ranks.
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedWaves = kFusedThreads / kWave;
+// At DeepSeek-V3 dimensions (top-8 of 256 experts) one workgroup beats the
+// two launches up to 2048 slots (dispatch 2.1-2.7 us faster at 64-256
+// tokens), ties at 4096 and loses beyond (8192 slots: +4 us; 12288 slots
+// at hidden 4096: layout 11 -> 30 us), as the waves walk their chunks in turn.
+constexpr int kFusedMaxSlots = 2048;
+constexpr int kFusedChunksPerWave = kFusedMaxSlots / kWave / kFusedWaves;
+constexpr int kFusedMaxExperts = 256;
+constexpr int kFusedMaxCols = 256;
+static_assert(kFusedThreads == kScanThreads, "the fused kernel reuses the scan's block scan");
+
+__global__ __launch_bounds__(kFusedThreads) void ep_layout_scan_kernel(
+    const int64_t *__restrict__ topk, int64_t T, int K, int E, int R, int experts_per_rank,
+    uint32_t epr_magic, int G, uint32_t node_magic, int Rn, int alignment,
+    uint8_t *__restrict__ in_rank, bool in_rank_vec16, int32_t *__restrict__ cnt,
+    int32_t *__restrict__ per_rank, int32_t *__restrict__ per_node, int32_t *__restrict__ start,
+    int32_t *__restrict__ block_count, int32_t *__restrict__ slot_rank,
+    int32_t *__restrict__ ws_counts, WsHeader *__restrict__ hdr, int32_t *__restrict__ total_out)
+{
+    __shared__ int32_t wave_cnt[kFusedWaves][kFusedMaxExperts];
+    __shared__ uint32_t chunk_cnt[kFusedWaves][kFusedMaxExperts / 4];
+    __shared__ int32_t rank_cnt[kFusedMaxCols];
+    __shared__ int s_wave[kFusedWaves];
+    __shared__ uint32_t s_err;
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid / kWave;
+    const int ns = (int)(T * K);
+    const int RC = R + Rn;
+
+    for (int i = tid; i < kFusedWaves * kFusedMaxExperts; i += kFusedThreads)
+        (&wave_cnt[0][0])[i] = 0;
+    for (int i = tid; i < kFusedWaves * (kFusedMaxExperts / 4); i += kFusedThreads)
+        (&chunk_cnt[0][0])[i] = 0u;
+    for (int i = tid; i < RC; i += kFusedThreads)
+        rank_cnt[i] = 0;
+    if (tid == 0)
+        s_err = 0u;
+    lds_barrier();
+
+    // Keys of this lane's slots, one per chunk of the wave's run.
+    const int nchunks = (ns + kWave - 1) / kWave;
+    const int cpw = (nchunks + kFusedWaves - 1) / kFusedWaves;
+    const int c0 = wave * cpw;
+    int key[kFusedChunksPerWave];
+    int lrank[kFusedChunksPerWave];
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < kFusedChunksPerWave; ++i) {
+        const int s = (c0 + i) * kWave + lane;
+        int64_t e = -1;
+        if (i < cpw && s < ns)
+            e = topk[s];
+        bad |= (e < -1 || e >= E);
+        key[i] = (e >= 0 && e < E) ? (int)e : -1;
+        lrank[i] = 0;
+    }
+    if (bad)
+        atomicOr(&s_err, 1u);
+
+    // In-wave ranks, chunk by chunk in order (see ep_layout_kernel).
+    {
+        int32_t *my_cnt = wave_cnt[wave];
+        uint32_t *my_chunk = chunk_cnt[wave];
+        const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+#pragma unroll
+        for (int i = 0; i < kFusedChunksPerWave; ++i) {
+            // chunks past the wave's run hold only -1 keys: no-ops
+            const int k16 = key[i] >= 0 ? key[i] : 0;
+            const bool valid = key[i] >= 0;
+            const int shift = 8 * (k16 & 3);
+            if (valid)
+                atomicAdd(&my_chunk[k16 >> 2], 1u << shift);
+            const int group = valid ? (int)((my_chunk[k16 >> 2] >> shift) & 0xFFu) : 0;
+            int rank = 0;
+            uint64_t todo = wave_ballot(group > 1);
+            while (todo) {
+                const int leader = (int)__builtin_ctzll(todo);
+                const int lkey = __builtin_amdgcn_readlane(k16, leader);
+                const uint64_t same = wave_ballot(valid && k16 == lkey);
+                if (valid && k16 == lkey)
+                    rank = __popcll(same & lower);
+                todo &= ~same;
+            }
+            if (valid) {
+                const int base = my_cnt[k16];
+                lrank[i] = base + rank;
+                if (rank == 0) {
+                    my_cnt[k16] = base + group;
+                    atomicAnd(&my_chunk[k16 >> 2], ~(0xFFu << shift));
+                }
+            }
+        }
+    }
+
+    // Token -> rank mask and tokens per rank / node (one thread per token,
+    // keys read again from topk_idx).
+    for (int64_t t = tid; t < T; t += kFusedThreads) {
+        const int64_t *row = topk + t * K;
+        for (int w0 = 0; w0 < R; w0 += 64) {
+            const int wr = min(64, R - w0);
+            uint64_t mask = 0;
+            for (int k = 0; k < K; ++k) {
+                const int64_t e = row[k];
+                if (e >= 0 && e < E) {
+                    const int r = div_small((uint32_t)e, experts_per_rank, epr_magic) - w0;
+                    if (r >= 0 && r < wr)
+                        mask |= 1ull << r;
+                }
+            }
+            if (in_rank)
+                store_mask_bytes(in_rank + t * R + w0, mask, wr, in_rank_vec16);
+            for (uint64_t m = mask; m; m &= m - 1)
+                atomicAdd(&rank_cnt[w0 + __builtin_ctzll(m)], 1);
+        }
+        for (int n0 = 0; n0 < Rn; n0 += 64) {
+            const int wn = min(64, Rn - n0);
+            uint64_t mask = 0;
+            for (int k = 0; k < K; ++k) {
+                const int64_t e = row[k];
+                if (e >= 0 && e < E) {
+                    const int r = div_small((uint32_t)e, experts_per_rank, epr_magic);
+                    const int n = div_small((uint32_t)r, G, node_magic) - n0;
+                    if (n >= 0 && n < wn)
+                        mask |= 1ull << n;
+                }
+            }
+            for (uint64_t m = mask; m; m &= m - 1)
+                atomicAdd(&rank_cnt[R + n0 + __builtin_ctzll(m)], 1);
+        }
+    }
+    lds_barrier();
+
+    // Per expert: exclusive prefix over the waves (in place) and the total.
+    int blk = 0;
+    if (tid < E) {
+        int run = 0;
+        for (int w = 0; w < kFusedWaves; ++w) {
+            const int c = wave_cnt[w][tid];
+            wave_cnt[w][tid] = run;
+            run += c;
+        }
+        if (cnt)
+            cnt[tid] = run;
+        ws_counts[tid] = run;
+        block_count[tid] = 0;
+        blk = (run + alignment - 1) / alignment * alignment;
+    }
+    for (int r = tid; r < RC; r += kFusedThreads) {
+        if (r < R) {
+            if (per_rank)
+                per_rank[r] = rank_cnt[r];
+        } else if (per_node) {
+            per_node[r - R] = rank_cnt[r];
+        }
+    }
+    if (tid == 0)
+        hdr->status = s_err ? kStatusBadExpert : 0u;
+    // expert_start_loc and N (the block scan has its own barriers, which
+    // also order the wave_cnt rewrite above before the slot ranks below)
+    const int incl = block_inclusive_scan(blk, s_wave);
+    if (start) {
+        if (tid < E)
+            start[tid] = incl - blk;
+        if (tid == kFusedThreads - 1) {
+            hdr->total = incl;
+            if (total_out)
+                *total_out = incl;
+        }
+    }
+
+    // Global rank of every slot.
+#pragma unroll
+    for (int i = 0; i < kFusedChunksPerWave; ++i) {
+        const int s = (c0 + i) * kWave + lane;
+        if (i < cpw && s < ns)
+            slot_rank[s] = key[i] >= 0 ? lrank[i] + wave_cnt[wave][key[i]] : -1;
+    }
+}
+
 // -------------------------------------------------------------- scatter --
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

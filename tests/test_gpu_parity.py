@@ -403,6 +403,10 @@ RAGGED = [
     # one-workgroup-per-token grid, with ragged rows
     ("many_tokens_h264", 9000, 5, 24, 6, 264, False, 0.1),
     ("many_tokens_scales_s9", 8500, 4, 32, 8, 1152, True, 0.05),
+    # the single-workgroup layout + scan holds at most 2048 slots: at the
+    # limit, and one token past it (the two-launch layout)
+    ("fused_limit_2048_slots", 256, 8, 256, 32, 128, False, 0.1),
+    ("fused_limit_plus_one_token", 257, 8, 256, 32, 128, False, 0.1),
     # 4096 .. 8191 tokens: scatter workgroups stride over 4 to 8 tokens each
     # and load the next token's row ahead, with uneven token counts per
     # workgroup
