@@ -25,6 +25,8 @@
 // expert in (token, k) order with wavefront ballots; the scan kernel turns
 // the per-block counts into per-block offsets (a prefix over blocks per
 // expert); the scatter kernel adds expert offset + block offset + rank.
+// Decode-sized batches (at most 2048 slots) take ep_layout_scan_kernel
+// instead: one workgroup, one block, both steps in a single launch.
 #pragma once
 
 #include <hip/hip_runtime.h>
