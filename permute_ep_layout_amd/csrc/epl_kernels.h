@@ -37,7 +37,8 @@
 namespace epl {
 
 constexpr int kWave = 64;
-constexpr int kLayoutThreads = 256;
+constexpr int kLayoutThreads = 256;       // any number of experts
+constexpr int kLayoutThreadsWide = 1024;  // when its per-wave counters fit in LDS
 constexpr int kLayoutWaves = kLayoutThreads / kWave;
 constexpr int kMaxSlotsPerBlock = 2048;   // B * K per layout block
 constexpr int kMaxTopk = 64;
@@ -160,36 +161,40 @@ __device__ __forceinline__ void store_mask_bytes(uint8_t *dst, uint64_t mask, in
 // (R ranks, then the nodes if asked for), B tokens of K slots. Kept <=
 // kLayoutLdsBytes by the host's choice of B.
 constexpr size_t kLayoutLdsBytes = 65536;
-__host__ __device__ constexpr size_t layout_lds_bytes(int B, int K, int E, int RC)
+__host__ __device__ constexpr size_t layout_lds_bytes(int B, int K, int E, int RC,
+                                                      int waves = kLayoutWaves)
 {
     return sizeof(int32_t) * ((size_t)2 * B * K              // keys, ranks
-                              + (size_t)kLayoutWaves * E      // running count per wave and expert
-                              + (size_t)kLayoutWaves * ((E + 3) / 4)   // per-chunk byte counters
+                              + (size_t)waves * E             // running count per wave and expert
+                              + (size_t)waves * ((E + 3) / 4) // per-chunk byte counters
                               + (size_t)RC + 1);              // tokens per rank / node, error flag
 }
 
-// One workgroup per block of B tokens (B <= kLayoutThreads, B * K <=
+// One workgroup of THREADS threads (kLayoutThreads, or kLayoutThreadsWide
+// when the per-wave counters fit) per block of B tokens (B <= THREADS, B * K <=
 // kMaxSlotsPerBlock). Outputs: in_rank rows of the block's tokens;
 // block_count[b][e] (slots of expert e in block b); block_rank[b][c] (tokens
 // of block b sent to rank c for c < R, to node c - R for R <= c < R + Rn,
 // a node being G consecutive ranks); block_err[b]; slot_rank[t*K+k] = rank
 // of slot (t,k) among the block's earlier slots of the same expert, or -1
 // for an invalid slot.
-__global__ __launch_bounds__(kLayoutThreads) void ep_layout_kernel(
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void ep_layout_kernel(
     const int64_t *__restrict__ topk, int64_t T, int K, int E, int R, int experts_per_rank,
     uint32_t epr_magic, int G, uint32_t node_magic, int Rn, int B, uint8_t *__restrict__ in_rank,
     bool in_rank_vec16,
     int32_t *__restrict__ block_count, int32_t *__restrict__ block_rank,
     uint32_t *__restrict__ block_err, int32_t *__restrict__ slot_rank)
 {
+    constexpr int WAVES = THREADS / kWave;
     extern __shared__ int32_t lds[];
     const int max_slots = B * K;
     const int cwords = (E + 3) / 4;
     int32_t *keys = lds;                                   // [B*K] key | owner << 16, or -1
     int32_t *lrank = keys + max_slots;                     // [B*K] rank within the owning wave
     int32_t *wave_cnt = lrank + max_slots;                 // [waves][E]
-    uint32_t *chunk_cnt = reinterpret_cast<uint32_t *>(wave_cnt + kLayoutWaves * E);  // [waves][E/4]
-    int32_t *rank_cnt = reinterpret_cast<int32_t *>(chunk_cnt + kLayoutWaves * cwords); // [R+Rn]
+    uint32_t *chunk_cnt = reinterpret_cast<uint32_t *>(wave_cnt + WAVES * E);  // [waves][E/4]
+    int32_t *rank_cnt = reinterpret_cast<int32_t *>(chunk_cnt + WAVES * cwords); // [R+Rn]
     const int RC = R + Rn;
     int32_t *s_err = rank_cnt + RC;                        // [1]
 
@@ -201,11 +206,11 @@ __global__ __launch_bounds__(kLayoutThreads) void ep_layout_kernel(
     const int lane = lane_id();
     const int wave = tid / kWave;
 
-    for (int i = tid; i < kLayoutWaves * E; i += kLayoutThreads)
+    for (int i = tid; i < WAVES * E; i += THREADS)
         wave_cnt[i] = 0;
-    for (int i = tid; i < kLayoutWaves * cwords; i += kLayoutThreads)
+    for (int i = tid; i < WAVES * cwords; i += THREADS)
         chunk_cnt[i] = 0;
-    for (int i = tid; i < RC; i += kLayoutThreads)
+    for (int i = tid; i < RC; i += THREADS)
         rank_cnt[i] = 0;
     if (tid == 0)
         *s_err = 0;
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(kLayoutThreads) void ep_layout_kernel(
     // rank; bad ids become -1.
     const int64_t *src = topk + t0 * K;
     bool bad = false;
-    for (int s = tid; s < ns; s += kLayoutThreads) {
+    for (int s = tid; s < ns; s += THREADS) {
         const int64_t e = src[s];
         int packed = -1;
         if (e >= 0 && e < E)
@@ -236,7 +241,7 @@ __global__ __launch_bounds__(kLayoutThreads) void ep_layout_kernel(
     // its key. Then every lane adds the wave's running count for its key, and
     // the lowest lane of each key advances that count and clears the byte.
     const int nchunks = (ns + kWave - 1) / kWave;
-    const int cpw = (nchunks + kLayoutWaves - 1) / kLayoutWaves;
+    const int cpw = (nchunks + WAVES - 1) / WAVES;
     {
         int32_t *my_cnt = wave_cnt + wave * E;
         uint32_t *my_chunk = chunk_cnt + wave * cwords;
@@ -313,22 +318,22 @@ __global__ __launch_bounds__(kLayoutThreads) void ep_layout_kernel(
     lds_barrier();
 
     // Per expert: exclusive prefix over the waves (in place) and block total.
-    for (int e = tid; e < E; e += kLayoutThreads) {
+    for (int e = tid; e < E; e += THREADS) {
         int run = 0;
-        for (int w = 0; w < kLayoutWaves; ++w) {
+        for (int w = 0; w < WAVES; ++w) {
             const int c = wave_cnt[w * E + e];
             wave_cnt[w * E + e] = run;
             run += c;
         }
         block_count[b * E + e] = run;
     }
-    for (int r = tid; r < RC; r += kLayoutThreads)
+    for (int r = tid; r < RC; r += THREADS)
         block_rank[b * RC + r] = rank_cnt[r];
     lds_barrier();
     if (tid == 0)
         block_err[b] = (uint32_t)*s_err;
 
-    for (int s = tid; s < ns; s += kLayoutThreads) {
+    for (int s = tid; s < ns; s += THREADS) {
         const int packed = keys[s];
         const int w = (s / kWave) / cpw;
         slot_rank[t0 * K + s] = packed >= 0 ? lrank[s] + wave_cnt[w * E + (packed & 0xFFFF)] : -1;
