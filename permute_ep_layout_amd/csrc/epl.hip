@@ -88,32 +88,31 @@ bool fp8_problem_ok(const epl_problem *p, int scale_format)
 #define EPL_LAYOUT_MATRIX_BUDGET 65536
 #endif
 
-// Tokens per layout block: enough blocks to spread the work (about 64), but
-// at most 256 tokens (one per thread) and at most 2048 slots (the LDS key
-// buffer), and at least 16 tokens so the per-block count matrix stays small.
-// With many tokens, blocks stay at 64 tokens (else 128) while the matrix the
-// scan reduces, blocks x (experts + rank and node columns), holds at most
-// EPL_LAYOUT_MATRIX_BUDGET entries: smaller blocks rank their slots sooner,
-// but a larger matrix makes the single-workgroup scan longer. Measured on
-// layout + reduce: 29765 tokens with 8 local experts 20.6 -> 14.9 us (64),
-// 16384 tokens with 256 experts 25.2 -> 22.9 us (128), while 65536 tokens
-// with 256 experts keep 256 (128 would take 35.3 -> 42.9 us).
-#ifndef EPL_LAYOUT_WIDE_BELOW
-#define EPL_LAYOUT_WIDE_BELOW 8192
-#endif
+// Tokens per layout block for 256-thread workgroups (expert counts too wide
+// for the 1024-thread layout): enough blocks to spread the work (about 64),
+// but at most 256 tokens (one per thread) and at most 2048 slots (the LDS
+// key buffer), and at least 16 tokens so the per-block count matrix stays
+// small. With many tokens, blocks stay at 64 tokens (else 128) while the
+// matrix the scan reduces, blocks x (experts + rank and node columns), holds
+// at most EPL_LAYOUT_MATRIX_BUDGET entries: smaller blocks rank their slots
+// sooner, but a larger matrix makes the single-workgroup scan longer.
+// Measured with 256-thread workgroups on layout + reduce: 29765 tokens with
+// 8 local experts 20.6 -> 14.9 us (64), 16384 tokens with 256 experts 25.2
+// -> 22.9 us (128), while 65536 tokens with 256 experts keep 256 (128 would
+// take 35.3 -> 42.9 us).
 #ifndef EPL_LAYOUT_BLOCKS_WIDE
 #define EPL_LAYOUT_BLOCKS_WIDE 32
 #endif
 
-// Below EPL_LAYOUT_WIDE_BELOW tokens, when the per-wave counters of 16 waves
-// fit in LDS (up to ~512 experts), the layout runs 1024-thread workgroups on
-// about 32 blocks: each block ranks its slots with 4x the waves, and the scan
-// reduces a matrix of half as many blocks (4096 tokens of hidden 7168:
-// layout + reduce 15.3 -> 13.9 us, dispatch 108.5 -> 106.4 us).
+// When the per-wave counters of 16 waves fit in LDS (up to ~512 experts),
+// the layout runs 1024-thread workgroups on about 32 blocks of at most 256
+// tokens: each block ranks its slots with 4x the waves, and the scan
+// reduces a matrix of fewer blocks. Layout + reduce: 4096 tokens of hidden
+// 7168 15.2 -> 13.8 us, 16384 tokens 22.8 -> 16.6 us, 65536 tokens 35.2 ->
+// 28.3 us; the receive side (29765 tokens, 8 experts) unchanged. Wider
+// expert counts keep 256-thread workgroups and the block rule below.
 bool wide_layout(const epl_problem &p)
 {
-    if (p.num_tokens >= EPL_LAYOUT_WIDE_BELOW)
-        return false;
     const int bmax = std::min(256, epl::kMaxSlotsPerBlock / p.num_topk);
     return epl::layout_lds_bytes(bmax, p.num_topk, p.num_experts, p.num_ranks + nodes_of(p),
                                  epl::kLayoutThreadsWide / epl::kWave) <= epl::kLayoutLdsBytes;
