@@ -407,9 +407,8 @@ RAGGED = [
     # limit, and one token past it (the two-launch layout)
     ("fused_limit_2048_slots", 256, 8, 256, 32, 128, False, 0.1),
     ("fused_limit_plus_one_token", 257, 8, 256, 32, 128, False, 0.1),
-    # 4096 .. 8191 tokens: scatter workgroups stride over 4 to 8 tokens each
-    # and load the next token's row ahead, with uneven token counts per
-    # workgroup
+    # 4096 .. 8191 tokens: each scatter workgroup strides over several
+    # tokens (4 to 16), with uneven token counts per workgroup
     ("prefetch_ragged_h264", 5555, 5, 24, 6, 264, False, 0.1),
     ("prefetch_scales_s9", 7000, 4, 32, 8, 1152, True, 0.05),
 ]
