@@ -371,8 +371,8 @@ def test_fp8_dsv3_ue8m0_parity():
     ("ue8m0_s5_aligned", 900, 640, 24, 5, 6, epl.EPL_SCALE_UE8M0, 32, 0, False),
     ("ue8m0_spare_capacity", 400, 512, 16, 2, 4, epl.EPL_SCALE_UE8M0, 0, 77, True),
     ("ue8m0_large_t", 9000, 256, 64, 6, 8, epl.EPL_SCALE_UE8M0, 16, 0, False),
-    ("ue8m0_prefetch", 6001, 384, 64, 6, 8, epl.EPL_SCALE_UE8M0, 0, 0, False),
-    ("none_prefetch_split_aligned", 4999, 272, 24, 3, 6, epl.EPL_SCALE_NONE, 8, 0, True),
+    ("ue8m0_striding", 6001, 384, 64, 6, 8, epl.EPL_SCALE_UE8M0, 0, 0, False),
+    ("none_striding_split_aligned", 4999, 272, 24, 3, 6, epl.EPL_SCALE_NONE, 8, 0, True),
 ], ids=lambda c: c[0])
 def test_fp8_shapes(case):
     name, T, H, E, K, R, fmt, a, extra, split = case
@@ -409,8 +409,8 @@ RAGGED = [
     ("fused_limit_plus_one_token", 257, 8, 256, 32, 128, False, 0.1),
     # 4096 .. 8191 tokens: each scatter workgroup strides over several
     # tokens (4 to 16), with uneven token counts per workgroup
-    ("prefetch_ragged_h264", 5555, 5, 24, 6, 264, False, 0.1),
-    ("prefetch_scales_s9", 7000, 4, 32, 8, 1152, True, 0.05),
+    ("striding_ragged_h264", 5555, 5, 24, 6, 264, False, 0.1),
+    ("striding_scales_s9", 7000, 4, 32, 8, 1152, True, 0.05),
 ]
 
 
