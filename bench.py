@@ -343,11 +343,9 @@ def stream_ceilings(mib):
     import numpy as np
     import torch
 
-    from permute_ep_layout_amd import build as B
+    import bench_probe
 
-    if not os.path.exists(B.PROBE_LIB):
-        raise RuntimeError(f"{B.PROBE_LIB} is not built (run python __graft_entry__.py build)")
-    lib = ctypes.CDLL(B.PROBE_LIB)
+    lib = ctypes.CDLL(bench_probe.ensure_built(verbose=True))
     for f in (lib.epl_probe_mix, lib.epl_probe_fan):
         f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                       ctypes.c_int, ctypes.c_int, ctypes.c_uint, ctypes.c_void_p]
@@ -426,67 +424,163 @@ def copy_calibration(nbytes):
 
 
 def cpu_baseline(w, inp, seconds, alignment=0):
-    """The CPU oracle as it stands, single-threaded, over full passes of the
-    same workload until about `seconds` of work."""
+    """The CPU oracle as it stands, single-threaded: full passes of the same
+    workload (layout, scan, scatter, expert stand-in if any, fp64 combine) in
+    the oracle's C timing harness, which times every step with the monotonic
+    clock on output buffers allocated once before the passes. At least three
+    passes, and more until about `seconds` of work; the reported rate and
+    step times are medians over the passes."""
     import numpy as np
 
     import oracle
     from permute_ep_layout_amd import workloads
 
     orc = oracle.default()
-    E, R = w.num_experts, w.num_ranks
     topk, wt = inp["topk_idx"], inp["topk_weights"]
     if w.payload == "fp8":
         # FP8 rows out; the combine reads the bf16 expert output, stood in for
         # (outside the timed passes) by the bf16 rows of the same tokens
-        cnt, _, _ = orc.layout(topk, E, R)
+        cnt, _, _ = orc.layout(topk, w.num_experts, w.num_ranks)
         start, total = orc.scan(cnt, alignment)
         eo = orc.scatter(workloads.make_x(w), None, topk, start, total)[0]
         fmt = orc.SCALE_COLS if w.scale_format == "ue8m0" else orc.SCALE_ROWS
         xs = None if inp["x_scale"] is None else inp["x_scale"].view(np.uint32)
+        run = orc.timed_passes(inp["x"], xs, fmt, topk, wt, w.num_experts, w.num_ranks,
+                               w.hidden, expert_mode=2, expert_out=eo, alignment=alignment)
         what = "layout, scan, FP8 row and scale-word scatter, fp64 combine of bf16 rows"
     else:
-        what = "layout, scan, scatter with row copies, fp64 combine"
-    step_s = {}
-
-    def timed(name, fn, *a, **kw):
-        t = time.perf_counter()
-        r = fn(*a, **kw)
-        step_s[name] = step_s.get(name, 0.0) + time.perf_counter() - t
-        return r
+        run = orc.timed_passes(inp["x"], inp["x_scale"], orc.SCALE_ROWS, topk, wt,
+                               w.num_experts, w.num_ranks, w.hidden,
+                               expert_mode=0 if w.expert_fn == "identity" else 1,
+                               alignment=alignment)
+        what = ("layout, scan, scatter with row copies, " +
+                ("" if w.expert_fn == "identity" else "expert stand-in, ") + "fp64 combine")
 
     # one core: the oracle is single-threaded C; pin the timing thread to one
     # of the CPUs it may use, and restore the mask afterwards
     mask = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else None
     if mask:
         os.sched_setaffinity(0, {min(mask)})
+    passes = []
     try:
-        passes, rows, t0 = 0, 0, time.perf_counter()
-        while True:
-            cnt, _, _ = timed("layout", orc.layout, topk, E, R)
-            start, total = timed("scan", orc.scan, cnt, alignment)
-            if w.payload == "fp8":
-                _, _, _, oi = timed("scatter", orc.scatter_rows, inp["x"], xs, fmt, topk, start,
-                                    total)
-            else:
-                out, _, m_idx, oi = timed("scatter", orc.scatter, inp["x"], inp["x_scale"], topk,
-                                          start, total)
-                eo = out if w.expert_fn == "identity" else timed("expert", orc.expert_scale, out,
-                                                                 m_idx)
-            timed("combine", orc.combine, eo, oi, wt)
-            passes += 1
-            rows += int((topk >= 0).sum())
-            el = time.perf_counter() - t0
-            if el >= seconds or passes >= 50:
-                break
+        spent = 0.0
+        while len(passes) < 3 or (spent < seconds and len(passes) < 50):
+            passes.append(run())
+            spent += sum(passes[-1].values())
     finally:
         if mask:
             os.sched_setaffinity(0, mask)
-    return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} full pass(es) of the {w.name} workload ({what}), {el:.1f} s, "
-                      f"pinned to one CPU",
-            "per_step_ms": {k: v * 1e3 / passes for k, v in step_s.items()},
+    rows = int((topk >= 0).sum())
+    per_pass = float(np.median([sum(p.values()) for p in passes]))
+    steps = [k for k in passes[0] if k != "expert" or w.expert_fn != "identity"]
+    return {"value": rows / per_pass, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(passes)} full pass(es) of the {w.name} workload ({what}), "
+                      f"{spent:.1f} s of steps, pinned to one CPU; median pass {per_pass * 1e3:.3f} ms",
+            "per_step_ms": {k: float(np.median([p[k] for p in passes])) * 1e3 for k in steps},
+            "timing": "monotonic clock around each step inside the C oracle, outputs allocated "
+                      "once before the passes, median over passes",
             "host": host_cpu()}
+
+
+def write_study(kind, workload, reps=3):
+    """The scatter's write pattern under a profiler: `reps` launches of one
+    kind of kernel, each timed with HIP events, for rocprofv3 --pmc runs
+    whose counters (write request sizes, write stalls, address translation)
+    set the scatter next to plain write patterns of the same size.
+
+    scatter-cold: layout and scan, then a 1 GiB read sweep (evicts L2 and the
+      Infinity Cache), then the scatter, so its reads come from HBM;
+    scatter-warm: the scatter right after a full dispatch (its input batch
+      cached, as in back-to-back steps);
+    pieces: the probe library's write-only pieces over the scatter's row bytes
+      (one row-sized piece per workgroup, 128 threads x 16-byte stores):
+      XCD-contiguous non-temporal, in address order non-temporal, and
+      XCD-contiguous write-back.
+    Prints one JSON line of median times."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import permute_ep_layout_amd as epl
+    from permute_ep_layout_amd import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.get(workload)
+    if w.payload != "bf16" or w.ll_segment:
+        raise ValueError("the write study takes a bf16 prefix-sum workload")
+    T, K, E, R, H, S = (w.num_tokens, w.num_topk, w.num_experts, w.num_ranks, w.hidden,
+                        w.scale_cols)
+    inp = workloads.make_inputs(w)
+    N = int((inp["topk_idx"] >= 0).sum())
+    stream = torch.cuda.current_stream(dev)
+    times = {}
+
+    def timed(name, fn):
+        a, b = Event(), Event()
+        a.record(stream)
+        fn()
+        b.record(stream)
+        times.setdefault(name, []).append((a, b))
+
+    if kind == "pieces":
+        import bench_probe
+
+        lib = ctypes.CDLL(bench_probe.ensure_built())
+        lib.epl_probe_pieces.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p]
+        words = 2 * H // 16
+        n = N * words
+        dst = torch.empty(n * 16, dtype=torch.uint8, device=dev)
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        for name, nt, xcd in (("xcd_nt", 1, 1), ("inorder_nt", 1, 0), ("xcd_wb", 0, 1)):
+            for _ in range(reps):
+                flush.sum()
+                timed(name, lambda: lib.epl_probe_pieces(dst.data_ptr(), n, words, 128, nt, xcd,
+                                                         stream.cuda_stream))
+        nbytes = n * 16
+    elif kind in ("scatter-cold", "scatter-warm"):
+        topk = torch.from_numpy(inp["topk_idx"]).to(dev)
+        x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+        xs = torch.from_numpy(inp["x_scale"]).to(dev) if S else None
+        p = epl.Problem.make(T, K, E, R, H, S, 0, w.ranks_per_node)
+        cap = epl.epl_capacity_rows(p)
+        i32 = torch.int32
+        ws = torch.empty(epl.epl_workspace_bytes(p), dtype=torch.uint8, device=dev)
+        cnt, per_rank = torch.empty(E, dtype=i32, device=dev), torch.empty(R, dtype=i32,
+                                                                              device=dev)
+        per_node = torch.empty(p.num_nodes, dtype=i32, device=dev) if p.num_nodes else None
+        in_rank = torch.empty((T, R), dtype=torch.uint8, device=dev)
+        start = torch.empty(E, dtype=i32, device=dev)
+        out = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+        out_scale = torch.empty((cap, S), dtype=torch.float32, device=dev) if S else None
+        m_idx = torch.empty(cap, dtype=i32, device=dev)
+        oi = torch.empty((T, K), dtype=i32, device=dev)
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        for _ in range(reps):
+            if kind == "scatter-cold":
+                epl.epl_layout(p, topk, cnt, per_rank, per_node, in_rank, ws)
+                epl.epl_scan(p, cnt, start, None, ws)
+                flush.sum()
+            else:
+                epl.epl_dispatch(p, topk, x, xs, cap, cnt, per_rank, per_node, in_rank, start,
+                                 None, out, out_scale, m_idx, oi, ws)
+            timed("scatter", lambda: epl.epl_scatter(p, x, xs, topk, start, ws, cap, out,
+                                                     out_scale, m_idx, oi))
+        torch.cuda.synchronize()
+        if epl.epl_status(ws) != epl.EPL_OK:
+            raise RuntimeError("scatter reported an error")
+        nbytes = algorithmic_bytes(w, N, int((inp["topk_idx"] >= 0).any(axis=1).sum()))["scatter"]
+    else:
+        raise ValueError(f"unknown study {kind!r}")
+    torch.cuda.synchronize()
+    res = {k: float(np.median([a.elapsed_time(b) for a, b in v])) for k, v in times.items()}
+    print(json.dumps({"study": kind, "workload": w.name, "reps": reps, "bytes": nbytes,
+                      "median_ms": res,
+                      "gbps": {k: nbytes / (v * 1e-3) / 1e9 for k, v in res.items()}}),
+          flush=True)
 
 
 def main():
@@ -495,6 +589,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--num-tokens", type=int, default=0,
+                    help="run the workload's recipe with this many tokens instead (e.g. a "
+                         "decode-sized batch of the DeepSeek-V3-shaped workload)")
     ap.add_argument("--out-dtype", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--alignment", type=int, default=0,
                     help="expert alignment (block_m padding of each expert's rows)")
@@ -507,6 +604,8 @@ def main():
                     help="only run a plain copy kernel of BYTES bytes (counter calibration)")
     ap.add_argument("--ceilings", type=int, metavar="MIB", default=0,
                     help="only run the streaming read:write mix probes, MIB MiB per stream")
+    ap.add_argument("--study", choices=["scatter-cold", "scatter-warm", "pieces"], default=None,
+                    help="only run a few launches of one write pattern (for counter runs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -519,6 +618,9 @@ def main():
         return
     if args.ceilings:
         stream_ceilings(args.ceilings)
+        return
+    if args.study:
+        write_study(args.study, args.workload)
         return
 
     import numpy as np
@@ -533,6 +635,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = workloads.get(args.workload)
+    if args.num_tokens:
+        w = w.with_(num_tokens=args.num_tokens, name=f"{w.name}_t{args.num_tokens}")
     T, K, E, R, H, S = (w.num_tokens, w.num_topk, w.num_experts, w.num_ranks, w.hidden,
                         w.scale_cols)
     log(f"workload {w.name}: T={T} K={K} E={E} R={R} H={H} S={S}; generating inputs")

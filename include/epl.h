@@ -118,7 +118,13 @@ int epl_validate(const epl_problem *p);
  * make the row order deterministic, the per-slot ranks, the device copy of
  * the total row count and the status word. It needs no initialisation;
  * epl_layout / epl_dispatch write every byte that later calls read. Its
- * address must be 256-byte aligned. Host-only; needs no GPU. */
+ * address must be 256-byte aligned. Host-only; needs no GPU.
+ * The calls take the workspace as a bare pointer and cannot check its size:
+ * the layout, scan and scatter calls need all epl_workspace_bytes(p) bytes
+ * for the same problem (a smaller one is written past its end), while
+ * epl_combine, epl_expert_scale, epl_status and epl_total touch only its
+ * first 256 bytes (status word and total). The Python binding checks the
+ * size before every call. */
 size_t epl_workspace_bytes(const epl_problem *p);
 
 /* Rows that always suffice for the ragged buffer of problem `p`: T * K
@@ -170,7 +176,12 @@ int epl_scan(const epl_problem *p, const int32_t *num_tokens_per_expert,
  * (capacity_rows >= N; epl_capacity_rows() always suffices); rows >= N are
  * not written.
  * If N > capacity_rows the rows past the capacity are skipped and the
- * status word records EPL_ECAPACITY. Requires that epl_layout and then
+ * status word records EPL_ECAPACITY: a slot whose row would fall at or past
+ * capacity_rows (or before row 0, with a caller-made expert_start_loc) is
+ * not placed -- nothing is written for it and its output_index is -1, the
+ * marker of an unplaced slot ("参考sglang代码，重构vllm021中EP高吞吐代码，
+ * 消除空泡问题", section 3.3) -- and alignment padding rows outside the
+ * buffer are skipped likewise. Requires that epl_layout and then
  * epl_scan (with the counts epl_layout produced) ran on the same
  * workspace and stream. x / out: 16-byte aligned; x_scale / out_scale may be
  * NULL iff S == 0. */

@@ -83,6 +83,11 @@ class Oracle:
         lib.epl_oracle_combine.argtypes = [_c_i64, _c_i32, _c_i32, _ptr, _c_i64, _ptr, _ptr,
                                            _ptr, _c_i64, _ptr]
         lib.epl_oracle_combine.restype = ctypes.c_int
+        lib.epl_oracle_time_pass.argtypes = [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _ptr,
+                                             _c_i32, _c_i32, _ptr, _ptr, _ptr, _c_i32, _c_i64,
+                                             _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
+                                             _c_i32, _ptr, _ptr, _ptr]
+        lib.epl_oracle_time_pass.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -250,6 +255,46 @@ class Oracle:
         _check(self.lib.epl_oracle_combine(T, K, H, _p(eo), rows, _p(oi), _p(w), _p(tk), n,
                                            _p(y)), "combine")
         return y
+
+    def timed_passes(self, x, x_scale, scale_format, topk_idx, topk_weights, num_experts,
+                     num_ranks, hidden, expert_mode=0, expert_out=None, alignment=0):
+        """A callable that runs one pass of layout, scan, byte-row scatter,
+        (expert) and combine in the C timing harness on buffers allocated
+        here once, and returns the step times in seconds. x is [T, row
+        bytes] as uint8 (a bf16 array is viewed as bytes); x_scale [T, W]
+        words or None; expert_mode 0 combines the scattered bf16 rows, 1
+        applies the expert stand-in first, 2 combines ``expert_out``."""
+        topk = _c(topk_idx, np.int64)
+        T, K = topk.shape
+        E, R, H = int(num_experts), int(num_ranks), int(hidden)
+        xb = np.ascontiguousarray(x).view(np.uint8).reshape(T, -1)
+        xs = None if x_scale is None else np.ascontiguousarray(x_scale).view(np.uint32)
+        W = 0 if xs is None else xs.shape[1]
+        fmt = int(scale_format) if xs is not None else self.SCALE_NONE
+        w = _c(topk_weights, np.float32)
+        a = max(int(alignment), 1)
+        cap = -(-(int((topk >= 0).sum()) + E * (a - 1)) // a) * a    # rows always enough
+        cnt, per_rank = np.empty(E, np.int32), np.empty(R, np.int32)
+        in_rank, start = np.empty((T, R), np.uint8), np.empty(E, np.int32)
+        out = np.empty((cap, xb.shape[1]), np.uint8)
+        out_scale = None if xs is None else np.empty(cap * W, np.uint32)
+        m_idx, oi = np.empty(cap, np.int32), np.empty((T, K), np.int32)
+        eo = None
+        if expert_mode == 1:
+            eo = np.empty((cap, H), np.uint16)
+        elif expert_mode == 2:
+            eo = _c(expert_out, np.uint16)
+        y = np.empty((T, H), np.float64)
+        ns = np.zeros(5, np.int64)
+
+        def run():
+            _check(self.lib.epl_oracle_time_pass(
+                T, K, E, R, H, xb.shape[1], _p(xb), fmt, W, _p(xs), _p(topk), _p(w),
+                int(alignment), cap,
+                _p(cnt), _p(per_rank), _p(in_rank), _p(start), _p(out), _p(out_scale),
+                _p(m_idx), _p(oi), int(expert_mode), _p(eo), _p(y), _p(ns)), "time_pass")
+            return dict(zip(("layout", "scan", "scatter", "expert", "combine"), ns * 1e-9))
+        return run
 
     def run_all(self, x, x_scale, topk_idx, topk_weights, num_experts, num_ranks,
                 expert_fn="identity", alignment=0):

@@ -46,10 +46,13 @@
  * fixed-rectangle layout against the (pinned) prefix-sum layout, and
  * invariants.
  */
+#define _POSIX_C_SOURCE 200809L   /* clock_gettime, for the timing harness at the end */
+
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#include <time.h>
 
 #define ORACLE_OK 0
 #define ORACLE_EINVAL (-1)
@@ -352,17 +355,42 @@ uint8_t epl_oracle_e4m3_from_double(double v)
     return (uint8_t)(sign | (uint8_t)(exp_field << 3) | (uint8_t)mant);
 }
 
+/* Round a double to binary32's 24-bit significand, ties to even, with no
+ * exponent limits (no overflow, no subnormal range): the value binary32
+ * arithmetic gives when its result is in the normal range, and beyond it
+ * the value it would give with a wider exponent. Zero and non-finite values
+ * pass through. */
+static double round_to_24_bits(double v)
+{
+    if (v == 0.0 || !isfinite(v))
+        return v;
+    int e;
+    double m = frexp(v, &e);                  /* v = m * 2^e, 0.5 <= |m| < 1 */
+    return ldexp(nearbyint(ldexp(m, 24)), e - 24);
+}
+
 /* The low-latency dispatch sends FP8 rows with one fp32 scale per 128
  * hidden columns ([DEEPEP] low_latency mode: the dispatch casts to FP8 on
  * the way, and returns scales of shape [..., hidden / 128]). The pages do
  * not give the cast; reading: per 128-column group of a token,
  *   amax = max |x|, scale = amax / 448, inv = 448 / amax (0 if amax = 0),
  *   q = e4m3(x * inv),
- * every operation in binary32 with round to nearest (the product x * inv
- * is rounded to binary32 before the e4m3 rounding; this file is built with
- * -ffp-contract=off for x86-64, where float arithmetic is binary32), so that the group's
- * largest magnitude lands on 448 and q * scale approximates x. x is bf16
- * [T, H], H a multiple of 128; q is [T, H] bytes, scale [T, H / 128]. */
+ * with round to nearest at binary32's precision at every step (scale in
+ * binary32 proper; inv and the product x * inv rounded to 24 significant
+ * bits before the e4m3 rounding), so that the group's largest magnitude
+ * lands on 448 and q * scale approximates x. inv and the product use no
+ * exponent limits: bf16 keeps binary32's exponent range, and for a group
+ * whose amax is below 448 / FLT_MAX (about 1.3e-36) binary32's 448 / amax
+ * would overflow to infinity, turning every zero of the group into a NaN
+ * code and every other value into +-448; without the limit the group
+ * encodes like the same group scaled by a power of two. (Where binary32 has
+ * the range -- every other group -- this is exactly binary32 arithmetic:
+ * the quotient is rounded once from the double quotient, which for a
+ * division is the same as rounding the exact quotient, since 53 >= 2 * 24
+ * + 2; the product of an 8-bit and a 24-bit significand is exact in double;
+ * a product below binary32's normal range would round to zero in e4m3
+ * either way.) x is bf16 [T, H], H a multiple of 128; q is [T, H] bytes,
+ * scale [T, H / 128]. */
 int epl_oracle_quantize_e4m3(int64_t T, int32_t H, const uint16_t *x, uint8_t *q, float *scale)
 {
     if (T < 0 || H < 0 || H % 128 != 0)
@@ -378,11 +406,11 @@ int epl_oracle_quantize_e4m3(int64_t T, int32_t H, const uint16_t *x, uint8_t *q
                     amax = v;
             }
             float s = amax / 448.0f;
-            float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+            double inv = amax > 0.0f ? round_to_24_bits(448.0 / (double)amax) : 0.0;
             scale[t * (int64_t)S + g] = s;
             for (int32_t i = 0; i < 128; ++i) {
-                float p = (float)epl_oracle_bf16_to_double(xg[i]) * inv;
-                q[t * (int64_t)H + (int64_t)g * 128 + i] = epl_oracle_e4m3_from_double((double)p);
+                double p = round_to_24_bits(epl_oracle_bf16_to_double(xg[i]) * inv);
+                q[t * (int64_t)H + (int64_t)g * 128 + i] = epl_oracle_e4m3_from_double(p);
             }
         }
     }
@@ -540,4 +568,75 @@ int epl_oracle_combine(int64_t T, int32_t K, int32_t H,
         }
     }
     return ORACLE_OK;
+}
+
+/* ----------------------------------------------------- timing harness -- */
+
+/* Not part of the method: a wall-clock harness for the CPU baseline of the
+ * benchmark. Runs one pass of the oracle's steps above on buffers the caller
+ * allocated once -- layout, scan, the byte-row scatter (rows of row_bytes
+ * bytes: 2H for bf16, H for FP8; W scale words per row in scale_format),
+ * then the combine -- timing each step with the monotonic clock. The
+ * combine's expert rows depend on expert_mode: 0 = the scattered rows
+ * themselves (bf16, row_bytes = 2H), 1 = the large workload's expert
+ * stand-in applied to them into expert_out, 2 = expert_out as given (a bf16
+ * stand-in for an FP8 payload's expert output). Step durations in
+ * nanoseconds: ns[0] layout, ns[1] scan, ns[2] scatter, ns[3] expert (0
+ * unless expert_mode is 1), ns[4] combine. Buffers: cnt [E], per_rank [R],
+ * in_rank [T, R], start [E], out [cap, row_bytes], out_scale for cap rows
+ * (NULL without scales), m_indices [cap], output_index [T, K], expert_out
+ * [cap, H] bf16 (modes 1 and 2), y [T, H] double; cap must be at least the
+ * buffer's row count (routed rows, plus the padding of an expert alignment
+ * a > 1). */
+static int64_t monotonic_ns(void)
+{
+    struct timespec ts;
+    clock_gettime(CLOCK_MONOTONIC, &ts);
+    return (int64_t)ts.tv_sec * 1000000000LL + (int64_t)ts.tv_nsec;
+}
+
+int epl_oracle_time_pass(int64_t T, int32_t K, int32_t E, int32_t R, int32_t H,
+                         int64_t row_bytes, const uint8_t *x, int32_t scale_format,
+                         int32_t scale_words, const uint32_t *x_scale, const int64_t *topk_idx,
+                         const float *topk_weights, int32_t alignment, int64_t cap, int32_t *cnt,
+                         int32_t *per_rank, uint8_t *in_rank, int32_t *start, uint8_t *out,
+                         uint32_t *out_scale, int32_t *m_indices, int32_t *output_index,
+                         int32_t expert_mode, uint16_t *expert_out, double *y, int64_t *ns)
+{
+    if (expert_mode < 0 || expert_mode > 2 || (expert_mode == 0 && row_bytes != 2 * (int64_t)H) ||
+        (expert_mode > 0 && !expert_out))
+        return ORACLE_EINVAL;
+    int64_t t0 = monotonic_ns();
+    int rc = epl_oracle_layout(T, K, E, R, topk_idx, cnt, per_rank, in_rank);
+    int64_t t1 = monotonic_ns();
+    if (rc != ORACLE_OK)
+        return rc;
+    int64_t total = 0;
+    rc = epl_oracle_scan(E, cnt, alignment, start, &total);
+    int64_t t2 = monotonic_ns();
+    if (rc != ORACLE_OK)
+        return rc;
+    if (total > cap)
+        return ORACLE_EINVAL;
+    rc = epl_oracle_scatter_rows(T, K, E, row_bytes, x, scale_format, scale_words, x_scale,
+                                 topk_idx, start, total, cap, out, out_scale, m_indices,
+                                 output_index);
+    int64_t t3 = monotonic_ns();
+    if (rc != ORACLE_OK)
+        return rc;
+    const uint16_t *rows = expert_mode == 0 ? (const uint16_t *)(const void *)out : expert_out;
+    if (expert_mode == 1)
+        rc = epl_oracle_expert_scale(total, H, (const uint16_t *)(const void *)out, m_indices,
+                                     expert_out);
+    int64_t t4 = monotonic_ns();
+    if (rc != ORACLE_OK)
+        return rc;
+    rc = epl_oracle_combine(T, K, H, rows, total, output_index, topk_weights, NULL, T, y);
+    int64_t t5 = monotonic_ns();
+    ns[0] = t1 - t0;
+    ns[1] = t2 - t1;
+    ns[2] = t3 - t2;
+    ns[3] = expert_mode == 1 ? t4 - t3 : 0;
+    ns[4] = t5 - t4;
+    return rc;
 }

@@ -207,6 +207,20 @@ def _need(t, name, dtype, shape=None, device=None, allow_none=False):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
+WS_HEADER_BYTES = 256   # status word and total: all that combine / expert_scale / status touch
+
+
+def _need_workspace(workspace, need: int, where: str):
+    """The C ABI takes the workspace as a bare pointer, so its size is checked
+    here, before any launch: a workspace smaller than the problem needs would
+    be written past its end."""
+    if need <= 0:
+        raise EplError(EPL_EINVAL, where)
+    if workspace.numel() < need:
+        raise ValueError(f"{where}: workspace holds {workspace.numel()} bytes, the problem needs "
+                         f"{need} (epl_workspace_bytes)")
+
+
 def _check(rc: int, where: str):
     if rc != EPL_OK:
         raise EplError(rc, where)
@@ -256,6 +270,7 @@ def epl_layout(p: Problem, topk_idx, num_tokens_per_expert, num_tokens_per_rank,
     _need_per_node(p, num_tokens_per_rdma_rank, dev)
     _need(is_token_in_rank, "is_token_in_rank", torch.uint8, (T, R), dev)
     _need(workspace, "workspace", torch.uint8, None, dev)
+    _need_workspace(workspace, epl_workspace_bytes(p), "epl_layout")
     _check(load().epl_layout(_prob(p), _ptr(topk_idx), _ptr(num_tokens_per_expert),
                              _ptr(num_tokens_per_rank), _ptr(num_tokens_per_rdma_rank),
                              _ptr(is_token_in_rank), _ptr(workspace), _stream(stream, dev)),
@@ -270,6 +285,7 @@ def epl_scan(p: Problem, num_tokens_per_expert, expert_start_loc, total_host, wo
     dev = num_tokens_per_expert.device
     _need(expert_start_loc, "expert_start_loc", torch.int32, (E,), dev)
     _need(workspace, "workspace", torch.uint8, None, dev)
+    _need_workspace(workspace, epl_workspace_bytes(p), "epl_scan")
     if total_host is not None:
         if total_host.device.type != "cpu" or not total_host.is_pinned() or \
                 total_host.dtype != torch.int32 or total_host.numel() < 1:
@@ -303,6 +319,7 @@ def epl_scatter(p: Problem, x, x_scale, topk_idx, expert_start_loc, workspace, c
                               output_index)
     _need(expert_start_loc, "expert_start_loc", torch.int32, (p.num_experts,), dev)
     _need(workspace, "workspace", torch.uint8, None, dev)
+    _need_workspace(workspace, epl_workspace_bytes(p), "epl_scatter")
     _check(load().epl_scatter(_prob(p), _ptr(x), _ptr(x_scale), _ptr(topk_idx),
                               _ptr(expert_start_loc), _ptr(workspace), int(capacity_rows),
                               _ptr(out), _ptr(out_scale), _ptr(m_indices), _ptr(output_index),
@@ -323,6 +340,7 @@ def epl_dispatch(p: Problem, topk_idx, x, x_scale, capacity_rows, num_tokens_per
     _need(is_token_in_rank, "is_token_in_rank", torch.uint8, (T, R), dev)
     _need(expert_start_loc, "expert_start_loc", torch.int32, (E,), dev)
     _need(workspace, "workspace", torch.uint8, None, dev)
+    _need_workspace(workspace, epl_workspace_bytes(p), "epl_dispatch")
     if total_host is not None and (total_host.device.type != "cpu" or not total_host.is_pinned()
                                    or total_host.dtype != torch.int32):
         raise ValueError("total_host must be a pinned CPU int32 tensor")
@@ -368,6 +386,7 @@ def epl_scatter_fp8(p: Problem, x, x_scale, scale_format, topk_idx, expert_start
                           m_indices, output_index)
     _need(expert_start_loc, "expert_start_loc", torch.int32, (p.num_experts,), dev)
     _need(workspace, "workspace", torch.uint8, None, dev)
+    _need_workspace(workspace, epl_workspace_bytes(p), "epl_scatter_fp8")
     _check(load().epl_scatter_fp8(_prob(p), _ptr(x), _ptr(x_scale), int(scale_format),
                                   _ptr(topk_idx), _ptr(expert_start_loc), _ptr(workspace),
                                   int(capacity_rows), _ptr(out), _ptr(out_scale), _ptr(m_indices),
@@ -388,6 +407,7 @@ def epl_dispatch_fp8(p: Problem, topk_idx, x, x_scale, scale_format, capacity_ro
     _need(is_token_in_rank, "is_token_in_rank", torch.uint8, (T, R), dev)
     _need(expert_start_loc, "expert_start_loc", torch.int32, (E,), dev)
     _need(workspace, "workspace", torch.uint8, None, dev)
+    _need_workspace(workspace, epl_workspace_bytes(p), "epl_dispatch_fp8")
     if total_host is not None and (total_host.device.type != "cpu" or not total_host.is_pinned()
                                    or total_host.dtype != torch.int32):
         raise ValueError("total_host must be a pinned CPU int32 tensor")
@@ -426,8 +446,7 @@ def epl_ll_dispatch(p: Problem, tokens_per_segment, rows_per_expert, topk_idx, x
     _need(layout_range, "layout_range", torch.int32, (E, T // M, 2), dev)
     _need(output_index, "output_index", torch.int32, (T, K), dev)
     _need(workspace, "workspace", torch.uint8, None, dev)
-    if workspace.numel() < epl_ll_workspace_bytes(p, M):
-        raise ValueError("workspace smaller than epl_ll_workspace_bytes")
+    _need_workspace(workspace, epl_ll_workspace_bytes(p, M), "epl_ll_dispatch")
     _check(load().epl_ll_dispatch(_prob(p), M, cap, _ptr(topk_idx), _ptr(x), _ptr(out),
                                   _ptr(out_scale), _ptr(recv_count), _ptr(src_info),
                                   _ptr(layout_range), _ptr(output_index), _ptr(workspace),
@@ -445,6 +464,8 @@ def epl_combine(p: Problem, expert_out, expert_rows, output_index, topk_weights,
     ydt = torch.bfloat16 if out_dtype == EPL_OUT_BF16 else torch.float32
     _need(y, "y", ydt, (T, H), dev)
     _need(workspace, "workspace", torch.uint8, None, dev, allow_none=True)
+    if workspace is not None:
+        _need_workspace(workspace, WS_HEADER_BYTES, "epl_combine")
     _check(load().epl_combine(_prob(p), _ptr(expert_out), int(expert_rows), _ptr(output_index),
                               _ptr(topk_weights), int(out_dtype), _ptr(y), _ptr(workspace),
                               _stream(stream, dev)), "epl_combine")
@@ -459,16 +480,19 @@ def epl_expert_scale(p: Problem, rows_in, m_indices, capacity_rows, rows_out, wo
     _need(m_indices, "m_indices", torch.int32, (capacity_rows,), dev)
     _need(rows_out, "rows_out", torch.bfloat16, (capacity_rows, H), dev)
     _need(workspace, "workspace", torch.uint8, None, dev)
+    _need_workspace(workspace, WS_HEADER_BYTES, "epl_expert_scale")
     _check(load().epl_expert_scale(_prob(p), _ptr(rows_in), _ptr(m_indices), int(capacity_rows),
                                    _ptr(rows_out), _ptr(workspace), _stream(stream, dev)),
            "epl_expert_scale")
 
 
 def epl_status(workspace, stream=None) -> int:
+    _need_workspace(workspace, WS_HEADER_BYTES, "epl_status")
     return int(load().epl_status(_ptr(workspace), _stream(stream, workspace.device)))
 
 
 def epl_total(workspace, stream=None) -> int:
+    _need_workspace(workspace, WS_HEADER_BYTES, "epl_total")
     n = int(load().epl_total(_ptr(workspace), _stream(stream, workspace.device)))
     if n < 0:
         raise EplError(n, "epl_total")

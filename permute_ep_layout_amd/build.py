@@ -16,9 +16,6 @@ CSRC = os.path.join(PKG, "csrc")
 SOURCES = [os.path.join(CSRC, "epl.hip")]
 DEPENDS = SOURCES + [os.path.join(CSRC, "epl_kernels.h"), os.path.join(INCLUDE, "epl.h")]
 LIB = os.path.join(PKG, "libepl.so")
-# streaming-bandwidth probes for bench.py --ceilings (not on the dispatch path)
-PROBE_SOURCES = [os.path.join(CSRC, "stream_probe.hip")]
-PROBE_LIB = os.path.join(PKG, "libepl_probe.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -61,10 +58,6 @@ def build(out: str = LIB, extra_flags=(), verbose: bool = False, sources=None) -
         print("\n".join(msgs))
     os.replace(out + ".tmp", out)
     return out
-
-
-def build_probe(verbose: bool = False) -> str:
-    return build(PROBE_LIB, verbose=verbose, sources=PROBE_SOURCES)
 
 
 if __name__ == "__main__":

@@ -133,10 +133,10 @@ int layout_block_tokens(const epl_problem &p)
             break;
         }
     }
-    // the LDS bound: keys and ranks take 8 bytes per slot
+    // the LDS bound: keys and ranks take 8 bytes per slot, plus a pad word per token
     const size_t fixed =
         epl::layout_lds_bytes(0, p.num_topk, p.num_experts, p.num_ranks + nodes_of(p));
-    cap = std::min<int64_t>(cap, (int64_t)((epl::kLayoutLdsBytes - fixed) / (8 * (size_t)p.num_topk)));
+    cap = std::min<int64_t>(cap, (int64_t)((epl::kLayoutLdsBytes - fixed) / (8 * (size_t)p.num_topk + 4)));
     int64_t want = (p.num_tokens + EPL_LAYOUT_BLOCKS - 1) / EPL_LAYOUT_BLOCKS;
     want = std::max<int64_t>(EPL_LAYOUT_MIN_TOKENS, want);
     return (int)std::max<int64_t>(1, std::min<int64_t>(want, cap));

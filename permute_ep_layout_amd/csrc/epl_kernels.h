@@ -164,7 +164,7 @@ constexpr size_t kLayoutLdsBytes = 65536;
 __host__ __device__ constexpr size_t layout_lds_bytes(int B, int K, int E, int RC,
                                                       int waves = kLayoutWaves)
 {
-    return sizeof(int32_t) * ((size_t)2 * B * K              // keys, ranks
+    return sizeof(int32_t) * ((size_t)B * (K + 1) + (size_t)B * K   // keys (padded), ranks
                               + (size_t)waves * E             // running count per wave and expert
                               + (size_t)waves * ((E + 3) / 4) // per-chunk byte counters
                               + (size_t)RC + 1);              // tokens per rank / node, error flag
@@ -190,8 +190,17 @@ __global__ __launch_bounds__(THREADS) void ep_layout_kernel(
     extern __shared__ int32_t lds[];
     const int max_slots = B * K;
     const int cwords = (E + 3) / 4;
-    int32_t *keys = lds;                                   // [B*K] key | owner << 16, or -1
-    int32_t *lrank = keys + max_slots;                     // [B*K] rank within the owning wave
+    // keys of slot s = (t, k) at t * (K + 1) + k: a token's K keys followed by
+    // one unused word, so that in the mask step, where thread t reads its
+    // token's keys, the lanes stride by K + 1 words, odd and so co-prime with
+    // the LDS bank count (a stride of K = 8 words put a wave's lanes on a few
+    // banks: 43 K of 72 K LDS-active cycles in bank conflicts at 4096 tokens
+    // of top-8, 32 K of 61 K with the pad; the rest are the histogram and
+    // rank-count atomics)
+    const uint32_t kmagic = div_magic((uint32_t)K);
+    auto kidx = [&](int s) { return s + div_small((uint32_t)s, K, kmagic); };
+    int32_t *keys = lds;                                   // [B*(K+1)] key | owner << 16, or -1
+    int32_t *lrank = keys + B * (K + 1);                   // [B*K] rank within the owning wave
     int32_t *wave_cnt = lrank + max_slots;                 // [waves][E]
     uint32_t *chunk_cnt = reinterpret_cast<uint32_t *>(wave_cnt + WAVES * E);  // [waves][E/4]
     int32_t *rank_cnt = reinterpret_cast<int32_t *>(chunk_cnt + WAVES * cwords); // [R+Rn]
@@ -226,7 +235,7 @@ __global__ __launch_bounds__(THREADS) void ep_layout_kernel(
             packed = (int)e | (div_small((uint32_t)e, experts_per_rank, epr_magic) << 16);
         else if (e != -1)
             bad = true;
-        keys[s] = packed;
+        keys[kidx(s)] = packed;
     }
     lds_barrier();
     if (bad)
@@ -249,7 +258,7 @@ __global__ __launch_bounds__(THREADS) void ep_layout_kernel(
         const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
         for (int c = wave * cpw; c < c_end; ++c) {
             const int s = c * kWave + lane;
-            const int packed = (s < ns) ? keys[s] : -1;
+            const int packed = (s < ns) ? keys[kidx(s)] : -1;
             const bool valid = packed >= 0;
             const int k16 = valid ? (packed & 0xFFFF) : 0;
             const int shift = 8 * (k16 & 3);
@@ -286,7 +295,7 @@ __global__ __launch_bounds__(THREADS) void ep_layout_kernel(
             const int wr = min(64, R - w0);
             uint64_t mask = 0;
             for (int k = 0; k < K; ++k) {
-                const int packed = keys[tid * K + k];
+                const int packed = keys[tid * (K + 1) + k];
                 if (packed >= 0) {
                     const int r = (packed >> 16) - w0;
                     if (r >= 0 && r < wr)
@@ -304,7 +313,7 @@ __global__ __launch_bounds__(THREADS) void ep_layout_kernel(
             const int wn = min(64, Rn - n0);
             uint64_t mask = 0;
             for (int k = 0; k < K; ++k) {
-                const int packed = keys[tid * K + k];
+                const int packed = keys[tid * (K + 1) + k];
                 if (packed >= 0) {
                     const int n = div_small((uint32_t)packed >> 16, G, node_magic) - n0;
                     if (n >= 0 && n < wn)
@@ -334,7 +343,7 @@ __global__ __launch_bounds__(THREADS) void ep_layout_kernel(
         block_err[b] = (uint32_t)*s_err;
 
     for (int s = tid; s < ns; s += THREADS) {
-        const int packed = keys[s];
+        const int packed = keys[kidx(s)];
         const int w = (s / kWave) / cpw;
         slot_rank[t0 * K + s] = packed >= 0 ? lrank[s] + wave_cnt[w * E + (packed & 0xFFFF)] : -1;
     }
@@ -867,7 +876,7 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
             const int64_t p0 = (int64_t)start[e] + c;
             const int64_t p1 = (int64_t)start[e] + (c + alignment - 1) / alignment * alignment;
             for (int64_t p = p0 + tid; p < p1; p += kScatterThreads) {
-                if (p < capacity)
+                if (p >= 0 && p < capacity)
                     m_indices[p] = -1;
                 else
                     atomicOr(status, kStatusCapacity);
@@ -926,10 +935,12 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
             int pos = -1;
             int64_t row = -1;
             if (valid(e0)) {
+                // a slot whose row falls outside the buffer is not placed:
+                // output_index -1, like a slot with no selection
                 const int64_t p = (int64_t)s0 + b0 + r0;
-                pos = (int)p;
                 if (p >= 0 && p < capacity) {
                     row = p;
+                    pos = (int)p;
                     m_indices[p] = (int32_t)e0;
                 } else {
                     atomicOr(status, kStatusCapacity);
@@ -1074,13 +1085,15 @@ constexpr int kLLGrid = EPL_LL_GRID;
 // consecutive values of the row (two 16-byte loads) per step, so a
 // 128-column group spans the 8 lanes of a half DPP row, which reduce |x|
 // to amax with lane permutes; scale = amax / 448 and codes = e4m3(x *
-// (448 / amax)) (zero codes for an all-zero group). Each thread's 16 codes
-// go to every placed row as one 16-byte non-temporal store, and each
-// group's scale to out_scale[(e * S + g) * cap + j] (column-major per
-// expert), the 8 lanes of the group sharing the slots. Before its tokens every workgroup also writes a share of
-// recv_count and layout_range (begin, count per expert and source segment
-// of M tokens), read off the per-block offsets: blocks of B tokens with B
-// dividing M, so segment s starts at block s * M / B. VPT = steps of 16
+// (448 / amax)) (zero codes for an all-zero group; a group too small for
+// binary32's 448 / amax is cast like the same group scaled by 2^64). Each
+// thread's 16 codes go to every placed row as one 16-byte non-temporal
+// store, and each group's scale to out_scale[(e * S + g) * cap + j]
+// (column-major per expert), the 8 lanes of the group sharing the slots.
+// Before its tokens every workgroup also writes a share of recv_count and
+// layout_range (begin, count per expert and source segment of M tokens),
+// read off the per-block offsets: blocks of B tokens with B dividing M, so
+// segment s starts at block s * M / B. VPT = steps of 16
 // values per thread per pass over the row.
 template <int VPT>
 __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
@@ -1209,7 +1222,16 @@ __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
                     amax = fmaxf(amax, fabsf(f[q]));
                 amax = half_row_max(amax);
                 const float scale = amax / 448.0f;
-                const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+                // 448 / amax overflows binary32 for amax below ~1.3e-36 (bf16
+                // keeps binary32's exponent range): such a group is first
+                // scaled by 2^64, which changes no rounding (a power of two,
+                // the values stay normal), so the codes are those of binary32
+                // arithmetic with an unbounded exponent
+                const float pre = amax < 0x1p-64f ? 0x1p64f : 1.0f;
+                const float inv = amax > 0.0f ? 448.0f / (amax * pre) : 0.0f;
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    f[q] *= pre;
                 u32x4 codes;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)

@@ -32,7 +32,8 @@ KERNEL_SOURCES = ("permute_ep_layout_amd/csrc/epl_kernels.h", "permute_ep_layout
 TRAFFIC_MARK = "traffic-json:"
 
 # short names of the library's kernels, matched against demangled names
-SHORT = (("ep_layout_kernel", "layout"), ("ep_scan_kernel", "scan"),
+SHORT = (("ep_layout_scan_kernel", "layout_scan"), ("ep_layout_kernel", "layout"),
+         ("ep_scan_kernel", "scan"),
          ("ep_ll_scatter_kernel", "ll_scatter"),
          ("ep_scatter_kernel", "scatter"), ("ep_combine_kernel", "combine"),
          ("ep_expert_scale_kernel", "expert"))
@@ -183,8 +184,9 @@ def write_traffic(fetch: str, write: str, copy_fetch: str, copy_write: str, copy
     return result
 
 
-def write_counters(d: str, cmd: str, out: str, title: str):
-    """Median per dispatch of every counter of one --pmc run, per kernel."""
+def write_counters(d: str, cmd: str, out: str, title: str, all_kernels: bool = False):
+    """Median per dispatch of every counter of one --pmc run, per kernel (the
+    library's kernels, or every kernel of the run with `all_kernels`)."""
     path = _one("*counter_collection.csv", d)
     per = {}
     for r in csv.DictReader(open(path)):
@@ -203,7 +205,7 @@ def write_counters(d: str, cmd: str, out: str, title: str):
              "| kernel | " + " | ".join(counters) + " |",
              "|---|" + "---|" * len(counters)]
     for k in sorted(table):
-        if k.split("<")[0] not in dict(SHORT).values():
+        if not all_kernels and k.split("<")[0] not in dict(SHORT).values():
             continue
         vals = [statistics.median(table[k][c]) if c in table[k] else float("nan") for c in counters]
         lines.append(f"| `{k}` | " + " | ".join(f"{v:.0f}" for v in vals) + " |")
@@ -240,6 +242,7 @@ def main():
     c.add_argument("--cmd", required=True)
     c.add_argument("--title", default="Counters (rocprofv3 --pmc)")
     c.add_argument("--out", required=True)
+    c.add_argument("--all-kernels", action="store_true")
     b.add_argument("--copy-bytes", type=int, required=True)
     b.add_argument("--workload", required=True)
     b.add_argument("--out", required=True)
@@ -247,7 +250,7 @@ def main():
     if args.what == "stats":
         write_stats(args.dir, args.cmd, args.out, args.title)
     elif args.what == "counters":
-        write_counters(args.dir, args.cmd, args.out, args.title)
+        write_counters(args.dir, args.cmd, args.out, args.title, args.all_kernels)
     else:
         cmds = {"fetch": args.fetch_cmd, "write": args.write_cmd,
                 "copy fetch": args.copy_fetch_cmd, "copy write": args.copy_write_cmd}

@@ -246,3 +246,78 @@ def test_small_division_by_multiply_high_is_exact():
     for d in range(2, 2049):
         magic = np.uint64(((1 << 32) + d - 1) // d)
         assert np.array_equal((n * magic) >> np.uint64(32), n // np.uint64(d)), d
+
+
+class _RecordingLib:
+    """Stands in for libepl.so in the workspace-size test: the host-only size
+    queries go to the real library, every other entry point is recorded and
+    must never be reached."""
+
+    HOST_ONLY = ("epl_workspace_bytes", "epl_ll_workspace_bytes", "epl_strerror",
+                 "epl_capacity_rows", "epl_validate")
+
+    def __init__(self, real):
+        self.real, self.calls = real, []
+
+    def __getattr__(self, name):
+        if name in self.HOST_ONLY:
+            return getattr(self.real, name)
+
+        def launch(*args):
+            self.calls.append(name)
+            return 0
+        return launch
+
+
+def test_wrappers_reject_an_undersized_workspace_before_any_call(lib, monkeypatch):
+    """The C ABI cannot see the workspace's size, so every Python wrapper that
+    takes one checks it against epl_workspace_bytes (or the 256-byte header
+    for combine / expert_scale / status / total) before it calls the
+    library: an undersized workspace raises and nothing is launched."""
+    torch = pytest.importorskip("torch")
+    rec = _RecordingLib(lib)
+    monkeypatch.setattr(epl, "load", lambda: rec)
+    monkeypatch.setattr(epl, "_need", lambda *a, **k: None)       # CPU tensors stand in
+    monkeypatch.setattr(epl, "_stream", lambda *a, **k: 0)
+    T, K, E, R, H, S = 64, 4, 16, 4, 128, 1
+    p = epl.Problem.make(T, K, E, R, H, S)
+    need = epl.epl_workspace_bytes(p)
+    assert need > 256
+    small = torch.empty(need - 1, dtype=torch.uint8)
+    header_only = torch.empty(255, dtype=torch.uint8)
+    t = torch.empty(1)
+    total = None
+    calls = {
+        "epl_layout": lambda ws: epl.epl_layout(p, t, t, t, None, t, ws),
+        "epl_scan": lambda ws: epl.epl_scan(p, t, t, total, ws),
+        "epl_scatter": lambda ws: epl.epl_scatter(p, t, t, t, t, ws, T * K, t, t, t, t),
+        "epl_dispatch": lambda ws: epl.epl_dispatch(p, t, t, t, T * K, t, t, None, t, t, total,
+                                                    t, t, t, t, ws),
+        "epl_scatter_fp8": lambda ws: epl.epl_scatter_fp8(p, t, t, epl.EPL_SCALE_F32, t, t, ws,
+                                                          T * K, t, t, t, t),
+        "epl_dispatch_fp8": lambda ws: epl.epl_dispatch_fp8(p, t, t, t, epl.EPL_SCALE_F32,
+                                                            T * K, t, t, None, t, t, total, t,
+                                                            t, t, t, ws),
+    }
+    for name, call in calls.items():
+        with pytest.raises(ValueError, match="workspace"):
+            call(small)
+    M = 16
+    ll_need = epl.epl_ll_workspace_bytes(p, M)
+    assert ll_need > 0
+    with pytest.raises(ValueError, match="workspace"):
+        epl.epl_ll_dispatch(p, M, T, t, t, t, t, t, t, t, t,
+                            torch.empty(ll_need - 1, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="workspace"):
+        epl.epl_combine(p, t, T * K, t, t, epl.EPL_OUT_F32, t, header_only)
+    with pytest.raises(ValueError, match="workspace"):
+        epl.epl_expert_scale(p, t, t, T * K, t, header_only)
+    with pytest.raises(ValueError, match="workspace"):
+        epl.epl_status(header_only)
+    with pytest.raises(ValueError, match="workspace"):
+        epl.epl_total(header_only)
+    assert rec.calls == []
+    # with exactly the size asked for, the same wrappers do reach the library
+    calls["epl_layout"](torch.empty(need, dtype=torch.uint8))
+    epl.epl_combine(p, t, T * K, t, t, epl.EPL_OUT_F32, t, torch.empty(256, dtype=torch.uint8))
+    assert rec.calls == ["epl_layout", "epl_combine"]

@@ -117,11 +117,9 @@ def test_probe_library_exports_and_checks_arguments():
     exists and rejects bad arguments on the host (no GPU call is made)."""
     import ctypes
 
-    from permute_ep_layout_amd import build as B
+    import bench_probe
 
-    if not os.path.exists(B.PROBE_LIB):
-        pytest.skip("probe library not built")
-    lib = ctypes.CDLL(B.PROBE_LIB)
+    lib = ctypes.CDLL(bench_probe.ensure_built())
     for name in ("epl_probe_mix", "epl_probe_fan"):
         f = getattr(lib, name)
         f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,

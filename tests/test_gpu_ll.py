@@ -167,6 +167,29 @@ def test_ll_zero_groups_and_exact_powers():
     check_ll(_topk(rng, T, 4, 16), x, 16, 16, 64)
 
 
+def test_ll_tiny_groups_encode_like_scaled_groups():
+    """Groups of bf16 values far below 1e-36 mixed with zeros, where
+    binary32's 448 / amax overflows: the kernel's codes equal the oracle's
+    (and those of the same groups scaled up by 2^120), zeros stay zero codes,
+    and the scales are binary32's subnormal amax / 448 -- also for bf16
+    subnormal values and groups of a single smallest subnormal."""
+    from test_oracle_pins import tiny_group_pair
+
+    g, x = tiny_group_pair(seed=33)
+    x = x.copy()
+    x[0, :128] = 0x0001                                 # the smallest bf16 subnormal, 2^-133
+    x[1, 128:256] = 0x0000
+    x[1, 130] = 0x8003                                  # one negative subnormal in zeros
+    x[2, :128] = np.where(np.arange(128) % 2, 0x0040, 0x0000).astype(np.uint16)   # 2^-127
+    q, sc = oracle.default().quantize_e4m3(x)
+    qg, _ = oracle.default().quantize_e4m3(g)
+    np.testing.assert_array_equal(q[3:], qg[3:])
+    assert not (q == 0x7F).any() and q[0, 0] == 0x7E and q[1, 130] == 0xFE
+    rng = np.random.default_rng(34)
+    T = x.shape[0]
+    check_ll(_topk(rng, T, 3, 8), x, 8, 4, T)
+
+
 def test_ll_non_finite_values_encode_like_the_oracle():
     """NaN and +-Inf in the token rows: a group's amax skips NaN (a group of
     NaNs only gets scale 0), an Inf makes the scale Inf and the factor 0, and

@@ -209,11 +209,18 @@ def test_deterministic_bitwise_repeat():
     assert torch.equal(ya.view(torch.int32), yb.view(torch.int32))
 
 
-def test_large_batch_sampled_parity():
-    """The 65536-token workload at full size: indices compared in full, rows
-    compared in full through the oracle's index map, the expert stand-in and
-    combine compared on sampled rows / tokens that the oracle computes one by
-    one."""
+@pytest.mark.timeout(900)
+def test_large_batch_full_parity():
+    """The 65536-token workload at full size, everything compared: layout,
+    scan and indices in full; every scattered row through the oracle's index
+    map; every one of the 524288 expert stand-in rows bit-exact against the
+    oracle's expert_scale; every token's combine output within 1e-5 of
+    sum |w v|. The oracle's side is computed in chunks of 4096 tokens (the
+    rows of a chunk are the chunk's slots; its expert rows come from the
+    oracle's expert_scale of the oracle-placed token rows) on a few CPU
+    threads, so host memory stays bounded."""
+    from concurrent.futures import ThreadPoolExecutor
+
     w = workloads.get("large")
     print("[parity] workload=large (generating inputs)", flush=True)
     topk = workloads.make_topk(w)
@@ -241,25 +248,37 @@ def test_large_batch_sampled_parity():
     for p0 in range(0, N, 1 << 16):
         p1 = min(N, p0 + (1 << 16))
         assert torch.equal(outd[p0:p1], xd[src_d[p0:p1]]), f"rows {p0}:{p1}"
-    # expert stand-in on sampled rows
-    rng = np.random.default_rng(0)
-    rows = np.sort(rng.choice(N, 4096, replace=False))
-    want = orc().expert_scale(x[src[rows]], m_ref[rows])
-    np.testing.assert_array_equal(u16(eo[torch.from_numpy(rows).to(DEV)]), want)
-    # combine on sampled tokens: a sub-problem holding only their rows
-    toks = np.sort(rng.choice(T, 512, replace=False))
-    sub_oi = -np.ones((toks.size, K), np.int32)
-    sub_rows, sub_m = [], []
-    for i, t in enumerate(toks):
-        for k in range(K):
-            if oi_ref[t, k] >= 0:
-                sub_oi[i, k] = len(sub_rows)
-                sub_rows.append(t)
-                sub_m.append(m_ref[oi_ref[t, k]])
-    sub_eo = orc().expert_scale(x[np.array(sub_rows)], np.array(sub_m, np.int32))
-    y_ref = orc().combine(sub_eo, sub_oi, wt[toks])
-    bound = combine_bound(sub_eo, sub_oi, wt[toks])
-    check_combine_f32(y[torch.from_numpy(toks).to(DEV)].cpu().numpy(), y_ref, bound)
+    del src_d
+    print("[parity] large: indices and scattered rows ok", flush=True)
+
+    def oracle_chunk(t0, t1):
+        """The oracle's expert rows of tokens [t0, t1) (in slot order), their
+        global row ids, and the oracle's combine of those tokens."""
+        oi = oi_ref[t0:t1]
+        ct, ck = np.nonzero(oi >= 0)
+        rows = oi[ct, ck].astype(np.int64)
+        sub_eo = orc().expert_scale(x[t0 + ct], m_ref[rows])
+        sub_oi = np.full(oi.shape, -1, np.int32)
+        sub_oi[ct, ck] = np.arange(ct.size, dtype=np.int32)
+        y_ref = orc().combine(sub_eo, sub_oi, wt[t0:t1])
+        bound = combine_bound(sub_eo, sub_oi, wt[t0:t1])
+        return rows, sub_eo, y_ref, bound
+
+    chunk, window = 4096, 6
+    spans = [(t0, min(T, t0 + chunk)) for t0 in range(0, T, chunk)]
+    seen = np.zeros(N, bool)
+    with ThreadPoolExecutor(window) as pool:
+        pending = [pool.submit(oracle_chunk, *sp) for sp in spans[:window]]
+        for n, (t0, t1) in enumerate(spans):
+            rows, sub_eo, y_ref, bound = pending.pop(0).result()
+            if n + window < len(spans):
+                pending.append(pool.submit(oracle_chunk, *spans[n + window]))
+            got = u16(eo[torch.from_numpy(rows).to(DEV)])
+            np.testing.assert_array_equal(got, sub_eo, err_msg=f"expert rows of tokens {t0}:{t1}")
+            check_combine_f32(y[t0:t1].cpu().numpy(), y_ref, bound)
+            seen[rows] = True
+            print(f"[parity] large: tokens {t0}:{t1} expert rows and combine ok", flush=True)
+    assert seen.all()          # every row of the buffer was compared once
 
 
 # -------------------------------------------------------- expert alignment --
@@ -291,6 +310,57 @@ def test_aligned_capacity_overflow_in_padding_is_flagged():
     r = gpu_dispatch(topk, x, None, E, R, cap=N - 1, alignment=a)
     assert epl.epl_status(r["ws"]) == epl.EPL_ECAPACITY
     np.testing.assert_array_equal(r["m"].cpu().numpy(), ref["m_indices"][:N - 1])
+
+
+def test_aligned_split_call_with_bad_expert_start_loc_is_flagged():
+    """epl_scatter takes expert_start_loc from the caller. With offsets that
+    put one expert's rows and alignment padding before row 0 and another's
+    partly past the capacity, the scatter writes nothing outside its buffers,
+    reports EPL_ECAPACITY, places every slot whose row is in range (with the
+    same in-expert rank as under the true offsets) and marks the others -1."""
+    rng = np.random.default_rng(13)
+    E, R, T, K, H, a = 8, 2, 60, 3, 64, 16
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    x, _, wt = _mk(topk, H)
+    ref = orc().run_all(x, None, topk, wt, E, R, alignment=a)
+    p = epl.Problem.make(T, K, E, R, H, 0, a)
+    cap = epl.epl_capacity_rows(p)
+    guard = 64
+    ws = poisoned(epl.epl_workspace_bytes(p), torch.uint8)
+    tk, xd = torch.from_numpy(topk).to(DEV), to_bf16(x)
+    cnt, per_rank = poisoned(E, torch.int32), poisoned(R, torch.int32)
+    in_rank, start = poisoned((T, R), torch.uint8), poisoned(E, torch.int32)
+    epl.epl_layout(p, tk, cnt, per_rank, None, in_rank, ws)
+    epl.epl_scan(p, cnt, start, None, ws)
+    bad = ref["expert_start_loc"].astype(np.int64).copy()
+    bad[0] = -40                       # all of expert 0's rows and padding before row 0
+    bad[E - 1] = cap - 5               # expert 7: 5 rows fit, the rest and its padding do not
+    out_full = poisoned((cap + 2 * guard, H), torch.bfloat16)
+    m_full = poisoned(cap + 2 * guard, torch.int32)
+    out, m = out_full[guard:guard + cap], m_full[guard:guard + cap]
+    oi = poisoned((T, K), torch.int32)
+    epl.epl_scatter(p, xd, None, tk, torch.from_numpy(bad.astype(np.int32)).to(DEV), ws, cap,
+                    out, None, m, oi)
+    assert epl.epl_status(ws) == epl.EPL_ECAPACITY
+    for t_ in (out_full[:guard], out_full[guard + cap:], m_full[:guard], m_full[guard + cap:]):
+        assert (t_.view(torch.uint8) == POISON).all()
+    # expected placement: the oracle's in-expert rank on top of the bad offsets
+    oi_ref = ref["output_index"]
+    e_of = np.where(topk >= 0, topk, 0)
+    rows = np.where(topk >= 0, bad[e_of] + (oi_ref - ref["expert_start_loc"][e_of]), -1)
+    want_oi = np.where((rows >= 0) & (rows < cap), rows, -1)
+    np.testing.assert_array_equal(oi.cpu().numpy(), want_oi)
+    assert (want_oi[topk == 0] == -1).all() and ((want_oi >= 0) & (topk == E - 1)).sum() == 5
+    want_m = np.full(cap, np.frombuffer(bytes([POISON] * 4), np.int32)[0], np.int32)
+    counts = ref["num_tokens_per_expert"].astype(np.int64)
+    for e in range(E):
+        blk = (counts[e] + a - 1) // a * a
+        for q in range(bad[e], bad[e] + blk):
+            if 0 <= q < cap:
+                want_m[q] = e if q < bad[e] + counts[e] else -1
+    np.testing.assert_array_equal(m.cpu().numpy(), want_m)
+    tt, kk = np.nonzero(want_oi >= 0)
+    np.testing.assert_array_equal(u16(out)[want_oi[tt, kk]], x[tt])
 
 
 # ------------------------------------------------------------- FP8 payload --
@@ -614,7 +684,11 @@ def test_capacity_overflow_flagged_without_out_of_bounds_writes():
     epl.epl_dispatch(p, torch.from_numpy(topk).to(DEV), to_bf16(x), None, cap, cnt, per_rank,
                      None, in_rank, start, None, out, None, m, oi, ws)
     assert epl.epl_status(ws) == epl.EPL_ECAPACITY
-    np.testing.assert_array_equal(oi.cpu().numpy(), ref["output_index"])
+    # slots whose rows fall past the capacity are not placed: output_index -1
+    # (the marker of an unplaced slot), never a row id outside the buffer
+    want_oi = np.where(ref["output_index"] >= cap, -1, ref["output_index"])
+    np.testing.assert_array_equal(oi.cpu().numpy(), want_oi)
+    assert (ref["output_index"] >= cap).sum() == 37
     np.testing.assert_array_equal(u16(out), ref["out"][:cap])
     np.testing.assert_array_equal(m.cpu().numpy(), ref["m_indices"][:cap])
     assert (out_full[cap:].view(torch.uint8) == POISON).all()

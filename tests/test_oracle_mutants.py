@@ -15,7 +15,7 @@ import pytest
 import oracle
 from conftest import load_golden
 from oracle import Oracle, OracleError
-from test_oracle_pins import brute_force
+from test_oracle_pins import brute_force, tiny_group_pair
 
 SRC = open(os.path.join(os.path.dirname(oracle.__file__), "epl_oracle.c"), encoding="utf-8").read()
 
@@ -69,6 +69,12 @@ MUTANTS = {
                           "float v = (float)epl_oracle_bf16_to_double(xg[i]);"),
     "quant_stores_inverse_scale": ("scale[t * (int64_t)S + g] = s;",
                                    "scale[t * (int64_t)S + g] = inv;"),
+    "quant_inverse_in_binary32_range": (
+        "double inv = amax > 0.0f ? round_to_24_bits(448.0 / (double)amax) : 0.0;",
+        "double inv = amax > 0.0f ? (double)(448.0f / amax) : 0.0;"),
+    "quant_product_not_rounded": (
+        "double p = round_to_24_bits(epl_oracle_bf16_to_double(xg[i]) * inv);",
+        "double p = epl_oracle_bf16_to_double(xg[i]) * inv;"),
     "ll_rows_without_expert_stride": ("int64_t row = e * cap + j;", "int64_t row = e + j;"),
     "ll_src_info_global_token": ("src_info[row] = (int32_t)(t - seg * M);",
                                  "src_info[row] = (int32_t)t;"),
@@ -282,7 +288,17 @@ def _battery(orc: Oracle):
         want = torch.from_numpy(p).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
         return np.array_equal(q, want) and np.array_equal(sc, (amax / np.float32(448)).astype(np.float32))
 
+    def quant_tiny_groups():
+        import torch
+        g, x = tiny_group_pair()
+        qg, _ = orc.quantize_e4m3(g)
+        qx, sx = orc.quantize_e4m3(x)
+        xf = (x.astype(np.uint32) << 16).view(np.float32).reshape(x.shape[0], -1, 128)
+        want_s = (np.abs(xf).max(axis=2) / np.float32(448)).astype(np.float32)
+        return np.array_equal(qx, qg) and np.array_equal(sx, want_s)
+
     for name, fn in [("golden_scan", golden_scan), ("golden_rdma", golden_rdma),
+                     ("quant_tiny_groups", quant_tiny_groups),
                      ("golden_ll", golden_ll), ("ll_src_segments", ll_src_segments),
                      ("quant_ref", quant_ref), ("golden_hand", golden_hand), ("brute", brute),
                      ("golden_alignment", golden_alignment), ("brute_aligned", brute_aligned),

@@ -620,6 +620,44 @@ def test_quantize_matches_float32_reference():
     np.testing.assert_array_equal(q, q_ref)
 
 
+def tiny_group_pair(seed=31, shift=120):
+    """Groups g of bf16 values with magnitudes in [2^-5, 1.5) (a sixth of
+    them zero, signs mixed) and the same groups times 2^-shift, built by
+    lowering the bf16 exponent field, which is exact while the values stay
+    normal (shift 120 keeps them in [2^-125, 1.5 * 2^-120), above bf16's
+    smallest normal 2^-126). Returns (g, x) as uint16 bit patterns."""
+    rng = np.random.default_rng(seed)
+    T, H = 8, 256
+    mag = np.exp2(rng.uniform(-5, np.log2(1.5), (T, H))).astype(np.float32)
+    f = np.where(rng.random((T, H)) < 0.5, -mag, mag)
+    f[rng.random((T, H)) < 1 / 6] = 0.0
+    g = (f.view(np.uint32) >> 16).astype(np.uint16)        # truncate to bf16: exact values
+    exp = (g >> 7) & 0xFF
+    x = np.where(exp > 0, g - np.uint16(shift << 7), g).astype(np.uint16)
+    assert ((x >> 7) & 0xFF)[exp > 0].min() >= 1           # still normal
+    return g, x
+
+
+def test_quantize_tiny_groups_encode_like_scaled_groups():
+    """A group's codes do not depend on a power-of-two scale of the group:
+    x * (448 / amax) is the same real number after the scale cancels, so
+    groups whose amax is below 448 / FLT_MAX (where binary32's 448 / amax
+    overflows) encode exactly like the same groups scaled up by 2^120 (zeros
+    stay zero codes, nothing saturates); their scales are binary32's
+    amax / 448, subnormal here, as numpy's IEEE division gives them."""
+    g, x = tiny_group_pair()
+    xf = (x.astype(np.uint32) << 16).view(np.float32).reshape(x.shape[0], -1, 128)
+    amax = np.abs(xf).max(axis=2)
+    assert (amax < np.float32(448) / np.finfo(np.float32).max).all()   # the overflow range
+    qg, _ = oracle.quantize_e4m3(g)
+    qx, sx = oracle.quantize_e4m3(x)
+    np.testing.assert_array_equal(qx, qg)
+    np.testing.assert_array_equal(qx == 0, g == 0)          # zeros, and only zeros, code 0
+    assert not (qx == 0x7F).any() and not (qx == 0xFF).any()
+    np.testing.assert_array_equal(sx, (amax / np.float32(448)).astype(np.float32))
+    assert (sx < np.finfo(np.float32).tiny).all() and (sx > 0).all()
+
+
 def test_quantize_properties():
     """The largest magnitude of each group encodes to +-448; q * scale is
     within e4m3's half-spacing of x (relative 2^-4 for normal codes); an
