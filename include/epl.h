@@ -28,7 +28,9 @@
  * - All tensor arguments are DEVICE pointers to row-major, densely packed
  *   arrays, except `total_host` (pinned host memory, see epl_scan).
  * - The caller owns every buffer, including the workspace. The library
- *   allocates no memory and keeps no global state between calls.
+ *   allocates no memory and keeps no global state between calls, except
+ *   the static workspace of epl_dispatch_static (a device array of
+ *   EPL_STATIC_WORKSPACE_BYTES per GPU, part of the loaded library).
  * - `stream` is a hipStream_t (NULL = the default stream). Every call only
  *   enqueues work on that stream; none synchronises it except epl_status.
  * - Return value: EPL_OK (0) or a negative EPL_E* code. Argument errors are
@@ -202,6 +204,35 @@ int epl_dispatch(const epl_problem *p, const int64_t *topk_idx,
                  int32_t *total_host, uint16_t *out, float *out_scale,
                  int32_t *m_indices, int32_t *output_index,
                  void *workspace, void *stream);
+
+/* epl_dispatch for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, work and results as epl_dispatch, except that there is no
+ * workspace argument: the call uses a static workspace, a device array of
+ * EPL_STATIC_WORKSPACE_BYTES that the library holds on each GPU it runs on
+ * (one per GPU, the current device's) until the process ends, and that this
+ * call neither allocates nor frees (no hipMalloc / hipFree, no allocating
+ * library routine). Limit: problems whose epl_workspace_bytes exceed
+ * EPL_STATIC_WORKSPACE_BYTES are rejected with EPL_EINVAL before anything
+ * touches the GPU (8 MiB holds the per-slot ranks of about two million
+ * (token, k) slots, e.g. 65536 tokens at top-8 with room to spare). If
+ * `workspace_used` is not NULL it receives the device address of the static
+ * workspace used, which the caller may pass as `workspace` to epl_status,
+ * epl_total, epl_expert_scale and epl_combine like any workspace. Every call
+ * on one GPU shares that GPU's static workspace and it keeps the last call's
+ * contents: calls that overlap on one GPU (several streams or host threads
+ * at once) race and must be ordered by the caller; the status word and
+ * total read afterwards are those of the last dispatch. No part of the
+ * static workspace needs to start at zero. */
+#define EPL_STATIC_WORKSPACE_BYTES ((size_t)8 << 20)
+int epl_dispatch_static(const epl_problem *p, const int64_t *topk_idx,
+                        const uint16_t *x, const float *x_scale, int64_t capacity_rows,
+                        int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,
+                        int32_t *num_tokens_per_rdma_rank,
+                        uint8_t *is_token_in_rank, int32_t *expert_start_loc,
+                        int32_t *total_host, uint16_t *out, float *out_scale,
+                        int32_t *m_indices, int32_t *output_index,
+                        void **workspace_used, void *stream);
 
 /* Steps 3 and 1-3 for an FP8 (e4m3) payload, as DeepEP dispatches it
  * ("[MoE] Deepseek的All-to-all通信: DeepEP代码解读", section Dispatch: x as a

@@ -25,7 +25,8 @@ __all__ = [
     "epl_strerror", "epl_version", "dispatch", "combine", "expert_scale", "DispatchResult",
     "EPL_OK", "EPL_EINVAL", "EPL_ERANGE", "EPL_ECAPACITY", "EPL_EHIP", "EPL_OUT_F32",
     "EPL_OUT_BF16", "prepare", "epl_scatter_fp8", "epl_dispatch_fp8", "EPL_SCALE_NONE",
-    "EPL_SCALE_F32", "EPL_SCALE_UE8M0",
+    "EPL_SCALE_F32", "EPL_SCALE_UE8M0", "epl_dispatch_static", "StaticWorkspace",
+    "EPL_STATIC_WORKSPACE_BYTES",
 ]
 
 EPL_OK = 0
@@ -38,13 +39,14 @@ EPL_OUT_BF16 = 1
 EPL_SCALE_NONE = 0
 EPL_SCALE_F32 = 1
 EPL_SCALE_UE8M0 = 2
+EPL_STATIC_WORKSPACE_BYTES = 8 << 20
 
 # Every function include/epl.h declares; tests check the library exports them.
 C_ENTRY_POINTS = (
     "epl_validate", "epl_workspace_bytes", "epl_capacity_rows", "epl_layout", "epl_scan",
     "epl_scatter", "epl_dispatch", "epl_scatter_fp8", "epl_dispatch_fp8", "epl_combine",
     "epl_expert_scale", "epl_status", "epl_total", "epl_strerror", "epl_version",
-    "epl_ll_workspace_bytes", "epl_ll_dispatch",
+    "epl_ll_workspace_bytes", "epl_ll_dispatch", "epl_dispatch_static",
 )
 
 
@@ -147,6 +149,9 @@ def load() -> ctypes.CDLL:
     lib.epl_dispatch_fp8.argtypes = [_PP, _P, _P, _P, i32, i64, _P, _P, _P, _P, _P, _P, _P, _P,
                                      _P, _P, _P, _P]
     lib.epl_dispatch_fp8.restype = i32
+    lib.epl_dispatch_static.argtypes = [_PP, _P, _P, _P, i64, _P, _P, _P, _P, _P, _P, _P, _P,
+                                        _P, _P, ctypes.POINTER(ctypes.c_void_p), _P]
+    lib.epl_dispatch_static.restype = i32
     lib.epl_ll_workspace_bytes.argtypes = [_PP, i32]
     lib.epl_ll_workspace_bytes.restype = ctypes.c_size_t
     lib.epl_ll_dispatch.argtypes = [_PP, i32, i64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
@@ -208,6 +213,34 @@ def _need(t, name, dtype, shape=None, device=None, allow_none=False):
 
 
 WS_HEADER_BYTES = 256   # status word and total: all that combine / expert_scale / status touch
+
+
+class StaticWorkspace:
+    """The library's static workspace on one GPU (epl_dispatch_static): a
+    device address, not a tensor. It can be passed wherever a workspace is
+    taken after the dispatch that used it (epl_status, epl_total,
+    epl_combine, epl_expert_scale)."""
+
+    def __init__(self, address: int, device):
+        self.address, self.device = int(address), device
+
+    def data_ptr(self) -> int:
+        return self.address
+
+    def numel(self) -> int:
+        return EPL_STATIC_WORKSPACE_BYTES
+
+    def __repr__(self):
+        return f"StaticWorkspace({self.address:#x}, {self.device})"
+
+
+def _need_ws_arg(workspace, dev, allow_none=False):
+    """A workspace argument: a uint8 tensor on `dev`, or the static workspace."""
+    if isinstance(workspace, StaticWorkspace):
+        if dev is not None and workspace.device != dev:
+            raise ValueError(f"workspace is on {workspace.device}, expected {dev}")
+        return
+    _need(workspace, "workspace", _torch().uint8, None, dev, allow_none=allow_none)
 
 
 def _need_workspace(workspace, need: int, where: str):
@@ -353,6 +386,43 @@ def epl_dispatch(p: Problem, topk_idx, x, x_scale, capacity_rows, num_tokens_per
                                _ptr(workspace), _stream(stream, dev)), "epl_dispatch")
 
 
+def epl_dispatch_static(p: Problem, topk_idx, x, x_scale, capacity_rows, num_tokens_per_expert,
+                        num_tokens_per_rank, num_tokens_per_rdma_rank, is_token_in_rank,
+                        expert_start_loc, total_host, out, out_scale, m_indices, output_index,
+                        stream=None) -> StaticWorkspace:
+    """epl_dispatch without a workspace argument, for callers that cannot
+    allocate: the library's static workspace on the current GPU is used
+    (EPL_STATIC_WORKSPACE_BYTES, shared by every such call on that GPU, so
+    calls that overlap on one GPU race). Returns that workspace, for
+    epl_status / epl_total / epl_combine / epl_expert_scale. Problems that
+    need a larger workspace are rejected."""
+    torch = _torch()
+    dev = _check_scatter_args(p, x, x_scale, topk_idx, capacity_rows, out, out_scale, m_indices,
+                              output_index)
+    E, R, T = p.num_experts, p.num_ranks, p.num_tokens
+    _need(num_tokens_per_expert, "num_tokens_per_expert", torch.int32, (E,), dev)
+    _need(num_tokens_per_rank, "num_tokens_per_rank", torch.int32, (R,), dev)
+    _need_per_node(p, num_tokens_per_rdma_rank, dev)
+    _need(is_token_in_rank, "is_token_in_rank", torch.uint8, (T, R), dev)
+    _need(expert_start_loc, "expert_start_loc", torch.int32, (E,), dev)
+    need = epl_workspace_bytes(p)
+    if need <= 0 or need > EPL_STATIC_WORKSPACE_BYTES:
+        raise ValueError(f"epl_dispatch_static: the problem needs {need} bytes of workspace, "
+                         f"the static workspace holds {EPL_STATIC_WORKSPACE_BYTES}")
+    if total_host is not None and (total_host.device.type != "cpu" or not total_host.is_pinned()
+                                   or total_host.dtype != torch.int32):
+        raise ValueError("total_host must be a pinned CPU int32 tensor")
+    addr = ctypes.c_void_p()
+    _check(load().epl_dispatch_static(_prob(p), _ptr(topk_idx), _ptr(x), _ptr(x_scale),
+                                      int(capacity_rows), _ptr(num_tokens_per_expert),
+                                      _ptr(num_tokens_per_rank), _ptr(num_tokens_per_rdma_rank),
+                                      _ptr(is_token_in_rank), _ptr(expert_start_loc),
+                                      _ptr(total_host), _ptr(out), _ptr(out_scale),
+                                      _ptr(m_indices), _ptr(output_index), ctypes.byref(addr),
+                                      _stream(stream, dev)), "epl_dispatch_static")
+    return StaticWorkspace(addr.value, dev)
+
+
 def _check_fp8_args(p, x, x_scale, scale_format, topk_idx, capacity_rows, out, out_scale,
                     m_indices, output_index):
     torch = _torch()
@@ -463,7 +533,7 @@ def epl_combine(p: Problem, expert_out, expert_rows, output_index, topk_weights,
     _need(topk_weights, "topk_weights", torch.float32, (T, K), dev)
     ydt = torch.bfloat16 if out_dtype == EPL_OUT_BF16 else torch.float32
     _need(y, "y", ydt, (T, H), dev)
-    _need(workspace, "workspace", torch.uint8, None, dev, allow_none=True)
+    _need_ws_arg(workspace, dev, allow_none=True)
     if workspace is not None:
         _need_workspace(workspace, WS_HEADER_BYTES, "epl_combine")
     _check(load().epl_combine(_prob(p), _ptr(expert_out), int(expert_rows), _ptr(output_index),
@@ -479,7 +549,7 @@ def epl_expert_scale(p: Problem, rows_in, m_indices, capacity_rows, rows_out, wo
     dev = rows_in.device
     _need(m_indices, "m_indices", torch.int32, (capacity_rows,), dev)
     _need(rows_out, "rows_out", torch.bfloat16, (capacity_rows, H), dev)
-    _need(workspace, "workspace", torch.uint8, None, dev)
+    _need_ws_arg(workspace, dev)
     _need_workspace(workspace, WS_HEADER_BYTES, "epl_expert_scale")
     _check(load().epl_expert_scale(_prob(p), _ptr(rows_in), _ptr(m_indices), int(capacity_rows),
                                    _ptr(rows_out), _ptr(workspace), _stream(stream, dev)),

@@ -8,6 +8,7 @@
 #include <climits>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 #include "epl.h"
 #include "epl_kernels.h"
@@ -446,6 +447,44 @@ void launch_ll_scatter(const epl_problem &p, const WsLayout &w, int32_t M, int64
                        &at<WsHeader>(ws, 0)->status);
 }
 
+// The workspace of epl_dispatch_static: a device array that the library
+// holds on every GPU it runs on until the process ends, for callers that
+// cannot allocate. The dispatch writes every byte of it that it later reads,
+// so no part needs to start at zero. In host code `scratch` only stands for
+// the symbol: its device address on each GPU comes from hipGetSymbolAddress
+// (taken once per device, with that device current) and only that address is
+// handed to kernels.
+constexpr size_t kStaticWorkspaceBytes = size_t(8) << 20;
+static_assert(kStaticWorkspaceBytes == EPL_STATIC_WORKSPACE_BYTES, "header and library agree");
+static __device__ __align__(256) uint8_t scratch[kStaticWorkspaceBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+// This GPU's copy of `scratch` (the current device's), looked up on the
+// device's first call.
+int static_workspace(void **ws)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return EPL_EHIP;
+    if (dev < 0 || dev >= kMaxDevices)
+        return EPL_EINVAL;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr ||
+            !aligned(ptr, kWsAlign)) {
+            (void)hipGetLastError();
+            return EPL_EHIP;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *ws = g_scratch_ptr[dev];
+    return EPL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -612,6 +651,29 @@ int epl_dispatch(const epl_problem *p, const int64_t *topk_idx, const uint16_t *
                          num_tokens_per_expert, num_tokens_per_rank, num_tokens_per_rdma_rank,
                          is_token_in_rank, expert_start_loc, total_host, m_indices, output_index,
                          workspace, stream);
+}
+
+int epl_dispatch_static(const epl_problem *p, const int64_t *topk_idx, const uint16_t *x,
+                        const float *x_scale, int64_t capacity_rows,
+                        int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,
+                        int32_t *num_tokens_per_rdma_rank, uint8_t *is_token_in_rank,
+                        int32_t *expert_start_loc, int32_t *total_host, uint16_t *out,
+                        float *out_scale, int32_t *m_indices, int32_t *output_index,
+                        void **workspace_used, void *stream)
+{
+    // host checks first: nothing touches the GPU for a problem that does not fit
+    if (!problem_ok(p) || ws_layout(*p).bytes > kStaticWorkspaceBytes)
+        return EPL_EINVAL;
+    void *ws = nullptr;
+    const int rc = static_workspace(&ws);
+    if (rc != EPL_OK)
+        return rc;
+    if (workspace_used)
+        *workspace_used = ws;
+    return dispatch_rows(p, topk_idx, bf16_rows(*p, x, x_scale, out, out_scale), capacity_rows,
+                         num_tokens_per_expert, num_tokens_per_rank, num_tokens_per_rdma_rank,
+                         is_token_in_rank, expert_start_loc, total_host, m_indices, output_index,
+                         ws, stream);
 }
 
 int epl_dispatch_fp8(const epl_problem *p, const int64_t *topk_idx, const uint8_t *x,

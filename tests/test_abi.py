@@ -321,3 +321,20 @@ def test_wrappers_reject_an_undersized_workspace_before_any_call(lib, monkeypatc
     calls["epl_layout"](torch.empty(need, dtype=torch.uint8))
     epl.epl_combine(p, t, T * K, t, t, epl.EPL_OUT_F32, t, torch.empty(256, dtype=torch.uint8))
     assert rec.calls == ["epl_layout", "epl_combine"]
+
+
+def test_static_dispatch_rejects_what_its_workspace_cannot_hold(lib):
+    """epl_dispatch_static checks the problem and the size of the workspace
+    it needs against its static workspace on the host, before any HIP call:
+    an invalid problem and one needing more than EPL_STATIC_WORKSPACE_BYTES
+    return EPL_EINVAL here, without a GPU."""
+    assert epl.EPL_STATIC_WORKSPACE_BYTES == 8 << 20
+    big = P(num_tokens=1 << 20, scale_cols=0)           # ~32 MB of per-slot ranks
+    assert epl.epl_workspace_bytes(big) > epl.EPL_STATIC_WORKSPACE_BYTES
+    assert epl.epl_workspace_bytes(P(num_tokens=65536)) <= epl.EPL_STATIC_WORKSPACE_BYTES
+    fake = 1 << 20
+    args = (fake, fake, None, 10, fake, fake, None, fake, fake, None, fake, None, fake, fake,
+            None, None)
+    assert lib.epl_dispatch_static(ctypes.byref(big), *args) == epl.EPL_EINVAL
+    assert lib.epl_dispatch_static(ctypes.byref(P(num_ranks=3)), *args) == epl.EPL_EINVAL
+    assert lib.epl_dispatch_static(None, *args) == epl.EPL_EINVAL
