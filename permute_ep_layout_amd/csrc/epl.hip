@@ -312,24 +312,46 @@ struct RowArgs {
     uint32_t *out_scale;
 };
 
+// Work split of the scatter: one workgroup per token from kScatterGridFrom
+// tokens on; below, a striding grid of kScatterGridLong (rows of at least
+// kScatterLongRowBytes) or kScatterGrid workgroups; and with fewer tokens
+// than that grid, each row cut into column parts (decode-sized batches).
+struct ScatterSplit {
+    int parts;
+    unsigned grid;
+};
+
+ScatterSplit scatter_split(const epl_problem &p, int64_t row_bytes)
+{
+    const int64_t T = p.num_tokens;
+    if (T >= epl::kScatterGridFrom)
+        return {1, row_grid(T, T)};
+    const int64_t limit =
+        row_bytes >= epl::kScatterLongRowBytes ? epl::kScatterGridLong : epl::kScatterGrid;
+    if (T >= limit)
+        return {1, row_grid(T, limit)};
+    const int64_t nvec = row_bytes / 16;
+    const int64_t by_items = (epl::kScatterSmallItems + T - 1) / std::max<int64_t>(T, 1);
+    const int64_t by_width = nvec / epl::kScatterThreads;
+    const int parts = (int)std::max<int64_t>(
+        1, std::min<int64_t>({(int64_t)epl::kScatterMaxParts, by_items, by_width}));
+    return {parts, row_grid(T * parts, T * parts)};
+}
+
 template <int VPT>
 void launch_scatter(const epl_problem &p, const WsLayout &w, const RowArgs &ra,
                     const int64_t *topk, const int32_t *start, void *ws, int64_t cap,
-                    int32_t *m_idx, int32_t *oi, hipStream_t s)
+                    int32_t *m_idx, int32_t *oi, const ScatterSplit &sp, hipStream_t s)
 {
-    const unsigned grid =
-        p.num_tokens >= epl::kScatterGridFrom ? row_grid(p.num_tokens, p.num_tokens)
-        : ra.row_bytes >= epl::kScatterLongRowBytes ? row_grid(p.num_tokens, epl::kScatterGridLong)
-                                                     : row_grid(p.num_tokens, epl::kScatterGrid);
     const bool vec16 = ra.scale_mode == epl::kScaleRows && ra.words % 4 == 0 &&
                        aligned(ra.x_scale, 16) && aligned(ra.out_scale, 16);
-    hipLaunchKernelGGL(epl::ep_scatter_kernel<VPT>, dim3(grid), dim3(epl::kScatterThreads), 0, s,
-                       ra.x, ra.row_bytes, ra.scale_mode, ra.x_scale, ra.words, vec16,
+    auto kernel = sp.parts > 1 ? epl::ep_scatter_kernel<VPT, true> : epl::ep_scatter_kernel<VPT, false>;
+    hipLaunchKernelGGL(kernel, dim3(sp.grid), dim3(epl::kScatterThreads), 0, s, ra.x, ra.row_bytes, ra.scale_mode, ra.x_scale, ra.words, vec16,
                        ra.scale_ld, topk, start, at<const int32_t>(ws, w.block_count),
                        at<const int32_t>(ws, w.slot_rank), p.num_tokens, p.num_topk,
                        p.num_experts, w.block_tokens, alignment_of(p),
-                       at<const int32_t>(ws, w.counts), cap, ra.out, ra.out_scale, m_idx, oi,
-                       &at<WsHeader>(ws, 0)->status);
+                       at<const int32_t>(ws, w.counts), cap, sp.parts, ra.out, ra.out_scale,
+                       m_idx, oi, &at<WsHeader>(ws, 0)->status);
 }
 
 int enqueue_scatter(const epl_problem &p, const WsLayout &w, const RowArgs &ra,
@@ -338,12 +360,14 @@ int enqueue_scatter(const epl_problem &p, const WsLayout &w, const RowArgs &ra,
 {
     if (p.num_tokens == 0)
         return EPL_OK;
+    const ScatterSplit sp = scatter_split(p, ra.row_bytes);
     const int64_t nvec = ra.row_bytes / 16;
-    const int vpt = (int)std::min<int64_t>(8, (nvec + epl::kScatterThreads - 1) / epl::kScatterThreads);
-    switch (vpt) {
+    const int64_t pvec = (nvec + sp.parts - 1) / sp.parts;
+    const int vpt = (int)std::min<int64_t>(8, (pvec + epl::kScatterThreads - 1) / epl::kScatterThreads);
+    switch (std::max(vpt, 1)) {
 #define EPL_SCATTER_CASE(V)                                                                        \
     case V:                                                                                        \
-        launch_scatter<V>(p, w, ra, topk, start, ws, cap, m_idx, oi, s);                           \
+        launch_scatter<V>(p, w, ra, topk, start, ws, cap, m_idx, oi, sp, s);                       \
         break;
         EPL_SCATTER_CASE(1)
         EPL_SCATTER_CASE(2)

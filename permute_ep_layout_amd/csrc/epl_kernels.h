@@ -776,6 +776,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // 14 KB rows fewer rows in flight write more efficiently (4096 tokens of
 // hidden 7168: 96.7 -> 93.2 us, five runs each); with 7-8 KB rows 512 and
 // 1024 workgroups tie.
+// Decode-sized batches: column parts per row so that about kScatterSmallItems
+// (token, part) items exist, each part at least one pass of the workgroup
+// (kScatterThreads 16-byte vectors), at most kScatterMaxParts parts.
+#ifndef EPL_SCATTER_SMALL_ITEMS
+#define EPL_SCATTER_SMALL_ITEMS 2048
+#endif
+constexpr int64_t kScatterSmallItems = EPL_SCATTER_SMALL_ITEMS;
+constexpr int kScatterMaxParts = 8;
 constexpr int kScatterGrid = EPL_SCATTER_GRID;
 constexpr int kScatterGridLong = EPL_SCATTER_GRID_LONG;
 constexpr int64_t kScatterLongRowBytes = EPL_SCATTER_LONG_ROW_BYTES;
@@ -854,19 +862,29 @@ constexpr int kScaleCols = 2;   // W words per row, column-major: word j of row 
 // table, so one barrier per token suffices: a thread can only overwrite a
 // buffer after every thread has passed the barrier of the token in between,
 // i.e. has finished reading that buffer.
-template <int VPT>
+//
+// Batches with fewer tokens than the striding grid has workgroups (decode
+// sizes) split each row into `parts` column ranges, one work item per
+// (token, part): more workgroups share a token's bytes and the launch ends
+// sooner (the first part of a token also writes its indices and scale row).
+// SPLIT: the launch may cut rows into parts (parts > 1 only then; without
+// it every item is a whole token and the part arithmetic folds away).
+template <int VPT, bool SPLIT>
 __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
     const uint8_t *__restrict__ x, int64_t row_bytes, int scale_mode,
     const uint32_t *__restrict__ x_scale, int W, bool scale_vec16, int64_t scale_ld,
     const int64_t *__restrict__ topk, const int32_t *__restrict__ start,
     const int32_t *__restrict__ block_base, const int32_t *__restrict__ slot_rank, int64_t T,
     int K, int E, int B, int alignment, const int32_t *__restrict__ counts, int64_t capacity,
-    uint8_t *__restrict__ out, uint32_t *__restrict__ out_scale, int32_t *__restrict__ m_indices,
-    int32_t *__restrict__ output_index, uint32_t *__restrict__ status)
+    int parts_arg, uint8_t *__restrict__ out, uint32_t *__restrict__ out_scale,
+    int32_t *__restrict__ m_indices, int32_t *__restrict__ output_index,
+    uint32_t *__restrict__ status)
 {
     __shared__ int64_t s_row[2][kMaxTopk];
     const int tid = threadIdx.x;
+    const int parts = SPLIT ? parts_arg : 1;
     const int nvec = (int)(row_bytes >> 4);
+    const int pvec = SPLIT ? (nvec + parts - 1) / parts : nvec;   // 16-byte vectors per part
 
     // Padding rows of the aligned blocks: between an expert's last row and
     // the end of its block, marked -1 (workgroup w takes experts w, w + G, ...).
@@ -887,50 +905,61 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
     // or single words (column-major)
     const int nq = scale_mode == kScaleRows && scale_vec16 ? (W >> 2) : 0;
     const int nw = scale_mode == kScaleCols ? W : 0;
-    const TokenRange tr = token_range(T);
-    const int64_t step = tr.stride, t_end = tr.end;
+    // Work items: (token, column part) pairs, item i = token i / parts, part
+    // i % parts (parts = 1 except for batches too small to fill the GPU).
+    const TokenRange tr = token_range(T * parts);
+    const int64_t step = tr.stride, i_end = tr.end;
     const bool lead = tid < K;
+    auto token_of = [=](int64_t item) { return SPLIT ? item / parts : item; };
 
-    // Lookup pipeline of the first K threads (slot tid of the token):
-    //   (e1, r1): expert id and block rank of the next token;
+    // Lookup pipeline of the first K threads (slot tid of the item's token):
+    //   (e1, r1): expert id and block rank for the next item;
     //   (e0, r0, s0, b0): expert id, block rank, expert offset and block offset
-    //   of the current one. The two offsets are kept apart (and added only when
-    //   used, one token later) so that no wave waits for them early.
+    //   for the current one. The two offsets are kept apart (and added only
+    //   when used, one item later) so that no wave waits for them early. The
+    //   first item's offsets are loaded only after its row loads are issued,
+    //   so that a workgroup with a single item waits for one lookup round
+    //   trip before its row load instead of two.
     int64_t e0 = -1, e1 = -1;
     int r0 = 0, r1 = 0, s0 = 0, b0 = 0;
     auto valid = [E](int64_t e) { return e >= 0 && e < E; };
-    if (lead && tr.first < t_end) {
-        const int64_t t = tr.first;
+    if (lead && tr.first < i_end) {
+        const int64_t t = token_of(tr.first);
         e0 = topk[t * K + tid];
         r0 = slot_rank[t * K + tid];
-        if (valid(e0)) {
-            s0 = start[e0];
-            b0 = block_base[(t / B) * E + e0];
-        }
-        if (t + step < t_end) {
-            e1 = topk[(t + step) * K + tid];
-            r1 = slot_rank[(t + step) * K + tid];
+        if (tr.first + step < i_end) {
+            const int64_t tn = token_of(tr.first + step);
+            e1 = topk[tn * K + tid];
+            r1 = slot_rank[tn * K + tid];
         }
     }
 
     int it = 0;
-    for (int64_t t = tr.first; t < t_end; t += step, ++it) {
+    for (int64_t item = tr.first; item < i_end; item += step, ++it) {
+        const int64_t t = token_of(item);
+        const int q = (int)(item - t * parts);
+        const int v0 = q * pvec, v1 = min(nvec, v0 + pvec);
+        const bool first_part = q == 0;   // writes the indices and the scale row
         int64_t *rows = s_row[it & 1];
         const u32x4 *xrow = reinterpret_cast<const u32x4 *>(x + t * row_bytes);
         u32x4 v[VPT];
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int idx = i * kScatterThreads + tid;
-            if (idx < nvec)
+            const int idx = v0 + i * kScatterThreads + tid;
+            if (idx < v1)
                 v[i] = xrow[idx];
         }
         u32x4 sv = {0u, 0u, 0u, 0u};
         uint32_t sw = 0u;
-        if (tid < nq)
+        if (first_part && tid < nq)
             sv = reinterpret_cast<const u32x4 *>(x_scale + t * W)[tid];
-        if (tid < nw)
+        if (first_part && tid < nw)
             sw = x_scale[t * W + tid];
 
+        if (lead && it == 0 && valid(e0)) {
+            s0 = start[e0];
+            b0 = block_base[(t / B) * E + e0];
+        }
         if (lead) {
             int pos = -1;
             int64_t row = -1;
@@ -941,34 +970,37 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
                 if (p >= 0 && p < capacity) {
                     row = p;
                     pos = (int)p;
-                    m_indices[p] = (int32_t)e0;
+                    if (first_part)
+                        m_indices[p] = (int32_t)e0;
                 } else {
                     atomicOr(status, kStatusCapacity);
                 }
             }
-            output_index[t * K + tid] = pos;
+            if (first_part)
+                output_index[t * K + tid] = pos;
             rows[tid] = row;
-            // advance the pipeline: offsets of the next token, ids of the one after
+            // advance the pipeline: offsets for the next item, ids for the one after
             e0 = e1;
             r0 = r1;
             s0 = 0;
             b0 = 0;
-            if (t + step < t_end && valid(e0)) {
+            if (item + step < i_end && valid(e0)) {
                 s0 = start[e0];
-                b0 = block_base[((t + step) / B) * E + e0];
+                b0 = block_base[(token_of(item + step) / B) * E + e0];
             }
             e1 = -1;
-            if (t + 2 * step < t_end) {
-                e1 = topk[(t + 2 * step) * K + tid];
-                r1 = slot_rank[(t + 2 * step) * K + tid];
+            if (item + 2 * step < i_end) {
+                const int64_t t2 = token_of(item + 2 * step);
+                e1 = topk[t2 * K + tid];
+                r1 = slot_rank[t2 * K + tid];
             }
         }
         lds_barrier();
-        for (int base = 0;;) {
+        for (int base = v0;;) {
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
                 const int idx = base + i * kScatterThreads + tid;
-                if (idx < nvec) {
+                if (idx < v1) {
                     for (int k = 0; k < K; ++k) {
                         const int64_t row = rows[k];
                         if (row >= 0) {
@@ -982,15 +1014,17 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
                 }
             }
             base += kScatterThreads * VPT;
-            if (base >= nvec)
+            if (base >= v1)
                 break;
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
                 const int idx = base + i * kScatterThreads + tid;
-                if (idx < nvec)
+                if (idx < v1)
                     v[i] = xrow[idx];
             }
         }
+        if (!first_part)
+            continue;
         if (nq > 0) {
             // 16-byte pieces of the scale row (W % 4 == 0 and 16-byte aligned
             // bases); threads past the first kScatterThreads pieces take the rest.

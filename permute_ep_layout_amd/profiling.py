@@ -36,7 +36,12 @@ SHORT = (("ep_layout_scan_kernel", "layout_scan"), ("ep_layout_kernel", "layout"
          ("ep_scan_kernel", "scan"),
          ("ep_ll_scatter_kernel", "ll_scatter"),
          ("ep_scatter_kernel", "scatter"), ("ep_combine_kernel", "combine"),
-         ("ep_expert_scale_kernel", "expert"))
+         ("ep_expert_scale_kernel", "expert"),
+         # the benchmark's write-piece probes (bench_probe/stream_probe.hip)
+         ("pieces_kernel<true, true>", "pieces_nt_xcd"),
+         ("pieces_kernel<true, false>", "pieces_nt_inorder"),
+         ("pieces_kernel<false, true>", "pieces_wb_xcd"),
+         ("pieces_kernel<false, false>", "pieces_wb_inorder"))
 
 
 def _code_only(text: str) -> str:

@@ -443,6 +443,9 @@ def test_fp8_dsv3_ue8m0_parity():
     ("ue8m0_large_t", 9000, 256, 64, 6, 8, epl.EPL_SCALE_UE8M0, 16, 0, False),
     ("ue8m0_striding", 6001, 384, 64, 6, 8, epl.EPL_SCALE_UE8M0, 0, 0, False),
     ("none_striding_split_aligned", 4999, 272, 24, 3, 6, epl.EPL_SCALE_NONE, 8, 0, True),
+    # decode-sized: column parts of byte rows (3 parts of 7168 bytes)
+    ("ue8m0_decode_t200", 200, 7168, 256, 8, 32, epl.EPL_SCALE_UE8M0, 0, 0, False),
+    ("f32_decode_t64_aligned", 64, 7168, 64, 8, 8, epl.EPL_SCALE_F32, 16, 0, True),
 ], ids=lambda c: c[0])
 def test_fp8_shapes(case):
     name, T, H, E, K, R, fmt, a, extra, split = case
@@ -481,6 +484,14 @@ RAGGED = [
     # tokens (4 to 16), with uneven token counts per workgroup
     ("striding_ragged_h264", 5555, 5, 24, 6, 264, False, 0.1),
     ("striding_scales_s9", 7000, 4, 32, 8, 1152, True, 0.05),
+    # decode-sized batches of long rows: fewer tokens than the striding grid,
+    # each row cut into column parts (7 at hidden 7168, 5 at hidden 8960, 3
+    # of 134, 134 and 132 vectors at hidden 3200); scale rows and indices
+    # are written by the first part only
+    ("decode_t256_dsv3", 256, 8, 256, 32, 7168, True, 0.0),
+    ("decode_t100_dsv3_drop", 100, 8, 256, 32, 7168, True, 0.1),
+    ("decode_t37_ragged_parts", 37, 4, 16, 4, 3200, True, 0.2),
+    ("decode_t500_h8960", 500, 4, 32, 8, 8960, True, 0.05),
 ]
 
 
