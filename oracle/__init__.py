@@ -88,6 +88,10 @@ class Oracle:
                                              _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
                                              _c_i32, _ptr, _ptr, _ptr]
         lib.epl_oracle_time_pass.restype = ctypes.c_int
+        lib.epl_oracle_time_ll_pass.argtypes = [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
+                                                _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
+                                                _ptr, _ptr, _c_i64, _ptr, _ptr, _ptr, _ptr]
+        lib.epl_oracle_time_ll_pass.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -294,6 +298,42 @@ class Oracle:
                 _p(cnt), _p(per_rank), _p(in_rank), _p(start), _p(out), _p(out_scale),
                 _p(m_idx), _p(oi), int(expert_mode), _p(eo), _p(y), _p(ns)), "time_pass")
             return dict(zip(("layout", "scan", "scatter", "expert", "combine"), ns * 1e-9))
+        return run
+
+    def timed_ll_passes(self, x, topk_idx, topk_weights, num_experts, tokens_per_segment, cap):
+        """A callable that runs one pass of the low-latency dispatch and the
+        combine over the experts' bf16 output rows in the C timing harness,
+        on buffers allocated here once, and returns the step times in
+        seconds. The expert output stands in as each placed row's bf16 token
+        row, gathered compactly once (the placement is deterministic)."""
+        xb = _c(x, np.uint16)
+        topk = _c(topk_idx, np.int64)
+        T, K = topk.shape
+        H = xb.shape[1]
+        E, M, cap = int(num_experts), int(tokens_per_segment), int(cap)
+        S = H // 128
+        out = np.empty((E, cap, H), np.uint8)          # only placed rows are touched
+        out_scale = np.empty((E, S, cap), np.float32)
+        recv = np.empty(E, np.int32)
+        src = np.empty((E, cap), np.int32)
+        rng = np.empty((E, T // M, 2), np.int32)
+        oi = np.empty((T, K), np.int32)
+        ovf = np.zeros(1, np.int32)
+        first = self.ll_dispatch(None, topk, E, M, cap, hidden=H)["output_index"]
+        valid = first >= 0
+        compact = np.full(first.shape, -1, np.int32)
+        compact[valid] = np.arange(int(valid.sum()), dtype=np.int32)
+        eo = np.ascontiguousarray(np.repeat(xb, K, axis=0)[valid.ravel()])
+        w = _c(topk_weights, np.float32)
+        y = np.empty((T, H), np.float64)
+        ns = np.zeros(2, np.int64)
+
+        def run():
+            _check(self.lib.epl_oracle_time_ll_pass(
+                T, K, E, H, M, cap, _p(xb), _p(topk), _p(out), _p(out_scale), _p(recv), _p(src),
+                _p(rng), _p(oi), _p(ovf), _p(eo), eo.shape[0], _p(compact), _p(w), _p(y),
+                _p(ns)), "time_ll_pass")
+            return dict(zip(("ll_dispatch", "combine"), ns * 1e-9))
         return run
 
     def run_all(self, x, x_scale, topk_idx, topk_weights, num_experts, num_ranks,

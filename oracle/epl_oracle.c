@@ -640,3 +640,30 @@ int epl_oracle_time_pass(int64_t T, int32_t K, int32_t E, int32_t R, int32_t H,
     ns[4] = t5 - t4;
     return rc;
 }
+
+/* The same harness for the low-latency step: epl_oracle_ll_dispatch into the
+ * caller's rectangle buffers, then the combine over the experts' bf16 output
+ * rows given compactly (expert_out [n_rows, H], the row of slot (t, k) being
+ * output_index_compact[t, k], prepared by the caller from a previous pass:
+ * the placement is deterministic). ns[0] dispatch, ns[1] combine. */
+int epl_oracle_time_ll_pass(int64_t T, int32_t K, int32_t E, int32_t H, int32_t M, int64_t cap,
+                            const uint16_t *x, const int64_t *topk_idx, uint8_t *out,
+                            float *out_scale, int32_t *recv_count, int32_t *src_info,
+                            int32_t *layout_range, int32_t *output_index, int32_t *overflow,
+                            const uint16_t *expert_out, int64_t n_rows,
+                            const int32_t *output_index_compact, const float *topk_weights,
+                            double *y, int64_t *ns)
+{
+    int64_t t0 = monotonic_ns();
+    int rc = epl_oracle_ll_dispatch(T, K, E, H, M, cap, x, topk_idx, out, out_scale, recv_count,
+                                    src_info, layout_range, output_index, overflow);
+    int64_t t1 = monotonic_ns();
+    if (rc != ORACLE_OK)
+        return rc;
+    rc = epl_oracle_combine(T, K, H, expert_out, n_rows, output_index_compact, topk_weights, NULL,
+                            T, y);
+    int64_t t2 = monotonic_ns();
+    ns[0] = t1 - t0;
+    ns[1] = t2 - t1;
+    return rc;
+}
