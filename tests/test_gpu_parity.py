@@ -760,3 +760,80 @@ def test_runs_on_a_side_stream():
     check_layout_and_scatter(r, ref, inp["x"], None)
     check_combine_f32(y.cpu().numpy(), ref["y"],
                       combine_bound(ref["out"], ref["output_index"], inp["topk_weights"]))
+
+
+# ----------------------------------------------------- randomized sweep --
+
+def _sweep_shape(rng):
+    """One seeded random problem: token count log-uniform in [1, 3000], any
+    top-k up to 16, ranks and experts per rank, hidden widths (multiples of
+    128 when there are scales), -1 rates, duplicate experts within a token,
+    expert alignment, ranks per node, split or fused calls."""
+    R = int(rng.choice([1, 2, 3, 4, 8, 16, 32]))
+    E = R * int(rng.choice([1, 2, 3, 5, 8]))
+    K = int(rng.integers(1, 17))
+    T = int(np.exp(rng.uniform(0, np.log(3000))))
+    scales = bool(rng.random() < 0.4)
+    H = 128 * int(rng.integers(1, 33)) if scales else 8 * int(rng.integers(1, 400))
+    a = int(rng.choice([0, 0, 1, 2, 7, 16, 64]))
+    G = int(rng.choice([0, 1, max(1, R // 2), R])) if R > 1 else 0
+    if G and R % G:
+        G = 0
+    drop = float(rng.choice([0.0, 0.1, 0.5]))
+    dup = bool(rng.random() < 0.3)
+    split = bool(rng.random() < 0.3)
+    if dup:   # ids drawn with replacement: a token may pick an expert twice
+        topk = rng.integers(0, E, size=(T, K)).astype(np.int64)
+    else:
+        topk = np.stack([rng.permutation(E)[:K] if K <= E else rng.integers(0, E, K)
+                         for _ in range(T)]).astype(np.int64)
+    topk[rng.random(topk.shape) < drop] = -1
+    return dict(T=T, K=K, E=E, R=R, H=H, scales=scales, a=a, G=G, split=split, topk=topk)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_shape_sweep(seed):
+    """40 seeded random problems through epl_dispatch (or the split calls)
+    against the oracle: counts, masks, per-node counts, offsets, every row,
+    scale row and index bit-exact; padding rows marked; combine within 1e-5
+    of sum |w v| (fp32) and the bf16 output the RNE of it."""
+    rng = np.random.default_rng(5000 + seed)
+    c = _sweep_shape(rng)
+    T, K, E, R, H = c["T"], c["K"], c["E"], c["R"], c["H"]
+    print(f"[parity] sweep seed={seed} T={T} K={K} E={E} R={R} H={H} scales={c['scales']} "
+          f"a={c['a']} G={c['G']} split={c['split']}", flush=True)
+    x, xs, wt = _mk(c["topk"], H, seed, c["scales"])
+    ref = orc().run_all(x, xs, c["topk"], wt, E, R, alignment=c["a"])
+    r = gpu_dispatch(c["topk"], x, xs, E, R, split=c["split"], alignment=c["a"], G=c["G"])
+    assert epl.epl_status(r["ws"]) == epl.EPL_OK
+    check_layout_and_scatter(r, ref, x, xs)
+    y = gpu_combine(r, r["out"], wt, epl.EPL_OUT_F32)
+    yb = gpu_combine(r, r["out"], wt, epl.EPL_OUT_BF16)
+    bound = combine_bound(ref["expert_out"], ref["output_index"], wt)
+    check_combine_f32(y.cpu().numpy(), ref["y"], bound)
+    check_bf16_is_rne_of_f32(u16(yb), y.cpu())
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_fp8_sweep(seed):
+    """12 seeded random FP8 problems (no scales, fp32 rows of scales, or
+    transposed UE8M0 words), fused or split, with or without alignment and
+    spare capacity, against the oracle's byte-row scatter."""
+    rng = np.random.default_rng(7000 + seed)
+    R = int(rng.choice([1, 2, 4, 8]))
+    E = R * int(rng.choice([1, 3, 8]))
+    K = int(rng.integers(1, min(E, 12) + 1))
+    T = int(np.exp(rng.uniform(0, np.log(3000))))
+    H = 128 * int(rng.integers(1, 40))
+    fmt = int(rng.choice([epl.EPL_SCALE_NONE, epl.EPL_SCALE_F32, epl.EPL_SCALE_UE8M0]))
+    a = int(rng.choice([0, 8, 32]))
+    extra = int(rng.choice([0, 0, 13]))
+    split = bool(rng.random() < 0.4)
+    print(f"[parity] fp8 sweep seed={seed} T={T} K={K} E={E} R={R} H={H} fmt={fmt} a={a} "
+          f"extra={extra} split={split}", flush=True)
+    w = workloads.Workload(f"sweep{seed}", seed=9000 + seed, num_tokens=T, hidden=H,
+                           num_experts=E, num_topk=K, num_ranks=R, scales=True,
+                           routing="uniform", drop_rate=0.1, payload="fp8",
+                           scale_format="f32" if fmt == epl.EPL_SCALE_F32 else "ue8m0",
+                           ranks_per_node=0)
+    fp8_parity(w, fmt, alignment=a, extra_cap=extra, split=split)
