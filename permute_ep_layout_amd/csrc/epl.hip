@@ -157,7 +157,7 @@ int ll_block_tokens(const epl_problem &p, int32_t M)
 struct WsLayout {
     int block_tokens;
     int64_t num_blocks;
-    size_t counts, block_count, block_rank, block_err, slot_rank, bytes;
+    size_t counts, block_count, block_base, block_rank, block_err, slot_rank, bytes;
 };
 
 WsLayout ws_layout(const epl_problem &p, int block_tokens)
@@ -169,6 +169,8 @@ WsLayout ws_layout(const epl_problem &p, int block_tokens)
     w.counts = off;
     off += round_up((size_t)p.num_experts * 4, kWsAlign);
     w.block_count = off;
+    off += round_up((size_t)w.num_blocks * (size_t)p.num_experts * 4, kWsAlign);
+    w.block_base = off;
     off += round_up((size_t)w.num_blocks * (size_t)p.num_experts * 4, kWsAlign);
     w.block_rank = off;
     off += round_up((size_t)w.num_blocks * (size_t)(p.num_ranks + nodes_of(p)) * 4, kWsAlign);
@@ -228,7 +230,7 @@ int enqueue_layout(const epl_problem &p, const WsLayout &w, const int64_t *topk,
                            p.ranks_per_node, epl::div_magic(std::max(p.ranks_per_node, 1)), Rn,
                            w.block_tokens, in_rank, vec16, at<int32_t>(ws, w.block_count),
                            at<int32_t>(ws, w.block_rank), at<uint32_t>(ws, w.block_err),
-                           at<int32_t>(ws, w.slot_rank));
+                           at<int32_t>(ws, w.slot_rank), &at<WsHeader>(ws, 0)->status);
     };
     if (wide_layout(p))
         launch(epl::ep_layout_kernel<epl::kLayoutThreadsWide>, epl::kLayoutThreadsWide);
@@ -266,7 +268,7 @@ int enqueue_fused(const epl_problem &p, const WsLayout &w, const int64_t *topk, 
                        p.num_experts / p.num_ranks, epl::div_magic(p.num_experts / p.num_ranks),
                        p.ranks_per_node, epl::div_magic(std::max(p.ranks_per_node, 1)), nodes_of(p),
                        alignment_of(p), in_rank, vec16, cnt, per_rank, per_node, start,
-                       at<int32_t>(ws, w.block_count), at<int32_t>(ws, w.slot_rank),
+                       at<int32_t>(ws, w.block_base), at<int32_t>(ws, w.slot_rank),
                        at<int32_t>(ws, w.counts), at<WsHeader>(ws, 0), mapped);
     int rc = launch_status();
     if (rc != EPL_OK)
@@ -285,7 +287,8 @@ int enqueue_scan(const epl_problem &p, const WsLayout &w, int mode, int32_t *cnt
     int32_t *mapped = (mode & epl::kScanPrefix) ? mapped_host_word(total_host) : nullptr;
     hipLaunchKernelGGL(epl::ep_scan_kernel, dim3(1), dim3(epl::kScanThreads), 0, s, mode,
                        w.num_blocks, p.num_experts, p.num_ranks, nodes_of(p), alignment_of(p),
-                       at<int32_t>(ws, w.block_count), at<int32_t>(ws, w.block_rank),
+                       at<const int32_t>(ws, w.block_count), at<int32_t>(ws, w.block_base),
+                       at<int32_t>(ws, w.block_rank),
                        at<uint32_t>(ws, w.block_err), cnt, per_rank, per_node, start,
                        at<int32_t>(ws, w.counts), at<WsHeader>(ws, 0), mapped);
     int rc = launch_status();
@@ -338,25 +341,111 @@ ScatterSplit scatter_split(const epl_problem &p, int64_t row_bytes)
     return {parts, row_grid(T * parts, T * parts)};
 }
 
+// The scan's work done by the scatter of a dispatch (epl::ScanInScatter):
+// for layouts of several blocks whose per-block count matrix every
+// workgroup of a striding scatter grid can read (at most
+// EPL_SCAN_IN_SCATTER_ENTRIES words), with the LDS rows of per-block
+// offsets that one workgroup's token range needs. Saves the scan launch
+// between layout and scatter. 0 turns it off.
+#ifndef EPL_SCAN_IN_SCATTER_ENTRIES
+#define EPL_SCAN_IN_SCATTER_ENTRIES 16384
+#endif
+// At most this many LDS rows of per-block offsets per workgroup (blocks
+// beyond them are summed from the count matrix by the slot's own thread).
+#ifndef EPL_SCAN_IN_SCATTER_ROWS
+#define EPL_SCAN_IN_SCATTER_ROWS 64
+#endif
+constexpr size_t kScanInScatterLds = 32768;
+
+struct ScanPlan {
+    bool on = false;
+    int nbl = 0;        // LDS rows of per-block offsets
+    size_t lds = 0;     // dynamic LDS bytes
+};
+
+ScanPlan scan_in_scatter(const epl_problem &p, const WsLayout &w, const ScatterSplit &sp)
+{
+    ScanPlan plan;
+    const int64_t T = p.num_tokens, E = p.num_experts, nb = w.num_blocks;
+    if (fused_layout(p) || T == 0 || nb == 0 || sp.parts != 1 ||
+        sp.grid > (unsigned)epl::kScatterGrid || nb * E > EPL_SCAN_IN_SCATTER_ENTRIES)
+        return plan;
+    // the kernel reads the count matrix in 16-byte pieces: E / 4 expert
+    // quads, each over kScatterThreads / (E / 4) segments of at most 16 blocks
+    if (E % 4 != 0 || E / 4 > epl::kScatterThreads)
+        return plan;
+    const int64_t segs = epl::kScatterThreads / (E / 4);
+    if ((nb + segs - 1) / segs > 16)
+        return plan;
+    // Blocks one workgroup's tokens can touch (the kernel's token_range):
+    // with the XCD-aware ranges tokens of a contiguous eighth of the batch,
+    // per = ceil(T / 8) tokens, which meet at most ceil((per - 1) / B) + 1
+    // blocks of B tokens; else any block.
+    int64_t nbl = nb;
+    if (EPL_XCD_MAP && sp.grid % epl::kNumXcd == 0 && sp.grid >= (unsigned)epl::kNumXcd) {
+        const int64_t per = (T + epl::kNumXcd - 1) / epl::kNumXcd;
+        nbl = std::min<int64_t>(nb, (per - 1 + w.block_tokens - 1) / w.block_tokens + 1);
+    }
+    nbl = std::min<int64_t>(nbl, EPL_SCAN_IN_SCATTER_ROWS);
+    const size_t lds = ((size_t)(2 + nbl) * (size_t)E + epl::kScanSegWords) * 4;
+    if (lds > kScanInScatterLds)
+        return plan;
+    plan.on = true;
+    plan.nbl = (int)nbl;
+    plan.lds = lds;
+    return plan;
+}
+
+// Where the scatter of a dispatch stores the scan's results.
+struct ScanOuts {
+    int32_t *cnt, *per_rank, *per_node, *start, *total_mapped;
+};
+
 template <int VPT>
 void launch_scatter(const epl_problem &p, const WsLayout &w, const RowArgs &ra,
                     const int64_t *topk, const int32_t *start, void *ws, int64_t cap,
-                    int32_t *m_idx, int32_t *oi, const ScatterSplit &sp, hipStream_t s)
+                    int32_t *m_idx, int32_t *oi, const ScatterSplit &sp, const ScanPlan &plan,
+                    const ScanOuts &so, hipStream_t s)
 {
     const bool vec16 = ra.scale_mode == epl::kScaleRows && ra.words % 4 == 0 &&
                        aligned(ra.x_scale, 16) && aligned(ra.out_scale, 16);
-    auto kernel = sp.parts > 1 ? epl::ep_scatter_kernel<VPT, true> : epl::ep_scatter_kernel<VPT, false>;
-    hipLaunchKernelGGL(kernel, dim3(sp.grid), dim3(epl::kScatterThreads), 0, s, ra.x, ra.row_bytes, ra.scale_mode, ra.x_scale, ra.words, vec16,
-                       ra.scale_ld, topk, start, at<const int32_t>(ws, w.block_count),
+    epl::ScanInScatter sc{};
+    if (plan.on) {
+        sc.block_count = at<const int32_t>(ws, w.block_count);
+        sc.block_rank = at<const int32_t>(ws, w.block_rank);
+        sc.block_err = at<const uint32_t>(ws, w.block_err);
+        sc.nb = w.num_blocks;
+        sc.R = p.num_ranks;
+        sc.Rn = nodes_of(p);
+        sc.nbl = plan.nbl;
+        sc.cnt = so.cnt;
+        sc.per_rank = so.per_rank;
+        sc.per_node = so.per_node;
+        sc.start = so.start;
+        sc.ws_counts = at<int32_t>(ws, w.counts);
+        sc.block_base = at<int32_t>(ws, w.block_base);
+        sc.hdr = at<WsHeader>(ws, 0);
+        sc.total_out = so.total_mapped;
+    }
+    auto kernel = plan.on ? epl::ep_scatter_kernel<VPT, false, true>
+                  : sp.parts > 1 ? epl::ep_scatter_kernel<VPT, true, false>
+                                 : epl::ep_scatter_kernel<VPT, false, false>;
+    hipLaunchKernelGGL(kernel, dim3(sp.grid), dim3(epl::kScatterThreads), plan.lds, s, ra.x,
+                       ra.row_bytes, ra.scale_mode, ra.x_scale, ra.words, vec16,
+                       ra.scale_ld, topk, start, at<const int32_t>(ws, w.block_base),
                        at<const int32_t>(ws, w.slot_rank), p.num_tokens, p.num_topk,
                        p.num_experts, w.block_tokens, alignment_of(p),
                        at<const int32_t>(ws, w.counts), cap, sp.parts, ra.out, ra.out_scale,
-                       m_idx, oi, &at<WsHeader>(ws, 0)->status);
+                       m_idx, oi, &at<WsHeader>(ws, 0)->status, sc);
 }
 
+// The scatter launch. With plan.on (a dispatch whose scan launch was left
+// out, see scan_in_scatter) it also does the scan's work and stores its
+// results where `outs` says; else the scan has run before it.
 int enqueue_scatter(const epl_problem &p, const WsLayout &w, const RowArgs &ra,
                     const int64_t *topk, const int32_t *start, void *ws, int64_t cap,
-                    int32_t *m_idx, int32_t *oi, hipStream_t s)
+                    int32_t *m_idx, int32_t *oi, hipStream_t s, const ScanPlan &plan = ScanPlan{},
+                    const ScanOuts &outs = ScanOuts{})
 {
     if (p.num_tokens == 0)
         return EPL_OK;
@@ -367,7 +456,7 @@ int enqueue_scatter(const epl_problem &p, const WsLayout &w, const RowArgs &ra,
     switch (std::max(vpt, 1)) {
 #define EPL_SCATTER_CASE(V)                                                                        \
     case V:                                                                                        \
-        launch_scatter<V>(p, w, ra, topk, start, ws, cap, m_idx, oi, sp, s);                       \
+        launch_scatter<V>(p, w, ra, topk, start, ws, cap, m_idx, oi, sp, plan, outs, s);           \
         break;
         EPL_SCATTER_CASE(1)
         EPL_SCATTER_CASE(2)
@@ -464,7 +553,7 @@ void launch_ll_scatter(const epl_problem &p, const WsLayout &w, int32_t M, int64
     const unsigned grid =
         row_grid(std::max<int64_t>(std::min<int64_t>(p.num_tokens, epl::kLLGrid), need), 1 << 30);
     hipLaunchKernelGGL(epl::ep_ll_scatter_kernel<VPT>, dim3(grid), dim3(epl::kScatterThreads), 0, s,
-                       x, p.hidden, topk, at<const int32_t>(ws, w.block_count),
+                       x, p.hidden, topk, at<const int32_t>(ws, w.block_base),
                        at<const int32_t>(ws, w.slot_rank), at<const int32_t>(ws, w.counts),
                        p.num_tokens, p.num_topk, p.num_experts, w.block_tokens, M, cap, out,
                        out_scale, recv_count, src_info, layout_range, output_index,
@@ -643,22 +732,35 @@ static int dispatch_rows(const epl_problem *p, const int64_t *topk_idx, const Ro
         return EPL_EINVAL;
     const WsLayout w = ws_layout(*p);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t *per_node = nodes_of(*p) ? num_tokens_per_rdma_rank : nullptr;
+    const ScanPlan plan = scan_in_scatter(*p, w, scatter_split(*p, ra.row_bytes));
     int rc;
     if (fused_layout(*p)) {
         rc = enqueue_fused(*p, w, topk_idx, is_token_in_rank, num_tokens_per_expert,
-                           num_tokens_per_rank, nodes_of(*p) ? num_tokens_per_rdma_rank : nullptr,
-                           expert_start_loc, total_host, workspace, s);
+                           num_tokens_per_rank, per_node, expert_start_loc, total_host,
+                           workspace, s);
     } else {
         rc = enqueue_layout(*p, w, topk_idx, is_token_in_rank, workspace, s);
-        if (rc == EPL_OK)
+        if (rc == EPL_OK && !plan.on)
             rc = enqueue_scan(*p, w, epl::kScanReduce | epl::kScanPrefix, num_tokens_per_expert,
-                              num_tokens_per_rank,
-                              nodes_of(*p) ? num_tokens_per_rdma_rank : nullptr,
-                              expert_start_loc, total_host, workspace, s);
+                              num_tokens_per_rank, per_node, expert_start_loc, total_host,
+                              workspace, s);
     }
-    if (rc == EPL_OK)
-        rc = enqueue_scatter(*p, w, ra, topk_idx, expert_start_loc, workspace, capacity_rows,
-                             m_indices, output_index, s);
+    if (rc != EPL_OK)
+        return rc;
+    if (!plan.on)
+        return enqueue_scatter(*p, w, ra, topk_idx, expert_start_loc, workspace, capacity_rows,
+                               m_indices, output_index, s);
+    int32_t *mapped = mapped_host_word(total_host);
+    rc = enqueue_scatter(*p, w, ra, topk_idx, nullptr, workspace, capacity_rows, m_indices,
+                         output_index, s, plan,
+                         ScanOuts{num_tokens_per_expert, num_tokens_per_rank, per_node,
+                                  expert_start_loc, mapped});
+    if (rc == EPL_OK && total_host && !mapped) {
+        if (hipMemcpyAsync(total_host, &at<WsHeader>(workspace, 0)->total, sizeof(int32_t),
+                           hipMemcpyDeviceToHost, s) != hipSuccess)
+            rc = EPL_EHIP;
+    }
     return rc;
 }
 

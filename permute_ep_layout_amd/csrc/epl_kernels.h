@@ -177,14 +177,16 @@ __host__ __device__ constexpr size_t layout_lds_bytes(int B, int K, int E, int R
 // of block b sent to rank c for c < R, to node c - R for R <= c < R + Rn,
 // a node being G consecutive ranks); block_err[b]; slot_rank[t*K+k] = rank
 // of slot (t,k) among the block's earlier slots of the same expert, or -1
-// for an invalid slot.
+// for an invalid slot. Block 0 also clears the status word, for the
+// kernels that only OR bits into it later in the chain.
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void ep_layout_kernel(
     const int64_t *__restrict__ topk, int64_t T, int K, int E, int R, int experts_per_rank,
     uint32_t epr_magic, int G, uint32_t node_magic, int Rn, int B, uint8_t *__restrict__ in_rank,
     bool in_rank_vec16,
     int32_t *__restrict__ block_count, int32_t *__restrict__ block_rank,
-    uint32_t *__restrict__ block_err, int32_t *__restrict__ slot_rank)
+    uint32_t *__restrict__ block_err, int32_t *__restrict__ slot_rank,
+    uint32_t *__restrict__ status)
 {
     constexpr int WAVES = THREADS / kWave;
     extern __shared__ int32_t lds[];
@@ -339,8 +341,11 @@ __global__ __launch_bounds__(THREADS) void ep_layout_kernel(
     for (int r = tid; r < RC; r += THREADS)
         block_rank[b * RC + r] = rank_cnt[r];
     lds_barrier();
-    if (tid == 0)
+    if (tid == 0) {
         block_err[b] = (uint32_t)*s_err;
+        if (b == 0)
+            *status = 0u;
+    }
 
     for (int s = tid; s < ns; s += THREADS) {
         const int packed = keys[kidx(s)];
@@ -351,7 +356,9 @@ __global__ __launch_bounds__(THREADS) void ep_layout_kernel(
 
 // ----------------------------------------------------------------- scan --
 
-// Inclusive prefix sum over the workgroup (kScanThreads threads).
+// Inclusive prefix sum over a workgroup of THREADS threads (s_wave holds
+// THREADS / 64 words).
+template <int THREADS = kScanThreads>
 __device__ __forceinline__ int block_inclusive_scan(int v, int *s_wave)
 {
     const int lane = lane_id();
@@ -365,7 +372,7 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int *s_wave)
         s_wave[wave] = v;
     lds_barrier();
     if (wave == 0) {
-        constexpr int nw = kScanThreads / kWave;
+        constexpr int nw = THREADS / kWave;
         int x = lane < nw ? s_wave[lane] : 0;
         for (int d = 1; d < nw; d <<= 1) {
             const int o = __shfl_up(x, d, kWave);
@@ -399,8 +406,9 @@ __device__ __forceinline__ int segment_sum(const int32_t *m, int ncols, int col,
 
 // Single workgroup. kScanReduce: column sums of block_count / block_rank
 // give num_tokens_per_expert / num_tokens_per_rank (and, for the Rn node
-// columns after the R rank columns, num_tokens_per_rdma_rank), block_count is replaced
-// by its exclusive prefix over blocks, and the status word is reset to the
+// columns after the R rank columns, num_tokens_per_rdma_rank), block_base
+// receives the exclusive prefix of block_count over blocks (block_count
+// itself stays as the layout wrote it), and the status word is reset to the
 // layout's error bits. kScanPrefix: exclusive prefix of the per-expert block
 // sizes (the counts, read from `cnt` unless kScanReduce produced them,
 // rounded up to a multiple of `alignment`) into expert_start_loc, total into
@@ -413,7 +421,8 @@ __device__ __forceinline__ int segment_sum(const int32_t *m, int ncols, int col,
 // per-column scan over the P segment sums gives each segment's offset, and
 // the thread then rewrites its segment as a running prefix.
 __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
-    int mode, int64_t nb, int E, int R, int Rn, int alignment, int32_t *__restrict__ block_count,
+    int mode, int64_t nb, int E, int R, int Rn, int alignment,
+    const int32_t *__restrict__ block_count, int32_t *__restrict__ block_base,
     const int32_t *__restrict__ block_rank, const uint32_t *__restrict__ block_err,
     int32_t *__restrict__ cnt, int32_t *__restrict__ per_rank, int32_t *__restrict__ per_node,
     int32_t *__restrict__ start,
@@ -502,7 +511,7 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
             }
         }
         lds_barrier();
-        // Rewrite block_count as the exclusive prefix over blocks.
+        // block_base = exclusive prefix of block_count over blocks.
         for (int col = tid; col < E * P; col += kScanThreads) {
             const int e = col % E, q = col / E;
             const int64_t b0 = q * L, b1 = min(nb, b0 + L);
@@ -511,7 +520,7 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     if (b0 + j < b1) {
-                        block_count[(b0 + j) * E + e] = run;
+                        block_base[(b0 + j) * E + e] = run;
                         run += seg[j];
                     }
                 }
@@ -525,7 +534,7 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     if (bb + j < b1) {
-                        block_count[(bb + j) * E + e] = run;
+                        block_base[(bb + j) * E + e] = run;
                         run += v[j];
                     }
                 }
@@ -568,7 +577,7 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
 // the slots need no per-block offsets, so the per-block count matrix and the
 // second launch that reduces it go away. The results are those of
 // ep_layout_kernel + ep_scan_kernel with a single block of all T tokens:
-// block_count (one row of E zeros), slot_rank = rank of slot (t, k) among
+// block_base (one row of E zeros), slot_rank = rank of slot (t, k) among
 // all earlier slots of its expert, per-expert / per-rank / per-node counts,
 // the token -> rank mask, the counts copy for the padding rows, the status
 // word, and, if `start` is not null, expert_start_loc and N (header, and the
@@ -595,7 +604,7 @@ __global__ __launch_bounds__(kFusedThreads) void ep_layout_scan_kernel(
     uint32_t epr_magic, int G, uint32_t node_magic, int Rn, int alignment,
     uint8_t *__restrict__ in_rank, bool in_rank_vec16, int32_t *__restrict__ cnt,
     int32_t *__restrict__ per_rank, int32_t *__restrict__ per_node, int32_t *__restrict__ start,
-    int32_t *__restrict__ block_count, int32_t *__restrict__ slot_rank,
+    int32_t *__restrict__ block_base, int32_t *__restrict__ slot_rank,
     int32_t *__restrict__ ws_counts, WsHeader *__restrict__ hdr, int32_t *__restrict__ total_out)
 {
     __shared__ int32_t wave_cnt[kFusedWaves][kFusedMaxExperts];
@@ -724,7 +733,7 @@ __global__ __launch_bounds__(kFusedThreads) void ep_layout_scan_kernel(
         if (cnt)
             cnt[tid] = run;
         ws_counts[tid] = run;
-        block_count[tid] = 0;
+        block_base[tid] = 0;
         blk = (run + alignment - 1) / alignment * alignment;
     }
     for (int r = tid; r < RC; r += kFusedThreads) {
@@ -764,6 +773,7 @@ __global__ __launch_bounds__(kFusedThreads) void ep_layout_scan_kernel(
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 // Workgroup counts of the row kernels. Combine: one workgroup per token (the
 // dispatcher starts a new workgroup as soon as one retires, which balances
@@ -869,7 +879,54 @@ constexpr int kScaleCols = 2;   // W words per row, column-major: word j of row 
 // sooner (the first part of a token also writes its indices and scale row).
 // SPLIT: the launch may cut rows into parts (parts > 1 only then; without
 // it every item is a whole token and the part arithmetic folds away).
-template <int VPT, bool SPLIT>
+//
+// OFFSETS: the scatter of a dispatch also does the scan's work, so the
+// chain needs no scan launch between layout and scatter (see ScanInScatter).
+// Every workgroup reads the layout's per-block counts (nb x E words, from
+// L2), sums each expert's column, scans the aligned sums into the expert
+// offsets and keeps in LDS the offsets and the per-block offsets of the
+// blocks its tokens fall in, so its slot lookups then read LDS instead of
+// global memory. Workgroup 0 also stores the scan's results (counts,
+// expert_start_loc, N, the per-block offsets for later scatter calls, the
+// layout's error bits into the status word, which the layout reset) and
+// workgroup 1 (or 0 in a one-workgroup grid) the per-rank and per-node
+// totals. Their values are those of ep_scan_kernel in reduce + prefix mode.
+// LDS words of the per-segment column sums (E / 4 expert quads x
+// kScatterThreads / (E / 4) segments, 4 words each).
+constexpr int kScanSegWords = 4 * kScatterThreads;
+
+struct ScanInScatter {
+    const int32_t *block_count;   // [nb, E] slots per layout block and expert
+    const int32_t *block_rank;    // [nb, R + Rn] tokens per block and rank / node
+    const uint32_t *block_err;    // [nb] error bits per block
+    int64_t nb;                   // layout blocks
+    int R, Rn;                    // rank columns, node columns
+    int nbl;                      // LDS rows of per-block offsets per workgroup
+    int32_t *cnt;                 // [E] num_tokens_per_expert (or null)
+    int32_t *per_rank;            // [R] (or null)
+    int32_t *per_node;            // [Rn] (or null)
+    int32_t *start;               // [E] expert_start_loc
+    int32_t *ws_counts;           // [E] the workspace's copy of the counts
+    int32_t *block_base;          // [nb, E] exclusive prefix of block_count over blocks
+    WsHeader *hdr;                // total
+    int32_t *total_out;           // host-mapped word for N (or null)
+};
+
+// Blocks of B tokens that the tokens of one grid-stride range touch: from
+// the first token's block to the last one's (b_hi < b_lo when it has none).
+__device__ __forceinline__ void range_blocks(const TokenRange &tr, int B, int64_t &b_lo,
+                                             int64_t &b_hi)
+{
+    b_lo = 0;
+    b_hi = -1;
+    if (tr.first < tr.end) {
+        const int64_t last = tr.first + (tr.end - 1 - tr.first) / tr.stride * tr.stride;
+        b_lo = tr.first / B;
+        b_hi = last / B;
+    }
+}
+
+template <int VPT, bool SPLIT, bool OFFSETS>
 __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
     const uint8_t *__restrict__ x, int64_t row_bytes, int scale_mode,
     const uint32_t *__restrict__ x_scale, int W, bool scale_vec16, int64_t scale_ld,
@@ -878,33 +935,15 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
     int K, int E, int B, int alignment, const int32_t *__restrict__ counts, int64_t capacity,
     int parts_arg, uint8_t *__restrict__ out, uint32_t *__restrict__ out_scale,
     int32_t *__restrict__ m_indices, int32_t *__restrict__ output_index,
-    uint32_t *__restrict__ status)
+    uint32_t *__restrict__ status, ScanInScatter sc)
 {
+    static_assert(!(SPLIT && OFFSETS), "the scan-in-scatter launch has whole-token items");
     __shared__ int64_t s_row[2][kMaxTopk];
+    extern __shared__ __align__(16) int32_t s_off[];   // OFFSETS only, see below
     const int tid = threadIdx.x;
     const int parts = SPLIT ? parts_arg : 1;
     const int nvec = (int)(row_bytes >> 4);
     const int pvec = SPLIT ? (nvec + parts - 1) / parts : nvec;   // 16-byte vectors per part
-
-    // Padding rows of the aligned blocks: between an expert's last row and
-    // the end of its block, marked -1 (workgroup w takes experts w, w + G, ...).
-    if (alignment > 1) {
-        for (int e = blockIdx.x; e < E; e += gridDim.x) {
-            const int64_t c = counts[e];
-            const int64_t p0 = (int64_t)start[e] + c;
-            const int64_t p1 = (int64_t)start[e] + (c + alignment - 1) / alignment * alignment;
-            for (int64_t p = p0 + tid; p < p1; p += kScatterThreads) {
-                if (p >= 0 && p < capacity)
-                    m_indices[p] = -1;
-                else
-                    atomicOr(status, kStatusCapacity);
-            }
-        }
-    }
-    // scale words prefetched with the row: 16-byte pieces (row-major, W % 4 == 0)
-    // or single words (column-major)
-    const int nq = scale_mode == kScaleRows && scale_vec16 ? (W >> 2) : 0;
-    const int nw = scale_mode == kScaleCols ? W : 0;
     // Work items: (token, column part) pairs, item i = token i / parts, part
     // i % parts (parts = 1 except for batches too small to fill the GPU).
     const TokenRange tr = token_range(T * parts);
@@ -934,6 +973,198 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
         }
     }
 
+    // OFFSETS LDS: [E] expert offsets, [E] counts, [kScanSegWords] segment
+    // sums, [nbl, E] per-block offsets of this workgroup's blocks
+    int32_t *s_start = s_off, *s_cnt = s_off + E, *s_seg = s_off + 2 * E;
+    int32_t *s_base = s_seg + kScanSegWords;
+    int64_t b_lo = 0, b_hi = -1;
+    u32x4 v[VPT];
+    if (OFFSETS) {
+        __shared__ int s_wave[kScatterThreads / kWave];
+        __shared__ int s_part[kScatterThreads];
+        range_blocks(tr, B, b_lo, b_hi);
+        b_hi = min(b_hi, b_lo + sc.nbl - 1);   // LDS rows held (the launch sizes nbl to cover the range)
+        const bool first_wg = blockIdx.x == 0;
+        // The count matrix in 16-byte pieces: thread (c, q) takes experts
+        // 4c .. 4c + 3 over the q-th segment of L blocks (the launch
+        // guarantees E % 4 == 0, E <= 4 * kScatterThreads and L <= 16), so
+        // all of a thread's loads are in flight at once and every workgroup
+        // waits for a single round trip.
+        const int nq4 = E >> 2;
+        const int Q = kScatterThreads / nq4;
+        const int64_t L = (sc.nb + Q - 1) / Q;
+        const int c = tid % nq4, q = tid / nq4;
+        const bool seg_thread = q < Q;
+        const int64_t sb0 = (int64_t)q * L, sb1 = min(sc.nb, sb0 + L);
+        const i32x4 *bc4 = reinterpret_cast<const i32x4 *>(sc.block_count);
+        i32x4 held[16];
+        i32x4 sum = {0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            held[j] = i32x4{0, 0, 0, 0};
+            if (seg_thread && sb0 + j < sb1)
+                held[j] = bc4[(sb0 + j) * nq4 + c];
+        }
+        // The first item's row loads go out now, behind the count loads, so
+        // that they travel while this prologue computes (the loop does not
+        // load them again).
+        if (tr.first < i_end) {
+            const u32x4 *xrow = reinterpret_cast<const u32x4 *>(x + tr.first * row_bytes);
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int idx = i * kScatterThreads + tid;
+                if (idx < nvec)
+                    v[i] = xrow[idx];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            sum += held[j];
+        if (seg_thread)
+            reinterpret_cast<i32x4 *>(s_seg)[q * nq4 + c] = sum;
+        lds_barrier();
+        // Segment offsets and column totals, then the running prefix over
+        // the held blocks: into LDS for this workgroup's blocks and, from
+        // workgroup 0, into the workspace for later scatter calls.
+        if (seg_thread) {
+            i32x4 run = {0, 0, 0, 0}, tot = {0, 0, 0, 0};
+            for (int g = 0; g < Q; ++g) {
+                const i32x4 v = reinterpret_cast<const i32x4 *>(s_seg)[g * nq4 + c];
+                if (g < q)
+                    run += v;
+                tot += v;
+            }
+            if (q == 0)
+                reinterpret_cast<i32x4 *>(s_cnt)[c] = tot;
+            i32x4 *bb4 = reinterpret_cast<i32x4 *>(sc.block_base);
+            i32x4 *sbase4 = reinterpret_cast<i32x4 *>(s_base);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int64_t b = sb0 + j;
+                if (b < sb1) {
+                    if (b >= b_lo && b <= b_hi)
+                        sbase4[(b - b_lo) * nq4 + c] = run;
+                    if (first_wg)
+                        bb4[b * nq4 + c] = run;
+                    run += held[j];
+                }
+            }
+        }
+        // Per-rank and per-node totals (workgroup 1, or 0 in a one-workgroup
+        // grid): thread (r, g) sums column r over the g-th of P block segments
+        // (16 loads in flight per pass), the P partial sums meet in LDS.
+        const bool rank_wg = blockIdx.x == min(1u, gridDim.x - 1);
+        const int RC = sc.R + sc.Rn;
+        const int P = RC < kScatterThreads ? kScatterThreads / RC : 1;
+        if (rank_wg) {
+            const int64_t PL = (sc.nb + P - 1) / P;
+            for (int i = tid; i < RC * P; i += kScatterThreads) {
+                const int r = i % RC, g = i / RC;
+                const int64_t g0 = (int64_t)g * PL, g1 = min(sc.nb, g0 + PL);
+                int part = 0;
+                for (int64_t bb = g0; bb < g1; bb += 16) {
+                    int v[16];
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        v[j] = bb + j < g1 ? sc.block_rank[(bb + j) * RC + r] : 0;
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        part += v[j];
+                }
+                if (P > 1)
+                    s_part[i] = part;
+                else if (r < sc.R) {
+                    if (sc.per_rank)
+                        sc.per_rank[r] = part;
+                } else if (sc.per_node) {
+                    sc.per_node[r - sc.R] = part;
+                }
+            }
+        }
+        lds_barrier();
+        if (rank_wg && P > 1) {
+            for (int r = tid; r < RC; r += kScatterThreads) {
+                int tot = 0;
+                for (int g = 0; g < P; ++g)
+                    tot += s_part[g * RC + r];
+                if (r < sc.R) {
+                    if (sc.per_rank)
+                        sc.per_rank[r] = tot;
+                } else if (sc.per_node) {
+                    sc.per_node[r - sc.R] = tot;
+                }
+            }
+        }
+        // Expert offsets: exclusive prefix of the block sizes (counts rounded
+        // up to the alignment); thread i owns experts [i * per, (i + 1) * per).
+        const int per = (E + kScatterThreads - 1) / kScatterThreads;
+        const int e_lo = min(E, tid * per), e_hi = min(E, e_lo + per);
+        auto block = [alignment](int n) { return (n + alignment - 1) / alignment * alignment; };
+        int own = 0;
+        for (int e = e_lo; e < e_hi; ++e)
+            own += block(s_cnt[e]);
+        const int incl = block_inclusive_scan<kScatterThreads>(own, s_wave);
+        int run = incl - own;
+        for (int e = e_lo; e < e_hi; ++e) {
+            s_start[e] = run;
+            if (first_wg) {
+                sc.start[e] = run;
+                sc.ws_counts[e] = s_cnt[e];
+                if (sc.cnt)
+                    sc.cnt[e] = s_cnt[e];
+            }
+            run += block(s_cnt[e]);
+        }
+        if (first_wg && tid == kScatterThreads - 1) {
+            sc.hdr->total = incl;
+            if (sc.total_out)
+                *sc.total_out = incl;
+        }
+        if (first_wg) {
+            uint32_t err = 0;
+            for (int64_t bb = tid; bb < sc.nb; bb += kScatterThreads)
+                err |= sc.block_err[bb];
+            if (err)
+                atomicOr(status, kStatusBadExpert);
+        }
+        lds_barrier();
+    }
+    auto expert_start = [&](int64_t e) { return OFFSETS ? s_start[e] : start[e]; };
+    auto expert_count = [&](int64_t e) { return OFFSETS ? s_cnt[e] : counts[e]; };
+    auto block_offset = [&](int64_t t, int64_t e) {
+        if (!OFFSETS)
+            return block_base[(t / B) * E + e];
+        const int64_t b = t / B;
+        if (b >= b_lo && b <= b_hi)
+            return s_base[(b - b_lo) * E + e];
+        // not reached when nbl covers the range (the launch sizes it so);
+        // kept so that a block outside it still gets its exact offset
+        int run = 0;
+        for (int64_t bb = 0; bb < b; ++bb)
+            run += sc.block_count[bb * E + e];
+        return run;
+    };
+
+    // Padding rows of the aligned blocks: between an expert's last row and
+    // the end of its block, marked -1 (workgroup w takes experts w, w + G, ...).
+    if (alignment > 1) {
+        for (int e = blockIdx.x; e < E; e += gridDim.x) {
+            const int64_t c = expert_count(e);
+            const int64_t p0 = (int64_t)expert_start(e) + c;
+            const int64_t p1 = (int64_t)expert_start(e) + (c + alignment - 1) / alignment * alignment;
+            for (int64_t p = p0 + tid; p < p1; p += kScatterThreads) {
+                if (p >= 0 && p < capacity)
+                    m_indices[p] = -1;
+                else
+                    atomicOr(status, kStatusCapacity);
+            }
+        }
+    }
+    // scale words prefetched with the row: 16-byte pieces (row-major, W % 4 == 0)
+    // or single words (column-major)
+    const int nq = scale_mode == kScaleRows && scale_vec16 ? (W >> 2) : 0;
+    const int nw = scale_mode == kScaleCols ? W : 0;
+
     int it = 0;
     for (int64_t item = tr.first; item < i_end; item += step, ++it) {
         const int64_t t = token_of(item);
@@ -942,12 +1173,13 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
         const bool first_part = q == 0;   // writes the indices and the scale row
         int64_t *rows = s_row[it & 1];
         const u32x4 *xrow = reinterpret_cast<const u32x4 *>(x + t * row_bytes);
-        u32x4 v[VPT];
+        if (!OFFSETS || it > 0) {
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int idx = v0 + i * kScatterThreads + tid;
-            if (idx < v1)
-                v[i] = xrow[idx];
+            for (int i = 0; i < VPT; ++i) {
+                const int idx = v0 + i * kScatterThreads + tid;
+                if (idx < v1)
+                    v[i] = xrow[idx];
+            }
         }
         u32x4 sv = {0u, 0u, 0u, 0u};
         uint32_t sw = 0u;
@@ -957,8 +1189,8 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
             sw = x_scale[t * W + tid];
 
         if (lead && it == 0 && valid(e0)) {
-            s0 = start[e0];
-            b0 = block_base[(t / B) * E + e0];
+            s0 = expert_start(e0);
+            b0 = block_offset(t, e0);
         }
         if (lead) {
             int pos = -1;
@@ -985,8 +1217,8 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
             s0 = 0;
             b0 = 0;
             if (item + step < i_end && valid(e0)) {
-                s0 = start[e0];
-                b0 = block_base[(token_of(item + step) / B) * E + e0];
+                s0 = expert_start(e0);
+                b0 = block_offset(token_of(item + step), e0);
             }
             e1 = -1;
             if (item + 2 * step < i_end) {

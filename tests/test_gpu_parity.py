@@ -837,3 +837,109 @@ def test_random_fp8_sweep(seed):
                            scale_format="f32" if fmt == epl.EPL_SCALE_F32 else "ue8m0",
                            ranks_per_node=0)
     fp8_parity(w, fmt, alignment=a, extra_cap=extra, split=split)
+
+
+# ------------------------------------ dispatch without a scan launch --
+
+# Dispatches of several layout blocks whose per-block count matrix is small
+# (at most 16384 words) and whose scatter runs a striding grid of at most
+# 1024 workgroups do the scan inside the scatter: every scatter workgroup
+# reduces the per-block counts itself. (T, K, E, R, H): 1500 tokens of
+# 128-byte rows take the XCD-aware grid of 1024 workgroups; 1001 tokens take
+# a grid of 1001, whose token ranges span every layout block.
+NO_SCAN = [("xcd_grid", 1500, 4, 32, 8, 64), ("plain_grid", 1001, 4, 32, 8, 64),
+           ("dsv3_like", 4096, 8, 256, 32, 128)]
+
+
+@pytest.mark.parametrize("case", NO_SCAN, ids=[c[0] for c in NO_SCAN])
+def test_scan_in_scatter_flags_bad_ids_then_resets(case):
+    """Out-of-range ids set EPL_ERANGE (the bits come from the layout blocks
+    through the scatter) and the next dispatch over clean ids on the same
+    workspace clears it again."""
+    name, T, K, E, R, H = case
+    print(f"[parity] scan-in-scatter bad ids case={name}", flush=True)
+    rng = np.random.default_rng(31)
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    topk[rng.random(topk.shape) < 0.05] = -1
+    bad = topk.copy()
+    bad[3, 1] = E
+    bad[T - 2, 0] = 1 << 40
+    bad[T // 2, K - 1] = -5
+    x, xs, wt = _mk(topk, H, scales=H % 128 == 0)
+    clean = np.where((bad < -1) | (bad >= E), -1, bad)
+    ref = orc().run_all(x, xs, clean, wt, E, R)
+    r = gpu_dispatch(bad, x, xs, E, R)
+    assert epl.epl_status(r["ws"]) == epl.EPL_ERANGE
+    check_layout_and_scatter(r, ref, x, xs)
+    tk = torch.from_numpy(clean).to(DEV)
+    epl.epl_dispatch(r["p"], tk, r["x"], None if xs is None else torch.from_numpy(xs).to(DEV),
+                     r["cap"], r["cnt"], r["per_rank"], r["per_node"], r["in_rank"], r["start"],
+                     r["total_host"], r["out"], r["out_scale"], r["m"], r["oi"], r["ws"])
+    assert epl.epl_status(r["ws"]) == epl.EPL_OK
+    check_layout_and_scatter(r, ref, x, xs)
+
+
+@pytest.mark.parametrize("alignment", [0, 16])
+@pytest.mark.parametrize("case", NO_SCAN[:2], ids=[c[0] for c in NO_SCAN[:2]])
+def test_scan_in_scatter_capacity_overflow(case, alignment):
+    """Rows (and alignment padding rows) past a short buffer are skipped and
+    flagged, unplaced slots get output_index -1, nothing is written past the
+    buffer, and N still reaches the host."""
+    name, T, K, E, R, H = case
+    print(f"[parity] scan-in-scatter overflow case={name} a={alignment}", flush=True)
+    rng = np.random.default_rng(32)
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    x, _, wt = _mk(topk, H)
+    ref = orc().run_all(x, None, topk, wt, E, R, alignment=alignment)
+    N = ref["total"]
+    cap, guard = N - 37, 64
+    p = epl.Problem.make(T, K, E, R, H, 0, alignment)
+    ws = poisoned(epl.epl_workspace_bytes(p), torch.uint8)
+    out_full = poisoned((cap + guard, H), torch.bfloat16)
+    m_full = poisoned(cap + guard, torch.int32)
+    out, m = out_full[:cap], m_full[:cap]
+    cnt, per_rank = poisoned(E, torch.int32), poisoned(R, torch.int32)
+    in_rank, start = poisoned((T, R), torch.uint8), poisoned(E, torch.int32)
+    oi = poisoned((T, K), torch.int32)
+    total_host = torch.full((1,), -7, dtype=torch.int32).pin_memory()
+    epl.epl_dispatch(p, torch.from_numpy(topk).to(DEV), to_bf16(x), None, cap, cnt, per_rank,
+                     None, in_rank, start, total_host, out, None, m, oi, ws)
+    assert epl.epl_status(ws) == epl.EPL_ECAPACITY
+    assert int(total_host[0]) == N and epl.epl_total(ws) == N
+    np.testing.assert_array_equal(start.cpu().numpy(), ref["expert_start_loc"])
+    np.testing.assert_array_equal(cnt.cpu().numpy(), ref["num_tokens_per_expert"])
+    want_oi = np.where(ref["output_index"] >= cap, -1, ref["output_index"])
+    np.testing.assert_array_equal(oi.cpu().numpy(), want_oi)
+    np.testing.assert_array_equal(m.cpu().numpy(), ref["m_indices"][:cap])
+    real = ref["m_indices"][:cap] >= 0
+    np.testing.assert_array_equal(u16(out)[real], ref["out"][:cap][real])
+    assert (out_full[cap:].view(torch.uint8) == POISON).all()
+    assert (m_full[cap:].view(torch.uint8) == POISON).all()
+
+
+@pytest.mark.parametrize("alignment", [0, 32])
+@pytest.mark.parametrize("case", NO_SCAN, ids=[c[0] for c in NO_SCAN])
+def test_scatter_after_dispatch_reuses_its_workspace(case, alignment):
+    """A dispatch that ran no scan launch leaves the workspace as layout +
+    scan would: a later epl_scatter of another payload with the same
+    routing, workspace and expert_start_loc places it exactly as the oracle
+    does."""
+    name, T, K, E, R, H = case
+    print(f"[parity] scatter after dispatch case={name} a={alignment}", flush=True)
+    rng = np.random.default_rng(33)
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    topk[rng.random(topk.shape) < 0.05] = -1
+    x, xs, wt = _mk(topk, H, seed=1, scales=H % 128 == 0)
+    x2, xs2, _ = _mk(topk, H, seed=2, scales=H % 128 == 0)
+    r = gpu_dispatch(topk, x, xs, E, R, alignment=alignment)
+    assert epl.epl_status(r["ws"]) == epl.EPL_OK
+    ref2 = orc().run_all(x2, xs2, topk, wt, E, R, alignment=alignment)
+    cap = r["cap"]
+    out2 = poisoned((cap, H), torch.bfloat16)
+    os2 = poisoned((cap, xs2.shape[1]), torch.float32) if xs2 is not None else None
+    m2, oi2 = poisoned(cap, torch.int32), poisoned((T, K), torch.int32)
+    epl.epl_scatter(r["p"], to_bf16(x2), None if xs2 is None else torch.from_numpy(xs2).to(DEV),
+                    r["topk"], r["start"], r["ws"], cap, out2, os2, m2, oi2)
+    assert epl.epl_status(r["ws"]) == epl.EPL_OK
+    r2 = dict(r, out=out2, out_scale=os2, m=m2, oi=oi2)
+    check_layout_and_scatter(r2, ref2, x2, xs2)
