@@ -195,11 +195,11 @@ int epl_scatter(const epl_problem *p, const uint16_t *x, const float *x_scale,
 
 /* Steps 1-3 in one call, all on `stream`, with no host wait between them:
  * layout, scan (the total is copied to *total_host if it is not NULL) and
- * scatter, with the arguments and results described above. Batches of a few
- * thousand tokens run the scan inside the scatter launch (every scatter
- * workgroup reduces the layout's per-block counts itself); the results, and
- * the workspace left for later epl_scatter / epl_scatter_fp8 calls, are the
- * same. */
+ * scatter, with the arguments and results described above. Decode-sized
+ * batches (at most 2048 (token, k) slots) run all three steps in one launch,
+ * and batches of a few thousand tokens run the scan inside the scatter
+ * launch; the results, and the workspace left for later epl_scatter /
+ * epl_scatter_fp8 calls, are the same. */
 int epl_dispatch(const epl_problem *p, const int64_t *topk_idx,
                  const uint16_t *x, const float *x_scale, int64_t capacity_rows,
                  int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,

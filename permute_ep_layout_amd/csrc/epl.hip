@@ -254,6 +254,40 @@ int32_t *mapped_host_word(int32_t *host)
     return static_cast<int32_t *>(dev);
 }
 
+// Arguments of the one-workgroup layout + scan; `capacity` >= 0 also
+// flags N > capacity in the status word.
+epl::LayoutScanArgs layout_scan_args(const epl_problem &p, const WsLayout &w, const int64_t *topk,
+                                     uint8_t *in_rank, int32_t *cnt, int32_t *per_rank,
+                                     int32_t *per_node, int32_t *start, void *ws,
+                                     int32_t *total_mapped, int64_t capacity)
+{
+    epl::LayoutScanArgs a{};
+    a.topk = topk;
+    a.T = p.num_tokens;
+    a.K = p.num_topk;
+    a.E = p.num_experts;
+    a.R = p.num_ranks;
+    a.experts_per_rank = p.num_experts / p.num_ranks;
+    a.epr_magic = epl::div_magic(p.num_experts / p.num_ranks);
+    a.G = p.ranks_per_node;
+    a.node_magic = epl::div_magic(std::max(p.ranks_per_node, 1));
+    a.Rn = nodes_of(p);
+    a.alignment = alignment_of(p);
+    a.in_rank = in_rank;
+    a.in_rank_vec16 = (p.num_ranks % 16 == 0) && aligned(in_rank, 16);
+    a.cnt = cnt;
+    a.per_rank = per_rank;
+    a.per_node = per_node;
+    a.start = start;
+    a.block_base = at<int32_t>(ws, w.block_base);
+    a.slot_rank = at<int32_t>(ws, w.slot_rank);
+    a.ws_counts = at<int32_t>(ws, w.counts);
+    a.hdr = at<WsHeader>(ws, 0);
+    a.total_out = total_mapped;
+    a.capacity = capacity;
+    return a;
+}
+
 // Layout and scan of a small batch in one launch (fused_layout(p)). With
 // `start` null only the layout's outputs are produced (epl_layout); with it,
 // also expert_start_loc and N, copied to *total_host if that is not null.
@@ -261,15 +295,10 @@ int enqueue_fused(const epl_problem &p, const WsLayout &w, const int64_t *topk, 
                   int32_t *cnt, int32_t *per_rank, int32_t *per_node, int32_t *start,
                   int32_t *total_host, void *ws, hipStream_t s)
 {
-    const bool vec16 = (p.num_ranks % 16 == 0) && aligned(in_rank, 16);
     int32_t *mapped = start ? mapped_host_word(total_host) : nullptr;
-    hipLaunchKernelGGL(epl::ep_layout_scan_kernel, dim3(1), dim3(epl::kFusedThreads), 0, s, topk,
-                       p.num_tokens, p.num_topk, p.num_experts, p.num_ranks,
-                       p.num_experts / p.num_ranks, epl::div_magic(p.num_experts / p.num_ranks),
-                       p.ranks_per_node, epl::div_magic(std::max(p.ranks_per_node, 1)), nodes_of(p),
-                       alignment_of(p), in_rank, vec16, cnt, per_rank, per_node, start,
-                       at<int32_t>(ws, w.block_base), at<int32_t>(ws, w.slot_rank),
-                       at<int32_t>(ws, w.counts), at<WsHeader>(ws, 0), mapped);
+    hipLaunchKernelGGL(epl::ep_layout_scan_kernel, dim3(1), dim3(epl::kFusedThreads), 0, s,
+                       layout_scan_args(p, w, topk, in_rank, cnt, per_rank, per_node, start, ws,
+                                        mapped, -1));
     int rc = launch_status();
     if (rc != EPL_OK)
         return rc;
@@ -496,6 +525,48 @@ RowArgs fp8_rows(const epl_problem &p, const uint8_t *x, const void *xs, int sca
         ra.words = (p.scale_cols + 3) / 4;
     }
     return ra;
+}
+
+// Decode-sized dispatches (fused_layout) in one launch: workgroup 0 lays
+// out and scans, workgroups 1 .. T place and copy one token each
+// (epl::ep_dispatch_decode_kernel). 0 turns it off (layout + scan launch,
+// then the scatter launch).
+#ifndef EPL_DECODE_DISPATCH
+#define EPL_DECODE_DISPATCH 1
+#endif
+
+int enqueue_decode_dispatch(const epl_problem &p, const WsLayout &w, const RowArgs &ra,
+                            const int64_t *topk, int64_t cap, uint8_t *in_rank, int32_t *cnt,
+                            int32_t *per_rank, int32_t *per_node, int32_t *start,
+                            int32_t *total_host, int32_t *m_idx, int32_t *oi, void *ws,
+                            hipStream_t s)
+{
+    int32_t *mapped = mapped_host_word(total_host);
+    const epl::LayoutScanArgs a =
+        layout_scan_args(p, w, topk, in_rank, cnt, per_rank, per_node, start, ws, mapped, cap);
+    epl::DecodeRows d{};
+    d.x = ra.x;
+    d.row_bytes = ra.row_bytes;
+    d.scale_mode = ra.scale_mode;
+    d.x_scale = ra.x_scale;
+    d.W = ra.words;
+    d.scale_vec16 = ra.scale_mode == epl::kScaleRows && ra.words % 4 == 0 &&
+                    aligned(ra.x_scale, 16) && aligned(ra.out_scale, 16);
+    d.scale_ld = ra.scale_ld;
+    d.capacity = cap;
+    d.out = ra.out;
+    d.out_scale = ra.out_scale;
+    d.m_indices = m_idx;
+    d.output_index = oi;
+    hipLaunchKernelGGL(epl::ep_dispatch_decode_kernel, dim3((unsigned)(p.num_tokens + 1)),
+                       dim3(epl::kFusedThreads), 0, s, a, d);
+    int rc = launch_status();
+    if (rc == EPL_OK && total_host && !mapped) {
+        if (hipMemcpyAsync(total_host, &at<WsHeader>(ws, 0)->total, sizeof(int32_t),
+                           hipMemcpyDeviceToHost, s) != hipSuccess)
+            rc = EPL_EHIP;
+    }
+    return rc;
 }
 
 // Pointer checks shared by the scatter entry points.
@@ -733,6 +804,11 @@ static int dispatch_rows(const epl_problem *p, const int64_t *topk_idx, const Ro
     const WsLayout w = ws_layout(*p);
     hipStream_t s = static_cast<hipStream_t>(stream);
     int32_t *per_node = nodes_of(*p) ? num_tokens_per_rdma_rank : nullptr;
+    if (EPL_DECODE_DISPATCH && fused_layout(*p))
+        return enqueue_decode_dispatch(*p, w, ra, topk_idx, capacity_rows, is_token_in_rank,
+                                       num_tokens_per_expert, num_tokens_per_rank, per_node,
+                                       expert_start_loc, total_host, m_indices, output_index,
+                                       workspace, s);
     const ScanPlan plan = scan_in_scatter(*p, w, scatter_split(*p, ra.row_bytes));
     int rc;
     if (fused_layout(*p)) {

@@ -599,14 +599,44 @@ constexpr int kFusedMaxExperts = 256;
 constexpr int kFusedMaxCols = 256;
 static_assert(kFusedThreads == kScanThreads, "the fused kernel reuses the scan's block scan");
 
-__global__ __launch_bounds__(kFusedThreads) void ep_layout_scan_kernel(
-    const int64_t *__restrict__ topk, int64_t T, int K, int E, int R, int experts_per_rank,
-    uint32_t epr_magic, int G, uint32_t node_magic, int Rn, int alignment,
-    uint8_t *__restrict__ in_rank, bool in_rank_vec16, int32_t *__restrict__ cnt,
-    int32_t *__restrict__ per_rank, int32_t *__restrict__ per_node, int32_t *__restrict__ start,
-    int32_t *__restrict__ block_base, int32_t *__restrict__ slot_rank,
-    int32_t *__restrict__ ws_counts, WsHeader *__restrict__ hdr, int32_t *__restrict__ total_out)
+// Arguments of the one-workgroup layout + scan.
+struct LayoutScanArgs {
+    const int64_t *topk;
+    int64_t T;
+    int K, E, R, experts_per_rank;
+    uint32_t epr_magic;
+    int G;
+    uint32_t node_magic;
+    int Rn, alignment;
+    uint8_t *in_rank;
+    bool in_rank_vec16;
+    int32_t *cnt, *per_rank, *per_node, *start, *block_base, *slot_rank, *ws_counts;
+    WsHeader *hdr;
+    int32_t *total_out;
+    int64_t capacity;   // < 0: none; else N > capacity also sets the capacity bit
+};
+
+// The whole layout + scan by one workgroup of kFusedThreads threads (the
+// body of ep_layout_scan_kernel, also run by workgroup 0 of
+// ep_dispatch_decode_kernel).
+__device__ __forceinline__ void layout_scan_block(const LayoutScanArgs &a)
 {
+    const int64_t *__restrict__ topk = a.topk;
+    const int64_t T = a.T;
+    const int K = a.K, E = a.E, R = a.R, experts_per_rank = a.experts_per_rank;
+    const uint32_t epr_magic = a.epr_magic, node_magic = a.node_magic;
+    const int G = a.G, Rn = a.Rn, alignment = a.alignment;
+    uint8_t *__restrict__ in_rank = a.in_rank;
+    const bool in_rank_vec16 = a.in_rank_vec16;
+    int32_t *__restrict__ cnt = a.cnt;
+    int32_t *__restrict__ per_rank = a.per_rank;
+    int32_t *__restrict__ per_node = a.per_node;
+    int32_t *__restrict__ start = a.start;
+    int32_t *__restrict__ block_base = a.block_base;
+    int32_t *__restrict__ slot_rank = a.slot_rank;
+    int32_t *__restrict__ ws_counts = a.ws_counts;
+    WsHeader *__restrict__ hdr = a.hdr;
+    int32_t *__restrict__ total_out = a.total_out;
     __shared__ int32_t wave_cnt[kFusedWaves][kFusedMaxExperts];
     __shared__ uint32_t chunk_cnt[kFusedWaves][kFusedMaxExperts / 4];
     __shared__ int32_t rank_cnt[kFusedMaxCols];
@@ -744,8 +774,6 @@ __global__ __launch_bounds__(kFusedThreads) void ep_layout_scan_kernel(
             per_node[r - R] = rank_cnt[r];
         }
     }
-    if (tid == 0)
-        hdr->status = s_err ? kStatusBadExpert : 0u;
     // expert_start_loc and N (the block scan has its own barriers, which
     // also order the wave_cnt rewrite above before the slot ranks below)
     const int incl = block_inclusive_scan(blk, s_wave);
@@ -758,6 +786,9 @@ __global__ __launch_bounds__(kFusedThreads) void ep_layout_scan_kernel(
                 *total_out = incl;
         }
     }
+    if (tid == kFusedThreads - 1)
+        hdr->status = (s_err ? kStatusBadExpert : 0u) |
+                      (a.capacity >= 0 && incl > a.capacity ? kStatusCapacity : 0u);
 
     // Global rank of every slot.
 #pragma unroll
@@ -766,6 +797,11 @@ __global__ __launch_bounds__(kFusedThreads) void ep_layout_scan_kernel(
         if (i < cpw && s < ns)
             slot_rank[s] = key[i] >= 0 ? lrank[i] + wave_cnt[wave][key[i]] : -1;
     }
+}
+
+__global__ __launch_bounds__(kFusedThreads) void ep_layout_scan_kernel(LayoutScanArgs a)
+{
+    layout_scan_block(a);
 }
 
 // -------------------------------------------------------------- scatter --
@@ -1288,6 +1324,309 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
                         store_scale(out_scale + (int64_t)j * scale_ld + row, f);
                 }
             }
+        }
+    }
+}
+
+// ------------------------------------------------ decode-sized dispatch --
+
+// Rows and outputs of ep_dispatch_decode_kernel (as in ep_scatter_kernel).
+struct DecodeRows {
+    const uint8_t *x;
+    int64_t row_bytes;
+    int scale_mode;
+    const uint32_t *x_scale;
+    int W;
+    bool scale_vec16;
+    int64_t scale_ld;
+    int64_t capacity;
+    uint8_t *out;
+    uint32_t *out_scale;
+    int32_t *m_indices;
+    int32_t *output_index;
+};
+
+// The counts side of a decode-sized dispatch, by one workgroup of
+// kFusedThreads threads: per-expert counts (and the workspace's copy), the
+// zero per-block offsets of the single layout block, expert_start_loc and
+// N, tokens per rank and per node, and the status word (out-of-range ids;
+// N > capacity, which is exactly when a slot row or a padding row would
+// fall outside the buffer). The token -> rank mask and the per-slot ranks
+// come from the token workgroups of ep_dispatch_decode_kernel.
+__device__ __forceinline__ void decode_counts_block(const LayoutScanArgs &a)
+{
+    __shared__ int32_t s_hist[kFusedMaxExperts];
+    __shared__ int32_t s_rc[kFusedMaxCols];
+    __shared__ int s_wave[kFusedWaves];
+    __shared__ uint32_t s_err;
+    const int tid = threadIdx.x;
+    const int K = a.K, E = a.E, R = a.R, Rn = a.Rn;
+    const int RC = R + Rn;
+    const int ns = (int)(a.T * K);
+    int64_t e_in[kFusedMaxSlots / kFusedThreads];
+#pragma unroll
+    for (int i = 0; i < kFusedMaxSlots / kFusedThreads; ++i) {
+        const int sl = i * kFusedThreads + tid;
+        e_in[i] = sl < ns ? a.topk[sl] : -1;
+    }
+    for (int e = tid; e < E; e += kFusedThreads)
+        s_hist[e] = 0;
+    for (int r = tid; r < RC; r += kFusedThreads)
+        s_rc[r] = 0;
+    if (tid == 0)
+        s_err = 0u;
+    lds_barrier();
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < kFusedMaxSlots / kFusedThreads; ++i) {
+        const int64_t e = e_in[i];
+        bad |= (e < -1 || e >= E);
+        if (e >= 0 && e < E)
+            atomicAdd(&s_hist[e], 1);
+    }
+    if (bad)
+        atomicOr(&s_err, 1u);
+    // Tokens per rank and per node: one thread per token, a token counted
+    // once per rank (node) that any of its valid slots goes to.
+    for (int64_t t = tid; t < a.T; t += kFusedThreads) {
+        const int64_t *row = a.topk + t * K;
+        for (int w0 = 0; w0 < R; w0 += 64) {
+            const int wr = min(64, R - w0);
+            uint64_t mask = 0;
+            for (int k = 0; k < K; ++k) {
+                const int64_t e = row[k];
+                if (e >= 0 && e < E) {
+                    const int r = div_small((uint32_t)e, a.experts_per_rank, a.epr_magic) - w0;
+                    if (r >= 0 && r < wr)
+                        mask |= 1ull << r;
+                }
+            }
+            for (uint64_t m = mask; m; m &= m - 1)
+                atomicAdd(&s_rc[w0 + __builtin_ctzll(m)], 1);
+        }
+        for (int n0 = 0; n0 < Rn; n0 += 64) {
+            const int wn = min(64, Rn - n0);
+            uint64_t mask = 0;
+            for (int k = 0; k < K; ++k) {
+                const int64_t e = row[k];
+                if (e >= 0 && e < E) {
+                    const int r = div_small((uint32_t)e, a.experts_per_rank, a.epr_magic);
+                    const int n = div_small((uint32_t)r, a.G, a.node_magic) - n0;
+                    if (n >= 0 && n < wn)
+                        mask |= 1ull << n;
+                }
+            }
+            for (uint64_t m = mask; m; m &= m - 1)
+                atomicAdd(&s_rc[R + n0 + __builtin_ctzll(m)], 1);
+        }
+    }
+    lds_barrier();
+    int blk = 0;
+    if (tid < E) {
+        const int c = s_hist[tid];
+        if (a.cnt)
+            a.cnt[tid] = c;
+        a.ws_counts[tid] = c;
+        a.block_base[tid] = 0;
+        blk = (c + a.alignment - 1) / a.alignment * a.alignment;
+    }
+    for (int r = tid; r < RC; r += kFusedThreads) {
+        if (r < R) {
+            if (a.per_rank)
+                a.per_rank[r] = s_rc[r];
+        } else if (a.per_node) {
+            a.per_node[r - R] = s_rc[r];
+        }
+    }
+    const int incl = block_inclusive_scan(blk, s_wave);
+    if (tid < E)
+        a.start[tid] = incl - blk;
+    if (tid == kFusedThreads - 1) {
+        a.hdr->total = incl;
+        if (a.total_out)
+            *a.total_out = incl;
+        a.hdr->status = (s_err ? kStatusBadExpert : 0u) | (incl > a.capacity ? kStatusCapacity : 0u);
+    }
+}
+
+// Layout, scan and scatter of a decode-sized batch (the batches that
+// ep_layout_scan_kernel lays out alone) in one launch of T + 1 workgroups.
+// Workgroup 0 produces the counts side (decode_counts_block). Workgroup
+// 1 + t places and copies token t without waiting for it: with its row
+// loads in flight it takes, for each slot (t, k) of expert e, the number of
+// valid slots of experts below e and of earlier slots of expert e (wave
+// ballots over all slots; with an expert alignment, the histogram of all
+// slots and its aligned prefix instead of the first number). Their sum is
+// the slot's row -- the same row as expert_start_loc[e] + the slot's rank
+// in (token, k) order -- and the second number is its rank, stored for
+// later scatter calls on the workspace. It also stores the token's row of
+// the token -> rank mask. Padding rows of expert e are marked by the
+// workgroup of token e mod T. Rows at or past the capacity are skipped (the
+// status bit comes from workgroup 0).
+__global__ __launch_bounds__(kFusedThreads) void ep_dispatch_decode_kernel(LayoutScanArgs a,
+                                                                           DecodeRows d)
+{
+    if (blockIdx.x == 0) {
+        decode_counts_block(a);
+        return;
+    }
+    constexpr int kSlotsPerThread = kFusedMaxSlots / kFusedThreads;
+    __shared__ int32_t s_tok[kMaxTopk];                  // the token's expert ids (-1: none)
+    __shared__ int32_t s_less[kMaxTopk][kFusedWaves];    // per wave: valid slots of lower experts
+    __shared__ int32_t s_same[kMaxTopk][kFusedWaves];    // per wave: earlier slots of the expert
+    __shared__ int32_t s_hist[kFusedMaxExperts];         // aligned batches: slots per expert
+    __shared__ int32_t s_start[kFusedMaxExperts];        // aligned batches: expert offsets
+    __shared__ int64_t s_rows[kMaxTopk];
+    __shared__ int s_wave[kFusedWaves];
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int64_t t = blockIdx.x - 1;
+    const int K = a.K, E = a.E, alignment = a.alignment;
+    const int ns = (int)(a.T * K);
+    const int nvec = (int)(d.row_bytes >> 4);
+    const bool aligned_blocks = alignment > 1;
+
+    // The token's first pass of its row and its scale words go out first,
+    // with the routing of every slot.
+    const u32x4 *xrow = reinterpret_cast<const u32x4 *>(d.x + t * d.row_bytes);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (tid < nvec)
+        v = xrow[tid];
+    const int nq = d.scale_mode == kScaleRows && d.scale_vec16 ? (d.W >> 2) : 0;
+    const int nw = nq == 0 && d.scale_mode != kScaleNone ? d.W : 0;
+    u32x4 sv = {0u, 0u, 0u, 0u};
+    uint32_t sw = 0u;
+    if (tid < nq)
+        sv = reinterpret_cast<const u32x4 *>(d.x_scale + t * d.W)[tid];
+    if (tid < nw)
+        sw = d.x_scale[t * d.W + tid];
+    int my_key[kSlotsPerThread];
+#pragma unroll
+    for (int i = 0; i < kSlotsPerThread; ++i) {
+        const int sl = i * kFusedThreads + tid;
+        const int64_t e = sl < ns ? a.topk[sl] : -1;
+        my_key[i] = (e >= 0 && e < E) ? (int)e : -1;
+    }
+    if (tid < K) {
+        const int64_t e = a.topk[t * K + tid];
+        s_tok[tid] = (e >= 0 && e < E) ? (int)e : -1;
+    }
+    if (aligned_blocks) {
+        for (int e = tid; e < E; e += kFusedThreads)
+            s_hist[e] = 0;
+    }
+    lds_barrier();
+    if (aligned_blocks) {
+#pragma unroll
+        for (int i = 0; i < kSlotsPerThread; ++i)
+            if (my_key[i] >= 0)
+                atomicAdd(&s_hist[my_key[i]], 1);
+    }
+    // The token's row of the token -> rank mask.
+    for (int r = tid; r < a.R; r += kFusedThreads) {
+        uint8_t hit = 0;
+        for (int k = 0; k < K; ++k) {
+            const int e = s_tok[k];
+            if (e >= 0 && div_small((uint32_t)e, a.experts_per_rank, a.epr_magic) == r)
+                hit = 1;
+        }
+        a.in_rank[t * a.R + r] = hit;
+    }
+    for (int k = 0; k < K; ++k) {
+        const int sk = (int)t * K + k;
+        const int ek = s_tok[k];
+        int less = 0, same = 0;
+#pragma unroll
+        for (int i = 0; i < kSlotsPerThread; ++i) {
+            const int sl = i * kFusedThreads + tid;
+            const int mk = my_key[i];
+            if (!aligned_blocks)
+                less += __popcll(wave_ballot(mk >= 0 && mk < ek));
+            same += __popcll(wave_ballot(ek >= 0 && mk == ek && sl < sk));
+        }
+        if (lane == 0) {
+            s_less[k][tid / kWave] = less;
+            s_same[k][tid / kWave] = same;
+        }
+    }
+    if (aligned_blocks) {
+        // expert offsets: exclusive prefix of the aligned counts
+        lds_barrier();
+        const int blk = tid < E ? (s_hist[tid] + alignment - 1) / alignment * alignment : 0;
+        const int incl = block_inclusive_scan(blk, s_wave);
+        if (tid < E)
+            s_start[tid] = incl - blk;
+    }
+    lds_barrier();
+    // Slot k's row: its two counts summed over the 16 waves (a serial sum
+    // by thread k measured faster than a shuffle reduction over 16 lanes).
+    if (tid < K) {
+        int less = 0, rank = 0;
+        for (int w = 0; w < kFusedWaves; ++w) {
+            less += s_less[tid][w];
+            rank += s_same[tid][w];
+        }
+        const int e = s_tok[tid];
+        int64_t row = -1;
+        if (e >= 0) {
+            const int64_t p = (aligned_blocks ? (int64_t)s_start[e] : (int64_t)less) + rank;
+            if (p < d.capacity) {
+                row = p;
+                d.m_indices[p] = e;
+            }
+        }
+        a.slot_rank[t * K + tid] = e >= 0 ? rank : -1;
+        d.output_index[t * K + tid] = (int32_t)row;
+        s_rows[tid] = row;
+    }
+    lds_barrier();
+
+    // Row copies: the first pass from registers, then any further passes.
+    for (int idx = tid; idx < nvec; idx += kFusedThreads) {
+        if (idx != tid)
+            v = xrow[idx];
+        for (int k = 0; k < K; ++k) {
+            const int64_t row = s_rows[k];
+            if (row >= 0) {
+                u32x4 *dst = reinterpret_cast<u32x4 *>(d.out + row * d.row_bytes) + idx;
+                if (EPL_ROW_NT)
+                    __builtin_nontemporal_store(v, dst);
+                else
+                    *dst = v;
+            }
+        }
+    }
+    if (nq > 0) {
+        for (int j = tid; j < nq; j += kFusedThreads) {
+            const u32x4 f = j == tid ? sv : reinterpret_cast<const u32x4 *>(d.x_scale + t * d.W)[j];
+            for (int k = 0; k < K; ++k) {
+                const int64_t row = s_rows[k];
+                if (row >= 0)
+                    store_scale(reinterpret_cast<u32x4 *>(d.out_scale + row * d.W) + j, f);
+            }
+        }
+    } else if (nw > 0) {
+        for (int j = tid; j < nw; j += kFusedThreads) {
+            const uint32_t f = j == tid ? sw : d.x_scale[t * d.W + j];
+            for (int k = 0; k < K; ++k) {
+                const int64_t row = s_rows[k];
+                if (row < 0)
+                    continue;
+                if (d.scale_mode == kScaleRows)
+                    store_scale(d.out_scale + row * d.W + j, f);
+                else
+                    store_scale(d.out_scale + (int64_t)j * d.scale_ld + row, f);
+            }
+        }
+    }
+    // Padding rows of the aligned blocks of experts t, t + T, ...
+    if (aligned_blocks) {
+        for (int64_t e = t; e < E; e += a.T) {
+            const int64_t c = s_hist[e];
+            const int64_t p0 = (int64_t)s_start[e] + c;
+            const int64_t p1 = (int64_t)s_start[e] + (c + alignment - 1) / alignment * alignment;
+            for (int64_t p = p0 + tid; p < p1 && p < d.capacity; p += kFusedThreads)
+                d.m_indices[p] = -1;
         }
     }
 }

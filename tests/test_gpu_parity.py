@@ -917,13 +917,18 @@ def test_scan_in_scatter_capacity_overflow(case, alignment):
     assert (m_full[cap:].view(torch.uint8) == POISON).all()
 
 
+# Decode-sized batches (at most 2048 slots) dispatch in one launch whose
+# token workgroups place their own slots.
+ONE_LAUNCH = [("decode_narrow", 300, 4, 32, 8, 64), ("decode_dsv3", 64, 8, 256, 32, 128)]
+
+
 @pytest.mark.parametrize("alignment", [0, 32])
-@pytest.mark.parametrize("case", NO_SCAN, ids=[c[0] for c in NO_SCAN])
+@pytest.mark.parametrize("case", NO_SCAN + ONE_LAUNCH, ids=[c[0] for c in NO_SCAN + ONE_LAUNCH])
 def test_scatter_after_dispatch_reuses_its_workspace(case, alignment):
-    """A dispatch that ran no scan launch leaves the workspace as layout +
-    scan would: a later epl_scatter of another payload with the same
-    routing, workspace and expert_start_loc places it exactly as the oracle
-    does."""
+    """A dispatch that ran no scan launch (or placed its slots in the
+    scatter's own workgroups) leaves the workspace as layout + scan would: a
+    later epl_scatter of another payload with the same routing, workspace
+    and expert_start_loc places it exactly as the oracle does."""
     name, T, K, E, R, H = case
     print(f"[parity] scatter after dispatch case={name} a={alignment}", flush=True)
     rng = np.random.default_rng(33)
