@@ -32,7 +32,8 @@ KERNEL_SOURCES = ("permute_ep_layout_amd/csrc/epl_kernels.h", "permute_ep_layout
 TRAFFIC_MARK = "traffic-json:"
 
 # short names of the library's kernels, matched against demangled names
-SHORT = (("ep_layout_scan_kernel", "layout_scan"), ("ep_layout_kernel", "layout"),
+SHORT = (("ep_dispatch_decode_kernel", "dispatch_decode"),
+         ("ep_layout_scan_kernel", "layout_scan"), ("ep_layout_kernel", "layout"),
          ("ep_scan_kernel", "scan"),
          ("ep_ll_scatter_kernel", "ll_scatter"),
          ("ep_scatter_kernel", "scatter"), ("ep_combine_kernel", "combine"),
