@@ -77,10 +77,20 @@ class Chain:
         self.total.fill_(-1)
 
 
-def test_graph_replays_match_eager():
+# The captured chain in each of the dispatch's launch shapes: the scatter
+# doing the scan's work (1536 DeepSeek-V3-shaped tokens), one launch for a
+# decode-sized batch (64 tokens), and layout, scan and a column-part scatter
+# (700 tokens of hidden 4096); the eager work in between is another shape.
+CASES = [("dsv3", 1536, "small", 700), ("dsv3", 64, "dsv3", 1536), ("small", 700, "dsv3", 64)]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}_t{c[1]}" for c in CASES])
+def test_graph_replays_match_eager(case):
+    name, T, other_name, other_T = case
+    print(f"[graph] {name} T={T}, eager {other_name} T={other_T}", flush=True)
     s = torch.cuda.Stream()
-    w = workloads.get("dsv3").with_(num_tokens=1536)
-    other = workloads.get("small").with_(num_tokens=700)
+    w = workloads.get(name).with_(num_tokens=T)
+    other = workloads.get(other_name).with_(num_tokens=other_T)
     with torch.cuda.stream(s):
         a = Chain(w, s)
         b = Chain(other, s)

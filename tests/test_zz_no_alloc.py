@@ -1,7 +1,8 @@
-"""The allocation-free dispatch (epl_dispatch_static) through the C ABI: two
+"""The allocation-free dispatch (epl_dispatch_static) through the C ABI:
 calls in a row -- the DeepSeek-V3-shaped batch (4096 tokens, hidden 7168 +
 56 fp32 scales, 256 experts, top-8), then a smaller ragged batch (777 tokens
-of hidden 4096, 64 experts, top-6, 5% of slots dropped) -- each against
+of hidden 4096, 64 experts, top-6, 5% of slots dropped), then a decode-sized
+one (100 DeepSeek-V3-shaped tokens, dispatched in one launch) -- each against
 epl_dispatch with a caller-owned workspace on the same inputs: every output
 bit-identical, the status and total read through the returned static
 workspace, and the combine run with it equal to the combine run with the
@@ -72,8 +73,10 @@ def run(w, inp, static, byte):
 def test_static_dispatch_matches_the_workspace_dispatch_on_two_calls():
     big = workloads.get("dsv3")
     small = workloads.get("small").with_(num_tokens=777)
+    # a third, decode-sized call: its dispatch is a single launch
+    decode = workloads.get("dsv3").with_(num_tokens=100)
     addrs = []
-    for w in (big, small):
+    for w in (big, small, decode):
         print(f"[no-alloc] {w.name}: T={w.num_tokens} H={w.hidden} E={w.num_experts} "
               f"K={w.num_topk}", flush=True)
         inp = workloads.make_inputs(w)
@@ -95,7 +98,7 @@ def test_static_dispatch_matches_the_workspace_dispatch_on_two_calls():
             assert (a[key][N:].view(torch.uint8) == 0x5A).all(), key
         assert torch.equal(a["y"].view(torch.int32), b["y"].view(torch.int32))
         addrs.append(a["ws"].data_ptr())
-    assert addrs[0] == addrs[1]            # one static workspace per GPU, reused
+    assert addrs[0] == addrs[1] == addrs[2]    # one static workspace per GPU, reused
 
 
 def test_static_dispatch_rejects_a_problem_beyond_its_workspace():
