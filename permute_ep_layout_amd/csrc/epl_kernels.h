@@ -25,8 +25,12 @@
 // expert in (token, k) order with wavefront ballots; the scan kernel turns
 // the per-block counts into per-block offsets (a prefix over blocks per
 // expert); the scatter kernel adds expert offset + block offset + rank.
-// Decode-sized batches (at most 2048 slots) take ep_layout_scan_kernel
-// instead: one workgroup, one block, both steps in a single launch.
+// For a dispatch of a few thousand tokens the scatter computes the offsets
+// itself from the per-block counts (ScanInScatter), so no scan launch sits
+// between layout and scatter. Decode-sized batches (at most 2048 slots) take
+// ep_layout_scan_kernel in the layout / scan calls (one workgroup, one
+// block) and ep_dispatch_decode_kernel in a dispatch (one launch, each token
+// placed by its own workgroup from the routing of all slots).
 #pragma once
 
 #include <hip/hip_runtime.h>
