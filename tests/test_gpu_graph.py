@@ -111,3 +111,45 @@ def test_graph_replays_match_eager(case):
             for key in ("y", "oi", "m", "out", "start", "cnt"):
                 assert torch.equal(got[key].view(torch.uint8), ref[key].view(torch.uint8)), (i, key)
             assert epl.epl_status(a.ws, s.cuda_stream) == epl.EPL_OK
+
+
+@pytest.mark.parametrize("T", [1536, 64])
+def test_graph_replays_of_the_allocation_free_dispatch(T):
+    """epl_dispatch_static (the entry point for callers that cannot allocate,
+    such as code under graph capture) captured with its combine: every replay
+    reproduces the eager workspace dispatch bit for bit, with eager work of
+    another shape (and its own workspace) in between."""
+    import ctypes
+    print(f"[graph] static dispatch T={T}", flush=True)
+    s = torch.cuda.Stream()
+    w = workloads.get("dsv3").with_(num_tokens=T)
+    with torch.cuda.stream(s):
+        a = Chain(w, s)                     # the workspace dispatch: reference and buffers
+        b = Chain(workloads.get("small").with_(num_tokens=700), s)
+        a.run()
+        s.synchronize()
+        ref = a.snapshot()
+        inp_p = epl.Problem.make(w.num_tokens, w.num_topk, w.num_experts, w.num_ranks, w.hidden,
+                                 w.scale_cols, 0, w.ranks_per_node)
+        static_ws = epl.epl_dispatch_static(inp_p, a.topk, a.x, a.xs, a.cap, a.cnt, a.per, a.node,
+                                            a.inr, a.start, a.total, a.out, a.osc, a.m, a.oi, s)
+        calls = [
+            epl.prepare("epl_dispatch_static", inp_p, a.topk, a.x, a.xs, a.cap, a.cnt, a.per,
+                        a.node, a.inr, a.start, a.total, a.out, a.osc, a.m, a.oi, None, stream=s),
+            epl.prepare("epl_combine", inp_p, a.out, a.cap, a.oi, a.wt, epl.EPL_OUT_F32, a.y,
+                        ctypes.c_void_p(static_ws.data_ptr()), stream=s),
+        ]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for c in calls:
+                c()
+        for i in range(4):
+            a.poison()
+            b.run()
+            g.replay()
+            s.synchronize()
+            got = a.snapshot()
+            assert got["n"] == ref["n"], i
+            for key in ("y", "oi", "m", "out", "start", "cnt"):
+                assert torch.equal(got[key].view(torch.uint8), ref[key].view(torch.uint8)), (i, key)
+            assert epl.epl_status(static_ws, s.cuda_stream) == epl.EPL_OK
