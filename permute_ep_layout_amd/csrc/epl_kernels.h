@@ -1344,6 +1344,10 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
 
 // ------------------------------------------------ decode-sized dispatch --
 
+// Top-k up to which ep_dispatch_decode_kernel keeps the token's experts in
+// registers for its slot counts.
+constexpr int kDecodeFastTopk = 8;
+
 // Rows and outputs of ep_dispatch_decode_kernel (as in ep_scatter_kernel).
 struct DecodeRows {
     const uint8_t *x;
@@ -1546,9 +1550,8 @@ __global__ __launch_bounds__(kFusedThreads) void ep_dispatch_decode_kernel(Layou
         }
         a.in_rank[t * a.R + r] = hit;
     }
-    for (int k = 0; k < K; ++k) {
+    auto count_slot = [&](int k, int ek) {
         const int sk = (int)t * K + k;
-        const int ek = s_tok[k];
         int less = 0, same = 0;
 #pragma unroll
         for (int i = 0; i < kSlotsPerThread; ++i) {
@@ -1562,6 +1565,21 @@ __global__ __launch_bounds__(kFusedThreads) void ep_dispatch_decode_kernel(Layou
             s_less[k][tid / kWave] = less;
             s_same[k][tid / kWave] = same;
         }
+    };
+    if (K <= kDecodeFastTopk) {
+        // the token's experts read from LDS all at once, then the slots in
+        // turn without an LDS round trip between them
+        int tok[kDecodeFastTopk];
+#pragma unroll
+        for (int k = 0; k < kDecodeFastTopk; ++k)
+            tok[k] = k < K ? s_tok[k] : -1;
+#pragma unroll
+        for (int k = 0; k < kDecodeFastTopk; ++k)
+            if (k < K)
+                count_slot(k, tok[k]);
+    } else {
+        for (int k = 0; k < K; ++k)
+            count_slot(k, s_tok[k]);
     }
     if (aligned_blocks) {
         // expert offsets: exclusive prefix of the aligned counts
