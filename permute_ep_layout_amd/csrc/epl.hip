@@ -224,6 +224,19 @@ unsigned row_grid(int64_t items, int64_t limit)
 // combine 4-5% slower, so larger grids keep their size. Capped, striding
 // grids keep theirs too.
 constexpr int64_t kXcdRoundBelow = 8192;
+
+// Grids of at least this many workgroups (one item each) walk their items
+// round-robin over the XCDs (workgroup w takes item w) instead of in
+// XCD-contiguous ranges: 4096 tokens of hidden 7168 (16384 combine items)
+// combine in 98.7-99.3 instead of 104.0-104.3 us, 16384 tokens in 392
+// instead of 410 us; from 257 to 2048 tokens (1028-4096 items) the ranges
+// are as fast or faster (at 300 tokens, 9.2 against 10.5 us).
+#ifndef EPL_COMBINE_XCD_BELOW
+#define EPL_COMBINE_XCD_BELOW 8192
+#endif
+#ifndef EPL_SCATTER_XCD_BELOW
+#define EPL_SCATTER_XCD_BELOW 8192
+#endif
 unsigned xcd_grid(int64_t items, int64_t limit)
 {
     const unsigned g = row_grid(items, limit);
@@ -430,7 +443,8 @@ ScanPlan scan_in_scatter(const epl_problem &p, const WsLayout &w, const ScatterS
     // per = ceil(T / 8) tokens, which meet at most ceil((per - 1) / B) + 1
     // blocks of B tokens; else any block.
     int64_t nbl = nb;
-    if (EPL_XCD_MAP && sp.grid % epl::kNumXcd == 0 && sp.grid >= (unsigned)epl::kNumXcd) {
+    if (EPL_XCD_MAP && sp.grid % epl::kNumXcd == 0 && sp.grid >= (unsigned)epl::kNumXcd &&
+        (int64_t)sp.grid < EPL_SCATTER_XCD_BELOW) {
         const int64_t per = (T + epl::kNumXcd - 1) / epl::kNumXcd;
         nbl = std::min<int64_t>(nb, (per - 1 + w.block_tokens - 1) / w.block_tokens + 1);
     }
@@ -483,8 +497,9 @@ void launch_scatter(const epl_problem &p, const WsLayout &w, const RowArgs &ra,
                        ra.scale_ld, topk, start, at<const int32_t>(ws, w.block_base),
                        at<const int32_t>(ws, w.slot_rank), p.num_tokens, p.num_topk,
                        p.num_experts, w.block_tokens, alignment_of(p),
-                       at<const int32_t>(ws, w.counts), cap, sp.parts, ra.out, ra.out_scale,
-                       m_idx, oi, &at<WsHeader>(ws, 0)->status, sc);
+                       at<const int32_t>(ws, w.counts), cap, sp.parts,
+                       (int64_t)sp.grid < EPL_SCATTER_XCD_BELOW, ra.out, ra.out_scale, m_idx, oi,
+                       &at<WsHeader>(ws, 0)->status, sc);
 }
 
 // The scatter launch. With plan.on (a dispatch whose scan launch was left
@@ -999,11 +1014,13 @@ int epl_combine(const epl_problem *p, const uint16_t *expert_out, int64_t expert
     const int64_t per_pass = (int64_t)th * epl::combine_units_per_thread(bf16, unroll);
     const int parts =
         (int)std::max<int64_t>(1, std::min<int64_t>(epl::kCombineMaxParts, (units + per_pass - 1) / per_pass));
-    const dim3 grid(xcd_grid(p->num_tokens * parts, epl::kCombineGrid));
+    const int64_t items = p->num_tokens * parts;
+    const dim3 grid(xcd_grid(items, epl::kCombineGrid));
+    const bool xcd = items < EPL_COMBINE_XCD_BELOW;
     auto launch = [&](auto kernel, int threads) {
         hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, s, expert_out, expert_rows,
                            output_index, topk_weights, p->num_tokens, p->num_topk, p->hidden,
-                           parts, y, status);
+                           parts, xcd, y, status);
     };
     constexpr int u1 = epl::kCombineUnrollFew, u2 = epl::kCombineUnroll;
     if (bf16) {
