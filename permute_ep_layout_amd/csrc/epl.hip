@@ -1016,11 +1016,11 @@ int epl_combine(const epl_problem *p, const uint16_t *expert_out, int64_t expert
         (int)std::max<int64_t>(1, std::min<int64_t>(epl::kCombineMaxParts, (units + per_pass - 1) / per_pass));
     const int64_t items = p->num_tokens * parts;
     const dim3 grid(xcd_grid(items, epl::kCombineGrid));
-    const bool xcd = items < EPL_COMBINE_XCD_BELOW;
+    const bool xcd_ranges = items < EPL_COMBINE_XCD_BELOW;
     auto launch = [&](auto kernel, int threads) {
         hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, s, expert_out, expert_rows,
                            output_index, topk_weights, p->num_tokens, p->num_topk, p->hidden,
-                           parts, xcd, y, status);
+                           parts, xcd_ranges, y, status);
     };
     constexpr int u1 = epl::kCombineUnrollFew, u2 = epl::kCombineUnroll;
     if (bf16) {

@@ -869,19 +869,23 @@ constexpr int64_t kYNtBytes = EPL_Y_NT_BYTES;
 constexpr int kNumXcd = 8;   // MI355X: 8 XCDs, workgroup i runs on XCD i % 8
 
 // Tokens of one workgroup of a grid-stride row kernel: first, first + stride,
-// ... below end. With the XCD-aware mapping each XCD owns one contiguous
-// range of ceil(T / 8) tokens, so rows written for neighbouring tokens (the
-// neighbouring rows of an expert's block, their scale rows and m_indices
-// entries) meet in the same L2, where partial-line writes can merge before
-// they reach HBM.
+// ... below end. With the XCD-aware mapping (xcd_ranges, and a grid that is a
+// multiple of 8) each XCD owns one contiguous range of ceil(T / 8) tokens, so
+// rows written for neighbouring tokens (the neighbouring rows of an
+// expert's block, their scale rows and m_indices entries) meet in the same
+// L2, where partial-line writes can merge before they reach HBM. Otherwise
+// workgroup w takes items w, w + G, ...: round-robin over the XCDs, which
+// the host picks for large one-item-per-workgroup grids (there, all XCDs
+// then work on a narrow window of neighbouring tokens, and the combine's
+// output rows are written close to one another in time).
 struct TokenRange {
     int64_t first, stride, end;
 };
 
-__device__ __forceinline__ TokenRange token_range(int64_t T, bool xcd = true)
+__device__ __forceinline__ TokenRange token_range(int64_t T, bool xcd_ranges = true)
 {
     const int64_t G = gridDim.x, w = blockIdx.x;
-    if (xcd && EPL_XCD_MAP && G % kNumXcd == 0 && G >= kNumXcd) {
+    if (xcd_ranges && EPL_XCD_MAP && G % kNumXcd == 0 && G >= kNumXcd) {
         const int64_t per = (T + kNumXcd - 1) / kNumXcd;
         const int64_t xcd = w % kNumXcd;
         return {xcd * per + w / kNumXcd, G / kNumXcd, min(T, (xcd + 1) * per)};
@@ -983,7 +987,7 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
     const int64_t *__restrict__ topk, const int32_t *__restrict__ start,
     const int32_t *__restrict__ block_base, const int32_t *__restrict__ slot_rank, int64_t T,
     int K, int E, int B, int alignment, const int32_t *__restrict__ counts, int64_t capacity,
-    int parts_arg, bool xcd, uint8_t *__restrict__ out, uint32_t *__restrict__ out_scale,
+    int parts_arg, bool xcd_ranges, uint8_t *__restrict__ out, uint32_t *__restrict__ out_scale,
     int32_t *__restrict__ m_indices, int32_t *__restrict__ output_index,
     uint32_t *__restrict__ status, ScanInScatter sc)
 {
@@ -996,7 +1000,7 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
     const int pvec = SPLIT ? (nvec + parts - 1) / parts : nvec;   // 16-byte vectors per part
     // Work items: (token, column part) pairs, item i = token i / parts, part
     // i % parts (parts = 1 except for batches too small to fill the GPU).
-    const TokenRange tr = token_range(T * parts, xcd);
+    const TokenRange tr = token_range(T * parts, xcd_ranges);
     const int64_t step = tr.stride, i_end = tr.end;
     const bool lead = tid < K;
     auto token_of = [=](int64_t item) { return SPLIT ? item / parts : item; };
@@ -1989,14 +1993,14 @@ __host__ __device__ constexpr int combine_units_per_thread(bool out_bf16, int un
 template <bool OUT_BF16, bool Y_NT, int THREADS, int UNROLL>
 __global__ __launch_bounds__(THREADS) void ep_combine_kernel(
     const uint16_t *__restrict__ expert_out, int64_t rows, const int32_t *__restrict__ oi,
-    const float *__restrict__ w, int64_t T, int K, int H, int parts, bool xcd,
+    const float *__restrict__ w, int64_t T, int K, int H, int parts, bool xcd_ranges,
     void *__restrict__ y, uint32_t *__restrict__ status)
 {
     __shared__ int64_t s_row[2][kMaxTopk];
     __shared__ float s_w[2][kMaxTopk];
     __shared__ int s_n[2];
     const int tid = threadIdx.x;
-    const TokenRange tr = token_range(T * parts, xcd);
+    const TokenRange tr = token_range(T * parts, xcd_ranges);
     const int64_t step = tr.stride, i_end = tr.end;
 
     int64_t p_next = -1;
