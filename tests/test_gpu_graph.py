@@ -1,7 +1,8 @@
 """The dispatch + combine chain captured in a HIP graph (torch.cuda.CUDAGraph
 over the C ABI calls): every replay, with eager work on other buffers in
 between, reproduces the eager results bit for bit. The chain records no
-memset node; the scan writes N through a mapped host word."""
+memset node; the scan writes N through a mapped host word. The chains'
+buffers sit between red zones (tests/redzones.py) checked after each test."""
 import numpy as np
 import pytest
 
@@ -9,6 +10,8 @@ torch = pytest.importorskip("torch")
 
 import permute_ep_layout_amd as epl  # noqa: E402
 from permute_ep_layout_amd import workloads  # noqa: E402
+
+import redzones  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -20,6 +23,13 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     epl.load()
+
+
+@pytest.fixture(autouse=True)
+def _red_zones():
+    """The chains' buffers have red zones: no replay may write past them."""
+    yield
+    redzones.check()
 
 
 class Chain:
@@ -36,18 +46,22 @@ class Chain:
         p = epl.Problem.make(T, K, E, R, H, S, 0, w.ranks_per_node)
         self.cap = cap = epl.epl_capacity_rows(p)
         i32 = torch.int32
-        self.ws = torch.empty(epl.epl_workspace_bytes(p), dtype=torch.uint8, device=DEV)
-        self.cnt = torch.empty(E, dtype=i32, device=DEV)
-        self.per = torch.empty(R, dtype=i32, device=DEV)
-        self.node = torch.empty(p.num_nodes, dtype=i32, device=DEV) if p.num_nodes else None
-        self.inr = torch.empty((T, R), dtype=torch.uint8, device=DEV)
-        self.start = torch.empty(E, dtype=i32, device=DEV)
+
+        def buf(shape, dtype):
+            return redzones.poisoned(shape, dtype, 0x5A, DEV)
+
+        self.ws = buf(epl.epl_workspace_bytes(p), torch.uint8)
+        self.cnt = buf(E, i32)
+        self.per = buf(R, i32)
+        self.node = buf(p.num_nodes, i32) if p.num_nodes else None
+        self.inr = buf((T, R), torch.uint8)
+        self.start = buf(E, i32)
         self.total = torch.zeros(1, dtype=i32).pin_memory()
-        self.out = torch.empty((cap, H), dtype=torch.bfloat16, device=DEV)
-        self.osc = torch.empty((cap, S), dtype=torch.float32, device=DEV) if S else None
-        self.m = torch.empty(cap, dtype=i32, device=DEV)
-        self.oi = torch.empty((T, K), dtype=i32, device=DEV)
-        self.y = torch.empty((T, H), dtype=torch.float32, device=DEV)
+        self.out = buf((cap, H), torch.bfloat16)
+        self.osc = buf((cap, S), torch.float32) if S else None
+        self.m = buf(cap, i32)
+        self.oi = buf((T, K), i32)
+        self.y = buf((T, H), torch.float32)
         # checked once through the validating wrappers, then pre-marshalled
         epl.epl_dispatch(p, self.topk, self.x, self.xs, cap, self.cnt, self.per, self.node,
                          self.inr, self.start, self.total, self.out, self.osc, self.m, self.oi,

@@ -2,7 +2,8 @@
 oracle, through the C ABI: recv_count, layout_range, output_index and
 src_info bit-exact; the FP8 codes and fp32 scales of every placed row
 bit-exact (the quantisation decision is taken in binary32 on both sides);
-rows past an expert's recv_count untouched (poisoned buffers)."""
+rows past an expert's recv_count untouched (poisoned buffers); nothing written
+past either end of a buffer (red zones, tests/redzones.py)."""
 import zlib
 
 import numpy as np
@@ -13,6 +14,8 @@ torch = pytest.importorskip("torch")
 import oracle  # noqa: E402
 import permute_ep_layout_amd as epl  # noqa: E402
 from permute_ep_layout_amd import workloads  # noqa: E402
+
+import redzones  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -28,9 +31,15 @@ def _gpu():
 
 
 def poisoned(shape, dtype):
-    t = torch.empty(shape, dtype=dtype, device=DEV)
-    t.view(torch.uint8).fill_(POISON)
-    return t
+    return redzones.poisoned(shape, dtype, POISON, DEV)
+
+
+@pytest.fixture(autouse=True)
+def _red_zones():
+    """Every buffer from poisoned() has red zones; a write past either end
+    of one fails the test."""
+    yield
+    redzones.check()
 
 
 def gpu_ll(topk, x, E, M, cap, stream=None):

@@ -8,7 +8,9 @@ absolute values (also computed by the oracle): "1e-5 relative" measured
 against the size of the terms, so cancellation cannot make it meaningless.
 bf16 combine output must be within half a bf16 ulp of that (RNE of the fp32
 sum). Output buffers are poisoned before every call so that a slot the
-kernels forget to write cannot pass.
+kernels forget to write cannot pass, and each sits between red zones
+(tests/redzones.py) checked after every test, so that a write past either
+end of a buffer cannot pass either.
 """
 import numpy as np
 import pytest
@@ -18,6 +20,8 @@ torch = pytest.importorskip("torch")
 import oracle  # noqa: E402
 import permute_ep_layout_amd as epl  # noqa: E402
 from permute_ep_layout_amd import workloads  # noqa: E402
+
+import redzones  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -51,9 +55,15 @@ def u16(t):
 
 
 def poisoned(shape, dtype, byte=POISON):
-    t = torch.empty(shape, dtype=dtype, device=DEV)
-    t.view(torch.uint8).fill_(byte)
-    return t
+    return redzones.poisoned(shape, dtype, byte, DEV)
+
+
+@pytest.fixture(autouse=True)
+def _red_zones():
+    """Every buffer from poisoned() has red zones; a write past either end
+    of one fails the test."""
+    yield
+    redzones.check()
 
 
 def gpu_dispatch(topk, x, xs, E, R, cap=None, byte=POISON, stream=None, split=False,
@@ -155,7 +165,7 @@ def full_parity(w: workloads.Workload, inp=None, split=False, alignment=0):
     if w.expert_fn == "identity":
         eo = r["out"]
     else:
-        eo = torch.empty_like(r["out"])
+        eo = poisoned(r["out"].shape, r["out"].dtype)
         epl.epl_expert_scale(r["p"], r["out"], r["m"], r["cap"], eo, r["ws"])
         real = ref["m_indices"] >= 0
         np.testing.assert_array_equal(u16(eo[:N])[real], ref["expert_out"][real])
@@ -233,7 +243,7 @@ def test_large_batch_full_parity():
     ref = dict(num_tokens_per_expert=cnt, num_tokens_per_rank=per_rank, is_token_in_rank=in_rank,
                expert_start_loc=start, total=N, m_indices=m_ref, output_index=oi_ref)
     r = gpu_dispatch(topk, x, None, E, R, G=w.ranks_per_node)
-    eo = torch.empty_like(r["out"])
+    eo = poisoned(r["out"].shape, r["out"].dtype)
     epl.epl_expert_scale(r["p"], r["out"], r["m"], r["cap"], eo, r["ws"])
     y = gpu_combine(r, eo, wt, epl.EPL_OUT_F32)
     assert epl.epl_status(r["ws"]) == epl.EPL_OK
@@ -717,9 +727,8 @@ def test_combine_flags_row_beyond_expert_output():
     ws = poisoned(epl.epl_workspace_bytes(p), torch.uint8)
     # a clean layout resets the status word
     epl.epl_layout(p, torch.zeros((T, K), dtype=torch.int64, device=DEV),
-                   torch.empty(4, dtype=torch.int32, device=DEV),
-                   torch.empty(2, dtype=torch.int32, device=DEV), None,
-                   torch.empty((T, 2), dtype=torch.uint8, device=DEV), ws)
+                   poisoned(4, torch.int32), poisoned(2, torch.int32), None,
+                   poisoned((T, 2), torch.uint8), ws)
     y = poisoned((T, H), torch.float32)
     epl.epl_combine(p, to_bf16(eo), 20, torch.from_numpy(oi).to(DEV),
                     torch.from_numpy(wt).to(DEV), epl.EPL_OUT_F32, y, ws)

@@ -7,7 +7,8 @@ epl_dispatch with a caller-owned workspace on the same inputs: every output
 bit-identical, the status and total read through the returned static
 workspace, and the combine run with it equal to the combine run with the
 caller's workspace. A problem too large for the static workspace is
-rejected before anything is launched."""
+rejected before anything is launched. The caller's buffers sit between red
+zones (tests/redzones.py) checked after each test."""
 import ctypes
 
 import numpy as np
@@ -17,6 +18,8 @@ torch = pytest.importorskip("torch")
 
 import permute_ep_layout_amd as epl  # noqa: E402
 from permute_ep_layout_amd import workloads  # noqa: E402
+
+import redzones  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -32,9 +35,15 @@ def _gpu():
 
 
 def poisoned(shape, dtype, byte):
-    t = torch.empty(shape, dtype=dtype, device=DEV)
-    t.view(torch.uint8).fill_(byte)
-    return t
+    return redzones.poisoned(shape, dtype, byte, DEV)
+
+
+@pytest.fixture(autouse=True)
+def _red_zones():
+    """Every buffer from poisoned() has red zones; a write past either end
+    of one fails the test."""
+    yield
+    redzones.check()
 
 
 def run(w, inp, static, byte):
