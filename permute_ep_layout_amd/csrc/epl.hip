@@ -644,6 +644,22 @@ bool ll_ok(const epl_problem *p, int32_t M, int64_t cap)
     return (int64_t)p->num_experts * cap <= (int64_t)INT32_MAX;
 }
 
+// Decode-sized low-latency dispatches (at most kFusedMaxSlots slots, and
+// at most kLLDecodeMaxCounts (segment, expert) counters, whose 56 KB of LDS
+// keep the workgroup within 64 KB) in one launch (epl::ep_ll_decode_kernel).
+// 0 turns it off (layout, reduction and cast launches).
+#ifndef EPL_LL_DECODE
+#define EPL_LL_DECODE 1
+#endif
+constexpr int64_t kLLDecodeMaxCounts = 14336;
+
+bool ll_decode(const epl_problem &p, int32_t M)
+{
+    return EPL_LL_DECODE && p.num_tokens >= 1 &&
+           p.num_tokens * (int64_t)p.num_topk <= epl::kFusedMaxSlots &&
+           (p.num_tokens / M) * (int64_t)p.num_experts <= kLLDecodeMaxCounts;
+}
+
 template <int VPT>
 void launch_ll_scatter(const epl_problem &p, const WsLayout &w, int32_t M, int64_t cap,
                        const uint16_t *x, const int64_t *topk, void *ws, uint8_t *out,
@@ -956,6 +972,15 @@ int epl_ll_dispatch(const epl_problem *p, int32_t tokens_per_segment, int64_t ro
         return EPL_EINVAL;
     const WsLayout w = ws_layout(*p, ll_block_tokens(*p, M));
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (ll_decode(*p, M)) {
+        const epl::LLArgs a{x, (int)p->hidden, topk_idx, p->num_tokens, p->num_topk,
+                            p->num_experts, M, cap, out, out_scale, recv_count, src_info,
+                            layout_range, output_index, &at<WsHeader>(workspace, 0)->status};
+        const size_t lds = sizeof(int32_t) * (size_t)(p->num_tokens / M) * p->num_experts;
+        hipLaunchKernelGGL(epl::ep_ll_decode_kernel, dim3((unsigned)(1 + p->num_tokens)),
+                           dim3(epl::kFusedThreads), lds, s, a);
+        return launch_status();
+    }
     int rc = enqueue_layout(*p, w, topk_idx, nullptr, workspace, s);
     if (rc == EPL_OK)
         rc = enqueue_scan(*p, w, epl::kScanReduce, nullptr, nullptr, nullptr, nullptr, nullptr,

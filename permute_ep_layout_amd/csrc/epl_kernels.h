@@ -1705,6 +1705,49 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d)
     return e4m3_rne(a) | (e4m3_rne(b) << 8) | (e4m3_rne(c) << 16) | (e4m3_rne(d) << 24);
 }
 
+// FP8 cast of the 16 bf16 values one lane holds (two 16-byte vectors, 8
+// values each) as part of a 128-column group spread over the 8 lanes of a
+// half DPP row, all of which must be active: codes = e4m3(x * (448 / amax))
+// packed four to a word, zero codes for an all-zero group, and the group's
+// scale amax / 448, the same in each of its lanes.
+struct Cast16 {
+    u32x4 codes;
+    float scale;
+};
+__device__ __forceinline__ Cast16 cast_e4m3_16(const u32x4 (&v)[2])
+{
+    float f[16];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            f[8 * h + 2 * q] = __uint_as_float(v[h][q] << 16);
+            f[8 * h + 2 * q + 1] = __uint_as_float(v[h][q] & 0xFFFF0000u);
+        }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+        amax = fmaxf(amax, fabsf(f[q]));
+    amax = half_row_max(amax);
+    const float scale = amax / 448.0f;
+    // 448 / amax overflows binary32 for amax below ~1.3e-36 (bf16 keeps
+    // binary32's exponent range): such a group is first scaled by 2^64, which
+    // changes no rounding (a power of two, the values stay normal), so the
+    // codes are those of binary32 arithmetic with an unbounded exponent
+    const float pre = amax < 0x1p-64f ? 0x1p64f : 1.0f;
+    const float inv = amax > 0.0f ? 448.0f / (amax * pre) : 0.0f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+        f[q] *= pre;
+    Cast16 c;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        c.codes[q] = e4m3x4(f[4 * q] * inv, f[4 * q + 1] * inv, f[4 * q + 2] * inv, f[4 * q + 3] * inv);
+    c.scale = scale;
+    return c;
+}
+
 #ifndef EPL_LL_GRID
 #define EPL_LL_GRID 2048
 #endif
@@ -1848,36 +1891,9 @@ __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
                 const int pi = base + i * kScatterThreads + tid;
                 if (pi >= npair)      // whole 8-lane groups drop out together (npair % 8 == 0)
                     continue;
-                float f[16];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        f[8 * h + 2 * q] = __uint_as_float(v[i][h][q] << 16);
-                        f[8 * h + 2 * q + 1] = __uint_as_float(v[i][h][q] & 0xFFFF0000u);
-                    }
-                }
-                float amax = 0.0f;
-#pragma unroll
-                for (int q = 0; q < 16; ++q)
-                    amax = fmaxf(amax, fabsf(f[q]));
-                amax = half_row_max(amax);
-                const float scale = amax / 448.0f;
-                // 448 / amax overflows binary32 for amax below ~1.3e-36 (bf16
-                // keeps binary32's exponent range): such a group is first
-                // scaled by 2^64, which changes no rounding (a power of two,
-                // the values stay normal), so the codes are those of binary32
-                // arithmetic with an unbounded exponent
-                const float pre = amax < 0x1p-64f ? 0x1p64f : 1.0f;
-                const float inv = amax > 0.0f ? 448.0f / (amax * pre) : 0.0f;
-#pragma unroll
-                for (int q = 0; q < 16; ++q)
-                    f[q] *= pre;
-                u32x4 codes;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    codes[q] = e4m3x4(f[4 * q] * inv, f[4 * q + 1] * inv, f[4 * q + 2] * inv,
-                                      f[4 * q + 3] * inv);
+                const Cast16 c = cast_e4m3_16(v[i]);
+                const u32x4 codes = c.codes;
+                const float scale = c.scale;
                 const int g = pi / 8;
                 for (int k = 0; k < K; ++k) {
                     const int e = se[k];
@@ -1907,6 +1923,189 @@ __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
             v[i][1] = vn[i][1];
         }
         any = any_next;
+    }
+}
+
+// ------------------------------- low-latency dispatch of decode sizes --
+
+// Arguments of ep_ll_decode_kernel (those of the three-launch path).
+struct LLArgs {
+    const uint16_t *x;
+    int H;
+    const int64_t *topk;
+    int64_t T;
+    int K, E, M;
+    int64_t cap;
+    uint8_t *out;
+    float *out_scale;
+    int32_t *recv_count;
+    int32_t *src_info;
+    int32_t *layout_range;
+    int32_t *output_index;
+    uint32_t *status;
+};
+
+// Workgroup 0 of ep_ll_decode_kernel: slots per (source segment, expert) in
+// LDS ([T / M][E] words of dynamic LDS), then per expert a running sum over
+// the segments clipped to the rectangle gives layout_range and recv_count.
+// The status word gets the id error bit and the capacity bit, set exactly
+// when an expert has more slots than rows, i.e. when some slot finds no row.
+__device__ __forceinline__ void ll_decode_counts_block(const LLArgs &a)
+{
+    extern __shared__ int32_t s_seg_cnt[];
+    __shared__ uint32_t s_err;
+    const int tid = threadIdx.x;
+    const int K = a.K, E = a.E;
+    const int64_t nseg = a.T / a.M;
+    const int64_t n = nseg * E;
+    const int ns = (int)(a.T * K);
+    for (int64_t i = tid; i < n; i += kFusedThreads)
+        s_seg_cnt[i] = 0;
+    if (tid == 0)
+        s_err = 0u;
+    lds_barrier();
+    bool bad = false;
+    for (int sl = tid; sl < ns; sl += kFusedThreads) {
+        const int64_t e = a.topk[sl];
+        bad |= (e < -1 || e >= E);
+        if (e >= 0 && e < E)
+            atomicAdd(&s_seg_cnt[(int64_t)(sl / K / a.M) * E + e], 1);
+    }
+    if (bad)
+        atomicOr(&s_err, kStatusBadExpert);
+    lds_barrier();
+    bool over = false;
+    for (int e = tid; e < E; e += kFusedThreads) {
+        int64_t run = 0;
+        for (int64_t sg = 0; sg < nseg; ++sg) {
+            const int64_t b0 = min(run, a.cap);
+            run += s_seg_cnt[sg * E + e];
+            const int64_t i = (int64_t)e * nseg + sg;
+            a.layout_range[2 * i] = (int32_t)b0;
+            a.layout_range[2 * i + 1] = (int32_t)(min(run, a.cap) - b0);
+        }
+        a.recv_count[e] = (int32_t)min(run, a.cap);
+        over |= run > a.cap;
+    }
+    if (over)
+        atomicOr(&s_err, kStatusCapacity);
+    lds_barrier();
+    if (tid == 0)
+        *a.status = s_err;
+}
+
+// The low-latency dispatch of a decode-sized batch (at most kFusedMaxSlots
+// slots) in one launch of 1 + T workgroups of kFusedThreads threads, with the
+// outputs of the layout, reduction and ep_ll_scatter_kernel launches.
+// Workgroup 0 writes recv_count, layout_range and the status word
+// (ll_decode_counts_block). Workgroup 1 + t issues token t's row loads, then
+// counts for each of its K slots, with wave ballots over all slots, the
+// earlier slots of the same expert in (token, k) order: that count is the
+// slot's row j in its expert's block. It stores output_index and src_info,
+// casts the row (16 values per thread, a 128-column group over 8 lanes, as in
+// ep_ll_scatter_kernel) and stores the codes and scales to every placed row.
+__global__ __launch_bounds__(kFusedThreads) void ep_ll_decode_kernel(LLArgs a)
+{
+    if (blockIdx.x == 0) {
+        ll_decode_counts_block(a);
+        return;
+    }
+    constexpr int kSlotsPerThread = kFusedMaxSlots / kFusedThreads;
+    __shared__ int32_t s_tok[kMaxTopk];                  // the token's expert ids (-1: none)
+    __shared__ int32_t s_same[kMaxTopk][kFusedWaves];    // per wave: earlier slots of the expert
+    __shared__ int32_t s_e[kMaxTopk];                    // expert of each placed slot, -1 if none
+    __shared__ int32_t s_j[kMaxTopk];                    // its row within the expert's block
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int64_t t = blockIdx.x - 1;
+    const int K = a.K, E = a.E;
+    const int S = a.H / 128;
+    const int ns = (int)(a.T * K);
+    const int npair = a.H / 16;                          // 16 bf16 values per thread and pass
+
+    const u32x4 *xrow = reinterpret_cast<const u32x4 *>(a.x + t * (int64_t)a.H);
+    u32x4 v[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    if (tid < npair) {
+        v[0] = xrow[2 * tid];
+        v[1] = xrow[2 * tid + 1];
+    }
+    int my_key[kSlotsPerThread];
+#pragma unroll
+    for (int i = 0; i < kSlotsPerThread; ++i) {
+        const int sl = i * kFusedThreads + tid;
+        const int64_t e = sl < ns ? a.topk[sl] : -1;
+        my_key[i] = (e >= 0 && e < E) ? (int)e : -1;
+    }
+    if (tid < K) {
+        const int64_t e = a.topk[t * K + tid];
+        s_tok[tid] = (e >= 0 && e < E) ? (int)e : -1;
+    }
+    lds_barrier();
+    auto count_slot = [&](int k, int ek) {
+        const int sk = (int)t * K + k;
+        int same = 0;
+#pragma unroll
+        for (int i = 0; i < kSlotsPerThread; ++i) {
+            const int sl = i * kFusedThreads + tid;
+            same += __popcll(wave_ballot(ek >= 0 && my_key[i] == ek && sl < sk));
+        }
+        if (lane == 0)
+            s_same[k][tid / kWave] = same;
+    };
+    if (K <= kDecodeFastTopk) {
+        int tok[kDecodeFastTopk];
+#pragma unroll
+        for (int k = 0; k < kDecodeFastTopk; ++k)
+            tok[k] = k < K ? s_tok[k] : -1;
+#pragma unroll
+        for (int k = 0; k < kDecodeFastTopk; ++k)
+            if (k < K)
+                count_slot(k, tok[k]);
+    } else {
+        for (int k = 0; k < K; ++k)
+            count_slot(k, s_tok[k]);
+    }
+    lds_barrier();
+    if (tid < K) {
+        int j = 0;
+        for (int w = 0; w < kFusedWaves; ++w)
+            j += s_same[tid][w];
+        const int e = s_tok[tid];
+        int32_t oi = -1;
+        int pe = -1;
+        if (e >= 0 && j < a.cap) {
+            const int64_t row = (int64_t)e * a.cap + j;
+            oi = (int32_t)row;
+            pe = e;
+            a.src_info[row] = (int32_t)(t % a.M);
+        }
+        a.output_index[t * K + tid] = oi;
+        s_e[tid] = pe;
+        s_j[tid] = j;
+    }
+    lds_barrier();
+
+    // whole 8-lane groups are active or idle together (npair % 8 == 0)
+    for (int pi = tid; pi < npair; pi += kFusedThreads) {
+        if (pi != tid) {
+            v[0] = xrow[2 * pi];
+            v[1] = xrow[2 * pi + 1];
+        }
+        const Cast16 c = cast_e4m3_16(v);
+        const int g = pi / 8;
+        for (int k = 0; k < K; ++k) {
+            const int e = s_e[k];
+            if (e < 0)
+                continue;
+            const int64_t row = (int64_t)e * a.cap + s_j[k];
+            __builtin_nontemporal_store(c.codes, reinterpret_cast<u32x4 *>(a.out + row * a.H) + pi);
+        }
+        for (int k = tid & 7; k < K; k += 8) {
+            const int e = s_e[k];
+            if (e < 0)
+                continue;
+            a.out_scale[((int64_t)e * S + g) * a.cap + s_j[k]] = c.scale;
+        }
     }
 }
 

@@ -35,7 +35,7 @@ TRAFFIC_MARK = "traffic-json:"
 SHORT = (("ep_dispatch_decode_kernel", "dispatch_decode"),
          ("ep_layout_scan_kernel", "layout_scan"), ("ep_layout_kernel", "layout"),
          ("ep_scan_kernel", "scan"),
-         ("ep_ll_scatter_kernel", "ll_scatter"),
+         ("ep_ll_scatter_kernel", "ll_scatter"), ("ep_ll_decode_kernel", "ll_decode"),
          ("ep_scatter_kernel", "scatter"), ("ep_combine_kernel", "combine"),
          ("ep_expert_scale_kernel", "expert"),
          # the benchmark's write-piece probes (bench_probe/stream_probe.hip)

@@ -42,11 +42,12 @@ def _red_zones():
     redzones.check()
 
 
-def gpu_ll(topk, x, E, M, cap, stream=None):
+def gpu_ll(topk, x, E, M, cap, stream=None, ws=None):
     T, K = topk.shape
     H = x.shape[1]
     p = epl.Problem.make(T, K, E, 1, H, H // 128)
-    ws = poisoned(epl.epl_ll_workspace_bytes(p, M), torch.uint8)
+    if ws is None:
+        ws = poisoned(epl.epl_ll_workspace_bytes(p, M), torch.uint8)
     r = dict(out=poisoned((E, cap, H), torch.uint8),
              out_scale=poisoned((E, H // 128, cap), torch.float32),
              recv_count=poisoned(E, torch.int32), src_info=poisoned((E, cap), torch.int32),
@@ -59,16 +60,21 @@ def gpu_ll(topk, x, E, M, cap, stream=None):
     return r
 
 
-def check_ll(topk, x, E, M, cap, expect_overflow=False, untouched_sample=64):
+def check_ll(topk, x, E, M, cap, expect_overflow=False, untouched_sample=64, ws=None):
+    """One low-latency dispatch against the oracle. Ids outside [-1, E) must
+    act as -1 and make the status EPL_ERANGE. `ws` reuses a workspace."""
     print(f"[ll] T={topk.shape[0]} K={topk.shape[1]} E={E} M={M} cap={cap} H={x.shape[1]}",
           flush=True)
     orc = oracle.default()
-    ref = orc.ll_dispatch(None, topk, E, M, cap, hidden=x.shape[1])
+    bad_ids = bool(((topk < -1) | (topk >= E)).any())
+    clean = np.where((topk < -1) | (topk >= E), -1, topk)
+    ref = orc.ll_dispatch(None, clean, E, M, cap, hidden=x.shape[1])
     q, sc = orc.quantize_e4m3(x)
-    r = gpu_ll(topk, x, E, M, cap)
+    r = gpu_ll(topk, x, E, M, cap, ws=ws)
     torch.cuda.synchronize()
     st = epl.epl_status(r["ws"])
-    assert st == (epl.EPL_ECAPACITY if expect_overflow else epl.EPL_OK)
+    assert st == (epl.EPL_ERANGE if bad_ids else
+                  epl.EPL_ECAPACITY if expect_overflow else epl.EPL_OK)
     assert ref["overflow"] == expect_overflow
     np.testing.assert_array_equal(r["recv_count"].cpu().numpy(), ref["recv_count"])
     np.testing.assert_array_equal(r["layout_range"].cpu().numpy(), ref["layout_range"])
@@ -137,6 +143,58 @@ def test_ll_shapes(case):
     T = nseg * M
     topk = _topk(rng, T, K, E, drop) if K <= E else rng.integers(-1, E, (T, K)).astype(np.int64)
     check_ll(topk, _x(rng, T, H), E, M, cap)
+
+
+# Decode-sized batches (at most 2048 slots and at most 14336 (segment,
+# expert) counters) are dispatched in one launch; these cases sit on both
+# sides of those limits, and one has rows longer than a workgroup's pass.
+LL_DECODE_CASES = [
+    # (name, segments, M, K, E, H, cap, drop)
+    ("decode_dsv3_t128", 1, 128, 8, 256, 7168, 128, 0.0),
+    ("decode_dsv3_8_segments", 8, 32, 8, 256, 7168, 256, 0.05),
+    ("decode_slot_limit_2048", 2, 128, 8, 256, 1024, 256, 0.1),
+    ("decode_slot_limit_plus_one_token", 1, 257, 8, 256, 1024, 257, 0.1),
+    ("decode_counter_limit_14336", 56, 2, 4, 256, 256, 112, 0.0),
+    ("decode_counter_limit_plus_one_segment", 57, 2, 4, 256, 256, 114, 0.0),
+    ("decode_k16_two_passes", 2, 16, 16, 64, 16512, 32, 0.1),
+    ("decode_e1000", 2, 64, 6, 1000, 384, 128, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", LL_DECODE_CASES, ids=[c[0] for c in LL_DECODE_CASES])
+def test_ll_decode_sizes(case):
+    name, nseg, M, K, E, H, cap, drop = case
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    T = nseg * M
+    check_ll(_topk(rng, T, K, E, drop), _x(rng, T, H), E, M, cap)
+
+
+def test_ll_decode_overflow_and_bad_ids_then_reset():
+    """A decode-sized batch of DeepSeek-V3 shape with 2 rows per expert:
+    the capacity bit, the first rows kept; then ids outside [-1, E) in the
+    same workspace: the id bit; then clean ids: the status clears."""
+    rng = np.random.default_rng(41)
+    T, K, E, H, M = 128, 8, 256, 7168, 128
+    topk, x = _topk(rng, T, K, E), _x(rng, T, H)
+    r, _ = check_ll(topk, x, E, M, 2, expect_overflow=True)
+    bad = topk.copy()
+    bad[3, 1] = E
+    bad[77, 0] = 1 << 40
+    bad[100, 7] = -5
+    check_ll(bad, x, E, M, M, ws=r["ws"])
+    check_ll(topk, x, E, M, M, ws=r["ws"])
+
+
+def test_ll_decode_receive_side_local_ids():
+    """128 tokens of the DeepSeek-V3 batch seen by one receiver: local ids of
+    its 8 experts, -1 elsewhere (most tokens select none of them)."""
+    w = workloads.get("dsv3_ll")
+    inp = workloads.make_inputs(w)
+    El, r, T = 8, 5, 128
+    topk = inp["topk_idx"][:T]
+    mine = (topk >= r * El) & (topk < (r + 1) * El)
+    local = np.ascontiguousarray(np.where(mine, topk - r * El, -1))
+    check_ll(local, np.ascontiguousarray(inp["x"][:T]), El, T, T)
 
 
 def test_ll_receive_side_local_ids():
