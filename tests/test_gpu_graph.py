@@ -1,6 +1,8 @@
 """The dispatch + combine chain captured in a HIP graph (torch.cuda.CUDAGraph
-over the C ABI calls): every replay, with eager work on other buffers in
-between, reproduces the eager results bit for bit. The chain records no
+over the C ABI calls), in each launch shape of epl_dispatch, for the
+allocation-free dispatch and for the low-latency dispatch: every replay, with
+eager work on other buffers in between, reproduces the eager results bit for
+bit. The chain records no
 memset node; the scan writes N through a mapped host word. The chains'
 buffers sit between red zones (tests/redzones.py) checked after each test."""
 import numpy as np
@@ -167,3 +169,64 @@ def test_graph_replays_of_the_allocation_free_dispatch(T):
             for key in ("y", "oi", "m", "out", "start", "cnt"):
                 assert torch.equal(got[key].view(torch.uint8), ref[key].view(torch.uint8)), (i, key)
             assert epl.epl_status(static_ws, s.cuda_stream) == epl.EPL_OK
+
+
+@pytest.mark.parametrize("T", [128, 512])
+def test_graph_replays_of_the_low_latency_dispatch(T):
+    """The low-latency dispatch and a combine over its rectangle captured in
+    a graph (one launch for 128 DeepSeek-V3-shaped tokens, three for 512):
+    every replay, with eager work of another shape in between, reproduces
+    the eager outputs bit for bit."""
+    print(f"[graph] low-latency T={T}", flush=True)
+    s = torch.cuda.Stream()
+    w = workloads.get("dsv3_ll").with_(num_tokens=T)
+    inp = workloads.make_inputs(w)
+    M, K, E, H = w.ll_segment, w.num_topk, w.num_experts, w.hidden
+    cap, S, i32 = T, H // 128, torch.int32
+
+    def buf(shape, dtype):
+        return redzones.poisoned(shape, dtype, 0x5A, DEV)
+
+    with torch.cuda.stream(s):
+        topk = torch.from_numpy(inp["topk_idx"]).to(DEV)
+        x = torch.from_numpy(inp["x"].view(np.int16)).to(DEV).view(torch.bfloat16)
+        wt = torch.from_numpy(inp["topk_weights"]).to(DEV)
+        eo = torch.randn((E * cap, H), device=DEV).to(torch.bfloat16)
+        p = epl.Problem.make(T, K, E, 1, H, S)
+        pc = epl.Problem.make(T, K, E, 1, H, 0)
+        ws = buf(epl.epl_ll_workspace_bytes(p, M), torch.uint8)
+        outs = dict(out=buf((E, cap, H), torch.uint8), osc=buf((E, S, cap), torch.float32),
+                    recv=buf(E, i32), src=buf((E, cap), i32), lr=buf((E, T // M, 2), i32),
+                    oi=buf((T, K), i32), y=buf((T, H), torch.float32))
+        o = outs
+        epl.epl_ll_dispatch(p, M, cap, topk, x, o["out"], o["osc"], o["recv"], o["src"], o["lr"],
+                            o["oi"], ws, s)
+        epl.epl_combine(pc, eo, E * cap, o["oi"], wt, epl.EPL_OUT_F32, o["y"], ws, s)
+        s.synchronize()
+        assert epl.epl_status(ws, s.cuda_stream) == epl.EPL_OK
+        flat = o["oi"].view(-1).long()
+        placed = flat[flat >= 0]
+        ref = {k: v.clone() for k, v in outs.items() if k != "out"}
+        ref["rows"] = o["out"].view(E * cap, H)[placed].clone()
+        calls = [
+            epl.prepare("epl_ll_dispatch", p, M, cap, topk, x, o["out"], o["osc"], o["recv"],
+                        o["src"], o["lr"], o["oi"], ws, stream=s),
+            epl.prepare("epl_combine", pc, eo, E * cap, o["oi"], wt, epl.EPL_OUT_F32, o["y"], ws,
+                        stream=s),
+        ]
+        b = Chain(workloads.get("small").with_(num_tokens=700), s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for c in calls:
+                c()
+        for i in range(4):
+            for t in outs.values():
+                t.view(torch.uint8).fill_(0x5A)
+            b.run()
+            g.replay()
+            s.synchronize()
+            for k in ("osc", "recv", "src", "lr", "oi", "y"):
+                assert torch.equal(outs[k].view(torch.uint8), ref[k].view(torch.uint8)), (i, k)
+            got_rows = o["out"].view(E * cap, H)[placed]
+            assert torch.equal(got_rows, ref["rows"]), i
+            assert epl.epl_status(ws, s.cuda_stream) == epl.EPL_OK
