@@ -660,6 +660,20 @@ bool ll_decode(const epl_problem &p, int32_t M)
            (p.num_tokens / M) * (int64_t)p.num_experts <= kLLDecodeMaxCounts;
 }
 
+// Low-latency dispatches of 1 to EPL_LL_SUMMED_BLOCKS layout blocks run no
+// reduction launch: the cast kernel sums the per-block offsets it needs from
+// the layout's per-block counts (ep_ll_scatter_kernel, SUMMED). Without
+// tokens the reduction still runs: it is what resets the status word then.
+// 0 turns it off.
+#ifndef EPL_LL_SUMMED_BLOCKS
+#define EPL_LL_SUMMED_BLOCKS 64
+#endif
+
+bool ll_summed(const WsLayout &w)
+{
+    return w.num_blocks >= 1 && w.num_blocks <= EPL_LL_SUMMED_BLOCKS;
+}
+
 template <int VPT>
 void launch_ll_scatter(const epl_problem &p, const WsLayout &w, int32_t M, int64_t cap,
                        const uint16_t *x, const int64_t *topk, void *ws, uint8_t *out,
@@ -673,12 +687,15 @@ void launch_ll_scatter(const epl_problem &p, const WsLayout &w, int32_t M, int64
     const int64_t need = (entries + epl::kScatterThreads - 1) / epl::kScatterThreads;
     const unsigned grid =
         xcd_grid(std::max<int64_t>(std::min<int64_t>(p.num_tokens, epl::kLLGrid), need), 1 << 30);
-    hipLaunchKernelGGL(epl::ep_ll_scatter_kernel<VPT>, dim3(grid), dim3(epl::kScatterThreads), 0, s,
+    auto kernel = ll_summed(w) ? epl::ep_ll_scatter_kernel<VPT, true>
+                               : epl::ep_ll_scatter_kernel<VPT, false>;
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(epl::kScatterThreads), 0, s,
                        x, p.hidden, topk, at<const int32_t>(ws, w.block_base),
                        at<const int32_t>(ws, w.slot_rank), at<const int32_t>(ws, w.counts),
                        p.num_tokens, p.num_topk, p.num_experts, w.block_tokens, M, cap, out,
                        out_scale, recv_count, src_info, layout_range, output_index,
-                       &at<WsHeader>(ws, 0)->status);
+                       &at<WsHeader>(ws, 0)->status, at<const int32_t>(ws, w.block_count),
+                       at<const uint32_t>(ws, w.block_err), w.num_blocks);
 }
 
 // The workspace of epl_dispatch_static: a device array that the library
@@ -982,7 +999,7 @@ int epl_ll_dispatch(const epl_problem *p, int32_t tokens_per_segment, int64_t ro
         return launch_status();
     }
     int rc = enqueue_layout(*p, w, topk_idx, nullptr, workspace, s);
-    if (rc == EPL_OK)
+    if (rc == EPL_OK && !ll_summed(w))
         rc = enqueue_scan(*p, w, epl::kScanReduce, nullptr, nullptr, nullptr, nullptr, nullptr,
                           workspace, s);
     if (rc != EPL_OK)

@@ -1779,14 +1779,24 @@ constexpr int kLLGrid = EPL_LL_GRID;
 // read off the per-block offsets: blocks of B tokens with B dividing M, so
 // segment s starts at block s * M / B. VPT = steps of 16
 // values per thread per pass over the row.
-template <int VPT>
+//
+// SUMMED: no reduction launch ran before this kernel; the per-block offsets
+// it would have produced are summed here from the layout's per-block counts
+// (nb blocks). A slot's offset is its expert's count over the blocks before
+// the token's block, summed by 16 lanes (lane l takes blocks l, l + 16, ...)
+// and combined with lane shuffles, one token ahead like the lookups it
+// replaces; each (expert, segment) entry of layout_range is summed by one
+// thread; workgroup 0 ORs the layout's error bits into the status word,
+// which layout block 0 has cleared.
+template <int VPT, bool SUMMED>
 __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
     const uint16_t *__restrict__ x, int H, const int64_t *__restrict__ topk,
     const int32_t *__restrict__ block_base, const int32_t *__restrict__ slot_rank,
     const int32_t *__restrict__ counts, int64_t T, int K, int E, int B, int M, int64_t cap,
     uint8_t *__restrict__ out, float *__restrict__ out_scale, int32_t *__restrict__ recv_count,
     int32_t *__restrict__ src_info, int32_t *__restrict__ layout_range,
-    int32_t *__restrict__ output_index, uint32_t *__restrict__ status)
+    int32_t *__restrict__ output_index, uint32_t *__restrict__ status,
+    const int32_t *__restrict__ block_count, const uint32_t *__restrict__ block_err, int64_t nb)
 {
     __shared__ int32_t s_e[2][kMaxTopk];      // expert of each placed slot, -1 if none
     __shared__ int32_t s_j[2][kMaxTopk];      // row within the expert's block
@@ -1801,16 +1811,48 @@ __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
         const int64_t n = (int64_t)E * nseg;
         const int64_t g0 = (int64_t)blockIdx.x * kScatterThreads + tid;
         const int64_t gs = (int64_t)gridDim.x * kScatterThreads;
-        for (int64_t e = g0; e < E; e += gs)
-            recv_count[e] = (int32_t)min((int64_t)counts[e], cap);
-        for (int64_t i = g0; i < n; i += gs) {
-            const int e = (int)(i / nseg);
-            const int64_t sg = i % nseg;
-            const int64_t b0 = min((int64_t)block_base[(sg * bps) * E + e], cap);
-            const int64_t b1 = sg + 1 < nseg ? min((int64_t)block_base[((sg + 1) * bps) * E + e], cap)
-                                             : min((int64_t)counts[e], cap);
-            layout_range[2 * i] = (int32_t)b0;
-            layout_range[2 * i + 1] = (int32_t)(b1 - b0);
+        if (SUMMED) {
+            // entry (e, sg): expert e's counts over the blocks before segment
+            // sg and through it; the last segment's end is e's total
+            for (int64_t i = g0; i < n; i += gs) {
+                const int e = (int)(i / nseg);
+                const int64_t sg = i % nseg;
+                const int64_t bb0 = sg * bps, bb1 = bb0 + bps;
+                int before = 0, within = 0;
+#pragma unroll 8
+                for (int64_t bb = 0; bb < bb1; ++bb) {
+                    const int c = block_count[bb * E + e];
+                    if (bb < bb0)
+                        before += c;
+                    else
+                        within += c;
+                }
+                const int64_t b0 = min((int64_t)before, cap);
+                const int64_t b1 = min((int64_t)before + within, cap);
+                layout_range[2 * i] = (int32_t)b0;
+                layout_range[2 * i + 1] = (int32_t)(b1 - b0);
+                if (sg == nseg - 1)
+                    recv_count[e] = (int32_t)b1;
+            }
+            if (blockIdx.x == 0) {
+                uint32_t err = 0;
+                for (int64_t bb = tid; bb < nb; bb += kScatterThreads)
+                    err |= block_err[bb];
+                if (err)
+                    atomicOr(status, kStatusBadExpert);
+            }
+        } else {
+            for (int64_t e = g0; e < E; e += gs)
+                recv_count[e] = (int32_t)min((int64_t)counts[e], cap);
+            for (int64_t i = g0; i < n; i += gs) {
+                const int e = (int)(i / nseg);
+                const int64_t sg = i % nseg;
+                const int64_t b0 = min((int64_t)block_base[(sg * bps) * E + e], cap);
+                const int64_t b1 = sg + 1 < nseg ? min((int64_t)block_base[((sg + 1) * bps) * E + e], cap)
+                                                 : min((int64_t)counts[e], cap);
+                layout_range[2 * i] = (int32_t)b0;
+                layout_range[2 * i + 1] = (int32_t)(b1 - b0);
+            }
         }
     }
 
@@ -1835,6 +1877,46 @@ __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
         output_index[t * K + tid] = oi;
         se[tid] = pe;
         sj[tid] = pj;
+    };
+    // SUMMED: all threads place token t, 16 lanes per slot (slots k0 + tid / 16)
+    auto place_summed = [&](int64_t t, int32_t *se, int32_t *sj) {
+        const int l = tid & 15;
+        const uint32_t tu = (uint32_t)t;   // T * K <= INT32_MAX
+        const int64_t b = tu / (uint32_t)B;
+        for (int k0 = 0; k0 < K; k0 += kScatterThreads / 16) {
+            const int k = k0 + tid / 16;
+            if (k >= K)                     // whole 16-lane groups drop out together
+                break;
+            const int64_t e = topk[t * K + k];
+            const bool ok = e >= 0 && e < E;
+            const int r = ok && l == 0 ? slot_rank[t * K + k] : 0;
+            int part = 0;
+            if (ok)
+                for (int64_t bb = l; bb < b; bb += 16)
+                    part += block_count[bb * E + e];
+            part += __shfl_xor(part, 8, 16);
+            part += __shfl_xor(part, 4, 16);
+            part += __shfl_xor(part, 2, 16);
+            part += __shfl_xor(part, 1, 16);
+            if (l == 0) {
+                int32_t pe = -1, pj = 0, oi = -1;
+                if (ok) {
+                    const int64_t j = (int64_t)part + r;
+                    if (j < cap) {
+                        const int64_t row = e * cap + j;
+                        pe = (int32_t)e;
+                        pj = (int32_t)j;
+                        oi = (int32_t)row;
+                        src_info[row] = (int32_t)(tu % (uint32_t)M);
+                    } else {
+                        atomicOr(status, kStatusCapacity);
+                    }
+                }
+                output_index[t * K + k] = oi;
+                se[k] = pe;
+                sj[k] = pj;
+            }
+        }
     };
     // whether token t has a slot at all (uniform: every wave reads the ids)
     auto has_slot = [&](int64_t t) {
@@ -1866,11 +1948,13 @@ __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
     u32x4 v[VPT][2], vn[VPT][2];
     bool any = false;
     if (tr.first < tr.end) {
-        if (lead)
+        if (!SUMMED && lead)
             place(tr.first, s_e[0], s_j[0]);
         any = has_slot(tr.first);
         if (any)
             load_row(tr.first, 0, v);
+        if (SUMMED)
+            place_summed(tr.first, s_e[0], s_j[0]);
     }
     int it = 0;
     for (int64_t t = tr.first; t < tr.end; t += tr.stride, ++it) {
@@ -1882,7 +1966,9 @@ __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
         const bool any_next = tn < tr.end && has_slot(tn);
         if (any_next)
             load_row(tn, 0, vn);
-        if (lead && tn < tr.end)
+        if (SUMMED && tn < tr.end)
+            place_summed(tn, s_e[(it + 1) & 1], s_j[(it + 1) & 1]);
+        else if (lead && tn < tr.end)
             place(tn, s_e[(it + 1) & 1], s_j[(it + 1) & 1]);
 
         for (int base = 0; any;) {
