@@ -161,6 +161,28 @@ LL_DECODE_CASES = [
 ]
 
 
+# Above the decode size, up to 64 layout blocks the cast kernel sums the
+# block offsets itself (no reduce launch); more blocks keep the reduce. With
+# M = 1 every token is a layout block of its own.
+LL_BLOCK_CASES = [
+    # (name, segments, M, K, E, H, cap, drop)
+    ("summed_limit_64_blocks", 64, 1, 40, 64, 256, 64, 0.1),
+    ("reduce_65_blocks", 65, 1, 40, 64, 256, 65, 0.1),
+    ("reduce_600_blocks_m7", 600, 7, 2, 16, 128, 4200, 0.1),
+    ("summed_dsv3_t1024_tight_cap", 8, 128, 8, 256, 7168, 40, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", LL_BLOCK_CASES, ids=[c[0] for c in LL_BLOCK_CASES])
+def test_ll_block_offsets_summed_or_reduced(case):
+    name, nseg, M, K, E, H, cap, drop = case
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    T = nseg * M
+    topk = _topk(rng, T, K, E, drop)
+    over = bool((np.bincount(topk[topk >= 0], minlength=E) > cap).any())
+    check_ll(topk, _x(rng, T, H), E, M, cap, expect_overflow=over)
+
+
 @pytest.mark.parametrize("case", LL_DECODE_CASES, ids=[c[0] for c in LL_DECODE_CASES])
 def test_ll_decode_sizes(case):
     name, nseg, M, K, E, H, cap, drop = case
@@ -169,20 +191,22 @@ def test_ll_decode_sizes(case):
     check_ll(_topk(rng, T, K, E, drop), _x(rng, T, H), E, M, cap)
 
 
-def test_ll_decode_overflow_and_bad_ids_then_reset():
-    """A decode-sized batch of DeepSeek-V3 shape with 2 rows per expert:
-    the capacity bit, the first rows kept; then ids outside [-1, E) in the
-    same workspace: the id bit; then clean ids: the status clears."""
+@pytest.mark.parametrize("T", [128, 1024])
+def test_ll_overflow_and_bad_ids_then_reset(T):
+    """DeepSeek-V3-shaped batches (128 tokens: one launch; 1024 tokens: the
+    cast kernel summing its block offsets) with 2 rows per expert: the
+    capacity bit, the first rows kept; then ids outside [-1, E) in the same
+    workspace: the id bit; then clean ids: the status clears."""
     rng = np.random.default_rng(41)
-    T, K, E, H, M = 128, 8, 256, 7168, 128
+    K, E, H, M = 8, 256, 7168, 128
     topk, x = _topk(rng, T, K, E), _x(rng, T, H)
     r, _ = check_ll(topk, x, E, M, 2, expect_overflow=True)
     bad = topk.copy()
     bad[3, 1] = E
     bad[77, 0] = 1 << 40
     bad[100, 7] = -5
-    check_ll(bad, x, E, M, M, ws=r["ws"])
-    check_ll(topk, x, E, M, M, ws=r["ws"])
+    check_ll(bad, x, E, M, T, ws=r["ws"])
+    check_ll(topk, x, E, M, T, ws=r["ws"])
 
 
 def test_ll_decode_receive_side_local_ids():
