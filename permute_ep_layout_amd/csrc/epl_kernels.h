@@ -1783,9 +1783,9 @@ constexpr int kLLGrid = EPL_LL_GRID;
 // SUMMED: no reduction launch ran before this kernel; the per-block offsets
 // it would have produced are summed here from the layout's per-block counts
 // (nb blocks). A slot's offset is its expert's count over the blocks before
-// the token's block, summed by 16 lanes (lane l takes blocks l, l + 16, ...)
-// and combined with lane shuffles, one token ahead like the lookups it
-// replaces; each (expert, segment) entry of layout_range is summed by one
+// the token's block, summed by 8 lanes of the first wave (lane l takes blocks
+// l, l + 8, ...) and combined with lane shuffles, one token ahead like the
+// lookups it replaces; each (expert, segment) entry of layout_range is summed by one
 // thread; workgroup 0 ORs the layout's error bits into the status word,
 // which layout block 0 has cleared.
 template <int VPT, bool SUMMED>
@@ -1878,26 +1878,28 @@ __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
         se[tid] = pe;
         sj[tid] = pj;
     };
-    // SUMMED: all threads place token t, 16 lanes per slot (slots k0 + tid / 16)
+    // SUMMED: the first wave places token t, 8 lanes per slot (slots k0 +
+    // lane / 8), while the other waves go on to the current token's cast
     auto place_summed = [&](int64_t t, int32_t *se, int32_t *sj) {
-        const int l = tid & 15;
+        if (tid >= kWave)
+            return;
+        const int l = tid & 7;
         const uint32_t tu = (uint32_t)t;   // T * K <= INT32_MAX
         const int64_t b = tu / (uint32_t)B;
-        for (int k0 = 0; k0 < K; k0 += kScatterThreads / 16) {
-            const int k = k0 + tid / 16;
-            if (k >= K)                     // whole 16-lane groups drop out together
+        for (int k0 = 0; k0 < K; k0 += kWave / 8) {
+            const int k = k0 + tid / 8;
+            if (k >= K)                     // whole 8-lane groups drop out together
                 break;
             const int64_t e = topk[t * K + k];
             const bool ok = e >= 0 && e < E;
             const int r = ok && l == 0 ? slot_rank[t * K + k] : 0;
             int part = 0;
             if (ok)
-                for (int64_t bb = l; bb < b; bb += 16)
+                for (int64_t bb = l; bb < b; bb += 8)
                     part += block_count[bb * E + e];
-            part += __shfl_xor(part, 8, 16);
-            part += __shfl_xor(part, 4, 16);
-            part += __shfl_xor(part, 2, 16);
-            part += __shfl_xor(part, 1, 16);
+            part += __shfl_xor(part, 4, 8);
+            part += __shfl_xor(part, 2, 8);
+            part += __shfl_xor(part, 1, 8);
             if (l == 0) {
                 int32_t pe = -1, pj = 0, oi = -1;
                 if (ok) {
