@@ -302,6 +302,27 @@ def test_aligned_blocks_parity(name, a):
     full_parity(workloads.get(name), alignment=a)
 
 
+@pytest.mark.parametrize("split", [False, True])
+def test_largest_alignment(split):
+    """The largest expert alignment the library takes (65536 rows): every
+    expert's block, even one with a single slot, is a whole 65536-row block,
+    so nearly every row of the 9-block buffer is padding marked -1."""
+    print(f"[parity] alignment 65536 split={split}", flush=True)
+    rng = np.random.default_rng(65536)
+    E, R, T, K, H = 8, 2, 100, 4, 256
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    topk[rng.random(topk.shape) < 0.1] = -1
+    x, xs, wt = _mk(topk, H, 3, True)
+    ref = orc().run_all(x, xs, topk, wt, E, R, alignment=65536)
+    r = gpu_dispatch(topk, x, xs, E, R, split=split, alignment=65536)
+    assert epl.epl_status(r["ws"]) == epl.EPL_OK
+    assert ref["total"] == 65536 * int((np.bincount(topk[topk >= 0], minlength=E) > 0).sum())
+    check_layout_and_scatter(r, ref, x, xs)
+    y = gpu_combine(r, r["out"], wt, epl.EPL_OUT_F32)
+    check_combine_f32(y.cpu().numpy(), ref["y"],
+                      combine_bound(ref["expert_out"], ref["output_index"], wt))
+
+
 def test_aligned_split_calls_and_expert_stand_in():
     w = workloads.get("small").with_(num_tokens=900, expert_fn="scale", drop_rate=0.2)
     full_parity(w, split=True, alignment=32)
