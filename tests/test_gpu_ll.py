@@ -158,6 +158,7 @@ LL_DECODE_CASES = [
     ("decode_counter_limit_plus_one_segment", 57, 2, 4, 256, 256, 114, 0.0),
     ("decode_k16_two_passes", 2, 16, 16, 64, 16512, 32, 0.1),
     ("decode_e1000", 2, 64, 6, 1000, 384, 128, 0.0),
+    ("decode_k64_2048_slots", 1, 32, 64, 128, 256, 32, 0.1),
 ]
 
 

@@ -523,6 +523,8 @@ RAGGED = [
     ("decode_t100_dsv3_drop", 100, 8, 256, 32, 7168, True, 0.1),
     ("decode_t37_ragged_parts", 37, 4, 16, 4, 3200, True, 0.2),
     ("decode_t500_h8960", 500, 4, 32, 8, 8960, True, 0.05),
+    # the largest top-k in a one-launch dispatch: 32 tokens x 64 slots
+    ("decode_k64_2048_slots", 32, 64, 128, 16, 256, True, 0.1),
 ]
 
 
