@@ -503,17 +503,45 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(
         lds_barrier();
         if (err)
             atomicOr(&s_err, err);
-        for (int e = tid; e < E; e += kScanThreads) {
-            int run = 0;
-            for (int q = 0; q < P; ++q) {
-                const int v = s_seg[q * E + e];
-                s_seg[q * E + e] = run;
-                run += v;
+        if (E * P <= kScanThreads) {
+            // Exclusive prefix over the P segments of each column, one
+            // segment per thread (thread q * E + e): log2(P) steps of
+            // Hillis-Steele in LDS instead of a serial walk of P dependent
+            // LDS round trips (P is 117 for 8 experts over 117 blocks).
+            const int col = tid, e = col % E, q = col / E;
+            const bool mine = col < E * P;
+            const int v = mine ? s_seg[col] : 0;
+            int incl = v;
+            for (int d = 1; d < P; d *= 2) {
+                const int add = mine && q >= d ? s_seg[col - d * E] : 0;
+                lds_barrier();
+                incl += add;
+                if (mine)
+                    s_seg[col] = incl;
+                lds_barrier();
             }
-            s_cnt[e] = run;
-            if (cnt)
-                cnt[e] = run;
-            ws_counts[e] = run;
+            if (mine) {
+                s_seg[col] = incl - v;
+                if (q == P - 1) {
+                    s_cnt[e] = incl;
+                    if (cnt)
+                        cnt[e] = incl;
+                    ws_counts[e] = incl;
+                }
+            }
+        } else {
+            for (int e = tid; e < E; e += kScanThreads) {
+                int run = 0;
+                for (int q = 0; q < P; ++q) {
+                    const int v = s_seg[q * E + e];
+                    s_seg[q * E + e] = run;
+                    run += v;
+                }
+                s_cnt[e] = run;
+                if (cnt)
+                    cnt[e] = run;
+                ws_counts[e] = run;
+            }
         }
         for (int r = tid; r < RC; r += kScanThreads) {
             const int run = s_rseg[r];
