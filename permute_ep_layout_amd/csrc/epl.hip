@@ -262,7 +262,8 @@ int enqueue_layout(const epl_problem &p, const WsLayout &w, const int64_t *topk,
                            p.ranks_per_node, epl::div_magic(std::max(p.ranks_per_node, 1)), Rn,
                            w.block_tokens, in_rank, vec16, at<int32_t>(ws, w.block_count),
                            at<int32_t>(ws, w.block_rank), at<uint32_t>(ws, w.block_err),
-                           at<int32_t>(ws, w.slot_rank), &at<WsHeader>(ws, 0)->status);
+                           at<int32_t>(ws, w.slot_rank), &at<WsHeader>(ws, 0)->status,
+                           &at<WsHeader>(ws, 0)->dense);
     };
     if (wide_layout(p))
         launch(epl::ep_layout_kernel<epl::kLayoutThreadsWide>, epl::kLayoutThreadsWide);
@@ -383,23 +384,30 @@ struct RowArgs {
 struct ScatterSplit {
     int parts;
     unsigned grid;
+    int grid_dense;     // > 0: workgroups kept when the layout found dense routing
 };
 
 ScatterSplit scatter_split(const epl_problem &p, int64_t row_bytes)
 {
     const int64_t T = p.num_tokens;
     if (T >= epl::kScatterGridFrom)
-        return {1, xcd_grid(T, T)};
-    const int64_t limit =
-        row_bytes >= epl::kScatterLongRowBytes ? epl::kScatterGridLong : epl::kScatterGrid;
-    if (T >= limit)
-        return {1, row_grid(T, limit)};
+        return {1, xcd_grid(T, T), 0};
+    // Long rows: kScatterGrid workgroups, of which the kernel keeps
+    // kScatterGridLong when the layout's first block is densely routed (the
+    // measured best for rows with many destinations; rows with one or two,
+    // as on a receive side, run faster with the whole grid)
+    const bool long_rows = row_bytes >= epl::kScatterLongRowBytes;
+    if (long_rows && T >= epl::kScatterGridLong)
+        return {1, xcd_grid(std::min<int64_t>(T, epl::kScatterGrid), epl::kScatterGrid),
+                epl::kScatterGridLong};
+    if (!long_rows && T >= epl::kScatterGrid)
+        return {1, row_grid(T, epl::kScatterGrid), 0};
     const int64_t nvec = row_bytes / 16;
     const int64_t by_items = (epl::kScatterSmallItems + T - 1) / std::max<int64_t>(T, 1);
     const int64_t by_width = nvec / epl::kScatterThreads;
     const int parts = (int)std::max<int64_t>(
         1, std::min<int64_t>({(int64_t)epl::kScatterMaxParts, by_items, by_width}));
-    return {parts, xcd_grid(T * parts, T * parts)};
+    return {parts, xcd_grid(T * parts, T * parts), 0};
 }
 
 // The scan's work done by the scatter of a dispatch (epl::ScanInScatter):
@@ -499,7 +507,8 @@ void launch_scatter(const epl_problem &p, const WsLayout &w, const RowArgs &ra,
                        p.num_experts, w.block_tokens, alignment_of(p),
                        at<const int32_t>(ws, w.counts), cap, sp.parts,
                        (int64_t)sp.grid < EPL_SCATTER_XCD_BELOW, ra.out, ra.out_scale, m_idx, oi,
-                       &at<WsHeader>(ws, 0)->status, sc);
+                       &at<WsHeader>(ws, 0)->status, sc,
+                       sp.grid_dense > 0 ? &at<WsHeader>(ws, 0)->dense : nullptr, sp.grid_dense);
 }
 
 // The scatter launch. With plan.on (a dispatch whose scan launch was left

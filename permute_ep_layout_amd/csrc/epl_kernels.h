@@ -98,7 +98,11 @@ constexpr int kScanPrefix = 2;   // totals -> expert_start_loc and N
 struct WsHeader {
     uint32_t status;
     int32_t total;
-    int32_t pad[62];
+    // 1 when at least half of the first layout block's slots name an expert
+    // (dense routing, as in a global dispatch), 0 when most are -1 (a receive
+    // side's local ids): the long-row scatter's grid size follows it
+    int32_t dense;
+    int32_t pad[61];
 };
 static_assert(sizeof(WsHeader) == 256, "workspace header is 256 bytes");
 
@@ -171,7 +175,8 @@ __host__ __device__ constexpr size_t layout_lds_bytes(int B, int K, int E, int R
     return sizeof(int32_t) * ((size_t)B * (K + 1) + (size_t)B * K   // keys (padded), ranks
                               + (size_t)waves * E             // running count per wave and expert
                               + (size_t)waves * ((E + 3) / 4) // per-chunk byte counters
-                              + (size_t)RC + 1);              // tokens per rank / node, error flag
+                              + (size_t)RC + 2);              // tokens per rank / node, error flag,
+                                                              // valid slots (block 0)
 }
 
 // One workgroup of THREADS threads (kLayoutThreads, or kLayoutThreadsWide
@@ -182,7 +187,8 @@ __host__ __device__ constexpr size_t layout_lds_bytes(int B, int K, int E, int R
 // a node being G consecutive ranks); block_err[b]; slot_rank[t*K+k] = rank
 // of slot (t,k) among the block's earlier slots of the same expert, or -1
 // for an invalid slot. Block 0 also clears the status word, for the
-// kernels that only OR bits into it later in the chain.
+// kernels that only OR bits into it later in the chain, and stores the
+// dense-routing hint (at least half of its slots valid).
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void ep_layout_kernel(
     const int64_t *__restrict__ topk, int64_t T, int K, int E, int R, int experts_per_rank,
@@ -190,7 +196,7 @@ __global__ __launch_bounds__(THREADS) void ep_layout_kernel(
     bool in_rank_vec16,
     int32_t *__restrict__ block_count, int32_t *__restrict__ block_rank,
     uint32_t *__restrict__ block_err, int32_t *__restrict__ slot_rank,
-    uint32_t *__restrict__ status)
+    uint32_t *__restrict__ status, int32_t *__restrict__ dense)
 {
     constexpr int WAVES = THREADS / kWave;
     extern __shared__ int32_t lds[];
@@ -212,6 +218,7 @@ __global__ __launch_bounds__(THREADS) void ep_layout_kernel(
     int32_t *rank_cnt = reinterpret_cast<int32_t *>(chunk_cnt + WAVES * cwords); // [R+Rn]
     const int RC = R + Rn;
     int32_t *s_err = rank_cnt + RC;                        // [1]
+    int32_t *s_valid = s_err + 1;                          // [1] valid slots (block 0)
 
     const int64_t b = blockIdx.x;
     const int64_t t0 = b * B;
@@ -227,25 +234,38 @@ __global__ __launch_bounds__(THREADS) void ep_layout_kernel(
         chunk_cnt[i] = 0;
     for (int i = tid; i < RC; i += THREADS)
         rank_cnt[i] = 0;
-    if (tid == 0)
+    if (tid == 0) {
         *s_err = 0;
+        *s_valid = 0;
+    }
 
     // Keys of the block's slots, in (token, k) order, packed with the owning
     // rank; bad ids become -1.
     const int64_t *src = topk + t0 * K;
     bool bad = false;
+    int nvalid = 0;
     for (int s = tid; s < ns; s += THREADS) {
         const int64_t e = src[s];
         int packed = -1;
-        if (e >= 0 && e < E)
+        if (e >= 0 && e < E) {
             packed = (int)e | (div_small((uint32_t)e, experts_per_rank, epr_magic) << 16);
-        else if (e != -1)
+            ++nvalid;
+        } else if (e != -1) {
             bad = true;
+        }
         keys[kidx(s)] = packed;
     }
     lds_barrier();
     if (bad)
         atomicOr(reinterpret_cast<uint32_t *>(s_err), 1u);
+    if (b == 0) {
+        // valid slots of block 0: a per-wave sum, one LDS atomic per wave
+        int v = nvalid;
+        for (int m = kWave / 2; m > 0; m /= 2)
+            v += __shfl_xor(v, m);
+        if (lane == 0 && v)
+            atomicAdd(s_valid, v);
+    }
 
     // Rank of each slot among the earlier slots with the same key. Wave w
     // owns a contiguous run of 64-slot chunks and walks it in order. For a
@@ -357,8 +377,10 @@ __global__ __launch_bounds__(THREADS) void ep_layout_kernel(
     lds_barrier();
     if (tid == 0) {
         block_err[b] = (uint32_t)*s_err;
-        if (b == 0)
+        if (b == 0) {
             *status = 0u;
+            *dense = 2 * *s_valid >= ns ? 1 : 0;
+        }
     }
 
     for (int s = tid; s < ns; s += THREADS) {
@@ -684,6 +706,7 @@ __device__ __forceinline__ void layout_scan_block(const LayoutScanArgs &a)
     __shared__ int32_t rank_cnt[kFusedMaxCols];
     __shared__ int s_wave[kFusedWaves];
     __shared__ uint32_t s_err;
+    __shared__ int s_valid;
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid / kWave;
@@ -696,8 +719,10 @@ __device__ __forceinline__ void layout_scan_block(const LayoutScanArgs &a)
         (&chunk_cnt[0][0])[i] = 0u;
     for (int i = tid; i < RC; i += kFusedThreads)
         rank_cnt[i] = 0;
-    if (tid == 0)
+    if (tid == 0) {
         s_err = 0u;
+        s_valid = 0;
+    }
     lds_barrier();
 
     // Keys of this lane's slots, one per chunk of the wave's run.
@@ -719,6 +744,14 @@ __device__ __forceinline__ void layout_scan_block(const LayoutScanArgs &a)
     }
     if (bad)
         atomicOr(&s_err, 1u);
+    {
+        int v = 0;
+#pragma unroll
+        for (int i = 0; i < kFusedChunksPerWave; ++i)
+            v += __popcll(wave_ballot(key[i] >= 0));
+        if (lane == 0 && v)
+            atomicAdd(&s_valid, v);
+    }
 
     // In-wave ranks, chunk by chunk in order (see ep_layout_kernel).
     {
@@ -828,9 +861,11 @@ __device__ __forceinline__ void layout_scan_block(const LayoutScanArgs &a)
                 *total_out = incl;
         }
     }
-    if (tid == kFusedThreads - 1)
+    if (tid == kFusedThreads - 1) {
         hdr->status = (s_err ? kStatusBadExpert : 0u) |
                       (a.capacity >= 0 && incl > a.capacity ? kStatusCapacity : 0u);
+        hdr->dense = 2 * s_valid >= ns ? 1 : 0;
+    }
 
     // Global rank of every slot.
 #pragma unroll
@@ -857,12 +892,15 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 // dispatcher starts a new workgroup as soon as one retires, which balances
 // better than striding). Scatter: also one per token from
 // kScatterGridFrom tokens on; below that, kScatterGrid workgroups striding
-// over the tokens, which measured faster at a few thousand tokens, and
-// kScatterGridLong for rows of at least kScatterLongRowBytes. Below
-// kScatterGridFrom tokens the batch (at most ~120 MB at hidden 7168) stays in
-// the Infinity Cache between steps, so the writes bound the kernel, and with
-// 14 KB rows fewer rows in flight write more efficiently (4096 tokens of
-// hidden 7168: 96.7 -> 93.2 us, five runs each); with 7-8 KB rows 512 and
+// over the tokens, which measured faster at a few thousand tokens, of which
+// only kScatterGridLong work for rows of at least kScatterLongRowBytes when
+// the layout found dense routing (WsHeader::dense). Below kScatterGridFrom
+// tokens the batch (at most ~120 MB at hidden 7168) stays in the Infinity
+// Cache between steps, so the writes bound the kernel, and with 14 KB rows of
+// eight destinations fewer rows in flight write more efficiently (4096
+// tokens of hidden 7168: 96.7 -> 93.2 us, five runs each), while rows of one
+// or two destinations (a receive side) want more tokens in flight (6000
+// tokens: step 130 -> 108 us with the whole grid); with 7-8 KB rows 512 and
 // 1024 workgroups tie.
 // Decode-sized batches: column parts per row so that about kScatterSmallItems
 // (token, part) items exist, each part at least one pass of the workgroup
@@ -896,7 +934,8 @@ constexpr int64_t kYNtBytes = EPL_Y_NT_BYTES;
 #endif
 constexpr int kNumXcd = 8;   // MI355X: 8 XCDs, workgroup i runs on XCD i % 8
 
-// Tokens of one workgroup of a grid-stride row kernel: first, first + stride,
+// Tokens of one workgroup of a grid-stride row kernel of G active workgroups
+// (the launch's grid unless the kernel retires some): first, first + stride,
 // ... below end. With the XCD-aware mapping (xcd_ranges, and a grid that is a
 // multiple of 8) each XCD owns one contiguous range of ceil(T / 8) tokens, so
 // rows written for neighbouring tokens (the neighbouring rows of an
@@ -910,9 +949,10 @@ struct TokenRange {
     int64_t first, stride, end;
 };
 
-__device__ __forceinline__ TokenRange token_range(int64_t T, bool xcd_ranges = true)
+__device__ __forceinline__ TokenRange token_range(int64_t T, bool xcd_ranges = true,
+                                                  int64_t G = gridDim.x)
 {
-    const int64_t G = gridDim.x, w = blockIdx.x;
+    const int64_t w = blockIdx.x;
     if (xcd_ranges && EPL_XCD_MAP && G % kNumXcd == 0 && G >= kNumXcd) {
         const int64_t per = (T + kNumXcd - 1) / kNumXcd;
         const int64_t xcd = w % kNumXcd;
@@ -1017,9 +1057,19 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
     int K, int E, int B, int alignment, const int32_t *__restrict__ counts, int64_t capacity,
     int parts_arg, bool xcd_ranges, uint8_t *__restrict__ out, uint32_t *__restrict__ out_scale,
     int32_t *__restrict__ m_indices, int32_t *__restrict__ output_index,
-    uint32_t *__restrict__ status, ScanInScatter sc)
+    uint32_t *__restrict__ status, ScanInScatter sc, const int32_t *__restrict__ dense,
+    int grid_dense)
 {
     static_assert(!(SPLIT && OFFSETS), "the scan-in-scatter launch has whole-token items");
+    // Active workgroups: the grid, or its first grid_dense workgroups when the
+    // layout found dense routing (`dense` null: always the grid). Rows with
+    // many destinations write best with fewer of them in flight, rows with
+    // one or two need more tokens in flight; the results are the same.
+    int G = gridDim.x;
+    if (dense != nullptr && *dense == 1)
+        G = grid_dense;
+    if ((int)blockIdx.x >= G)
+        return;
     __shared__ int64_t s_row[2][kMaxTopk];
     extern __shared__ __align__(16) int32_t s_off[];   // OFFSETS only, see below
     const int tid = threadIdx.x;
@@ -1028,7 +1078,7 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
     const int pvec = SPLIT ? (nvec + parts - 1) / parts : nvec;   // 16-byte vectors per part
     // Work items: (token, column part) pairs, item i = token i / parts, part
     // i % parts (parts = 1 except for batches too small to fill the GPU).
-    const TokenRange tr = token_range(T * parts, xcd_ranges);
+    const TokenRange tr = token_range(T * parts, xcd_ranges, G);
     const int64_t step = tr.stride, i_end = tr.end;
     const bool lead = tid < K;
     auto token_of = [=](int64_t item) { return SPLIT ? item / parts : item; };
@@ -1135,7 +1185,7 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
         // Per-rank and per-node totals (workgroup 1, or 0 in a one-workgroup
         // grid): thread (r, g) sums column r over the g-th of P block segments
         // (16 loads in flight per pass), the P partial sums meet in LDS.
-        const bool rank_wg = blockIdx.x == min(1u, gridDim.x - 1);
+        const bool rank_wg = (int)blockIdx.x == min(1, G - 1);
         const int RC = sc.R + sc.Rn;
         const int P = RC < kScatterThreads ? kScatterThreads / RC : 1;
         if (rank_wg) {
@@ -1230,7 +1280,7 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
     // Padding rows of the aligned blocks: between an expert's last row and
     // the end of its block, marked -1 (workgroup w takes experts w, w + G, ...).
     if (alignment > 1) {
-        for (int e = blockIdx.x; e < E; e += gridDim.x) {
+        for (int e = blockIdx.x; e < E; e += G) {
             const int64_t c = expert_count(e);
             const int64_t p0 = (int64_t)expert_start(e) + c;
             const int64_t p1 = (int64_t)expert_start(e) + (c + alignment - 1) / alignment * alignment;
@@ -1409,6 +1459,7 @@ __device__ __forceinline__ void decode_counts_block(const LayoutScanArgs &a)
     __shared__ int32_t s_rc[kFusedMaxCols];
     __shared__ int s_wave[kFusedWaves];
     __shared__ uint32_t s_err;
+    __shared__ int s_valid;
     const int tid = threadIdx.x;
     const int K = a.K, E = a.E, R = a.R, Rn = a.Rn;
     const int RC = R + Rn;
@@ -1423,19 +1474,25 @@ __device__ __forceinline__ void decode_counts_block(const LayoutScanArgs &a)
         s_hist[e] = 0;
     for (int r = tid; r < RC; r += kFusedThreads)
         s_rc[r] = 0;
-    if (tid == 0)
+    if (tid == 0) {
         s_err = 0u;
+        s_valid = 0;
+    }
     lds_barrier();
     bool bad = false;
+    int nvalid = 0;
 #pragma unroll
     for (int i = 0; i < kFusedMaxSlots / kFusedThreads; ++i) {
         const int64_t e = e_in[i];
         bad |= (e < -1 || e >= E);
         if (e >= 0 && e < E)
             atomicAdd(&s_hist[e], 1);
+        nvalid += __popcll(wave_ballot(e >= 0 && e < E));
     }
     if (bad)
         atomicOr(&s_err, 1u);
+    if (lane_id() == 0 && nvalid)
+        atomicAdd(&s_valid, nvalid);
     // Tokens per rank and per node: one thread per token, a token counted
     // once per rank (node) that any of its valid slots goes to.
     for (int64_t t = tid; t < a.T; t += kFusedThreads) {
@@ -1496,6 +1553,7 @@ __device__ __forceinline__ void decode_counts_block(const LayoutScanArgs &a)
         if (a.total_out)
             *a.total_out = incl;
         a.hdr->status = (s_err ? kStatusBadExpert : 0u) | (incl > a.capacity ? kStatusCapacity : 0u);
+        a.hdr->dense = 2 * s_valid >= ns ? 1 : 0;
     }
 }
 

@@ -576,6 +576,30 @@ def test_tokens_per_node(case):
         assert torch.equal(r["per_node"], r["per_rank"])
 
 
+@pytest.mark.parametrize("T,split", [(700, False), (3000, False), (6000, True)])
+def test_receive_side_mid_sizes(T, split):
+    """Receive-side batches of a few thousand tokens (local ids, about one
+    valid slot in eight): the long-row scatter keeps its whole grid for such
+    sparse routing; full parity, fused and split."""
+    print(f"[parity] receive side T={T} split={split}", flush=True)
+    full_parity(workloads.get("dsv3_recv").with_(num_tokens=T), split=split)
+
+
+@pytest.mark.parametrize("dense_first", [True, False])
+def test_dense_hint_from_an_unrepresentative_first_block(dense_first):
+    """The scatter's grid follows the routing density of the layout's first
+    block only; a batch whose first block is dense and the rest sparse (or
+    the reverse) must still be placed exactly, whichever grid runs."""
+    print(f"[parity] density hint, dense first block={dense_first}", flush=True)
+    rng = np.random.default_rng(77 if dense_first else 78)
+    T, K, E, R, H = 3000, 8, 64, 8, 7168
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    sparse = rng.random(topk.shape) < 0.9
+    head = np.arange(T)[:, None] < 200
+    topk[(sparse & ~head) if dense_first else (sparse & head)] = -1
+    _edge(topk, E, R, H=H, scales=True, seed=5)
+
+
 def test_receive_side_is_the_global_buffer_restricted():
     """The batch of rank 3 with local ids, dispatched on the GPU, reproduces
     the stretch of rank 3's experts in the GPU's global buffer."""
