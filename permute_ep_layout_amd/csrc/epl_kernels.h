@@ -98,13 +98,20 @@ constexpr int kScanPrefix = 2;   // totals -> expert_start_loc and N
 struct WsHeader {
     uint32_t status;
     int32_t total;
-    // 1 when at least half of the first layout block's slots name an expert
+    // 1 when at least half of the batch's first 64 slots name an expert
     // (dense routing, as in a global dispatch), 0 when most are -1 (a receive
     // side's local ids): the long-row scatter's grid size follows it
     int32_t dense;
     int32_t pad[61];
 };
 static_assert(sizeof(WsHeader) == 256, "workspace header is 256 bytes");
+
+// The dense-routing hint from the validity ballot of the first min(ns, 64)
+// slots (bit i: slot i names an expert).
+__device__ __forceinline__ int32_t dense_sample(uint64_t valid, int ns)
+{
+    return 2 * __popcll(valid) >= min(ns, 64) ? 1 : 0;
+}
 
 __device__ __forceinline__ uint64_t wave_ballot(bool pred)
 {
@@ -175,8 +182,7 @@ __host__ __device__ constexpr size_t layout_lds_bytes(int B, int K, int E, int R
     return sizeof(int32_t) * ((size_t)B * (K + 1) + (size_t)B * K   // keys (padded), ranks
                               + (size_t)waves * E             // running count per wave and expert
                               + (size_t)waves * ((E + 3) / 4) // per-chunk byte counters
-                              + (size_t)RC + 2);              // tokens per rank / node, error flag,
-                                                              // valid slots (block 0)
+                              + (size_t)RC + 1);              // tokens per rank / node, error flag
 }
 
 // One workgroup of THREADS threads (kLayoutThreads, or kLayoutThreadsWide
@@ -188,7 +194,7 @@ __host__ __device__ constexpr size_t layout_lds_bytes(int B, int K, int E, int R
 // of slot (t,k) among the block's earlier slots of the same expert, or -1
 // for an invalid slot. Block 0 also clears the status word, for the
 // kernels that only OR bits into it later in the chain, and stores the
-// dense-routing hint (at least half of its slots valid).
+// dense-routing hint (dense_sample).
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void ep_layout_kernel(
     const int64_t *__restrict__ topk, int64_t T, int K, int E, int R, int experts_per_rank,
@@ -218,7 +224,6 @@ __global__ __launch_bounds__(THREADS) void ep_layout_kernel(
     int32_t *rank_cnt = reinterpret_cast<int32_t *>(chunk_cnt + WAVES * cwords); // [R+Rn]
     const int RC = R + Rn;
     int32_t *s_err = rank_cnt + RC;                        // [1]
-    int32_t *s_valid = s_err + 1;                          // [1] valid slots (block 0)
 
     const int64_t b = blockIdx.x;
     const int64_t t0 = b * B;
@@ -234,38 +239,25 @@ __global__ __launch_bounds__(THREADS) void ep_layout_kernel(
         chunk_cnt[i] = 0;
     for (int i = tid; i < RC; i += THREADS)
         rank_cnt[i] = 0;
-    if (tid == 0) {
+    if (tid == 0)
         *s_err = 0;
-        *s_valid = 0;
-    }
 
     // Keys of the block's slots, in (token, k) order, packed with the owning
     // rank; bad ids become -1.
     const int64_t *src = topk + t0 * K;
     bool bad = false;
-    int nvalid = 0;
     for (int s = tid; s < ns; s += THREADS) {
         const int64_t e = src[s];
         int packed = -1;
-        if (e >= 0 && e < E) {
+        if (e >= 0 && e < E)
             packed = (int)e | (div_small((uint32_t)e, experts_per_rank, epr_magic) << 16);
-            ++nvalid;
-        } else if (e != -1) {
+        else if (e != -1)
             bad = true;
-        }
         keys[kidx(s)] = packed;
     }
     lds_barrier();
     if (bad)
         atomicOr(reinterpret_cast<uint32_t *>(s_err), 1u);
-    if (b == 0) {
-        // valid slots of block 0: a per-wave sum, one LDS atomic per wave
-        int v = nvalid;
-        for (int m = kWave / 2; m > 0; m /= 2)
-            v += __shfl_xor(v, m);
-        if (lane == 0 && v)
-            atomicAdd(s_valid, v);
-    }
 
     // Rank of each slot among the earlier slots with the same key. Wave w
     // owns a contiguous run of 64-slot chunks and walks it in order. For a
@@ -377,10 +369,14 @@ __global__ __launch_bounds__(THREADS) void ep_layout_kernel(
     lds_barrier();
     if (tid == 0) {
         block_err[b] = (uint32_t)*s_err;
-        if (b == 0) {
+        if (b == 0)
             *status = 0u;
-            *dense = 2 * *s_valid >= ns ? 1 : 0;
-        }
+    }
+    if (b == 0 && tid < kWave) {
+        // the dense-routing hint from the batch's first 64 slots
+        const uint64_t m = wave_ballot(tid < ns && keys[kidx(tid)] >= 0);
+        if (tid == 0)
+            *dense = dense_sample(m, ns);
     }
 
     for (int s = tid; s < ns; s += THREADS) {
@@ -706,7 +702,6 @@ __device__ __forceinline__ void layout_scan_block(const LayoutScanArgs &a)
     __shared__ int32_t rank_cnt[kFusedMaxCols];
     __shared__ int s_wave[kFusedWaves];
     __shared__ uint32_t s_err;
-    __shared__ int s_valid;
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid / kWave;
@@ -719,10 +714,8 @@ __device__ __forceinline__ void layout_scan_block(const LayoutScanArgs &a)
         (&chunk_cnt[0][0])[i] = 0u;
     for (int i = tid; i < RC; i += kFusedThreads)
         rank_cnt[i] = 0;
-    if (tid == 0) {
+    if (tid == 0)
         s_err = 0u;
-        s_valid = 0;
-    }
     lds_barrier();
 
     // Keys of this lane's slots, one per chunk of the wave's run.
@@ -744,13 +737,11 @@ __device__ __forceinline__ void layout_scan_block(const LayoutScanArgs &a)
     }
     if (bad)
         atomicOr(&s_err, 1u);
-    {
-        int v = 0;
-#pragma unroll
-        for (int i = 0; i < kFusedChunksPerWave; ++i)
-            v += __popcll(wave_ballot(key[i] >= 0));
-        if (lane == 0 && v)
-            atomicAdd(&s_valid, v);
+    if (wave == 0) {
+        // wave 0's first chunk is the batch's first 64 slots
+        const uint64_t m = wave_ballot(key[0] >= 0);
+        if (lane == 0)
+            hdr->dense = dense_sample(m, ns);
     }
 
     // In-wave ranks, chunk by chunk in order (see ep_layout_kernel).
@@ -861,11 +852,9 @@ __device__ __forceinline__ void layout_scan_block(const LayoutScanArgs &a)
                 *total_out = incl;
         }
     }
-    if (tid == kFusedThreads - 1) {
+    if (tid == kFusedThreads - 1)
         hdr->status = (s_err ? kStatusBadExpert : 0u) |
                       (a.capacity >= 0 && incl > a.capacity ? kStatusCapacity : 0u);
-        hdr->dense = 2 * s_valid >= ns ? 1 : 0;
-    }
 
     // Global rank of every slot.
 #pragma unroll
@@ -1459,7 +1448,6 @@ __device__ __forceinline__ void decode_counts_block(const LayoutScanArgs &a)
     __shared__ int32_t s_rc[kFusedMaxCols];
     __shared__ int s_wave[kFusedWaves];
     __shared__ uint32_t s_err;
-    __shared__ int s_valid;
     const int tid = threadIdx.x;
     const int K = a.K, E = a.E, R = a.R, Rn = a.Rn;
     const int RC = R + Rn;
@@ -1474,25 +1462,25 @@ __device__ __forceinline__ void decode_counts_block(const LayoutScanArgs &a)
         s_hist[e] = 0;
     for (int r = tid; r < RC; r += kFusedThreads)
         s_rc[r] = 0;
-    if (tid == 0) {
+    if (tid == 0)
         s_err = 0u;
-        s_valid = 0;
-    }
     lds_barrier();
     bool bad = false;
-    int nvalid = 0;
 #pragma unroll
     for (int i = 0; i < kFusedMaxSlots / kFusedThreads; ++i) {
         const int64_t e = e_in[i];
         bad |= (e < -1 || e >= E);
         if (e >= 0 && e < E)
             atomicAdd(&s_hist[e], 1);
-        nvalid += __popcll(wave_ballot(e >= 0 && e < E));
     }
     if (bad)
         atomicOr(&s_err, 1u);
-    if (lane_id() == 0 && nvalid)
-        atomicAdd(&s_valid, nvalid);
+    if (tid < kWave) {
+        // the dense-routing hint from the first 64 slots (wave 0's e_in[0])
+        const uint64_t m = wave_ballot(e_in[0] >= 0 && e_in[0] < E);
+        if (tid == 0)
+            a.hdr->dense = dense_sample(m, ns);
+    }
     // Tokens per rank and per node: one thread per token, a token counted
     // once per rank (node) that any of its valid slots goes to.
     for (int64_t t = tid; t < a.T; t += kFusedThreads) {
@@ -1553,7 +1541,6 @@ __device__ __forceinline__ void decode_counts_block(const LayoutScanArgs &a)
         if (a.total_out)
             *a.total_out = incl;
         a.hdr->status = (s_err ? kStatusBadExpert : 0u) | (incl > a.capacity ? kStatusCapacity : 0u);
-        a.hdr->dense = 2 * s_valid >= ns ? 1 : 0;
     }
 }
 

@@ -587,8 +587,8 @@ def test_receive_side_mid_sizes(T, split):
 
 @pytest.mark.parametrize("dense_first", [True, False])
 def test_dense_hint_from_an_unrepresentative_first_block(dense_first):
-    """The scatter's grid follows the routing density of the layout's first
-    block only; a batch whose first block is dense and the rest sparse (or
+    """The scatter's grid follows the routing density of the batch's first
+    slots only; a batch whose first tokens are dense and the rest sparse (or
     the reverse) must still be placed exactly, whichever grid runs."""
     print(f"[parity] density hint, dense first block={dense_first}", flush=True)
     rng = np.random.default_rng(77 if dense_first else 78)
