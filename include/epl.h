@@ -290,7 +290,7 @@ int epl_dispatch_fp8(const epl_problem *p, const int64_t *topk_idx, const uint8_
  * (256-byte aligned); the call runs on `stream` the layout and the
  * cast-and-place kernel (with a per-block reduction between them when the
  * layout has more than 64 blocks), or, for a decode-sized batch (T * K <=
- * 2048 and (T / M) * E <= 14336), one kernel that does it all, always with
+ * 4096 and (T / M) * E <= 14336), one kernel that does it all, always with
  * the same results. Receive side: pass local expert ids (-1 for other ranks'
  * experts) and E = the local expert count. */
 size_t epl_ll_workspace_bytes(const epl_problem *p, int32_t tokens_per_segment);

@@ -653,7 +653,7 @@ bool ll_ok(const epl_problem *p, int32_t M, int64_t cap)
     return (int64_t)p->num_experts * cap <= (int64_t)INT32_MAX;
 }
 
-// Decode-sized low-latency dispatches (at most kFusedMaxSlots slots, and
+// Decode-sized low-latency dispatches (at most kLLDecodeMaxSlots slots, and
 // at most kLLDecodeMaxCounts (segment, expert) counters, whose 56 KB of LDS
 // keep the workgroup within 64 KB) in one launch (epl::ep_ll_decode_kernel).
 // 0 turns it off (layout, reduction and cast launches).
@@ -665,7 +665,7 @@ constexpr int64_t kLLDecodeMaxCounts = 14336;
 bool ll_decode(const epl_problem &p, int32_t M)
 {
     return EPL_LL_DECODE && p.num_tokens >= 1 &&
-           p.num_tokens * (int64_t)p.num_topk <= epl::kFusedMaxSlots &&
+           p.num_tokens * (int64_t)p.num_topk <= epl::kLLDecodeMaxSlots &&
            (p.num_tokens / M) * (int64_t)p.num_experts <= kLLDecodeMaxCounts;
 }
 
@@ -1003,8 +1003,11 @@ int epl_ll_dispatch(const epl_problem *p, int32_t tokens_per_segment, int64_t ro
                             p->num_experts, M, cap, out, out_scale, recv_count, src_info,
                             layout_range, output_index, &at<WsHeader>(workspace, 0)->status};
         const size_t lds = sizeof(int32_t) * (size_t)(p->num_tokens / M) * p->num_experts;
-        hipLaunchKernelGGL(epl::ep_ll_decode_kernel, dim3((unsigned)(1 + p->num_tokens)),
-                           dim3(epl::kFusedThreads), lds, s, a);
+        const bool wide = p->num_tokens * (int64_t)p->num_topk > epl::kFusedMaxSlots;
+        auto kernel = wide ? epl::ep_ll_decode_kernel<epl::kLLDecodeMaxSlots / epl::kFusedThreads>
+                           : epl::ep_ll_decode_kernel<epl::kFusedMaxSlots / epl::kFusedThreads>;
+        hipLaunchKernelGGL(kernel, dim3((unsigned)(1 + p->num_tokens)), dim3(epl::kFusedThreads),
+                           lds, s, a);
         return launch_status();
     }
     int rc = enqueue_layout(*p, w, topk_idx, nullptr, workspace, s);

@@ -653,7 +653,11 @@ constexpr int kFusedWaves = kFusedThreads / kWave;
 // two launches up to 2048 slots (dispatch 2.1-2.7 us faster at 64-256
 // tokens), ties at 4096 and loses beyond (8192 slots: +4 us; 12288 slots
 // at hidden 4096: layout 11 -> 30 us), as the waves walk their chunks in turn.
-constexpr int kFusedMaxSlots = 2048;
+#ifndef EPL_FUSED_MAX_SLOTS
+#define EPL_FUSED_MAX_SLOTS 2048
+#endif
+constexpr int kFusedMaxSlots = EPL_FUSED_MAX_SLOTS;
+static_assert(kFusedMaxSlots % kFusedThreads == 0, "whole slots per thread");
 constexpr int kFusedChunksPerWave = kFusedMaxSlots / kWave / kFusedWaves;
 constexpr int kFusedMaxExperts = 256;
 constexpr int kFusedMaxCols = 256;
@@ -2106,6 +2110,13 @@ struct LLArgs {
     uint32_t *status;
 };
 
+// Slots of a low-latency batch dispatched in one launch, at most: twice the
+// bf16 decode limit, since the cast (one row in, K rows out, all by one
+// workgroup) gains more from the one launch than the bf16 copy does (512
+// DeepSeek-V3-shaped tokens: step 39.0 -> 30.9 us, where the bf16 dispatch
+// got slower at 4096 slots).
+constexpr int kLLDecodeMaxSlots = 2 * kFusedMaxSlots;
+
 // Workgroup 0 of ep_ll_decode_kernel: slots per (source segment, expert) in
 // LDS ([T / M][E] words of dynamic LDS), then per expert a running sum over
 // the segments clipped to the rectangle gives layout_range and recv_count.
@@ -2155,8 +2166,9 @@ __device__ __forceinline__ void ll_decode_counts_block(const LLArgs &a)
         *a.status = s_err;
 }
 
-// The low-latency dispatch of a decode-sized batch (at most kFusedMaxSlots
-// slots) in one launch of 1 + T workgroups of kFusedThreads threads, with the
+// The low-latency dispatch of a decode-sized batch (at most kLLDecodeMaxSlots
+// slots; SLOTS_PER_THREAD = 2 up to 2048 slots, 4 up to 4096) in one launch
+// of 1 + T workgroups of kFusedThreads threads, with the
 // outputs of the layout, reduction and ep_ll_scatter_kernel launches.
 // Workgroup 0 writes recv_count, layout_range and the status word
 // (ll_decode_counts_block). Workgroup 1 + t issues token t's row loads, then
@@ -2165,13 +2177,14 @@ __device__ __forceinline__ void ll_decode_counts_block(const LLArgs &a)
 // slot's row j in its expert's block. It stores output_index and src_info,
 // casts the row (16 values per thread, a 128-column group over 8 lanes, as in
 // ep_ll_scatter_kernel) and stores the codes and scales to every placed row.
+template <int SLOTS_PER_THREAD>
 __global__ __launch_bounds__(kFusedThreads) void ep_ll_decode_kernel(LLArgs a)
 {
     if (blockIdx.x == 0) {
         ll_decode_counts_block(a);
         return;
     }
-    constexpr int kSlotsPerThread = kFusedMaxSlots / kFusedThreads;
+    constexpr int kSlotsPerThread = SLOTS_PER_THREAD;
     __shared__ int32_t s_tok[kMaxTopk];                  // the token's expert ids (-1: none)
     __shared__ int32_t s_same[kMaxTopk][kFusedWaves];    // per wave: earlier slots of the expert
     __shared__ int32_t s_e[kMaxTopk];                    // expert of each placed slot, -1 if none

@@ -145,15 +145,18 @@ def test_ll_shapes(case):
     check_ll(topk, _x(rng, T, H), E, M, cap)
 
 
-# Decode-sized batches (at most 2048 slots and at most 14336 (segment,
-# expert) counters) are dispatched in one launch; these cases sit on both
-# sides of those limits, and one has rows longer than a workgroup's pass.
+# Decode-sized batches (at most 4096 slots and at most 14336 (segment,
+# expert) counters) are dispatched in one launch, with 2 slots per thread up
+# to 2048 slots and 4 above; these cases sit on both sides of those limits,
+# and one has rows longer than a workgroup's pass.
 LL_DECODE_CASES = [
     # (name, segments, M, K, E, H, cap, drop)
     ("decode_dsv3_t128", 1, 128, 8, 256, 7168, 128, 0.0),
     ("decode_dsv3_8_segments", 8, 32, 8, 256, 7168, 256, 0.05),
     ("decode_slot_limit_2048", 2, 128, 8, 256, 1024, 256, 0.1),
-    ("decode_slot_limit_plus_one_token", 1, 257, 8, 256, 1024, 257, 0.1),
+    ("decode_wide_2056_slots", 1, 257, 8, 256, 1024, 257, 0.1),
+    ("decode_wide_limit_4096", 4, 128, 8, 256, 7168, 512, 0.05),
+    ("decode_wide_limit_plus_one_token", 1, 513, 8, 256, 1024, 513, 0.1),
     ("decode_counter_limit_14336", 56, 2, 4, 256, 256, 112, 0.0),
     ("decode_counter_limit_plus_one_segment", 57, 2, 4, 256, 256, 114, 0.0),
     ("decode_k16_two_passes", 2, 16, 16, 64, 16512, 32, 0.1),
