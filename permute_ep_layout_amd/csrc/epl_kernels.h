@@ -30,7 +30,10 @@
 // between layout and scatter. Decode-sized batches (at most 2048 slots) take
 // ep_layout_scan_kernel in the layout / scan calls (one workgroup, one
 // block) and ep_dispatch_decode_kernel in a dispatch (one launch, each token
-// placed by its own workgroup from the routing of all slots).
+// placed by its own workgroup from the routing of all slots); the
+// low-latency dispatch does the same up to 4096 slots (ep_ll_decode_kernel)
+// and, up to 64 layout blocks, sums its block offsets in the cast kernel
+// instead of running the scan's reduction.
 #pragma once
 
 #include <hip/hip_runtime.h>
