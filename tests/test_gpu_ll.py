@@ -225,6 +225,30 @@ def test_ll_decode_receive_side_local_ids():
     check_ll(local, np.ascontiguousarray(inp["x"][:T]), El, T, T)
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_ll_random_shape_sweep(seed):
+    """24 seeded random low-latency problems against the oracle: segment
+    sizes and counts that land in the one-launch kernel (2 or 4 slots per
+    thread), the cast kernel summing its block offsets, or the reduce launch;
+    top-k up to 16, drops, receive-side-like sparse ids, rectangles from
+    tight (overflowing) to the worst case, hidden widths from 128 to 8192."""
+    rng = np.random.default_rng(11000 + seed)
+    K = int(rng.integers(1, 17))
+    E = int(rng.choice([K, 16, 64, 256]))
+    M = int(rng.choice([1, 7, 32, 128, 200]))
+    nseg = int(np.exp(rng.uniform(0, np.log(max(2, 6000 // M)))))
+    T = M * max(1, nseg)
+    H = 128 * int(rng.integers(1, 65))
+    drop = float(rng.choice([0.0, 0.1, 0.85]))
+    worst = M * (T // M)
+    cap = int(rng.choice([worst, max(1, worst // 4), max(1, T * K // max(E, 1) // 2)]))
+    print(f"[ll] sweep seed={seed} T={T} M={M} K={K} E={E} H={H} cap={cap} drop={drop}",
+          flush=True)
+    topk = _topk(rng, T, K, E, drop) if K <= E else rng.integers(-1, E, (T, K)).astype(np.int64)
+    over = bool((np.bincount(topk[topk >= 0], minlength=E) > cap).any())
+    check_ll(topk, _x(rng, T, H), E, M, cap, expect_overflow=over, untouched_sample=16)
+
+
 def test_ll_receive_side_local_ids():
     """One receiver's rectangle: local ids (8 experts), -1 elsewhere."""
     w = workloads.get("dsv3_ll")
