@@ -678,6 +678,10 @@ bool ll_decode(const epl_problem &p, int32_t M)
 #define EPL_LL_SUMMED_BLOCKS 64
 #endif
 
+#ifndef EPL_LL_MAX_PARTS
+#define EPL_LL_MAX_PARTS 8
+#endif
+
 bool ll_summed(const WsLayout &w)
 {
     return w.num_blocks >= 1 && w.num_blocks <= EPL_LL_SUMMED_BLOCKS;
@@ -689,13 +693,20 @@ void launch_ll_scatter(const epl_problem &p, const WsLayout &w, int32_t M, int64
                        float *out_scale, int32_t *recv_count, int32_t *src_info,
                        int32_t *layout_range, int32_t *output_index, hipStream_t s)
 {
-    // kLLGrid workgroups striding over the tokens (fewer with fewer tokens),
+    // kLLGrid workgroups striding over the items (fewer with fewer items),
     // and at least enough for the recv_count / layout_range entries (also
-    // when there are no tokens)
+    // when there are no tokens). With fewer tokens than kLLGrid each row is
+    // cut into column parts (whole 128-column groups, at most
+    // EPL_LL_MAX_PARTS), so that about kLLGrid (token, part) items exist.
+    int parts = 1;
+    if (p.num_tokens > 0 && p.num_tokens < epl::kLLGrid)
+        parts = (int)std::min<int64_t>({(int64_t)EPL_LL_MAX_PARTS, p.hidden / 128,
+                                        (epl::kLLGrid + p.num_tokens - 1) / p.num_tokens});
+    const int64_t items = p.num_tokens * parts;
     const int64_t entries = (int64_t)p.num_experts * std::max<int64_t>(1, p.num_tokens / M);
     const int64_t need = (entries + epl::kScatterThreads - 1) / epl::kScatterThreads;
     const unsigned grid =
-        xcd_grid(std::max<int64_t>(std::min<int64_t>(p.num_tokens, epl::kLLGrid), need), 1 << 30);
+        xcd_grid(std::max<int64_t>(std::min<int64_t>(items, epl::kLLGrid), need), 1 << 30);
     auto kernel = ll_summed(w) ? epl::ep_ll_scatter_kernel<VPT, true>
                                : epl::ep_ll_scatter_kernel<VPT, false>;
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(epl::kScatterThreads), 0, s,
@@ -704,7 +715,7 @@ void launch_ll_scatter(const epl_problem &p, const WsLayout &w, int32_t M, int64
                        p.num_tokens, p.num_topk, p.num_experts, w.block_tokens, M, cap, out,
                        out_scale, recv_count, src_info, layout_range, output_index,
                        &at<WsHeader>(ws, 0)->status, at<const int32_t>(ws, w.block_count),
-                       at<const uint32_t>(ws, w.block_err), w.num_blocks);
+                       at<const uint32_t>(ws, w.block_err), w.num_blocks, parts);
 }
 
 // The workspace of epl_dispatch_static: a device array that the library

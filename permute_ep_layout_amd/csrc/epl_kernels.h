@@ -1839,10 +1839,11 @@ constexpr int kLLGrid = EPL_LL_GRID;
 // order, j = block offset + in-block rank (the same per-expert position as
 // the prefix-sum layout, without the prefix over experts).
 //
-// Workgroups stride over the tokens (XCD-aware ranges), one token ahead:
-// while a token is cast and stored, its workgroup already loads the next
-// token's row (if that token selects any expert) and the first K threads
-// place the next token's slots (output_index = e * cap + j, src_info[row] =
+// Workgroups stride over the tokens (XCD-aware ranges) -- or, with fewer
+// tokens than the grid, over (token, column part) items, a part being a run
+// of whole 128-column groups -- one item ahead: while an item is cast and
+// stored, its workgroup already loads the next item's row (if that token
+// selects any expert) and the first K threads place the next token's slots (output_index = e * cap + j, src_info[row] =
 // t mod M, or -1 past the rectangle with the capacity bit in the status
 // word); the placements reach the other threads through a double-buffered
 // LDS table and one LDS-only barrier per token. A thread owns 16
@@ -1876,13 +1877,22 @@ __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
     uint8_t *__restrict__ out, float *__restrict__ out_scale, int32_t *__restrict__ recv_count,
     int32_t *__restrict__ src_info, int32_t *__restrict__ layout_range,
     int32_t *__restrict__ output_index, uint32_t *__restrict__ status,
-    const int32_t *__restrict__ block_count, const uint32_t *__restrict__ block_err, int64_t nb)
+    const int32_t *__restrict__ block_count, const uint32_t *__restrict__ block_err, int64_t nb,
+    int parts)
 {
     __shared__ int32_t s_e[2][kMaxTopk];      // expert of each placed slot, -1 if none
     __shared__ int32_t s_j[2][kMaxTopk];      // row within the expert's block
     const int tid = threadIdx.x;
-    const int S = H / 128;
-    const int npair = H / 16;                 // pairs of 16-byte vectors: 16 bf16 values
+    const int S = H / 128;                    // 128-column groups: 8 pairs of 16-byte vectors
+    // Work items: (token, column part) pairs, item i = token i / parts, part
+    // i % parts; a part is a run of whole 128-column groups (8 pairs each).
+    const int gpp = (S + parts - 1) / parts;  // groups per part
+    auto item_token = [&](int64_t i) { return (int64_t)((uint64_t)i / (uint32_t)parts); };
+    auto item_pairs = [&](int64_t i, int &p0, int &p1) {
+        const int q = (int)((uint64_t)i % (uint32_t)parts);
+        p0 = 8 * min(S, q * gpp);
+        p1 = 8 * min(S, (q + 1) * gpp);
+    };
 
     // recv_count and layout_range
     {
@@ -1936,8 +1946,9 @@ __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
         }
     }
 
-    // slot `tid` of token t: place it and publish (expert, row) in the table
-    auto place = [&](int64_t t, int32_t *se, int32_t *sj) {
+    // slot `tid` of token t: place it and publish (expert, row) in the table;
+    // the token's first part also stores its indices
+    auto place = [&](int64_t t, bool first, int32_t *se, int32_t *sj) {
         const int64_t e = topk[t * K + tid];
         int32_t pe = -1, pj = 0, oi = -1;
         if (e >= 0 && e < E) {
@@ -1949,18 +1960,20 @@ __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
                 pe = (int32_t)e;
                 pj = (int32_t)j;
                 oi = (int32_t)row;
-                src_info[row] = (int32_t)(tu % (uint32_t)M);
-            } else {
+                if (first)
+                    src_info[row] = (int32_t)(tu % (uint32_t)M);
+            } else if (first) {
                 atomicOr(status, kStatusCapacity);
             }
         }
-        output_index[t * K + tid] = oi;
+        if (first)
+            output_index[t * K + tid] = oi;
         se[tid] = pe;
         sj[tid] = pj;
     };
     // SUMMED: the first wave places token t, 8 lanes per slot (slots k0 +
     // lane / 8), while the other waves go on to the current token's cast
-    auto place_summed = [&](int64_t t, int32_t *se, int32_t *sj) {
+    auto place_summed = [&](int64_t t, bool first, int32_t *se, int32_t *sj) {
         if (tid >= kWave)
             return;
         const int l = tid & 7;
@@ -1989,12 +2002,14 @@ __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
                         pe = (int32_t)e;
                         pj = (int32_t)j;
                         oi = (int32_t)row;
-                        src_info[row] = (int32_t)(tu % (uint32_t)M);
-                    } else {
+                        if (first)
+                            src_info[row] = (int32_t)(tu % (uint32_t)M);
+                    } else if (first) {
                         atomicOr(status, kStatusCapacity);
                     }
                 }
-                output_index[t * K + k] = oi;
+                if (first)
+                    output_index[t * K + k] = oi;
                 se[k] = pe;
                 sj[k] = pj;
             }
@@ -2013,51 +2028,65 @@ __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
     // scatter (non-temporal loads of the token rows were slower here: 80.7
     // against 71.9 us with the batch in the Infinity Cache, 81.6 against
     // 80.3 us without)
-    auto load_row = [&](int64_t t, int base, u32x4 (*v)[2]) {
+    // pairs [p0 + base, p1) of token t's row, VPT steps of the workgroup;
+    // ordinary loads, as in the scatter (non-temporal loads of the token rows
+    // were slower here: 80.7 against 71.9 us with the batch in the Infinity
+    // Cache, 81.6 against 80.3 us without)
+    auto load_row = [&](int64_t t, int p0, int p1, int base, u32x4 (*v)[2]) {
         const u32x4 *xrow = reinterpret_cast<const u32x4 *>(x + t * (int64_t)H);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int pi = base + i * kScatterThreads + tid;
-            if (pi < npair) {
+            const int pi = p0 + base + i * kScatterThreads + tid;
+            if (pi < p1) {
                 v[i][0] = xrow[2 * pi];
                 v[i][1] = xrow[2 * pi + 1];
             }
         }
     };
 
-    const TokenRange tr = token_range(T);
+    const TokenRange tr = token_range(T * parts);
     const bool lead = tid < K;
     u32x4 v[VPT][2], vn[VPT][2];
     bool any = false;
+    int p0 = 0, p1 = 0;
     if (tr.first < tr.end) {
+        const int64_t t = item_token(tr.first);
+        const bool first = t * parts == tr.first;
+        item_pairs(tr.first, p0, p1);
         if (!SUMMED && lead)
-            place(tr.first, s_e[0], s_j[0]);
-        any = has_slot(tr.first);
+            place(t, first, s_e[0], s_j[0]);
+        any = has_slot(t);
         if (any)
-            load_row(tr.first, 0, v);
+            load_row(t, p0, p1, 0, v);
         if (SUMMED)
-            place_summed(tr.first, s_e[0], s_j[0]);
+            place_summed(t, first, s_e[0], s_j[0]);
     }
     int it = 0;
-    for (int64_t t = tr.first; t < tr.end; t += tr.stride, ++it) {
+    for (int64_t item = tr.first; item < tr.end; item += tr.stride, ++it) {
         lds_barrier();
+        const int64_t t = item_token(item);
         const int32_t *se = s_e[it & 1], *sj = s_j[it & 1];
-        // the next token: its row loads and its placements overlap this
-        // token's cast and stores
-        const int64_t tn = t + tr.stride;
-        const bool any_next = tn < tr.end && has_slot(tn);
+        // the next item: its row loads and its placements overlap this
+        // item's cast and stores
+        const int64_t in = item + tr.stride;
+        const int64_t tn = in < tr.end ? item_token(in) : 0;
+        const bool first_next = tn * parts == in;
+        int q0 = 0, q1 = 0;
+        if (in < tr.end)
+            item_pairs(in, q0, q1);
+        const bool any_next = in < tr.end && has_slot(tn);
         if (any_next)
-            load_row(tn, 0, vn);
-        if (SUMMED && tn < tr.end)
-            place_summed(tn, s_e[(it + 1) & 1], s_j[(it + 1) & 1]);
-        else if (lead && tn < tr.end)
-            place(tn, s_e[(it + 1) & 1], s_j[(it + 1) & 1]);
+            load_row(tn, q0, q1, 0, vn);
+        if (SUMMED && in < tr.end)
+            place_summed(tn, first_next, s_e[(it + 1) & 1], s_j[(it + 1) & 1]);
+        else if (lead && in < tr.end)
+            place(tn, first_next, s_e[(it + 1) & 1], s_j[(it + 1) & 1]);
 
         for (int base = 0; any;) {
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
-                const int pi = base + i * kScatterThreads + tid;
-                if (pi >= npair)      // whole 8-lane groups drop out together (npair % 8 == 0)
+                const int pi = p0 + base + i * kScatterThreads + tid;
+                if (pi >= p1)         // whole 8-lane groups drop out together (p0, p1 % 8 == 0)
                     continue;
                 const Cast16 c = cast_e4m3_16(v[i]);
                 const u32x4 codes = c.codes;
@@ -2081,9 +2110,9 @@ __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
                 }
             }
             base += kScatterThreads * VPT;
-            if (base >= npair)
+            if (p0 + base >= p1)
                 break;
-            load_row(t, base, v);
+            load_row(t, p0, p1, base, v);
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
@@ -2091,6 +2120,8 @@ __global__ __launch_bounds__(kScatterThreads) void ep_ll_scatter_kernel(
             v[i][1] = vn[i][1];
         }
         any = any_next;
+        p0 = q0;
+        p1 = q1;
     }
 }
 
