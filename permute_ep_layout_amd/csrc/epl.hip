@@ -393,9 +393,10 @@ ScatterSplit scatter_split(const epl_problem &p, int64_t row_bytes)
     if (T >= epl::kScatterGridFrom)
         return {1, xcd_grid(T, T), 0};
     // Long rows: kScatterGrid workgroups, of which the kernel keeps
-    // kScatterGridLong when the layout's first block is densely routed (the
-    // measured best for rows with many destinations; rows with one or two,
-    // as on a receive side, run faster with the whole grid)
+    // kScatterGridLong when the layout found the batch's first slots densely
+    // routed (WsHeader::dense; the measured best for rows with many
+    // destinations, while rows with one or two, as on a receive side, run
+    // faster with the whole grid)
     const bool long_rows = row_bytes >= epl::kScatterLongRowBytes;
     if (long_rows && T >= epl::kScatterGridLong)
         return {1, xcd_grid(std::min<int64_t>(T, epl::kScatterGrid), epl::kScatterGrid),
@@ -678,14 +679,16 @@ bool ll_decode(const epl_problem &p, int32_t M)
 #define EPL_LL_SUMMED_BLOCKS 64
 #endif
 
-#ifndef EPL_LL_MAX_PARTS
-#define EPL_LL_MAX_PARTS 8
-#endif
-
 bool ll_summed(const WsLayout &w)
 {
     return w.num_blocks >= 1 && w.num_blocks <= EPL_LL_SUMMED_BLOCKS;
 }
+
+// Column parts per row of the low-latency cast kernel, at most (1 turns
+// them off).
+#ifndef EPL_LL_MAX_PARTS
+#define EPL_LL_MAX_PARTS 8
+#endif
 
 template <int VPT>
 void launch_ll_scatter(const epl_problem &p, const WsLayout &w, int32_t M, int64_t cap,
