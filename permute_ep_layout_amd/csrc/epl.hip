@@ -679,16 +679,16 @@ bool ll_decode(const epl_problem &p, int32_t M)
 #define EPL_LL_SUMMED_BLOCKS 64
 #endif
 
+// (Column parts per row of the low-latency cast kernel, at most; 1 turns
+// them off.)
+#ifndef EPL_LL_MAX_PARTS
+#define EPL_LL_MAX_PARTS 8
+#endif
+
 bool ll_summed(const WsLayout &w)
 {
     return w.num_blocks >= 1 && w.num_blocks <= EPL_LL_SUMMED_BLOCKS;
 }
-
-// Column parts per row of the low-latency cast kernel, at most (1 turns
-// them off).
-#ifndef EPL_LL_MAX_PARTS
-#define EPL_LL_MAX_PARTS 8
-#endif
 
 template <int VPT>
 void launch_ll_scatter(const epl_problem &p, const WsLayout &w, int32_t M, int64_t cap,
