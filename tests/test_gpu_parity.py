@@ -585,6 +585,27 @@ def test_receive_side_mid_sizes(T, split):
     full_parity(workloads.get("dsv3_recv").with_(num_tokens=T), split=split)
 
 
+@pytest.mark.parametrize("name,T,split,want", [
+    ("dsv3", 2048, False, 1), ("dsv3", 2048, True, 1), ("dsv3_recv", 3000, False, 0),
+    ("dsv3_recv", 3000, True, 0), ("dsv3", 64, False, 1), ("dsv3_recv", 100, True, 0)])
+def test_dense_hint_recorded_by_the_layout(name, T, split, want):
+    """The routing-density hint in the workspace header (its third word): 1
+    when at least half of the first 64 slots name an expert, as in a global
+    dispatch, 0 for a receive side's mostly -1 local ids; written by the
+    layout kernel, by the one-workgroup layout + scan and by the one-launch
+    decode dispatch alike."""
+    w = workloads.get(name).with_(num_tokens=T)
+    inp = workloads.make_inputs(w)
+    topk = inp["topk_idx"]
+    first = topk.reshape(-1)[:64]
+    assert (2 * int((first >= 0).sum()) >= len(first)) == bool(want)
+    r = gpu_dispatch(topk, inp["x"], inp["x_scale"], w.num_experts, w.num_ranks, split=split,
+                     G=w.ranks_per_node)
+    torch.cuda.synchronize()
+    assert epl.epl_status(r["ws"]) == epl.EPL_OK
+    assert int(r["ws"][8:12].view(torch.int32)[0]) == want
+
+
 @pytest.mark.parametrize("dense_first", [True, False])
 def test_dense_hint_from_an_unrepresentative_first_block(dense_first):
     """The scatter's grid follows the routing density of the batch's first
