@@ -891,6 +891,66 @@ def test_random_shape_sweep(seed):
     check_bf16_is_rne_of_f32(u16(yb), y.cpu())
 
 
+def _long_row_shape(rng, seed):
+    """One seeded problem on the long-row striding grid (bf16 rows of 12 KB
+    or more, 512 to 2500 tokens): routing density from every slot valid
+    down to a receive side's few, and sometimes a first block whose density
+    is the opposite of the rest, so that either active grid the layout's
+    sample picks meets either kind of batch. The seed fixes the mix: the
+    drop rate cycles over four values and seeds 8 to 11 invert the head."""
+    R = int(rng.choice([1, 4, 8, 32]))
+    E = R * int(rng.choice([1, 2, 8]))
+    K = int(rng.integers(1, 9))
+    T = int(np.exp(rng.uniform(np.log(512), np.log(2500))))
+    scales = bool(rng.random() < 0.5)
+    H = 128 * int(rng.integers(48, 65)) if scales else 8 * int(rng.integers(768, 1025))
+    a = int(rng.choice([0, 0, 1, 16, 64]))
+    G = int(rng.choice([0, max(1, R // 4), R])) if R > 1 else 0
+    if G and R % G:
+        G = 0
+    drop = (0.0, 0.5, 0.875, 0.97)[seed % 4]
+    split = bool(rng.random() < 0.3)
+    topk = np.stack([rng.permutation(E)[:K] if K <= E else rng.integers(0, E, K)
+                     for _ in range(T)]).astype(np.int64)
+    gone = rng.random(topk.shape) < drop
+    if seed >= 8:   # the first 64 tokens routed unlike the rest
+        head = np.arange(T)[:, None] < 64
+        gone = np.where(head, rng.random(topk.shape) < (0.9 if drop < 0.5 else 0.0), gone)
+    topk[gone] = -1
+    return dict(T=T, K=K, E=E, R=R, H=H, scales=scales, a=a, G=G, split=split, topk=topk)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_long_row_sweep(seed):
+    """12 seeded problems on the long-row grid, whose active size follows
+    the density of the batch's first slots: every index, row and scale row
+    bit-exact against the oracle and the fp32 combine within 1e-5 of
+    sum |w v|, whichever grid ran."""
+    rng = np.random.default_rng(11000 + seed)
+    c = _long_row_shape(rng, seed)
+    T, K, E, R, H = c["T"], c["K"], c["E"], c["R"], c["H"]
+    # The hint samples the first min(64, slots of the first layout block)
+    # slots, a block holding 16 tokens or more; where every such window
+    # gives the same answer, the hint must be that answer.
+    valid = np.cumsum(c["topk"].reshape(-1)[:64] >= 0)
+    votes = {bool(2 * valid[n - 1] >= n) for n in range(min(64, 16 * K), 65)}
+    print(f"[parity] long-row sweep seed={seed} T={T} K={K} E={E} R={R} H={H} "
+          f"scales={c['scales']} a={c['a']} G={c['G']} split={c['split']} dense={votes}",
+          flush=True)
+    x, xs, wt = _mk(c["topk"], H, seed, c["scales"])
+    ref = orc().run_all(x, xs, c["topk"], wt, E, R, alignment=c["a"])
+    r = gpu_dispatch(c["topk"], x, xs, E, R, split=c["split"], alignment=c["a"], G=c["G"])
+    assert epl.epl_status(r["ws"]) == epl.EPL_OK
+    hint = int(r["ws"][8:12].view(torch.int32)[0])
+    assert hint in (0, 1)
+    if len(votes) == 1:
+        assert hint == int(votes.pop())
+    check_layout_and_scatter(r, ref, x, xs)
+    y = gpu_combine(r, r["out"], wt, epl.EPL_OUT_F32)
+    bound = combine_bound(ref["expert_out"], ref["output_index"], wt)
+    check_combine_f32(y.cpu().numpy(), ref["y"], bound)
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_random_fp8_sweep(seed):
     """12 seeded random FP8 problems (no scales, fp32 rows of scales, or
