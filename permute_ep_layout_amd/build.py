@@ -25,6 +25,8 @@ HIPCC_FLAGS = [
     "-fPIC",
     "-shared",
     "-Wall",
+    "-Wextra",
+    "-Wshadow",
     # keep the compiler from emitting packed fp32 VALU ops (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

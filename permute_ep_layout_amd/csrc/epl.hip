@@ -148,7 +148,7 @@ int layout_block_tokens(const epl_problem &p)
 // divisor of M not above the usual block size.
 int ll_block_tokens(const epl_problem &p, int32_t M)
 {
-    int b = std::min<int64_t>(layout_block_tokens(p), M);
+    int b = (int)std::min<int64_t>(layout_block_tokens(p), M);
     while (b > 1 && M % b != 0)
         --b;
     return std::max(b, 1);

@@ -113,7 +113,7 @@ static_assert(sizeof(WsHeader) == 256, "workspace header is 256 bytes");
 // slots (bit i: slot i names an expert).
 __device__ __forceinline__ int32_t dense_sample(uint64_t valid, int ns)
 {
-    return 2 * __popcll(valid) >= min(ns, 64) ? 1 : 0;
+    return 2 * (int)__popcll(valid) >= min(ns, 64) ? 1 : 0;
 }
 
 __device__ __forceinline__ uint64_t wave_ballot(bool pred)
@@ -1157,10 +1157,10 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
         if (seg_thread) {
             i32x4 run = {0, 0, 0, 0}, tot = {0, 0, 0, 0};
             for (int g = 0; g < Q; ++g) {
-                const i32x4 v = reinterpret_cast<const i32x4 *>(s_seg)[g * nq4 + c];
+                const i32x4 seg = reinterpret_cast<const i32x4 *>(s_seg)[g * nq4 + c];
                 if (g < q)
-                    run += v;
-                tot += v;
+                    run += seg;
+                tot += seg;
             }
             if (q == 0)
                 reinterpret_cast<i32x4 *>(s_cnt)[c] = tot;
@@ -1191,13 +1191,13 @@ __global__ __launch_bounds__(kScatterThreads) void ep_scatter_kernel(
                 const int64_t g0 = (int64_t)g * PL, g1 = min(sc.nb, g0 + PL);
                 int part = 0;
                 for (int64_t bb = g0; bb < g1; bb += 16) {
-                    int v[16];
+                    int rv[16];
 #pragma unroll
                     for (int j = 0; j < 16; ++j)
-                        v[j] = bb + j < g1 ? sc.block_rank[(bb + j) * RC + r] : 0;
+                        rv[j] = bb + j < g1 ? sc.block_rank[(bb + j) * RC + r] : 0;
 #pragma unroll
                     for (int j = 0; j < 16; ++j)
-                        part += v[j];
+                        part += rv[j];
                 }
                 if (P > 1)
                     s_part[i] = part;
@@ -2485,9 +2485,10 @@ __global__ __launch_bounds__(THREADS) void ep_combine_kernel(
                         if (g + j < n) {
                             const float wj = sw[g + j];
 #pragma unroll
-                            for (int q = 0; q < CW / 2; ++q) {
-                                acc[u][2 * q] = fmaf(wj, bf16_lo(v[u][j][q]), acc[u][2 * q]);
-                                acc[u][2 * q + 1] = fmaf(wj, bf16_hi(v[u][j][q]), acc[u][2 * q + 1]);
+                            for (int pr = 0; pr < CW / 2; ++pr) {
+                                acc[u][2 * pr] = fmaf(wj, bf16_lo(v[u][j][pr]), acc[u][2 * pr]);
+                                acc[u][2 * pr + 1] =
+                                    fmaf(wj, bf16_hi(v[u][j][pr]), acc[u][2 * pr + 1]);
                             }
                         }
             }
