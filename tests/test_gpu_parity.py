@@ -507,6 +507,12 @@ RAGGED = [
     # one-workgroup-per-token grid, with ragged rows
     ("many_tokens_h264", 9000, 5, 24, 6, 264, False, 0.1),
     ("many_tokens_scales_s9", 8500, 4, 32, 8, 1152, True, 0.05),
+    # the widest expert count and the largest top-k over many layout blocks:
+    # 64 blocks of 141 tokens in 256-thread workgroups with a 2048-expert
+    # count matrix (the scan's serial column reduce), and 282 blocks of 32
+    # tokens of 64 slots each in 1024-thread workgroups
+    ("e2048_many_tokens", 9000, 8, 2048, 256, 64, False, 0.1),
+    ("k64_many_tokens", 9000, 64, 512, 64, 8, False, 0.1),
     # the single-workgroup layout + scan holds at most 2048 slots: at the
     # limit, and one token past it (the two-launch layout)
     ("fused_limit_2048_slots", 256, 8, 256, 32, 128, False, 0.1),
