@@ -174,6 +174,9 @@ LL_BLOCK_CASES = [
     ("reduce_65_blocks", 65, 1, 40, 64, 256, 65, 0.1),
     ("reduce_600_blocks_m7", 600, 7, 2, 16, 128, 4200, 0.1),
     ("summed_dsv3_t1024_tight_cap", 8, 128, 8, 256, 7168, 40, 0.0),
+    # the widest expert count and the largest top-k above the decode size
+    ("e2048_40_segments_tight_cap", 40, 128, 8, 2048, 256, 28, 0.1),
+    ("k64_16_segments", 16, 64, 64, 512, 128, 192, 0.1),
 ]
 
 
