@@ -477,6 +477,10 @@ def test_fp8_dsv3_ue8m0_parity():
     # decode-sized: column parts of byte rows (3 parts of 7168 bytes)
     ("ue8m0_decode_t200", 200, 7168, 256, 8, 32, epl.EPL_SCALE_UE8M0, 0, 0, False),
     ("f32_decode_t64_aligned", 64, 7168, 64, 8, 8, epl.EPL_SCALE_F32, 16, 0, True),
+    # byte rows of 12 KB: the long-row grid, whose active size follows the
+    # routing density, with 24 packed scale words per row
+    ("ue8m0_long_rows_h12288", 1500, 12288, 64, 4, 8, epl.EPL_SCALE_UE8M0, 0, 0, False),
+    ("f32_k64", 300, 256, 512, 64, 64, epl.EPL_SCALE_F32, 0, 0, False),
 ], ids=lambda c: c[0])
 def test_fp8_shapes(case):
     name, T, H, E, K, R, fmt, a, extra, split = case
