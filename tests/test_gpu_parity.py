@@ -526,7 +526,7 @@ RAGGED = [
     ("striding_ragged_h264", 5555, 5, 24, 6, 264, False, 0.1),
     ("striding_scales_s9", 7000, 4, 32, 8, 1152, True, 0.05),
     # decode-sized batches of long rows: fewer tokens than the striding grid,
-    # each row cut into column parts (7 at hidden 7168, 5 at hidden 8960, 3
+    # each row cut into column parts (7 at hidden 7168, 8 at hidden 8960, 3
     # of 134, 134 and 132 vectors at hidden 3200); scale rows and indices
     # are written by the first part only
     ("decode_t256_dsv3", 256, 8, 256, 32, 7168, True, 0.0),
